@@ -1,0 +1,195 @@
+"""fp64 CPU oracle for the fine-grained FP8 e4m3 GEMM -- TEST INFRASTRUCTURE.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import this package.  The GPU library never imports, links or calls it, and
+the two share no code.  The arithmetic lives in oracle.c (plain C, built with
+gcc, -ffp-contract=off); this wrapper only marshals numpy arrays.
+
+Every function returns float64 arrays.  Rows with no reference value (padding
+rows of the contiguous layout, rows at or past masked_m) come back as NaN.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+_lib = None
+_override = None
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc + OpenMP build of one oracle source file into a shared library."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (next to this file)."""
+    if force or not os.path.exists(LIB_PATH):
+        compile_source(SRC_PATH, LIB_PATH)
+    return LIB_PATH
+
+
+class use_library:
+    """Context manager: route the wrappers to another build of the oracle
+    (the mutation tests load deliberately broken copies this way)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _override
+        self.prev = _override
+        _override = _bind(ctypes.CDLL(self.path))
+        return self
+
+    def __exit__(self, *exc):
+        global _override
+        _override = self.prev
+        return False
+
+
+def _load():
+    global _lib
+    if _override is not None:
+        return _override
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _lib = _bind(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    I = ctypes.c_int64
+    lib.oracle_e4m3_decode.argtypes = [P, P, I]
+    lib.oracle_e4m3_decode.restype = None
+    lib.oracle_gemm_nt.argtypes = [P, P, P, P, P, I, I, I, P, I, P]
+    lib.oracle_gemm_nt.restype = ctypes.c_int
+    lib.oracle_m_grouped_contiguous.argtypes = [P, P, P, P, P, I, I, I, I, P, I, P]
+    lib.oracle_m_grouped_contiguous.restype = ctypes.c_int
+    lib.oracle_m_grouped_masked.argtypes = [P, P, P, P, P, I, I, I, I, P, P, I, P]
+    lib.oracle_m_grouped_masked.restype = ctypes.c_int
+    lib.oracle_k_grouped_tn.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P, I, P]
+    lib.oracle_k_grouped_tn.restype = ctypes.c_int
+    return lib
+
+
+def _c(x, dtype):
+    return np.ascontiguousarray(x, dtype=dtype)
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle will use (OMP_NUM_THREADS, else all cores)."""
+    v = os.environ.get("OMP_NUM_THREADS")
+    if v and v.isdigit():
+        return int(v)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().oracle_e4m3_decode(_ptr(c), _ptr(out), c.size)
+    return out
+
+
+def gemm_nt(a, sfa, b, sfb, c=None, rows=None) -> np.ndarray:
+    """D[rows] of D = C + A @ B^T.  a [M,K] u8, sfa [K/128,M], b [N,K] u8,
+    sfb [ceil(N/128),K/128], c [M,N] (any float dtype) or None."""
+    a = _c(a, np.uint8); b = _c(b, np.uint8)
+    sfa = _c(sfa, np.float32); sfb = _c(sfb, np.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K and sfa.shape == (K // 128, M)
+    assert sfb.shape == ((N + 127) // 128, K // 128)
+    cc = None if c is None else _c(c, np.float32)
+    if cc is not None:
+        assert cc.shape == (M, N)
+    r = np.arange(M, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    out = np.empty((len(r), N), dtype=np.float64)
+    rc = _load().oracle_gemm_nt(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(cc),
+                                M, N, K, _ptr(r), len(r), _ptr(out))
+    if rc:
+        raise ValueError("oracle_gemm_nt: bad arguments")
+    return out
+
+
+def m_grouped_contiguous(a, sfa, b, sfb, m_indices, rows=None) -> np.ndarray:
+    """D[rows] of the contiguous M-grouped GEMM.  b [G,N,K], sfb [G,NB,KB]."""
+    a = _c(a, np.uint8); b = _c(b, np.uint8)
+    sfa = _c(sfa, np.float32); sfb = _c(sfb, np.float32)
+    mi = _c(m_indices, np.int32)
+    M_tot, K = a.shape
+    G, N, _ = b.shape
+    assert sfa.shape == (K // 128, M_tot) and mi.shape == (M_tot,)
+    r = np.arange(M_tot, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    out = np.empty((len(r), N), dtype=np.float64)
+    rc = _load().oracle_m_grouped_contiguous(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(mi),
+                                             M_tot, N, K, G, _ptr(r), len(r), _ptr(out))
+    if rc:
+        raise ValueError("oracle_m_grouped_contiguous: bad arguments")
+    return out
+
+
+def m_grouped_masked(a, sfa, b, sfb, masked_m, groups=None, rows=None) -> np.ndarray:
+    """Selected (group, row) outputs of the masked M-grouped GEMM; with no
+    selection, the full [G, M_max, N] array.  a [G,M_max,K], sfa [G,KB,M_max]."""
+    a = _c(a, np.uint8); b = _c(b, np.uint8)
+    sfa = _c(sfa, np.float32); sfb = _c(sfb, np.float32)
+    mm = _c(masked_m, np.int32)
+    G, M_max, K = a.shape
+    N = b.shape[1]
+    full = groups is None
+    if full:
+        groups = np.repeat(np.arange(G), M_max)
+        rows = np.tile(np.arange(M_max), G)
+    g = _c(groups, np.int64); r = _c(rows, np.int64)
+    out = np.empty((len(r), N), dtype=np.float64)
+    rc = _load().oracle_m_grouped_masked(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(mm),
+                                         G, M_max, N, K, _ptr(g), _ptr(r), len(r), _ptr(out))
+    if rc:
+        raise ValueError("oracle_m_grouped_masked: bad arguments")
+    return out.reshape(G, M_max, N) if full else out
+
+
+def k_grouped_tn(a, sfa, b, sfb, k_sizes, c=None, groups=None, rows=None) -> np.ndarray:
+    """Selected (group, m) rows of D[g] = C[g] + A_g^T @ B_g; with no
+    selection, the full [G, M, N].  a [K_tot,M], b [K_tot,N], sf [K_tot/128, M|N]."""
+    a = _c(a, np.uint8); b = _c(b, np.uint8)
+    sfa = _c(sfa, np.float32); sfb = _c(sfb, np.float32)
+    ks = _c(k_sizes, np.int32)
+    K_tot, M = a.shape
+    N = b.shape[1]
+    G = len(ks)
+    cc = None if c is None else _c(c, np.float32)
+    full = groups is None
+    if full:
+        groups = np.repeat(np.arange(G), M)
+        rows = np.tile(np.arange(M), G)
+    g = _c(groups, np.int64); r = _c(rows, np.int64)
+    out = np.empty((len(r), N), dtype=np.float64)
+    rc = _load().oracle_k_grouped_tn(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(ks), _ptr(cc),
+                                     G, M, N, K_tot, _ptr(g), _ptr(r), len(r), _ptr(out))
+    if rc:
+        raise ValueError("oracle_k_grouped_tn: bad arguments")
+    return out.reshape(G, M, N) if full else out

@@ -1,0 +1,235 @@
+/*
+ * CPU oracle for the fine-grained FP8 (e4m3) GEMM -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library.  The GPU library shares no code, header, table or
+ * constant with it, and it never calls into the GPU library.
+ *
+ * What it computes is the plain definition, in fp64:
+ *
+ *   D = C + A @ B^T   (the NT GEMM of the "DeepGEMM" README, yuguo-Jack fork,
+ *                      section "Interfaces", subsection "Notices": A row-major,
+ *                      B stored [N, K])
+ *
+ * on block-scaled e4m3 operands.  The news article "Deepseek AI Libera
+ * Deepgemm: a GEMM FP8 Library ..." (section "Details and technical benefits")
+ * describes fine-grained scaling plus a two-level accumulation: tensor-core
+ * FP8 partial sums are promoted into a higher-precision accumulator.  The scale of a product
+ * term depends on its K block, so it cannot be pulled out of the K sum; the
+ * definition is therefore
+ *
+ *   D[m,n] = C[m,n] + sum_kb ( sa[kb,m] * sb[n/128,kb] ) * P_kb[m,n]
+ *   P_kb[m,n] = sum_{k = 128 kb .. 128 kb + 127} dec(a[m,k]) * dec(b[n,k])
+ *
+ * Every e4m3 value is an integer multiple of 2^-9 of magnitude <= 448, so each
+ * product is an integer multiple of 2^-18 whose magnitude is below 2^36 such
+ * units, and a 128-term sum stays below 2^43 units: inside fp64's 53-bit
+ * significand, so P_kb is computed exactly.  The
+ * scale product sa*sb of two fp32 values is exact in fp64.  The only roundings
+ * are the fp64 products s * P_kb and the running sum over kb (kb ascending).
+ *
+ * dec() is the OCP FP8 E4M3FN decoding: sign bit 7, exponent bits 6..3 with
+ * bias 7, mantissa bits 2..0; exponent 0 is subnormal (m * 2^-9); exponent 15
+ * with mantissa 7 is NaN; there is no infinity; the largest finite value is
+ * 448 (the workloads quantise with scale = amax / 448).
+ *
+ * Grouped forms are the dense definition applied per group:
+ *   M-grouped contiguous: row r uses expert m_indices[r]; rows whose index is
+ *     -1 (or outside [0, G)) have no reference (NaN is written).
+ *     ("DeepGEMM" README, "Interfaces", "Grouped GEMMs (contiguous layout)")
+ *   M-grouped masked: group g, row r < masked_m[g] gets a reference; rows at or
+ *     past masked_m[g] have none (NaN).  masked_m is clamped to [0, M_max].
+ *     ("DeepGEMM" README, "Interfaces", "Grouped GEMMs (masked layout)")
+ *   K-grouped TN: D[g] = C[g] + sum over group g's K blocks of
+ *     (sa[kb,m] * sb[kb,n]) * sum_k dec(a[k,m]) * dec(b[k,n]), with A stored
+ *     [K_total, M] and B [K_total, N]; a group with K_g = 0 gives D[g] = C[g].
+ *     ("DeepGEMM" README, "Interfaces", "Grouped GEMMs (contiguous layout)",
+ *      the K-axis-grouped API for the MoE weight backward pass)
+ *
+ * C, where present, is passed as fp32 (bf16 and fp32 values are exact in it).
+ * Outputs are fp64.  Row selections let a test ask for sampled rows of a
+ * large problem; rows are independent, so OpenMP splits them across threads
+ * without changing any arithmetic.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#define KBLK 128
+
+/* OCP E4M3FN closed form. */
+static double e4m3_value(uint8_t code)
+{
+    int s = code >> 7;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+static double g_dec[256];
+static int g_dec_ready = 0;
+
+static void build_table(void)
+{
+    if (g_dec_ready)
+        return;
+    for (int i = 0; i < 256; ++i)
+        g_dec[i] = e4m3_value((uint8_t)i);
+    g_dec_ready = 1;
+}
+
+void oracle_e4m3_decode(const uint8_t* codes, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = e4m3_value(codes[i]);
+}
+
+/*
+ * One output row of the NT definition.
+ *   a_row [K] codes; sa_row[kb * sa_stride] is this row's scale for block kb;
+ *   b [N, K] codes; sfb [ceil(N/128), K/128]; c_row [N] or NULL.
+ */
+static void nt_row(const uint8_t* a_row, const float* sa_row, int64_t sa_stride,
+                   const uint8_t* b, const float* sfb, const float* c_row,
+                   int64_t N, int64_t K, double* out)
+{
+    const int64_t KB = K / KBLK;
+    for (int64_t n = 0; n < N; ++n) {
+        const uint8_t* b_row = b + n * K;
+        double acc = 0.0;
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            double p = 0.0;                               /* exact block sum */
+            for (int64_t k = kb * KBLK; k < (kb + 1) * KBLK; ++k)
+                p += g_dec[a_row[k]] * g_dec[b_row[k]];
+            double s = (double)sa_row[kb * sa_stride] * (double)sfb[(n / KBLK) * KB + kb];
+            acc += s * p;                                 /* promotion, kb ascending */
+        }
+        out[n] = acc + (c_row ? (double)c_row[n] : 0.0);
+    }
+}
+
+/* Dense NT: out[i, :] = D[rows[i], :].  sfa is [K/128, M]. */
+int oracle_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   const float* c, int64_t M, int64_t N, int64_t K,
+                   const int64_t* rows, int64_t n_rows, double* out)
+{
+    if (K % KBLK != 0)
+        return 1;
+    build_table();
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        int64_t m = rows[i];
+        if (m < 0 || m >= M) { bad |= 1; continue; }
+        nt_row(a + m * K, sfa + m, M, b, sfb, c ? c + m * N : NULL, N, K, out + i * N);
+    }
+    return bad;
+}
+
+/* M-grouped contiguous: A [M_tot, K], sfa [K/128, M_tot], B [G, N, K],
+ * sfb [G, ceil(N/128), K/128], m_indices [M_tot]. */
+int oracle_m_grouped_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                const float* sfb, const int32_t* m_indices,
+                                int64_t M_tot, int64_t N, int64_t K, int64_t G,
+                                const int64_t* rows, int64_t n_rows, double* out)
+{
+    if (K % KBLK != 0)
+        return 1;
+    build_table();
+    const int64_t NB = (N + KBLK - 1) / KBLK, KB = K / KBLK;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        int64_t r = rows[i];
+        if (r < 0 || r >= M_tot) { bad |= 1; continue; }
+        int64_t e = m_indices[r];
+        if (e < 0 || e >= G) {
+            for (int64_t n = 0; n < N; ++n)
+                out[i * N + n] = NAN;
+            continue;
+        }
+        nt_row(a + r * K, sfa + r, M_tot, b + e * N * K, sfb + e * NB * KB, NULL, N, K,
+               out + i * N);
+    }
+    return bad;
+}
+
+/* M-grouped masked: A [G, M_max, K], sfa [G, K/128, M_max], B [G, N, K],
+ * sfb [G, ceil(N/128), K/128], masked_m [G].  Selection is (groups[i], rows[i]). */
+int oracle_m_grouped_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
+                            const float* sfb, const int32_t* masked_m,
+                            int64_t G, int64_t M_max, int64_t N, int64_t K,
+                            const int64_t* groups, const int64_t* rows, int64_t n_sel,
+                            double* out)
+{
+    if (K % KBLK != 0)
+        return 1;
+    build_table();
+    const int64_t NB = (N + KBLK - 1) / KBLK, KB = K / KBLK;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t i = 0; i < n_sel; ++i) {
+        int64_t g = groups[i], r = rows[i];
+        if (g < 0 || g >= G || r < 0 || r >= M_max) { bad |= 1; continue; }
+        int64_t mm = masked_m[g];
+        if (mm < 0) mm = 0;
+        if (mm > M_max) mm = M_max;
+        if (r >= mm) {
+            for (int64_t n = 0; n < N; ++n)
+                out[i * N + n] = NAN;
+            continue;
+        }
+        nt_row(a + (g * M_max + r) * K, sfa + g * KB * M_max + r, M_max,
+               b + g * N * K, sfb + g * NB * KB, NULL, N, K, out + i * N);
+    }
+    return bad;
+}
+
+/* K-grouped TN: A [K_tot, M], sfa [K_tot/128, M], B [K_tot, N], sfb [K_tot/128, N],
+ * k_sizes [G] (multiples of 128, summing to K_tot), c [G, M, N] fp32 or NULL.
+ * Selection is (groups[i], rows[i] = m); out[i, :] = D[g, m, :]. */
+int oracle_k_grouped_tn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                        const int32_t* k_sizes, const float* c,
+                        int64_t G, int64_t M, int64_t N, int64_t K_tot,
+                        const int64_t* groups, const int64_t* rows, int64_t n_sel,
+                        double* out)
+{
+    build_table();
+    int64_t total = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        if (k_sizes[g] < 0 || k_sizes[g] % KBLK != 0)
+            return 1;
+        total += k_sizes[g];
+    }
+    if (total != K_tot)
+        return 1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t i = 0; i < n_sel; ++i) {
+        int64_t g = groups[i], m = rows[i];
+        if (g < 0 || g >= G || m < 0 || m >= M) { bad |= 1; continue; }
+        int64_t k0 = 0;
+        for (int64_t h = 0; h < g; ++h)
+            k0 += k_sizes[h];
+        int64_t k1 = k0 + k_sizes[g];
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t kb = k0 / KBLK; kb < k1 / KBLK; ++kb) {
+                double p = 0.0;                           /* exact block sum */
+                for (int64_t k = kb * KBLK; k < (kb + 1) * KBLK; ++k)
+                    p += g_dec[a[k * M + m]] * g_dec[b[k * N + n]];
+                double s = (double)sfa[kb * M + m] * (double)sfb[kb * N + n];
+                acc += s * p;
+            }
+            out[i * N + n] = acc + (c ? (double)c[(g * M + m) * N + n] : 0.0);
+        }
+    }
+    return bad;
+}

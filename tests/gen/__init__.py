@@ -1,0 +1,332 @@
+"""Seeded synthetic inputs for the fine-grained FP8 e4m3 GEMM workloads.
+
+This module is shared by the CPU oracle and the HIP path: both must consume the
+same bytes.  It holds input preparation only -- random draws, MoE routing /
+masking / K-splitting, and the FP8 casting that the pages leave to the
+library's users (DeepGEMM Documentation, section 4 "Understand DeepGEMM GEMM
+Naming and Layouts": casting and transposition happen outside the GEMM).  It
+holds none of the GEMM arithmetic (no decode, no block product, no promotion).
+
+Quantisation recipe (the pages say only "fine grain scale"; the 1x128 and
+128x128 granularities and scale = amax/448 are the workload definitions):
+  * activations: one fp32 scale per row per 128-wide K block, stored MN-major
+    as SF[K/128, rows] (the pages ask for a transposed, MN-major LHS scale
+    layout, DeepGEMM Documentation, section 4);
+  * weights: one fp32 scale per 128x128 block, SF[ceil(N/128), K/128];
+  * K-grouped operands: one scale per column per 128-row block of the
+    [K_total, M] / [K_total, N] matrices, SF[K_total/128, M|N].
+  scale = amax / 448 in fp32 (amax == 0 -> scale 1.0), q = e4m3fn(RNE(clamp(x/scale,
+  -448, 448))).  torch's float8_e4m3fn cast is RNE but does not saturate, hence
+  the clamp.
+
+Every generator takes a seed and uses numpy.random.Generator(PCG64(seed)).
+Draw order: routing / mask / K-split first, then A, then B (per expert, in
+expert order), then C.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0
+BLOCK = 128
+
+# --------------------------------------------------------------------------
+# FP8 casting (input preparation)
+# --------------------------------------------------------------------------
+
+def _cast_e4m3(y: torch.Tensor) -> torch.Tensor:
+    """fp32 -> e4m3fn codes (uint8), RNE, after clamping to +-448."""
+    y = torch.clamp(y, -E4M3_MAX, E4M3_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def _safe_scale(amax: torch.Tensor) -> torch.Tensor:
+    scale = amax / torch.tensor(E4M3_MAX, dtype=torch.float32)
+    return torch.where(amax == 0, torch.ones_like(scale), scale)
+
+
+def quantize_rows(x: np.ndarray | torch.Tensor):
+    """Per-row, per-128-K-block quantisation of an activation matrix.
+
+    x: fp32 [R, K] with K % 128 == 0.
+    Returns (codes uint8 [R, K], sf fp32 [K/128, R]) as numpy arrays; sf is
+    MN-major (row index fastest).
+    """
+    xt = torch.as_tensor(x, dtype=torch.float32)
+    R, K = xt.shape
+    assert K % BLOCK == 0
+    KB = K // BLOCK
+    xb = xt.reshape(R, KB, BLOCK)
+    scale = _safe_scale(xb.abs().amax(dim=2))            # [R, KB]
+    codes = _cast_e4m3(xb / scale[:, :, None]).reshape(R, K)
+    return codes.numpy(), scale.t().contiguous().numpy()
+
+
+def quantize_blocks(w: np.ndarray | torch.Tensor):
+    """Per-128x128-block quantisation of a weight matrix [N, K].
+
+    Partial blocks (N % 128 != 0) take their amax over the rows that exist.
+    Returns (codes uint8 [N, K], sf fp32 [ceil(N/128), K/128]).
+    """
+    wt = torch.as_tensor(w, dtype=torch.float32)
+    N, K = wt.shape
+    assert K % BLOCK == 0
+    KB = K // BLOCK
+    NB = (N + BLOCK - 1) // BLOCK
+    pad = NB * BLOCK - N
+    wp = torch.nn.functional.pad(wt, (0, 0, 0, pad)) if pad else wt
+    blocks = wp.reshape(NB, BLOCK, KB, BLOCK)
+    scale = _safe_scale(blocks.abs().amax(dim=(1, 3)))    # [NB, KB]
+    full = scale[:, None, :, None].expand(NB, BLOCK, KB, BLOCK).reshape(NB * BLOCK, K)[:N]
+    codes = _cast_e4m3(wt / full)
+    return codes.numpy(), scale.contiguous().numpy()
+
+
+def quantize_cols(x: np.ndarray | torch.Tensor):
+    """Per-column, per-128-row-block quantisation of an MN-major operand [Kt, C].
+
+    Used by the K-grouped TN form: A is [K_total, M], B is [K_total, N].
+    Returns (codes uint8 [Kt, C], sf fp32 [Kt/128, C]).
+    """
+    xt = torch.as_tensor(x, dtype=torch.float32)
+    Kt, C = xt.shape
+    assert Kt % BLOCK == 0
+    KB = Kt // BLOCK
+    xb = xt.reshape(KB, BLOCK, C)
+    scale = _safe_scale(xb.abs().amax(dim=1))             # [KB, C]
+    codes = _cast_e4m3(xb / scale[:, None, :]).reshape(Kt, C)
+    return codes.numpy(), scale.contiguous().numpy()
+
+
+# --------------------------------------------------------------------------
+# Workload containers
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class DenseInputs:
+    a: np.ndarray      # uint8 [M, K]
+    sfa: np.ndarray    # fp32 [K/128, M]
+    b: np.ndarray      # uint8 [N, K]
+    sfb: np.ndarray    # fp32 [ceil(N/128), K/128]
+    M: int
+    N: int
+    K: int
+    c: Optional[np.ndarray] = None   # fp32 values of C (bf16-representable), [M, N]
+
+
+@dataclasses.dataclass
+class ContiguousInputs:
+    a: np.ndarray          # uint8 [M_tot, K]
+    sfa: np.ndarray        # fp32 [K/128, M_tot]
+    b: np.ndarray          # uint8 [G, N, K]
+    sfb: np.ndarray        # fp32 [G, ceil(N/128), K/128]
+    m_indices: np.ndarray  # int32 [M_tot], expert id or -1
+    counts: np.ndarray     # int64 [G], valid rows per expert
+    M_tot: int
+    N: int
+    K: int
+    G: int
+
+
+@dataclasses.dataclass
+class MaskedInputs:
+    a: np.ndarray          # uint8 [G, M_max, K]
+    sfa: np.ndarray        # fp32 [G, K/128, M_max]
+    b: np.ndarray          # uint8 [G, N, K]
+    sfb: np.ndarray        # fp32 [G, ceil(N/128), K/128]
+    masked_m: np.ndarray   # int32 [G]
+    G: int
+    M_max: int
+    N: int
+    K: int
+
+
+@dataclasses.dataclass
+class KGroupedInputs:
+    a: np.ndarray          # uint8 [K_tot, M]
+    sfa: np.ndarray        # fp32 [K_tot/128, M]
+    b: np.ndarray          # uint8 [K_tot, N]
+    sfb: np.ndarray        # fp32 [K_tot/128, N]
+    k_sizes: np.ndarray    # int32 [G], multiples of 128
+    valid_tokens: np.ndarray  # int64 [G]
+    c: Optional[np.ndarray]   # fp32 [G, M, N]
+    G: int
+    M: int
+    N: int
+    K_tot: int
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _normal(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return x
+
+
+# --------------------------------------------------------------------------
+# Dense NT (workloads 1 and 2)
+# --------------------------------------------------------------------------
+
+DENSE_SMALL = (128, 256, 512)
+DENSE_SWEEP = [(m, n, k) for m in (64, 128, 4096)
+               for (n, k) in ((2112, 7168), (24576, 1536), (7168, 16384),
+                              (4096, 7168), (7168, 2048))]
+
+
+def gen_dense(M: int, N: int, K: int, seed: int = 0, with_c: bool = False) -> DenseInputs:
+    """A[M,K], B[N,K] ~ N(0,1) fp32, quantised 1x128 / 128x128.
+
+    with_c adds a bf16-representable C ~ N(0,1) drawn after B (not part of
+    the named workloads; used to exercise D = C + A @ B^T)."""
+    rng = _rng(seed)
+    a32 = _normal(rng, (M, K))
+    b32 = _normal(rng, (N, K))
+    a, sfa = quantize_rows(a32)
+    b, sfb = quantize_blocks(b32)
+    c = None
+    if with_c:
+        c = torch.from_numpy(_normal(rng, (M, N))).to(torch.bfloat16).float().numpy()
+    return DenseInputs(a, sfa, b, sfb, M, N, K, c)
+
+
+# --------------------------------------------------------------------------
+# M-grouped contiguous (workload 3): Zipf(1.1) top-6 routing
+# --------------------------------------------------------------------------
+
+def zipf_probs(G: int, s: float = 1.1) -> np.ndarray:
+    p = (np.arange(1, G + 1, dtype=np.float64)) ** (-s)
+    return p / p.sum()
+
+
+def route_topk_zipf(rng: np.random.Generator, tokens: int, G: int, topk: int,
+                    s: float = 1.1) -> np.ndarray:
+    """Per-expert token counts for `tokens` tokens each choosing `topk`
+    distinct experts, expert e drawn with weight (e+1)^-s (Gumbel top-k)."""
+    logp = np.log(zipf_probs(G, s))
+    g = rng.gumbel(size=(tokens, G))
+    choice = np.argsort(-(logp[None, :] + g), axis=1)[:, :topk]
+    return np.bincount(choice.ravel(), minlength=G).astype(np.int64)
+
+
+def contiguous_layout(counts: np.ndarray, align: int = BLOCK):
+    """Segments in expert order, each padded at its tail to `align` rows.
+    Returns (m_indices int32 [M_tot], row offset of each segment)."""
+    G = len(counts)
+    padded = ((counts + align - 1) // align) * align
+    M_tot = int(padded.sum())
+    m_idx = np.full(M_tot, -1, dtype=np.int32)
+    offs = np.zeros(G + 1, dtype=np.int64)
+    offs[1:] = np.cumsum(padded)
+    for e in range(G):
+        m_idx[offs[e]: offs[e] + counts[e]] = e
+    return m_idx, offs
+
+
+def gen_contiguous(G: int = 32, N: int = 4096, K: int = 4096, tokens: int = 8192,
+                   topk: int = 6, seed: int = 0, counts: Optional[np.ndarray] = None,
+                   zipf_s: float = 1.1) -> ContiguousInputs:
+    """Workload 3 (or a smaller variant).  `counts` overrides the routing."""
+    rng = _rng(seed)
+    if counts is None:
+        counts = route_topk_zipf(rng, tokens, G, topk, zipf_s)
+    counts = np.asarray(counts, dtype=np.int64)
+    m_idx, offs = contiguous_layout(counts)
+    M_tot = len(m_idx)
+    a32 = np.zeros((M_tot, K), dtype=np.float32)
+    valid = _normal(rng, (int(counts.sum()), K))
+    r = 0
+    for e in range(G):
+        c = int(counts[e])
+        a32[offs[e]: offs[e] + c] = valid[r: r + c]
+        r += c
+    del valid
+    a, sfa = quantize_rows(a32)
+    del a32
+    NB = (N + BLOCK - 1) // BLOCK
+    b = np.empty((G, N, K), dtype=np.uint8)
+    sfb = np.empty((G, NB, K // BLOCK), dtype=np.float32)
+    for e in range(G):
+        b[e], sfb[e] = quantize_blocks(_normal(rng, (N, K)))
+    return ContiguousInputs(a, sfa, b, sfb, m_idx, counts, M_tot, N, K, G)
+
+
+# --------------------------------------------------------------------------
+# M-grouped masked (workload 4)
+# --------------------------------------------------------------------------
+
+def gen_masked(G: int = 32, M_max: int = 256, N: int = 4096, K: int = 2048,
+               seed: int = 0, masked_m: Optional[np.ndarray] = None) -> MaskedInputs:
+    """masked_m ~ U{0..M_max} per group; A fully drawn (rows past masked_m are
+    junk the kernel must never let into D)."""
+    rng = _rng(seed)
+    if masked_m is None:
+        masked_m = rng.integers(0, M_max + 1, G)
+    masked_m = np.asarray(masked_m, dtype=np.int32)
+    a = np.empty((G, M_max, K), dtype=np.uint8)
+    sfa = np.empty((G, K // BLOCK, M_max), dtype=np.float32)
+    for g in range(G):
+        a[g], sfa[g] = quantize_rows(_normal(rng, (M_max, K)))
+    NB = (N + BLOCK - 1) // BLOCK
+    b = np.empty((G, N, K), dtype=np.uint8)
+    sfb = np.empty((G, NB, K // BLOCK), dtype=np.float32)
+    for g in range(G):
+        b[g], sfb[g] = quantize_blocks(_normal(rng, (N, K)))
+    return MaskedInputs(a, sfa, b, sfb, masked_m, G, M_max, N, K)
+
+
+# --------------------------------------------------------------------------
+# K-grouped TN (workload 5)
+# --------------------------------------------------------------------------
+
+def gen_k_grouped(G: int = 32, M: int = 2048, N: int = 4096, K_tot: int = 49152,
+                  seed: int = 0, k_sizes: Optional[np.ndarray] = None,
+                  c_std: float = 0.01, with_c: bool = True,
+                  zipf_s: float = 1.1) -> KGroupedInputs:
+    """Per-group K = 128 * multinomial(K_tot/128, Zipf(1.1)); inside a group of
+    K_g > 0 the first K_g - U{0..127} tokens are N(0,1), the tail is zero (the
+    padding).  C ~ N(0, c_std) fp32 [G, M, N]."""
+    rng = _rng(seed)
+    if k_sizes is None:
+        blocks = rng.multinomial(K_tot // BLOCK, zipf_probs(G, zipf_s))
+        k_sizes = blocks * BLOCK
+    k_sizes = np.asarray(k_sizes, dtype=np.int64)
+    assert int(k_sizes.sum()) == K_tot and np.all(k_sizes % BLOCK == 0)
+    pad = np.where(k_sizes > 0, rng.integers(0, BLOCK, G), 0)
+    valid = k_sizes - pad
+    a32 = _normal(rng, (K_tot, M))
+    b32 = _normal(rng, (K_tot, N))
+    off = 0
+    for g in range(G):
+        a32[off + valid[g]: off + k_sizes[g]] = 0
+        b32[off + valid[g]: off + k_sizes[g]] = 0
+        off += int(k_sizes[g])
+    a, sfa = quantize_cols(a32)
+    del a32
+    b, sfb = quantize_cols(b32)
+    del b32
+    c = _normal(rng, (G, M, N), c_std) if with_c else None
+    return KGroupedInputs(a, sfa, b, sfb, k_sizes.astype(np.int32), valid, c,
+                          G, M, N, K_tot)
+
+
+def gen_config(i: int, seed: int = 0):
+    """The five named workloads by index 1..5 (2 returns the 15-shape list)."""
+    if i == 1:
+        return gen_dense(*DENSE_SMALL, seed=seed)
+    if i == 2:
+        return [gen_dense(m, n, k, seed=seed) for (m, n, k) in DENSE_SWEEP]
+    if i == 3:
+        return gen_contiguous(seed=seed)
+    if i == 4:
+        return gen_masked(seed=seed)
+    if i == 5:
+        return gen_k_grouped(seed=seed)
+    raise ValueError(i)

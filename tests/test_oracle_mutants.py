@@ -1,0 +1,100 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies oracle/oracle.c, applies one plausible mistake (a dropped
+term, a wrong index, a wrong sign, a wrong exponent bias, ...), builds the copy
+with the same gcc flags into a temporary library, routes the oracle wrappers to
+it and runs the pin tests of test_oracle_pins.py.  At least one pin must fail
+for every mutant.  All of this runs on the CPU; nothing here touches the GPU
+library.
+"""
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+MUTANTS = {
+    "exponent_bias": ("mag = ldexp(1.0 + (double)m / 8.0, e - 7);",
+                      "mag = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "subnormal_scale": ("mag = ldexp((double)m, -9);", "mag = ldexp((double)m, -10);"),
+    "nan_code": ("if (e == 15 && m == 7)", "if (e == 15 && m == 6)"),
+    "dropped_accumulation": ("acc += s * p;                                 /* promotion",
+                             "acc = s * p;                                 /* promotion"),
+    "sfb_ignores_n_block": ("sfb[(n / KBLK) * KB + kb]", "sfb[kb]"),
+    "sfb_transposed": ("sfb[(n / KBLK) * KB + kb]", "sfb[kb * ((N + KBLK - 1) / KBLK) + n / KBLK]"),
+    "sfa_ignores_stride": ("double s = (double)sa_row[kb * sa_stride]", "double s = (double)sa_row[kb]"),
+    "b_index_shifted": ("p += g_dec[a_row[k]] * g_dec[b_row[k]];",
+                        "p += g_dec[a_row[k]] * g_dec[b_row[(k + 1) % K]];"),
+    "c_sign": ("out[n] = acc + (c_row ? (double)c_row[n] : 0.0);",
+               "out[n] = acc - (c_row ? (double)c_row[n] : 0.0);"),
+    "block_sum_in_float": ("double p = 0.0;                               /* exact block sum */\n"
+                           "            for (int64_t k = kb * KBLK; k < (kb + 1) * KBLK; ++k)\n"
+                           "                p += g_dec[a_row[k]] * g_dec[b_row[k]];",
+                           "float p = 0.0f;                               /* exact block sum */\n"
+                           "            for (int64_t k = kb * KBLK; k < (kb + 1) * KBLK; ++k)\n"
+                           "                p += (float)(g_dec[a_row[k]] * g_dec[b_row[k]]);"),
+    "scale_block_off_by_one": ("double s = (double)sa_row[kb * sa_stride]",
+                               "double s = (double)sa_row[((kb + 1) % KB) * sa_stride]"),
+    "contiguous_expert_zero": ("nt_row(a + r * K, sfa + r, M_tot, b + e * N * K, sfb + e * NB * KB,",
+                               "nt_row(a + r * K, sfa + r, M_tot, b, sfb + e * NB * KB,"),
+    "masked_off_by_one": ("if (r >= mm) {", "if (r > mm) {"),
+    "masked_no_clamp": ("if (mm > M_max) mm = M_max;", "if (mm > M_max) mm = 1;"),
+    "tn_sfb_row_only": ("(double)sfb[kb * N + n];", "(double)sfb[kb * N];"),
+    "tn_group_start": ("for (int64_t kb = k0 / KBLK; kb < k1 / KBLK; ++kb) {",
+                       "for (int64_t kb = 0; kb < k1 / KBLK; ++kb) {"),
+    "tn_c_dropped": ("out[i * N + n] = acc + (c ? (double)c[(g * M + m) * N + n] : 0.0);",
+                     "out[i * N + n] = acc;"),
+}
+
+
+def _pin_suite():
+    """The pins, as plain calls; returns the names of those that failed."""
+    checks = [
+        ("decode_all", pins.test_decode_all_codes_match_torch),
+        ("decode_448", lambda: pins.test_decode_special_values(0x7E, 448.0)),
+        ("decode_sub", lambda: pins.test_decode_special_values(0x01, 2.0 ** -9)),
+        ("dense_exact_0", lambda: pins.test_dense_matches_exact_rationals(0, 3, 5, 128)),
+        ("dense_exact_1", lambda: pins.test_dense_matches_exact_rationals(1, 4, 3, 256)),
+        ("dense_exact_2", lambda: pins.test_dense_matches_exact_rationals(2, 2, 130, 384)),
+        ("all_ones", lambda: pins.test_all_ones_gives_K(512)),
+        ("pow2_scales", pins.test_power_of_two_scales_pick_the_right_blocks),
+        ("one_hot_b", pins.test_one_hot_b_selects_a_column),
+        ("one_hot_a", pins.test_one_hot_a_selects_a_row_of_b),
+        ("f64_matmul", pins.test_dense_against_float64_matmul),
+        ("golden", pins.test_hand_worked_golden),
+        ("contiguous", pins.test_contiguous_matches_exact_rationals),
+        ("masked", pins.test_masked_matches_exact_rationals_and_masks_rows),
+        ("k_grouped", pins.test_k_grouped_matches_exact_rationals_with_empty_group),
+    ]
+    failed = []
+    for name, fn in checks:
+        try:
+            fn()
+        except AssertionError:
+            failed.append(name)
+    return failed
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SRC_PATH) as f:
+        return f.read()
+
+
+def test_unmutated_copy_passes_every_pin(tmp_path, source):
+    src = tmp_path / "oracle_copy.c"
+    src.write_text(source)
+    lib = oracle.compile_source(str(src), str(tmp_path / "liboracle_copy.so"))
+    with oracle.use_library(lib):
+        assert _pin_suite() == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, source, name):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation site for {name} not found exactly once"
+    src = tmp_path / f"oracle_{name}.c"
+    src.write_text(source.replace(old, new))
+    lib = oracle.compile_source(str(src), str(tmp_path / f"liboracle_{name}.so"))
+    with oracle.use_library(lib):
+        failed = _pin_suite()
+    assert failed, f"mutant {name} passed every pin"
