@@ -1,0 +1,267 @@
+"""Benchmark: fine-grained FP8 e4m3 GEMM throughput on one MI355X.
+
+One step = one pass of the hot path over the dense NT sweep workload: the 15
+shapes M in {64, 128, 4096} x (N, K) in {(2112, 7168), (24576, 1536),
+(7168, 16384), (4096, 7168), (7168, 2048)}, bf16 out, inputs N(0,1) quantised
+with 1x128 (A) and 128x128 (B) fp32 scales, all resident in HBM before the
+timed region.  value = total algorithmic FLOP of a step (sum of 2*M*N*K) over
+the measured time, in TFLOP/s.
+
+Also reported on the same JSON line:
+  roofline     -- the dominant launch of the step (largest share of time),
+                  timed live with HIP events on the launch stream, against the
+                  MFMA (fp8 dense 5.0 PFLOP/s) or HBM (8 TB/s) roof, whichever
+                  bounds its arithmetic intensity;
+  cpu_baseline -- the fp64 CPU oracle on a bounded sample of that shape's rows;
+  detail       -- per-shape times, and the three grouped MoE workloads
+                  (contiguous, masked, K-grouped) timed the same way.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-detail]
+                       [--no-cpu] [--json-out PATH]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (published)
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
+MACHINE_BALANCE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # FLOP per byte
+
+
+def dense_bytes(M, N, K, d_bytes=2):
+    return M * K + N * K + 4 * (K // 128) * M + 4 * ((N + 127) // 128) * (K // 128) + d_bytes * M * N
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--json-out", default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the kernels are single-GPU; see the sharding notes in the design document)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_fine_grained_e4m3_amd as dg
+    from tests import gen
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    dg.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    # ---- inputs (host generation, then resident in HBM) ---------------------------
+    t0 = time.time()
+    shapes = list(gen.DENSE_SWEEP)
+    ops = []
+    for (M, N, K) in shapes:
+        x = gen.gen_dense(M, N, K, seed=0)
+        a, sa, b, sb = up(x.a), up(x.sfa), up(x.b), up(x.sfb)
+        d = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        ops.append(dict(shape=(M, N, K), args=((a, sa), (b, sb), d), flop=2.0 * M * N * K,
+                        bytes=dense_bytes(M, N, K)))
+        del x
+    gen_s = time.time() - t0
+    print(f"[bench] generated dense sweep in {gen_s:.1f}s", file=sys.stderr, flush=True)
+
+    def step(events=None):
+        for i, op in enumerate(ops):
+            if events is not None:
+                events[i][0].record(stream)
+            dg.fp8_gemm_nt(*op["args"])
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps ---------------------------------------------
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in ops] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    per_launch_ms = np.array([[ev[s][i][0].elapsed_time(ev[s][i][1]) for i in range(len(ops))]
+                              for s in range(args.steps)])
+    avg_ms = per_launch_ms.mean(axis=0)
+    flop_step = sum(op["flop"] for op in ops)
+    value = flop_step * args.steps / elapsed / 1e12
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    dom = int(np.argmax(avg_ms))
+    dop = ops[dom]
+    M, N, K = dop["shape"]
+    intensity = dop["flop"] / dop["bytes"]
+    if intensity >= MACHINE_BALANCE:
+        achieved = dop["flop"] / (avg_ms[dom] * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_FP8_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / PEAK_FP8_TFLOPS, 4), traffic=None)
+    else:
+        achieved = dop["bytes"] / (avg_ms[dom] * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None)
+    roof["kernel"] = f"nt_fp8_kernel dense {M}x{N}x{K}"
+    roof["avg_launch_us"] = round(avg_ms[dom] * 1e3, 2)
+
+    per_shape = []
+    for op, t in zip(ops, avg_ms):
+        m, n, k = op["shape"]
+        per_shape.append(dict(M=m, N=n, K=k, us=round(t * 1e3, 2),
+                              tflops=round(op["flop"] / (t * 1e-3) / 1e12, 1),
+                              gbs=round(op["bytes"] / (t * 1e-3) / 1e9, 1)))
+    print(f"[bench] step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    # ---- grouped workloads (detail, timed the same way) ------------------------------
+    grouped = {}
+    if not args.no_detail:
+        del ops
+        torch.cuda.empty_cache()
+        grouped = bench_grouped(dg, gen, up, dev, stream, args)
+
+    # ---- CPU baseline: the oracle on a bounded sample ----------------------------------
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(gen, (M, N, K), args.cpu_seconds)
+
+    result = {
+        "metric": "FP8 GEMM TFLOPS + % of MI355X FP8 MFMA peak (dense NT, grouped MoE)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": "dense FP8 NT GEMM sweep: 15 shapes, M in {64,128,4096} x "
+                               "(N,K) in {(2112,7168),(24576,1536),(7168,16384),(4096,7168),"
+                               "(7168,2048)}, bf16 out, 1x128 / 128x128 fp32 scales, seed 0",
+                   "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": {"dense": per_shape, "grouped": grouped},
+    }
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+def bench_grouped(dg, gen, up, dev, stream, args):
+    import torch
+    out = {}
+    reps = max(3, min(args.steps, 10))
+
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        fn()
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    # contiguous (MoE forward)
+    x = gen.gen_contiguous(seed=0)
+    a, sa, b, sb, mi = up(x.a), up(x.sfa), up(x.b), up(x.sfb), up(x.m_indices)
+    d = torch.empty(x.M_tot, x.N, dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: dg.m_grouped_fp8_gemm_nt_contiguous((a, sa), (b, sb), d, mi), reps)
+    valid = int(x.counts.sum())
+    flop = 2.0 * valid * x.N * x.K
+    byts = x.a.nbytes + x.sfa.nbytes + x.b.nbytes + x.sfb.nbytes + x.m_indices.nbytes + 2 * x.M_tot * x.N
+    out["contiguous_32x4096x4096"] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
+                                         frac_mfma=round(flop / ms / 1e9 / PEAK_FP8_TFLOPS, 4),
+                                         gbs=round(byts / ms / 1e6, 1))
+    del a, sa, b, sb, mi, d, x
+    torch.cuda.empty_cache()
+
+    # masked (MoE decode)
+    x = gen.gen_masked(seed=0)
+    a, sa, b, sb, mm = up(x.a), up(x.sfa), up(x.b), up(x.sfb), up(x.masked_m)
+    d = torch.empty(x.G, x.M_max, x.N, dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d, mm), reps)
+    valid = int(x.masked_m.sum())
+    live = int((x.masked_m > 0).sum())
+    flop = 2.0 * valid * x.N * x.K
+    byts = (valid * x.K + valid * 4 * (x.K // 128) + live * x.N * x.K
+            + live * 4 * ((x.N + 127) // 128) * (x.K // 128) + 2 * valid * x.N + 4 * x.G)
+    out["masked_32x256x4096x2048"] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
+                                         gbs=round(byts / ms / 1e6, 1),
+                                         frac_hbm=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
+    del a, sa, b, sb, mm, d, x
+    torch.cuda.empty_cache()
+
+    # K-grouped TN (MoE weight gradient)
+    x = gen.gen_k_grouped(seed=0)
+    a, sa, b, sb, c = up(x.a), up(x.sfa), up(x.b), up(x.sfb), up(x.c)
+    d = torch.empty(x.G, x.M, x.N, dtype=torch.float32, device=dev)
+    ks = x.k_sizes
+    ms = timed(lambda: dg.k_grouped_fp8_gemm_tn_contiguous((a, sa), (b, sb), d, ks, c=c), reps)
+    flop = 2.0 * x.M * x.N * x.K_tot
+    byts = x.a.nbytes + x.sfa.nbytes + x.b.nbytes + x.sfb.nbytes + 2 * 4 * x.G * x.M * x.N
+    out["k_grouped_32x2048x4096"] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
+                                        gbs=round(byts / ms / 1e6, 1),
+                                        frac_hbm=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
+    del a, sa, b, sb, c, d, x
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(gen, shape, target_s):
+    """The fp64 oracle (as it stands) on sampled rows of the dominant shape."""
+    import oracle
+    M, N, K = shape
+    x = gen.gen_dense(M, N, K, seed=0)
+    threads = oracle.num_threads()
+    rows = np.arange(min(M, threads), dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.gemm_nt(x.a, x.sfa, x.b, x.sfb, rows=rows)
+    t = time.perf_counter() - t0
+    n = int(min(M, max(len(rows), len(rows) * target_s / max(t, 1e-3))))
+    n = max(threads, (n // threads) * threads) if n >= threads else n
+    rows = np.arange(n, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.gemm_nt(x.a, x.sfa, x.b, x.sfb, rows=rows)
+    t = time.perf_counter() - t0
+    flop = 2.0 * n * N * K
+    return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} of {M} rows of the dense {M}x{N}x{K} shape (all {N} columns), "
+                      f"{t:.1f} s, fp64 exact block sums"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,237 @@
+"""Python binding of libdg.so, the MI355X (gfx950) fine-grained FP8 e4m3 GEMM.
+
+Argument marshalling only: every step of every GEMM runs in the HIP kernels
+behind the C ABI declared in include/dg.h.  PyTorch supplies device memory and
+the current stream.  There is no fallback path: if libdg.so is missing or a
+call fails, an exception is raised.
+
+FP8 operands are passed as (data, scale) pairs, data being uint8 (raw e4m3
+bytes) or torch.float8_e4m3fn, scales fp32 (the operand convention of the
+"DeepGEMM" README, yuguo-Jack fork, section "Interfaces").  The caller
+allocates the output and passes it in.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdg.so")
+
+DG_OK, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP = 0, 1, 2, 3
+DG_BF16, DG_F32 = 1, 2
+
+# Every symbol include/dg.h declares (the CPU tests check the library exports them).
+EXPORTED = (
+    "dg_fp8_gemm_nt",
+    "dg_m_grouped_fp8_gemm_nt_contiguous",
+    "dg_m_grouped_fp8_gemm_nt_masked",
+    "dg_k_grouped_fp8_gemm_tn_contiguous",
+    "dg_last_error",
+    "dg_get_num_cus",
+    "dg_set_num_cus",
+    "dg_get_mk_alignment_for_contiguous_layout",
+)
+
+_lib = None
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"dg status {status}: {message}")
+        self.status = status
+
+
+def load_library(path: Optional[str] = None):
+    """Load libdg.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with `python -m fp8_fine_grained_e4m3_amd.build` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(p)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.dg_fp8_gemm_nt.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
+    lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
+    lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
+    lib.dg_k_grouped_fp8_gemm_tn_contiguous.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, P]
+    for name in EXPORTED[:4]:
+        getattr(lib, name).restype = I
+    lib.dg_last_error.argtypes = []
+    lib.dg_last_error.restype = ctypes.c_char_p
+    lib.dg_get_num_cus.argtypes = []
+    lib.dg_get_num_cus.restype = I
+    lib.dg_set_num_cus.argtypes = [I]
+    lib.dg_set_num_cus.restype = I
+    lib.dg_get_mk_alignment_for_contiguous_layout.argtypes = []
+    lib.dg_get_mk_alignment_for_contiguous_layout.restype = I
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != DG_OK:
+        raise DGError(status, load_library().dg_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _fp8(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be uint8 or float8_e4m3fn, got {t.dtype}")
+    return _dev(t, name)
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _f32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    return _dev(t, name)
+
+
+def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32, got {t.dtype}")
+    return _dev(t, name)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, torch.Tensor],
+                d: torch.Tensor, c: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """d[M,N] = c + a @ b^T.  a = (A [M,K], SFA [K/128, M]), b = (B [N,K],
+    SFB [ceil(N/128), K/128]); d bf16 or fp32; c None or like d (may be d)."""
+    A, SA = _fp8(a[0], "A"), _f32(a[1], "SFA")
+    B, SB = _fp8(b[0], "B"), _f32(b[1], "SFB")
+    d = _dev(d, "d")
+    if d.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("d must be bfloat16 or float32")
+    if c is not None:
+        c = _dev(c, "c")
+        if c.dtype != d.dtype or c.shape != d.shape:
+            raise ValueError("c must match d in dtype and shape")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(d.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)} B {tuple(B.shape)} d {tuple(d.shape)}")
+    if tuple(SA.shape) != (K // 128, M) or tuple(SB.shape) != ((N + 127) // 128, K // 128):
+        raise ValueError(f"scale shapes: SFA {tuple(SA.shape)} SFB {tuple(SB.shape)}")
+    with torch.cuda.device(d.device):
+        _check(load_library().dg_fp8_gemm_nt(
+            _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(c), _ptr(d),
+            DG_F32 if d.dtype == torch.float32 else DG_BF16, M, N, K, _stream(d)))
+    return d
+
+
+def m_grouped_fp8_gemm_nt_contiguous(a: Tuple[torch.Tensor, torch.Tensor],
+                                     b: Tuple[torch.Tensor, torch.Tensor],
+                                     d: torch.Tensor, m_indices: torch.Tensor) -> torch.Tensor:
+    """d[r] = a[r] @ b[m_indices[r]]^T; a = (A [M_tot,K], SFA [K/128, M_tot]),
+    b = (B [G,N,K], SFB [G, ceil(N/128), K/128]); d bf16 [M_tot, N]."""
+    A, SA = _fp8(a[0], "A"), _f32(a[1], "SFA")
+    B, SB = _fp8(b[0], "B"), _f32(b[1], "SFB")
+    d, mi = _dev(d, "d"), _i32(m_indices, "m_indices")
+    if d.dtype != torch.bfloat16:
+        raise TypeError("d must be bfloat16")
+    M_tot, K = A.shape
+    G, N, Kb = B.shape
+    if Kb != K or tuple(d.shape) != (M_tot, N) or tuple(mi.shape) != (M_tot,):
+        raise ValueError("shape mismatch")
+    if tuple(SA.shape) != (K // 128, M_tot) or tuple(SB.shape) != (G, (N + 127) // 128, K // 128):
+        raise ValueError("scale shape mismatch")
+    with torch.cuda.device(d.device):
+        _check(load_library().dg_m_grouped_fp8_gemm_nt_contiguous(
+            _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(mi), _ptr(d), M_tot, N, K, G, _stream(d)))
+    return d
+
+
+def m_grouped_fp8_gemm_nt_masked(a: Tuple[torch.Tensor, torch.Tensor],
+                                 b: Tuple[torch.Tensor, torch.Tensor],
+                                 d: torch.Tensor, masked_m: torch.Tensor) -> torch.Tensor:
+    """d[g, r] = a[g, r] @ b[g]^T for r < masked_m[g]; other rows untouched.
+    a = (A [G,M_max,K], SFA [G, K/128, M_max]), b = (B [G,N,K], SFB [G,NB,KB])."""
+    A, SA = _fp8(a[0], "A"), _f32(a[1], "SFA")
+    B, SB = _fp8(b[0], "B"), _f32(b[1], "SFB")
+    d, mm = _dev(d, "d"), _i32(masked_m, "masked_m")
+    if d.dtype != torch.bfloat16:
+        raise TypeError("d must be bfloat16")
+    G, M_max, K = A.shape
+    N = B.shape[1]
+    if tuple(B.shape) != (G, N, K) or tuple(d.shape) != (G, M_max, N) or tuple(mm.shape) != (G,):
+        raise ValueError("shape mismatch")
+    if tuple(SA.shape) != (G, K // 128, M_max) or tuple(SB.shape) != (G, (N + 127) // 128, K // 128):
+        raise ValueError("scale shape mismatch")
+    with torch.cuda.device(d.device):
+        _check(load_library().dg_m_grouped_fp8_gemm_nt_masked(
+            _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(mm), _ptr(d), G, M_max, N, K, _stream(d)))
+    return d
+
+
+def k_grouped_fp8_gemm_tn_contiguous(a: Tuple[torch.Tensor, torch.Tensor],
+                                     b: Tuple[torch.Tensor, torch.Tensor],
+                                     d: torch.Tensor, k_sizes: Sequence[int],
+                                     c: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """d[g] = c[g] + a_g^T @ b_g over group g's K rows.  a = (A [K_tot, M],
+    SFA [K_tot/128, M]), b = (B [K_tot, N], SFB [K_tot/128, N]); k_sizes is a
+    host sequence; d (and c) fp32 [G, M, N]."""
+    A, SA = _fp8(a[0], "A"), _f32(a[1], "SFA")
+    B, SB = _fp8(b[0], "B"), _f32(b[1], "SFB")
+    d = _f32(d, "d")
+    if c is not None:
+        c = _f32(c, "c")
+        if c.shape != d.shape:
+            raise ValueError("c must match d")
+    ks = np.ascontiguousarray(np.asarray(k_sizes, dtype=np.int64))
+    if ks.ndim != 1 or np.any(ks > np.iinfo(np.int32).max) or np.any(ks < np.iinfo(np.int32).min):
+        raise ValueError("k_sizes must be a 1-D sequence of int32 values")
+    ks = ks.astype(np.int32)
+    K_tot, M = A.shape
+    N = B.shape[1]
+    G = len(ks)
+    if B.shape[0] != K_tot or tuple(d.shape) != (G, M, N):
+        raise ValueError("shape mismatch")
+    if tuple(SA.shape) != (K_tot // 128, M) or tuple(SB.shape) != (K_tot // 128, N):
+        raise ValueError("scale shape mismatch")
+    with torch.cuda.device(d.device):
+        _check(load_library().dg_k_grouped_fp8_gemm_tn_contiguous(
+            _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), ks.ctypes.data_as(ctypes.c_void_p), _ptr(c),
+            _ptr(d), G, M, N, K_tot, _stream(d)))
+    return d
+
+
+def get_num_cus() -> int:
+    return load_library().dg_get_num_cus()
+
+
+def set_num_cus(n: int) -> None:
+    _check(load_library().dg_set_num_cus(int(n)))
+
+
+def get_mk_alignment_for_contiguous_layout() -> int:
+    return load_library().dg_get_mk_alignment_for_contiguous_layout()
+
+
+def to_mn_major_sf(sf: torch.Tensor) -> torch.Tensor:
+    """[rows, K/128] per-row scales -> the MN-major [K/128, rows] layout the
+    A-side scale factors use (a transpose + copy; layout only)."""
+    return sf.transpose(-1, -2).contiguous()

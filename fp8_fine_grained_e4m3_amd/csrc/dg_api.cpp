@@ -1,0 +1,281 @@
+// C-ABI layer: argument validation (before any HIP call), device checks,
+// CU-count cap, error reporting, and dispatch to the kernels.
+#include "../../include/dg.h"
+#include "dg_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dg_status fail(dg_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+dg_status ok() {
+    g_last_error.clear();
+    return DG_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// c must be NULL, equal to d, or not overlap [d, d + bytes).
+bool alias_ok(const void* c, const void* d, int64_t bytes) {
+    if (c == nullptr || c == d) return true;
+    const uintptr_t c0 = reinterpret_cast<uintptr_t>(c), d0 = reinterpret_cast<uintptr_t>(d);
+    return c0 + (uintptr_t)bytes <= d0 || d0 + (uintptr_t)bytes <= c0;
+}
+
+#define REQUIRE(cond, ...)                                   \
+    do {                                                     \
+        if (!(cond)) return fail(DG_ERR_INVALID_ARG, __VA_ARGS__); \
+    } while (0)
+
+#define REQUIRE_PTR(p, align)                                                         \
+    do {                                                                              \
+        if ((p) == nullptr) return fail(DG_ERR_INVALID_ARG, "%s is NULL", #p);        \
+        if (!aligned((p), (align)))                                                   \
+            return fail(DG_ERR_INVALID_ARG, "%s is not %d-byte aligned", #p, (int)(align)); \
+    } while (0)
+
+constexpr int64_t kOffsetLimit = INT_MAX;   // kernels index one matrix with 32-bit offsets
+
+// ---- device state -------------------------------------------------------------
+
+constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+    bool probed = false;
+    bool gfx950 = false;
+    int cus = 0;
+    char arch[64] = {0};
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mutex;
+int g_cu_cap = 0;   // 0 = use every CU
+
+dg_status current_device(int& dev, DeviceInfo& info) {
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(DG_ERR_UNSUPPORTED, "device index %d", dev);
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    DeviceInfo& d = g_dev[dev];
+    if (!d.probed) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(DG_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        snprintf(d.arch, sizeof d.arch, "%s", prop.gcnArchName);
+        d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        d.cus = prop.multiProcessorCount;
+        d.probed = true;
+    }
+    info = d;
+    if (!info.gfx950)
+        return fail(DG_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev,
+                    info.arch);
+    return DG_OK;
+}
+
+int cu_cap_for(const DeviceInfo& info) {
+    const int cap = g_cu_cap;
+    return (cap > 0 && cap < info.cus) ? cap : info.cus;
+}
+
+bool print_configs() {
+    static int v = -1;
+    if (v < 0) {
+        const char* s = getenv("DG_PRINT_CONFIGS");
+        v = (s && s[0] == '1') ? 1 : 0;
+    }
+    return v == 1;
+}
+
+dg_status run_nt(const dg::NtProblem& p, void* stream) {
+    int dev = 0;
+    DeviceInfo info;
+    dg_status st = current_device(dev, info);
+    if (st != DG_OK) return st;
+    if (print_configs()) fprintf(stderr, "[dg] %s\n", dg::describe_nt_config(p));
+    hipError_t e = dg::launch_nt(p, cu_cap_for(info), reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                         const void* c, void* d, dg_dtype d_dtype, int64_t M, int64_t N,
+                         int64_t K, void* stream) {
+    REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size (M=%lld N=%lld K=%lld)", (long long)M,
+            (long long)N, (long long)K);
+    REQUIRE(K % 128 == 0, "K=%lld is not a multiple of 128", (long long)K);
+    REQUIRE(N % 16 == 0, "N=%lld is not a multiple of 16", (long long)N);
+    REQUIRE(d_dtype == DG_BF16 || d_dtype == DG_F32, "d_dtype must be DG_BF16 or DG_F32");
+    if (M == 0 || N == 0) return ok();
+    REQUIRE_PTR(d, 16);
+    if (c) REQUIRE_PTR(c, 16);
+    if (K > 0) {   // with K == 0 the operands are empty: D = C (or 0)
+        REQUIRE_PTR(a, 16);
+        REQUIRE_PTR(b, 16);
+        REQUIRE_PTR(sfa, 4);
+        REQUIRE_PTR(sfb, 4);
+    }
+    REQUIRE(M <= kOffsetLimit / (K > 0 ? K : 1) && N <= kOffsetLimit / (K > 0 ? K : 1),
+            "M*K and N*K must stay below 2^31");
+    REQUIRE(M <= INT_MAX && N <= INT_MAX, "size too large");
+    const int64_t dbytes = M * N * (d_dtype == DG_F32 ? 4 : 2);
+    REQUIRE(alias_ok(c, d, dbytes), "c overlaps d without being equal to it");
+    dg::NtProblem p{};
+    p.form = dg::kDense;
+    p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.c = c; p.d = d;
+    p.rows = M; p.N = N; p.K = K; p.G = 1;
+    p.out_f32 = d_dtype == DG_F32;
+    return run_nt(p, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa,
+                                              const uint8_t* b, const float* sfb,
+                                              const int32_t* m_indices, void* d, int64_t M_tot,
+                                              int64_t N, int64_t K, int64_t G, void* stream) {
+    REQUIRE(M_tot >= 0 && N >= 0 && K >= 0, "negative size");
+    REQUIRE(G >= 1, "G=%lld must be >= 1", (long long)G);
+    REQUIRE(M_tot % 128 == 0, "M_tot=%lld is not a multiple of 128 (the contiguous-layout alignment)",
+            (long long)M_tot);
+    REQUIRE(K % 128 == 0, "K=%lld is not a multiple of 128", (long long)K);
+    REQUIRE(N % 16 == 0, "N=%lld is not a multiple of 16", (long long)N);
+    if (M_tot == 0 || N == 0) return ok();
+    REQUIRE_PTR(a, 16);
+    REQUIRE_PTR(b, 16);
+    REQUIRE_PTR(d, 16);
+    REQUIRE_PTR(sfa, 4);
+    REQUIRE_PTR(sfb, 4);
+    REQUIRE_PTR(m_indices, 4);
+    REQUIRE(M_tot <= kOffsetLimit / (K > 0 ? K : 1) && N <= kOffsetLimit / (K > 0 ? K : 1),
+            "M_tot*K and N*K must stay below 2^31");
+    REQUIRE(G <= INT_MAX, "G too large");
+    dg::NtProblem p{};
+    p.form = dg::kContiguous;
+    p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.c = nullptr; p.d = d;
+    p.m_indices = m_indices;
+    p.rows = M_tot; p.N = N; p.K = K; p.G = G;
+    p.out_f32 = false;
+    return run_nt(p, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                          const float* sfb, const int32_t* masked_m, void* d,
+                                          int64_t G, int64_t M_max, int64_t N, int64_t K,
+                                          void* stream) {
+    REQUIRE(G >= 0 && M_max >= 0 && N >= 0 && K >= 0, "negative size");
+    REQUIRE(K % 128 == 0, "K=%lld is not a multiple of 128", (long long)K);
+    REQUIRE(N % 16 == 0, "N=%lld is not a multiple of 16", (long long)N);
+    if (G == 0 || M_max == 0 || N == 0) return ok();
+    REQUIRE_PTR(a, 16);
+    REQUIRE_PTR(b, 16);
+    REQUIRE_PTR(d, 16);
+    REQUIRE_PTR(sfa, 4);
+    REQUIRE_PTR(sfb, 4);
+    REQUIRE_PTR(masked_m, 4);
+    REQUIRE(M_max <= kOffsetLimit / (K > 0 ? K : 1) && N <= kOffsetLimit / (K > 0 ? K : 1),
+            "M_max*K and N*K must stay below 2^31");
+    REQUIRE(G * ((M_max + 63) / 64) * ((N + 127) / 128) <= INT_MAX, "too many tiles");
+    dg::NtProblem p{};
+    p.form = dg::kMasked;
+    p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.c = nullptr; p.d = d;
+    p.masked_m = masked_m;
+    p.rows = M_max; p.N = N; p.K = K; p.G = G;
+    p.out_f32 = false;
+    return run_nt(p, stream);
+}
+
+dg_status dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t* a, const float* sfa,
+                                              const uint8_t* b, const float* sfb,
+                                              const int32_t* k_sizes_host, const float* c,
+                                              float* d, int64_t G, int64_t M, int64_t N,
+                                              int64_t K_tot, void* stream) {
+    REQUIRE(M >= 0 && N >= 0 && K_tot >= 0, "negative size");
+    REQUIRE(G >= 1 && G <= dg::kMaxTnGroups, "G=%lld must be in [1, %d]", (long long)G,
+            dg::kMaxTnGroups);
+    REQUIRE(M % 16 == 0, "M=%lld is not a multiple of 16", (long long)M);
+    REQUIRE(N % 16 == 0, "N=%lld is not a multiple of 16", (long long)N);
+    REQUIRE(k_sizes_host != nullptr, "k_sizes_host is NULL");
+    int64_t total = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        const int64_t kg = k_sizes_host[g];
+        REQUIRE(kg >= 0 && kg % 128 == 0, "k_sizes_host[%lld]=%lld must be >= 0 and a multiple of 128",
+                (long long)g, (long long)kg);
+        total += kg;
+    }
+    REQUIRE(total == K_tot, "sum of k_sizes_host (%lld) != K_tot (%lld)", (long long)total,
+            (long long)K_tot);
+    if (M == 0 || N == 0) return ok();
+    REQUIRE_PTR(d, 16);
+    if (c) REQUIRE_PTR(c, 16);
+    if (K_tot > 0) {
+        REQUIRE_PTR(a, 16);
+        REQUIRE_PTR(b, 16);
+        REQUIRE_PTR(sfa, 16);
+        REQUIRE_PTR(sfb, 16);
+    }
+    REQUIRE(K_tot <= kOffsetLimit / M && K_tot <= kOffsetLimit / N,
+            "K_tot*M and K_tot*N must stay below 2^31");
+    REQUIRE(G * ((M + 127) / 128) * ((N + 127) / 128) <= INT_MAX, "too many tiles");
+    REQUIRE(alias_ok(c, d, G * M * N * 4), "c overlaps d without being equal to it");
+    dg::TnProblem p{};
+    p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.k_sizes_host = k_sizes_host;
+    p.c = c; p.d = d; p.G = G; p.M = M; p.N = N; p.K_tot = K_tot;
+
+    int dev = 0;
+    DeviceInfo info;
+    dg_status st = current_device(dev, info);
+    if (st != DG_OK) return st;
+    if (print_configs()) fprintf(stderr, "[dg] %s\n", dg::describe_tn_config(p));
+    hipError_t e = dg::launch_tn(p, cu_cap_for(info), reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+const char* dg_last_error(void) { return g_last_error.c_str(); }
+
+int dg_get_num_cus(void) {
+    int dev = 0;
+    DeviceInfo info;
+    if (current_device(dev, info) != DG_OK && !info.probed) return 0;
+    return cu_cap_for(info);
+}
+
+dg_status dg_set_num_cus(int n) {
+    if (n == 0) {
+        g_cu_cap = 0;
+        return ok();
+    }
+    int dev = 0;
+    DeviceInfo info;
+    dg_status st = current_device(dev, info);
+    if (st != DG_OK) return st;
+    if (n < 0 || n > info.cus)
+        return fail(DG_ERR_INVALID_ARG, "num_cus=%d must be in [1, %d] (or 0 for all)", n, info.cus);
+    g_cu_cap = n;
+    return ok();
+}
+
+int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal interface between the C-ABI layer (dg_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+// Which M-axis scheduling the NT kernel uses.
+enum NtForm : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+
+struct NtProblem {
+    NtForm form;
+    const uint8_t* a;
+    const float* sfa;
+    const uint8_t* b;
+    const float* sfb;
+    const void* c;            // dense only, same dtype as d, may be NULL
+    void* d;
+    const int32_t* m_indices; // contiguous
+    const int32_t* masked_m;  // masked
+    int64_t rows;             // dense: M, contiguous: M_tot, masked: M_max
+    int64_t N, K, G;
+    bool out_f32;
+};
+
+struct TnProblem {
+    const uint8_t* a;
+    const float* sfa;
+    const uint8_t* b;
+    const float* sfb;
+    const int32_t* k_sizes_host;
+    const float* c;
+    float* d;
+    int64_t G, M, N, K_tot;
+};
+
+constexpr int kMaxTnGroups = 256;
+
+// Launch on `stream`; `cu_cap` bounds the persistent grid.  Return the HIP
+// status of the launch.  Shapes have already been validated.
+hipError_t launch_nt(const NtProblem& p, int cu_cap, hipStream_t stream);
+hipError_t launch_tn(const TnProblem& p, int cu_cap, hipStream_t stream);
+
+// Short description of the tile configuration chosen for a problem (for
+// DG_PRINT_CONFIGS).
+const char* describe_nt_config(const NtProblem& p);
+const char* describe_tn_config(const TnProblem& p);
+
+}  // namespace dg

@@ -1,0 +1,71 @@
+// Device helpers shared by the NT and TN kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKBlk = 128;   // K extent of one scale block = one MFMA K step
+
+// LDS tiles hold 128-byte rows (one 128-wide K block of one row of A or B).
+// A row is eight 16-byte chunks; chunk c of row r lives at position
+// c ^ swz(r).  Eight consecutive rows therefore spread one chunk index over
+// all eight positions (conflict-free fragment reads), and rows eight apart
+// are permuted too (conflict-light transposed writes in the TN kernel).
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+__device__ __forceinline__ int lds_chunk_off(int row, int chunk) {
+    return row * kKBlk + ((chunk ^ swz(row)) << 4);
+}
+
+// One e4m3 x e4m3 block product over exactly one 128-wide K block into a
+// fresh fp32 accumulator: v_mfma_f32_16x16x128_f8f6f4 with both operands in
+// the FP8 E4M3 format (format code 0) and no block scaling (the scale operands
+// of 0 select the unscaled instruction).
+//
+// Operand layout (16 rows x 128 K each): lane l holds row (l & 15) and the 32
+// K bytes [32 * (l >> 4), 32 * (l >> 4) + 32).  Both operands use the same
+// lane -> K map, so the product pairs matching K indices whatever order the
+// unit sums them in.  Result: lane l holds out[4 * (l >> 4) + i][l & 15],
+// i = 0..3, where the first operand indexes rows and the second columns.
+__device__ __forceinline__ f32x4 mfma_e4m3_block(const i32x8& rows, const i32x8& cols) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rows, cols, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// Fragment of 16 consecutive LDS rows starting at row0 (see the layout above).
+__device__ __forceinline__ i32x8 lds_fragment(const uint8_t* tile, int row0, int lane) {
+    const int row = row0 + (lane & 15);
+    const int c0 = (lane >> 4) * 2;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(tile + lds_chunk_off(row, c0));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(tile + lds_chunk_off(row, c0 + 1));
+    i32x8 r;
+    r.s0 = lo.x; r.s1 = lo.y; r.s2 = lo.z; r.s3 = lo.w;
+    r.s4 = hi.x; r.s5 = hi.y; r.s6 = hi.z; r.s7 = hi.w;
+    return r;
+}
+
+// Round-to-nearest-even fp32 -> bf16 of four values, packed as two dwords
+// (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ i32x2 pack_bf16x4(float x0, float x1, float x2, float x3) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 lo, hi;
+    lo.x = (__bf16)x0; lo.y = (__bf16)x1;
+    hi.x = (__bf16)x2; hi.y = (__bf16)x3;
+    i32x2 r;
+    r.x = __builtin_bit_cast(int, lo);
+    r.y = __builtin_bit_cast(int, hi);
+    return r;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
+    return __uint_as_float(h16 << 16);
+}
+
+}  // namespace dg

@@ -1,0 +1,176 @@
+/*
+ * dg.h -- C ABI of the MI355X (gfx950) fine-grained FP8 e4m3 GEMM library.
+ *
+ * The operation, for every entry point, is D = C + A @ B^T on FP8 operands in
+ * the OCP E4M3FN encoding, each carrying fp32 scale factors at a fine
+ * granularity, with the FP8 partial sums of every 128-wide K block scaled and
+ * promoted into an fp32 accumulator:
+ *
+ *   D[m,n] = C[m,n] + sum_kb (sa[kb,m] * sb(n,kb)) * sum_{k in block kb} a[m,k] * b[n,k]
+ *
+ * Sources (the pages this library is built from):
+ *   - "DeepGEMM" README (GitHub, yuguo-Jack fork), section "Interfaces":
+ *     subsection "Notices" (the D = C + A @ B naming, NT = row-major A and
+ *     B stored [N, K], LHS scale factors in a transposed (MN-major) layout,
+ *     fp32 scale factors on the SM90 path, casting and transposition left to
+ *     the caller); "Grouped GEMMs (contiguous layout)" (M-axis grouping with
+ *     fixed N and K, expert segments aligned to the M block, and the K-axis
+ *     grouped TN form for the MoE weight backward pass); "Grouped GEMMs
+ *     (masked layout)" (decode under graph capture, the host does not know the
+ *     per-expert token counts, only the valid rows are computed).
+ *   - News article "Deepseek AI Libera Deepgemm: a GEMM FP8 Library ...",
+ *     section "Details and technical benefits" (fine-grained scaling and the
+ *     two-level accumulation, i.e. promotion).
+ *   - DeepGEMM Documentation (docsearch page), section 10 "Use DeepGEMM
+ *     Utility Functions" (SM-count cap and the contiguous-layout alignment
+ *     getter, here CU count and 128).
+ *   The block sizes (1 x 128 for A, 128 x 128 for B) and the promotion interval
+ *   of one 128-wide K block are the workload definitions this library serves;
+ *   the pages themselves only say "fine-grained".
+ *
+ * Conventions for every GEMM entry point:
+ *   - All pointers are DEVICE pointers unless the name ends in _host.  The
+ *     caller owns every buffer; the library keeps no pointer after it returns
+ *     and allocates nothing.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Each call
+ *     enqueues one kernel on it and returns; there is no host synchronisation,
+ *     so the masked form may be captured into a HIP graph.
+ *   - FP8 operands are raw e4m3 bytes (uint8_t).  Scale factors are fp32.
+ *   - Outputs: bf16 is stored as uint16_t bit patterns (round to nearest
+ *     even, once, from the fp32 accumulator); fp32 as float.
+ *   - Host-side validation runs before any HIP call.  On a non-OK status
+ *     nothing is launched and no output is touched; dg_last_error() explains
+ *     the failure.  A zero-sized problem returns DG_OK without launching.
+ *   - Every device pointer must be 16-byte aligned except the scale-factor and
+ *     metadata pointers, which must be 4-byte aligned.
+ *   - Device-side metadata cannot be checked without a synchronisation, so it
+ *     gets fixed readings instead: masked_m values are clamped to [0, M_max];
+ *     m_indices values outside [0, G) mark padding rows.
+ *   - Results are deterministic: the same inputs and launch give bitwise
+ *     identical outputs (no atomics, fixed summation order).
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DG_OK = 0,
+    DG_ERR_INVALID_ARG = 1,   /* a shape, pointer, alignment or dtype rule is broken */
+    DG_ERR_UNSUPPORTED = 2,   /* current device is not gfx950, or a size limit is hit  */
+    DG_ERR_HIP = 3            /* a HIP runtime call or the kernel launch failed        */
+} dg_status;
+
+typedef enum {
+    DG_BF16 = 1,
+    DG_F32 = 2
+} dg_dtype;
+
+/*
+ * Dense NT GEMM:  D[M,N] = C + A @ B^T.
+ *   a    [M, K]            e4m3, row-major (K contiguous)
+ *   sfa  [K/128, M]        fp32, one scale per (row, 128-K block), MN-major
+ *   b    [N, K]            e4m3, row-major (K contiguous), i.e. B^T column-major
+ *   sfb  [ceil(N/128), K/128] fp32, one scale per 128 x 128 block of B
+ *   c    NULL (treated as 0), or [M, N] of d_dtype; c == d (in-place
+ *        accumulate) is allowed, any other overlap with d is rejected
+ *   d    [M, N] of d_dtype (DG_BF16 or DG_F32)
+ * Rules: K % 128 == 0, N % 16 == 0, M >= 0.
+ * Source: "DeepGEMM" README, "Interfaces", "Notices" and "Normal dense GEMMs
+ * (non-grouped)".
+ */
+dg_status dg_fp8_gemm_nt(const uint8_t* a, const float* sfa,
+                         const uint8_t* b, const float* sfb,
+                         const void* c, void* d, dg_dtype d_dtype,
+                         int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * M-grouped contiguous NT GEMM (MoE forward / prefill):
+ *   D[r,:] = A[r,:] @ B[e_r]^T  with e_r = m_indices[r].
+ *   a         [M_tot, K]   e4m3; segments of rows per expert, concatenated
+ *   sfa       [K/128, M_tot] fp32
+ *   b         [G, N, K]    e4m3, one [N, K] matrix per expert
+ *   sfb       [G, ceil(N/128), K/128] fp32
+ *   m_indices [M_tot]      int32: expert of each row, or -1 for padding
+ *   d         [M_tot, N]   bf16
+ * Rules: M_tot % 128 == 0 (every expert segment is padded to a multiple of
+ * dg_get_mk_alignment_for_contiguous_layout() == 128 rows, padding at the
+ * segment's tail), K % 128 == 0, N % 16 == 0, G >= 1.
+ * The expert of a 128-row block is the index of its first row; a block whose
+ * first index is outside [0, G) is skipped.  Rows whose index differs from
+ * their block's expert (the padding rows) are not written.
+ * Source: "DeepGEMM" README, "Interfaces", "Grouped GEMMs (contiguous layout)".
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa,
+                                              const uint8_t* b, const float* sfb,
+                                              const int32_t* m_indices, void* d,
+                                              int64_t M_tot, int64_t N, int64_t K, int64_t G,
+                                              void* stream);
+
+/*
+ * M-grouped masked NT GEMM (MoE decode, graph-capturable):
+ *   D[g,r,:] = A[g,r,:] @ B[g]^T  for r < masked_m[g].
+ *   a        [G, M_max, K]   e4m3 (rows >= masked_m[g] may hold anything)
+ *   sfa      [G, K/128, M_max] fp32
+ *   b        [G, N, K]       e4m3
+ *   sfb      [G, ceil(N/128), K/128] fp32
+ *   masked_m [G]             int32, device memory, read by the kernel only;
+ *                            each value is clamped to [0, M_max]
+ *   d        [G, M_max, N]   bf16; rows >= masked_m[g] are never written
+ * Rules: K % 128 == 0, N % 16 == 0, G >= 0, M_max >= 0.
+ * Source: "DeepGEMM" README, "Interfaces", "Grouped GEMMs (masked layout)".
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa,
+                                          const uint8_t* b, const float* sfb,
+                                          const int32_t* masked_m, void* d,
+                                          int64_t G, int64_t M_max, int64_t N, int64_t K,
+                                          void* stream);
+
+/*
+ * K-grouped contiguous TN GEMM (MoE weight gradient), fp32 out:
+ *   D[g] = C[g] + A_g^T @ B_g, A_g / B_g = the k_sizes_host[g] rows of group g.
+ *   a            [K_tot, M]  e4m3, M contiguous (group segments along K)
+ *   sfa          [K_tot/128, M] fp32, one scale per (column m, 128-K block)
+ *   b            [K_tot, N]  e4m3, N contiguous
+ *   sfb          [K_tot/128, N] fp32, one scale per (column n, 128-K block)
+ *   k_sizes_host [G]         HOST int32 array, read during the call: each
+ *                            >= 0 and a multiple of 128, summing to K_tot
+ *   c            NULL (treated as 0) or [G, M, N] fp32; c == d allowed
+ *   d            [G, M, N]   fp32; a group with k_sizes_host[g] == 0 gets C[g]
+ * Rules: M % 16 == 0, N % 16 == 0, 1 <= G <= 256.
+ * Source: "DeepGEMM" README, "Interfaces", "Grouped GEMMs (contiguous
+ * layout)" (the K-axis-grouped API for the MoE weight backward pass).
+ */
+dg_status dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t* a, const float* sfa,
+                                              const uint8_t* b, const float* sfb,
+                                              const int32_t* k_sizes_host,
+                                              const float* c, float* d,
+                                              int64_t G, int64_t M, int64_t N, int64_t K_tot,
+                                              void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* dg_last_error(void);
+
+/*
+ * Cap on the compute units the persistent kernels size their grid for
+ * (DeepGEMM Documentation, section 10: set/get the maximum SM count).
+ * dg_get_num_cus() returns the current cap (the device's CU count by
+ * default, 0 if no device is visible); dg_set_num_cus(n) accepts
+ * 1 <= n <= device CU count, or 0 to restore the default.
+ */
+int dg_get_num_cus(void);
+dg_status dg_set_num_cus(int n);
+
+/* Row alignment of every expert segment in the contiguous layout: 128
+ * (DeepGEMM Documentation, section 9, and section 10's alignment getter). */
+int dg_get_mk_alignment_for_contiguous_layout(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

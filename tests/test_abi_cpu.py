@@ -1,0 +1,159 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host-side validation rejects bad arguments before any HIP call.
+
+No GPU is needed: invalid arguments never reach the device (validation runs
+first), so fake, never-dereferenced device addresses are enough.  Nothing here
+launches a kernel.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import fp8_fine_grained_e4m3_amd as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+P16 = ctypes.c_void_p(0x10000)      # fake 16-byte-aligned device addresses
+P16b = ctypes.c_void_p(0x20000)
+P16c = ctypes.c_void_p(0x30000)
+BAD = ctypes.c_void_p(0x10008)      # 8-byte aligned only
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dg.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return dg.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:dg_status|const char\*|int)\s+(dg_\w+)\s*\(", text,
+                                 re.M)))
+
+
+def test_header_declares_the_four_gemms_and_utilities():
+    syms = declared_symbols()
+    for name in ("dg_fp8_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous",
+                 "dg_m_grouped_fp8_gemm_nt_masked", "dg_k_grouped_fp8_gemm_tn_contiguous"):
+        assert name in syms
+    assert set(syms) == set(dg.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    nm = os.popen(f"nm -D --defined-only {dg.LIB_PATH}").read()
+    for name in declared_symbols():
+        assert re.search(rf"\bT {name}\b", nm), name
+
+
+def test_alignment_getter(lib):
+    assert lib.dg_get_mk_alignment_for_contiguous_layout() == 128
+
+
+def err(lib):
+    return lib.dg_last_error().decode()
+
+
+def nt(lib, a=P16, sfa=P16, b=P16b, sfb=P16, c=NULL, d=P16c, dt=dg.DG_BF16, M=128, N=256, K=512):
+    return lib.dg_fp8_gemm_nt(a, sfa, b, sfb, c, d, dt, M, N, K, None)
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(K=500), "K=500"),
+    (dict(N=250), "N=250"),
+    (dict(M=-1), "negative"),
+    (dict(dt=7), "d_dtype"),
+    (dict(a=NULL), "a is NULL"),
+    (dict(b=BAD), "b is not 16-byte"),
+    (dict(d=NULL), "d is NULL"),
+    (dict(sfa=NULL), "sfa is NULL"),
+    (dict(c=ctypes.c_void_p(0x30000 + 64)), "overlaps"),
+    (dict(M=1 << 22, K=1024), "2^31"),
+])
+def test_dense_rejects(lib, kw, needle):
+    st = nt(lib, **kw)
+    assert st == dg.DG_ERR_INVALID_ARG
+    assert needle in err(lib)
+
+
+def test_dense_zero_size_is_a_noop(lib):
+    assert nt(lib, M=0) == dg.DG_OK
+    assert nt(lib, N=0, a=NULL) == dg.DG_OK
+    assert err(lib) == ""
+
+
+def test_contiguous_rejects(lib):
+    f = lib.dg_m_grouped_fp8_gemm_nt_contiguous
+    assert f(P16, P16, P16b, P16, P16, P16c, 200, 256, 512, 4, None) == dg.DG_ERR_INVALID_ARG
+    assert "multiple of 128" in err(lib)
+    assert f(P16, P16, P16b, P16, P16, P16c, 256, 256, 512, 0, None) == dg.DG_ERR_INVALID_ARG
+    assert "G=0" in err(lib)
+    assert f(P16, P16, P16b, P16, NULL, P16c, 256, 256, 512, 4, None) == dg.DG_ERR_INVALID_ARG
+    assert "m_indices is NULL" in err(lib)
+    assert f(P16, P16, P16b, P16, P16, P16c, 0, 256, 512, 4, None) == dg.DG_OK
+
+
+def test_masked_rejects(lib):
+    f = lib.dg_m_grouped_fp8_gemm_nt_masked
+    assert f(P16, P16, P16b, P16, NULL, P16c, 4, 256, 256, 512, None) == dg.DG_ERR_INVALID_ARG
+    assert "masked_m is NULL" in err(lib)
+    assert f(P16, P16, P16b, P16, P16, P16c, 4, 256, 250, 512, None) == dg.DG_ERR_INVALID_ARG
+    assert f(P16, P16, P16b, P16, P16, P16c, 0, 256, 256, 512, None) == dg.DG_OK
+
+
+def test_k_grouped_rejects(lib):
+    f = lib.dg_k_grouped_fp8_gemm_tn_contiguous
+
+    def call(ks, M=256, N=256, K_tot=None, c=NULL, d=P16c, G=None):
+        ks = np.asarray(ks, np.int32)
+        K_tot = int(ks.sum()) if K_tot is None else K_tot
+        G = len(ks) if G is None else G
+        return f(P16, P16, P16b, P16, ks.ctypes.data_as(ctypes.c_void_p), c, d, G, M, N, K_tot,
+                 None)
+
+    assert call([128, 100]) == dg.DG_ERR_INVALID_ARG and "multiple of 128" in err(lib)
+    assert call([128, 256], K_tot=512) == dg.DG_ERR_INVALID_ARG and "K_tot" in err(lib)
+    assert call([128], M=200) == dg.DG_ERR_INVALID_ARG
+    assert call([128] * 257) == dg.DG_ERR_INVALID_ARG and "G=257" in err(lib)
+    assert call([128], c=ctypes.c_void_p(0x30000 + 16)) == dg.DG_ERR_INVALID_ARG
+    assert call([128, 0], M=0) == dg.DG_OK
+
+
+def test_valid_call_without_gpu_fails_cleanly(lib):
+    """With valid arguments the library asks HIP for the device; with no GPU
+    that fails with a HIP or unsupported-device status, never a crash."""
+    st = nt(lib)
+    assert st in (dg.DG_ERR_HIP, dg.DG_ERR_UNSUPPORTED, dg.DG_OK)
+    if st != dg.DG_OK:
+        assert err(lib)
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    a = torch.zeros(128, 512, dtype=torch.uint8)
+    sa = torch.ones(4, 128)
+    b = torch.zeros(256, 512, dtype=torch.uint8)
+    sb = torch.ones(2, 4)
+    d = torch.empty(128, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        dg.fp8_gemm_nt((a, sa), (b, sb), d)
+
+
+def test_no_oracle_in_product_path():
+    """The GPU package neither imports nor links the oracle."""
+    pkg = os.path.join(ROOT, "fp8_fine_grained_e4m3_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in text.lower(), fn
+    nm = os.popen(f"nm -D {dg.LIB_PATH}").read()
+    assert "oracle" not in nm

@@ -1,0 +1,408 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 CPU oracle.
+
+Every test builds seeded inputs with tests/gen, runs the GPU path and compares
+element by element to the oracle under the stated tolerance (tests/parity.py),
+or bit-exactly where the arithmetic is exact (one-hot operands, all-ones,
+power-of-two scales, grouped-vs-dense identities, run-to-run determinism).
+Full-size workloads are compared on sampled rows the oracle computes one by
+one; guard bands and sentinel rows catch out-of-bounds and masked-row stores.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_fine_grained_e4m3_amd as dg
+import oracle
+from tests import gen
+from tests.parity import Guarded, announce, check_close, dev, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dg.load_library()
+    yield
+    dg.set_num_cus(0)
+
+
+def run_dense(x, out_dtype=torch.bfloat16, c=None, guarded=True):
+    d = Guarded((x.M, x.N), out_dtype) if guarded else None
+    out = d.view if guarded else torch.empty(x.M, x.N, dtype=out_dtype, device="cuda")
+    dg.fp8_gemm_nt((dev(x.a), dev(x.sfa)), (dev(x.b), dev(x.sfb)), out, c=c)
+    torch.cuda.synchronize()
+    if guarded:
+        assert d.intact(), "store outside D"
+    return out
+
+
+def sample_rows(M, n, rng):
+    base = {0, M - 1, M // 2}
+    base |= set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    return np.array(sorted(base), dtype=np.int64)
+
+
+# ------------------------------------------------------------------------------
+# dense NT
+# ------------------------------------------------------------------------------
+
+def test_c1_dense_128x256x512_full():
+    announce("dense C1 128x256x512 seed0")
+    x = gen.gen_dense(128, 256, 512, seed=0)
+    got = to64(run_dense(x))
+    stats = check_close(got, oracle.gemm_nt(x.a, x.sfa, x.b, x.sfb), "C1")
+    print(stats)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 16, 128), (16, 16, 128), (65, 144, 384), (127, 272, 640), (129, 400, 256),
+    (300, 528, 1152), (64, 2112, 1024), (257, 2112, 256),
+])
+def test_dense_ragged_shapes(M, N, K):
+    announce(f"dense ragged {M}x{N}x{K}")
+    x = gen.gen_dense(M, N, K, seed=M * 7 + N)
+    got = to64(run_dense(x))
+    check_close(got, oracle.gemm_nt(x.a, x.sfa, x.b, x.sfb), f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_dense_with_c_and_in_place(out):
+    announce(f"dense with C ({out})")
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    x = gen.gen_dense(200, 384, 768, seed=5, with_c=True)
+    c = dev(x.c).to(dt)
+    ref = oracle.gemm_nt(x.a, x.sfa, x.b, x.sfb, c=x.c)
+    out = run_dense(x, dt, c=c)
+    check_close(to64(out), ref, "with C")
+    # in place (c == d) must give the same bits
+    d = c.clone()
+    dg.fp8_gemm_nt((dev(x.a), dev(x.sfa)), (dev(x.b), dev(x.sfb)), d, c=d)
+    torch.cuda.synchronize()
+    assert torch.equal(d, out)
+
+
+def test_dense_k_zero_gives_c():
+    announce("dense K=0")
+    M, N = 32, 64
+    c = torch.randn(M, N, device="cuda").to(torch.bfloat16)
+    d = torch.empty_like(c)
+    a = torch.empty(M, 0, dtype=torch.uint8, device="cuda")
+    b = torch.empty(N, 0, dtype=torch.uint8, device="cuda")
+    sa = torch.empty(0, M, device="cuda")
+    sb = torch.empty(1, 0, device="cuda")
+    dg.fp8_gemm_nt((a, sa), (b, sb), d, c=c)
+    torch.cuda.synchronize()
+    assert torch.equal(d, c)
+
+
+@pytest.mark.parametrize("idx", range(len(gen.DENSE_SWEEP)))
+def test_c2_dense_sweep_full_size(idx):
+    M, N, K = gen.DENSE_SWEEP[idx]
+    announce(f"dense C2 {M}x{N}x{K} seed0")
+    x = gen.gen_dense(M, N, K, seed=0)
+    out = run_dense(x)
+    rng = np.random.default_rng(idx)
+    rows = sample_rows(M, 12, rng)
+    got = to64(out[torch.from_numpy(rows).cuda()])
+    ref = oracle.gemm_nt(x.a, x.sfa, x.b, x.sfb, rows=rows)
+    print(check_close(got, ref, f"C2 {M}x{N}x{K}"))
+    full = out.float()
+    assert torch.isfinite(full).all()
+
+
+# ------------------------------------------------------------------------------
+# bit-exact pins on the GPU
+# ------------------------------------------------------------------------------
+
+def test_one_hot_b_is_bit_exact():
+    """b[n, pi(n)] = 1, sfb = 1: D[m,n] = fp32(dec(a[m,pi(n)]) * sa) exactly
+    (one nonzero product), then one RNE to bf16 / exact in fp32."""
+    announce("one-hot B")
+    rng = np.random.default_rng(1)
+    M, N, K = 160, 272, 512
+    x = gen.gen_dense(M, N, K, seed=3)
+    pi = rng.integers(0, K, N)
+    b = np.zeros((N, K), np.uint8)
+    b[np.arange(N), pi] = 0x38
+    sfb = np.ones(((N + 127) // 128, K // 128), np.float32)
+    x.b, x.sfb = b, sfb
+    ref = oracle.gemm_nt(x.a, x.sfa, b, sfb)
+    got32 = run_dense(x, torch.float32).cpu().numpy()
+    assert np.array_equal(got32.astype(np.float64), ref.astype(np.float32).astype(np.float64))
+    got16 = run_dense(x, torch.bfloat16).cpu()
+    assert torch.equal(got16, torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16))
+
+
+def test_one_hot_a_is_bit_exact():
+    announce("one-hot A")
+    rng = np.random.default_rng(2)
+    M, N, K = 144, 400, 384
+    x = gen.gen_dense(M, N, K, seed=4)
+    pi = rng.integers(0, K, M)
+    a = np.zeros((M, K), np.uint8)
+    a[np.arange(M), pi] = 0x38
+    x.a, x.sfa = a, np.ones((K // 128, M), np.float32)
+    ref = oracle.gemm_nt(a, x.sfa, x.b, x.sfb)
+    got32 = run_dense(x, torch.float32).cpu().numpy()
+    assert np.array_equal(got32.astype(np.float64), ref.astype(np.float32).astype(np.float64))
+
+
+@pytest.mark.parametrize("K", [128, 1536, 7168])
+def test_all_ones_gives_exactly_K(K):
+    announce(f"all ones K={K}")
+    M, N = 130, 160
+    x = gen.DenseInputs(np.full((M, K), 0x38, np.uint8), np.ones((K // 128, M), np.float32),
+                        np.full((N, K), 0x38, np.uint8),
+                        np.ones(((N + 127) // 128, K // 128), np.float32), M, N, K)
+    got = run_dense(x, torch.float32)
+    assert torch.all(got == K)
+
+
+def test_power_of_two_scales_are_bit_exact():
+    """A = B = 1, sa = 2^(m%5 + kb%3), sb = 2^-(kb + 2 nb): every block product is
+    128 and every promoted term is a power of two -> exact fp32 sums."""
+    announce("power-of-two scales")
+    M, N, K = 96, 384, 1024
+    KB, NB = K // 128, 3
+    sfa = np.array([[2.0 ** ((m % 5) + (kb % 3)) for m in range(M)] for kb in range(KB)], np.float32)
+    sfb = np.array([[2.0 ** (-kb - 2 * nb) for kb in range(KB)] for nb in range(NB)], np.float32)
+    x = gen.DenseInputs(np.full((M, K), 0x38, np.uint8), sfa, np.full((N, K), 0x38, np.uint8), sfb,
+                        M, N, K)
+    ref = oracle.gemm_nt(x.a, sfa, x.b, sfb)
+    got = run_dense(x, torch.float32).cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, ref)
+
+
+def test_determinism_and_cu_cap():
+    """Bitwise identical results run to run, and with the persistent grid capped
+    to a few CUs (each workgroup then walks many tiles)."""
+    announce("determinism + cu cap")
+    x = gen.gen_dense(512, 1024, 1024, seed=9)
+    d1 = run_dense(x)
+    d2 = run_dense(x)
+    assert torch.equal(d1, d2)
+    dg.set_num_cus(3)
+    try:
+        assert dg.get_num_cus() == 3
+        d3 = run_dense(x)
+    finally:
+        dg.set_num_cus(0)
+    assert torch.equal(d1, d3)
+
+
+# ------------------------------------------------------------------------------
+# M-grouped contiguous
+# ------------------------------------------------------------------------------
+
+def run_contiguous(x):
+    d = Guarded((x.M_tot, x.N), torch.bfloat16)
+    dg.m_grouped_fp8_gemm_nt_contiguous((dev(x.a), dev(x.sfa)), (dev(x.b), dev(x.sfb)), d.view,
+                                        dev(x.m_indices))
+    torch.cuda.synchronize()
+    assert d.intact(), "store outside D"
+    return d
+
+
+def test_contiguous_small_with_empty_expert_and_padding():
+    announce("contiguous small, empty expert")
+    x = gen.gen_contiguous(G=5, N=272, K=384, counts=np.array([130, 0, 5, 256, 1]), seed=11)
+    d = run_contiguous(x)
+    ref = oracle.m_grouped_contiguous(x.a, x.sfa, x.b, x.sfb, x.m_indices)
+    got = to64(d.view)
+    check_close(got, ref, "contiguous small")
+    pad = np.nonzero(x.m_indices < 0)[0]
+    assert d.untouched(torch.from_numpy(pad).cuda()), "padding rows were written"
+
+
+def test_contiguous_all_padding_is_noop():
+    announce("contiguous all -1")
+    x = gen.gen_contiguous(G=2, N=128, K=256, counts=np.array([3, 0]), seed=12)
+    x.m_indices[:] = -1
+    d = run_contiguous(x)
+    assert d.untouched(slice(None))
+
+
+def test_contiguous_matches_dense_bitwise():
+    """Each expert segment of the grouped call equals a dense call on that
+    segment, bit for bit (same kernel arithmetic, same order)."""
+    announce("contiguous vs dense bitwise")
+    x = gen.gen_contiguous(G=3, N=256, K=512, counts=np.array([200, 128, 70]), seed=13)
+    d = run_contiguous(x).view
+    start = 0
+    for e in range(3):
+        rows = int(x.counts[e])
+        seg = gen.DenseInputs(x.a[start:start + rows], np.ascontiguousarray(x.sfa[:, start:start + rows]),
+                              x.b[e], x.sfb[e], rows, x.N, x.K)
+        de = run_dense(seg)
+        assert torch.equal(d[start:start + rows], de), f"expert {e}"
+        start += ((rows + 127) // 128) * 128
+
+
+def test_contiguous_expert_isolation():
+    """Changing expert 1's weights changes only expert 1's rows."""
+    announce("contiguous expert isolation")
+    x = gen.gen_contiguous(G=3, N=128, K=256, counts=np.array([128, 128, 128]), seed=14)
+    d0 = run_contiguous(x).view.clone()
+    x.b[1] = np.roll(x.b[1], 1, axis=1)
+    d1 = run_contiguous(x).view
+    assert torch.equal(d0[:128], d1[:128]) and torch.equal(d0[256:], d1[256:])
+    assert not torch.equal(d0[128:256], d1[128:256])
+
+
+def test_c3_contiguous_full_size():
+    announce("contiguous C3 32 experts N=K=4096 zipf top6 seed0")
+    x = gen.gen_contiguous(seed=0)
+    d = run_contiguous(x)
+    rng = np.random.default_rng(0)
+    offs = np.concatenate([[0], np.cumsum(((x.counts + 127) // 128) * 128)])
+    rows = []
+    for e in range(x.G):
+        if x.counts[e] == 0:
+            continue
+        c = int(x.counts[e])
+        rows += [offs[e], offs[e] + c - 1] + list(offs[e] + rng.integers(0, c, 2))
+    rows = np.array(sorted(set(rows)), np.int64)
+    got = to64(d.view[torch.from_numpy(rows).cuda()])
+    ref = oracle.m_grouped_contiguous(x.a, x.sfa, x.b, x.sfb, x.m_indices, rows=rows)
+    print(check_close(got, ref, "C3"))
+    pad = np.nonzero(x.m_indices < 0)[0]
+    assert d.untouched(torch.from_numpy(pad).cuda())
+
+
+# ------------------------------------------------------------------------------
+# M-grouped masked
+# ------------------------------------------------------------------------------
+
+def run_masked(x, masked_m=None):
+    mm = x.masked_m if masked_m is None else masked_m
+    d = Guarded((x.G, x.M_max, x.N), torch.bfloat16)
+    dg.m_grouped_fp8_gemm_nt_masked((dev(x.a), dev(x.sfa)), (dev(x.b), dev(x.sfb)), d.view,
+                                    dev(np.asarray(mm, np.int32)))
+    torch.cuda.synchronize()
+    assert d.intact(), "store outside D"
+    return d
+
+
+def check_masked_rows_untouched(d, mm, M_max):
+    for g, m in enumerate(mm):
+        v = min(max(int(m), 0), M_max)
+        if v < M_max:
+            assert d.untouched((g, slice(v, None))), f"group {g}: rows >= {v} written"
+
+
+def test_masked_edge_counts():
+    mm = np.array([0, 1, 127, 128, 129, 256, -5, 999], np.int32)
+    announce(f"masked edges {mm.tolist()}")
+    x = gen.gen_masked(G=8, M_max=256, N=272, K=384, masked_m=mm, seed=21)
+    d = run_masked(x)
+    ref = oracle.m_grouped_masked(x.a, x.sfa, x.b, x.sfb, mm)
+    check_close(to64(d.view), ref, "masked edges")
+    check_masked_rows_untouched(d, mm, 256)
+
+
+def test_masked_all_zero_writes_nothing():
+    announce("masked all zero")
+    x = gen.gen_masked(G=3, M_max=64, N=128, K=256, masked_m=np.zeros(3, np.int32), seed=22)
+    d = run_masked(x)
+    assert d.untouched(slice(None))
+
+
+def test_masked_small_m_max():
+    announce("masked M_max=40 (64-row tiles)")
+    mm = np.array([40, 17, 0, 33], np.int32)
+    x = gen.gen_masked(G=4, M_max=40, N=144, K=256, masked_m=mm, seed=23)
+    d = run_masked(x)
+    check_close(to64(d.view), oracle.m_grouped_masked(x.a, x.sfa, x.b, x.sfb, mm), "masked small")
+    check_masked_rows_untouched(d, mm, 40)
+
+
+def test_c4_masked_full_size():
+    announce("masked C4 32 groups M_max=256 N=4096 K=2048 seed0")
+    x = gen.gen_masked(seed=0)
+    d = run_masked(x)
+    rng = np.random.default_rng(4)
+    groups, rows = [], []
+    for g in range(x.G):
+        v = int(x.masked_m[g])
+        if v == 0:
+            continue
+        for r in {0, v - 1, int(rng.integers(0, v))}:
+            groups.append(g)
+            rows.append(r)
+    groups, rows = np.array(groups), np.array(rows)
+    got = to64(d.view[torch.from_numpy(groups).cuda(), torch.from_numpy(rows).cuda()])
+    ref = oracle.m_grouped_masked(x.a, x.sfa, x.b, x.sfb, x.masked_m, groups=groups, rows=rows)
+    print(check_close(got, ref, "C4"))
+    check_masked_rows_untouched(d, x.masked_m, x.M_max)
+
+
+# ------------------------------------------------------------------------------
+# K-grouped TN
+# ------------------------------------------------------------------------------
+
+def run_tn(x, c=None, in_place=False):
+    d = Guarded((x.G, x.M, x.N), torch.float32)
+    cc = None
+    if c is not None:
+        if in_place:
+            d.view.copy_(dev(c))
+            cc = d.view
+        else:
+            cc = dev(c)
+    dg.k_grouped_fp8_gemm_tn_contiguous((dev(x.a), dev(x.sfa)), (dev(x.b), dev(x.sfb)), d.view,
+                                        x.k_sizes, c=cc)
+    torch.cuda.synchronize()
+    assert d.intact(), "store outside D"
+    return d.view
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_k_grouped_small_with_empty_groups(in_place):
+    announce(f"k-grouped small in_place={in_place}")
+    ks = np.array([256, 0, 640, 128, 0], np.int32)
+    x = gen.gen_k_grouped(G=5, M=144, N=272, K_tot=int(ks.sum()), k_sizes=ks, seed=31)
+    d = run_tn(x, c=x.c, in_place=in_place)
+    ref = oracle.k_grouped_tn(x.a, x.sfa, x.b, x.sfb, x.k_sizes, x.c)
+    got = d.cpu().numpy().astype(np.float64)
+    check_close(got, ref, "tn small")
+    for g in (1, 4):
+        assert np.array_equal(got[g], x.c[g].astype(np.float64)), "K_g = 0 must give C"
+
+
+def test_k_grouped_without_c():
+    announce("k-grouped no C")
+    ks = np.array([384, 128, 0], np.int32)
+    x = gen.gen_k_grouped(G=3, M=128, N=256, K_tot=512, k_sizes=ks, seed=32, with_c=False)
+    d = run_tn(x)
+    ref = oracle.k_grouped_tn(x.a, x.sfa, x.b, x.sfb, x.k_sizes, None)
+    got = d.cpu().numpy().astype(np.float64)
+    check_close(got[:2], ref[:2], "tn no C")
+    assert np.all(got[2] == 0)
+
+
+def test_k_grouped_power_of_two_is_bit_exact():
+    announce("k-grouped pow2 exact")
+    ks = np.array([256, 128], np.int32)
+    K_tot, M, N = 384, 64, 96
+    a = np.full((K_tot, M), 0x38, np.uint8)
+    b = np.full((K_tot, N), 0x38, np.uint8)
+    sfa = np.array([[2.0 ** ((m % 4) - kb) for m in range(M)] for kb in range(3)], np.float32)
+    sfb = np.array([[2.0 ** ((n % 3) + kb) for n in range(N)] for kb in range(3)], np.float32)
+    x = gen.KGroupedInputs(a, sfa, b, sfb, ks, ks.astype(np.int64), None, 2, M, N, K_tot)
+    got = run_tn(x).cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, oracle.k_grouped_tn(a, sfa, b, sfb, ks))
+
+
+def test_c5_k_grouped_full_size():
+    announce("k-grouped C5 32 groups M=2048 N=4096 K_tot=49152 seed0")
+    x = gen.gen_k_grouped(seed=0)
+    d = run_tn(x, c=x.c)
+    rng = np.random.default_rng(5)
+    groups = np.repeat(np.arange(x.G), 2)
+    rows = rng.integers(0, x.M, len(groups))
+    rows[0], rows[-1] = 0, x.M - 1
+    got = d[torch.from_numpy(groups).cuda(), torch.from_numpy(rows).cuda()].cpu().numpy()
+    ref = oracle.k_grouped_tn(x.a, x.sfa, x.b, x.sfb, x.k_sizes, x.c, groups=groups, rows=rows)
+    print(check_close(got.astype(np.float64), ref, "C5"))
