@@ -63,24 +63,34 @@ struct NtCfg {
     static constexpr int SN = WTN / 16;        // along n
     static constexpr int A_BYTES = BM * kKBlk;
     static constexpr int B_BYTES = BN * kKBlk;
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int A_LD = A_BYTES / (16 * THREADS);   // 16-byte loads per thread
-    static constexpr int B_LD = B_BYTES / (16 * THREADS);
+    static constexpr int SA_BYTES = BM * 4;    // this tile's A scales for the stage's K block
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES;
+    static constexpr int SA_DMA = BM / 64;     // 256-byte (64-float) wave copies per stage
+    static constexpr int A_DMA = BM / 8;       // 1 KiB (8-row) wave copies per stage for A
+    static constexpr int B_DMA = BN / 8;
+    static constexpr int DMA_PER_WAVE = (A_DMA + B_DMA) / WAVES;
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
-    static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0,
-                  "tile bytes must split evenly over the workgroup");
-    static_assert(BN <= 128 || BN % 128 == 0, "an MFMA tile must not straddle a B scale block");
+    static_assert((A_DMA + B_DMA) % WAVES == 0, "stage copies must split evenly over waves");
+    static_assert(SA_DMA >= 1 && SA_DMA <= WAVES, "one scale copy per wave at most");
+    static_assert(SM % 4 == 0, "a lane reads its A scales as float4s");
+    static_assert(kKBlk % WTN == 0 && (BN % kKBlk == 0 || kKBlk % BN == 0),
+                  "a wave's columns must sit inside one 128-column B scale block");
 };
 
+// Rows of a wave tile are dealt to lanes so that lane l owns the SM
+// consecutive rows SM * (l & 15) + i, i = 0..SM-1 (MFMA tile i takes row
+// SM * r + i as its r-th column).  A lane's A scales are then SM consecutive
+// floats.  Columns follow the MFMA layout: tile j, lane l owns the four
+// columns 16 j + 4 (l >> 4) + {0, 1, 2, 3}.
 template <class Cfg, int FORM, bool OUT_F32>
 __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, THREADS = Cfg::THREADS;
-    constexpr int SM = Cfg::SM, SN = Cfg::SN, A_LD = Cfg::A_LD, B_LD = Cfg::B_LD;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Cfg::STAGE_BYTES];
+    constexpr int BM = Cfg::BM, BN = Cfg::BN;
+    constexpr int SM = Cfg::SM, SN = Cfg::SN;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * Cfg::STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / Cfg::WAVES_N;
     const int wn = wave % Cfg::WAVES_N;
     const int KB = p.K / kKBlk;
@@ -99,7 +109,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
         const int tn = local / p.tiles_m;
         const int r0 = tm * BM;        // first row of the tile, relative to its group
         const int n0 = tn * BN;
-        int grp_rows = p.rows;         // rows that exist in memory for this group
+        const int grp_rows = p.rows;   // rows that exist in memory for this group
         int store_rows = p.rows;       // rows that may be written
         int64_t grp_row0 = 0;          // first row of the group in A / D
         if (FORM == kMasked) {
@@ -115,38 +125,42 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
 
         const uint8_t* __restrict__ a_t = p.a + grp_row0 * p.K;
         const uint8_t* __restrict__ b_t = p.b + (int64_t)e * p.N * p.K;
-        const int sfa_ld = p.rows;
         const float* __restrict__ sfa_t = p.sfa + (FORM == kMasked ? (int64_t)g * KB * p.rows : 0);
         const float* __restrict__ sfb_t = p.sfb + (int64_t)e * NB * KB;
 
-        // per-thread global offsets (rows clamped to what exists) and LDS offsets
-        uint32_t ga_off[A_LD], gb_off[B_LD];
-        int la_off[A_LD], lb_off[B_LD];
+        // Stage copies: wave copy u (uniform) moves 8 rows x 128 bytes; lane l
+        // fetches chunk (l & 7) ^ swz(row) of row 8 u' + (l >> 3) so that the
+        // LDS image is the swizzled layout.  Rows past the edge re-read the
+        // last row (never stored).
+        uint32_t goff[Cfg::DMA_PER_WAVE];
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            const int ch = tid + i * THREADS;
-            const int rr = ch >> 3, cc = ch & 7;
-            const int row = min(r0 + rr, grp_rows - 1);
-            ga_off[i] = (uint32_t)row * (uint32_t)p.K + cc * 16;
-            la_off[i] = lds_chunk_off(rr, cc);
+        for (int q = 0; q < Cfg::DMA_PER_WAVE; ++q) {
+            const int u = wave * Cfg::DMA_PER_WAVE + q;
+            const bool is_a = u < Cfg::A_DMA;
+            const int lrow = 8 * (is_a ? u : u - Cfg::A_DMA) + (lane >> 3);
+            const int chunk = (lane & 7) ^ swz(lrow);
+            const int row = is_a ? min(r0 + lrow, grp_rows - 1) : min(n0 + lrow, p.N - 1);
+            goff[q] = (uint32_t)row * (uint32_t)p.K + (uint32_t)(chunk * 16);
         }
+        // A scales: wave w < SA_DMA copies floats [64 w, 64 w + 64) of this
+        // tile's rows for the K block (one float per lane, rows clamped).
+        const uint32_t sa_off = 4u * (uint32_t)min(r0 + 64 * wave + lane, grp_rows - 1);
+        const uint32_t lds0 = lds_addr(smem);
+        auto issue_stage = [&](int kb, int stage) {
+            const uint32_t dst = lds0 + stage * Cfg::STAGE_BYTES;
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i) {
-            const int ch = tid + i * THREADS;
-            const int rr = ch >> 3, cc = ch & 7;
-            const int row = min(n0 + rr, p.N - 1);
-            gb_off[i] = (uint32_t)row * (uint32_t)p.K + cc * 16;
-            lb_off[i] = BM * kKBlk + lds_chunk_off(rr, cc);
-        }
-        // scale indices of this lane's rows and of this wave's 16-column tiles
-        int sa_idx[SM];
-#pragma unroll
-        for (int i = 0; i < SM; ++i)
-            sa_idx[i] = min(r0 + wm * Cfg::WTM + 16 * i + (lane & 15), grp_rows - 1);
-        int sb_idx[SN];
-#pragma unroll
-        for (int j = 0; j < SN; ++j)
-            sb_idx[j] = min((n0 + wn * Cfg::WTN + 16 * j) / kKBlk, NB - 1) * KB;
+            for (int q = 0; q < Cfg::DMA_PER_WAVE; ++q) {
+                const int u = wave * Cfg::DMA_PER_WAVE + q;
+                const uint8_t* src = (u < Cfg::A_DMA ? a_t : b_t) + (size_t)kb * kKBlk;
+                dma16(src, goff[q], dst + u * 1024);
+            }
+            if (wave < Cfg::SA_DMA)
+                dma4(sfa_t + (size_t)kb * grp_rows, sa_off,
+                     dst + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256);
+        };
+
+        const int m_lane0 = r0 + wm * Cfg::WTM + SM * (lane & 15);
+        const int sb_row = min((n0 + wn * Cfg::WTN) / kKBlk, NB - 1) * KB;
 
         f32x4 acc[SM][SN];
 #pragma unroll
@@ -155,89 +169,98 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             for (int j = 0; j < SN; ++j)
                 acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        i32x4 ra[A_LD], rb[B_LD];
-        float sa_cur[SM], sb_cur[SN], sa_nxt[SM], sb_nxt[SN];
-
-        // ---- prologue: block 0 into stage 0 ------------------------------------
+        float sb_nxt = 0.f;
         if (KB > 0) {
-#pragma unroll
-            for (int i = 0; i < A_LD; ++i)
-                ra[i] = *reinterpret_cast<const i32x4*>(a_t + ga_off[i]);
-#pragma unroll
-            for (int i = 0; i < B_LD; ++i)
-                rb[i] = *reinterpret_cast<const i32x4*>(b_t + gb_off[i]);
-#pragma unroll
-            for (int i = 0; i < SM; ++i) sa_nxt[i] = sfa_t[sa_idx[i]];
-#pragma unroll
-            for (int j = 0; j < SN; ++j) sb_nxt[j] = sfb_t[sb_idx[j]];
-#pragma unroll
-            for (int i = 0; i < A_LD; ++i)
-                *reinterpret_cast<i32x4*>(smem + la_off[i]) = ra[i];
-#pragma unroll
-            for (int i = 0; i < B_LD; ++i)
-                *reinterpret_cast<i32x4*>(smem + lb_off[i]) = rb[i];
+            issue_stage(0, 0);
+            sb_nxt = sfb_t[sb_row];
         }
-        __syncthreads();
-
-        // ---- main loop over 128-wide K blocks ------------------------------------
         for (int kb = 0; kb < KB; ++kb) {
-            const int cur = kb & 1;
-#pragma unroll
-            for (int i = 0; i < SM; ++i) sa_cur[i] = sa_nxt[i];
-#pragma unroll
-            for (int j = 0; j < SN; ++j) sb_cur[j] = sb_nxt[j];
-            const bool more = kb + 1 < KB;
-            if (more) {
-                const uint8_t* an = a_t + (kb + 1) * kKBlk;
-                const uint8_t* bn = b_t + (kb + 1) * kKBlk;
-#pragma unroll
-                for (int i = 0; i < A_LD; ++i)
-                    ra[i] = *reinterpret_cast<const i32x4*>(an + ga_off[i]);
-#pragma unroll
-                for (int i = 0; i < B_LD; ++i)
-                    rb[i] = *reinterpret_cast<const i32x4*>(bn + gb_off[i]);
-#pragma unroll
-                for (int i = 0; i < SM; ++i) sa_nxt[i] = sfa_t[(kb + 1) * sfa_ld + sa_idx[i]];
-#pragma unroll
-                for (int j = 0; j < SN; ++j) sb_nxt[j] = sfb_t[sb_idx[j] + kb + 1];
-            }
-
-            const uint8_t* sA = smem + cur * Cfg::STAGE_BYTES;
+            // stage kb has landed for every wave, and every wave is done with
+            // the stage the next copies overwrite
+            vm_lgkm_drain_barrier();
+            // Take the B scale (loaded last iteration, so already here) into a
+            // scalar register now: the compiler's wait for it must come before
+            // the copies below, or it would also wait for them.
+            int sb_bits = __builtin_amdgcn_readfirstlane(__float_as_int(sb_nxt));
+            asm volatile("" : "+s"(sb_bits));
+            const float sb = __int_as_float(sb_bits);
+            // The copy for block kb+1 goes to the other stage (a branch here,
+            // ahead of the compute, leaves the compute one basic block).
+            const int kn = kb + 1 < KB ? kb + 1 : kb;
+            if (kb + 1 < KB) issue_stage(kn, (kb + 1) & 1);
+            const uint8_t* sA = smem + (kb & 1) * Cfg::STAGE_BYTES;
             const uint8_t* sB = sA + Cfg::A_BYTES;
+            const float* sS = reinterpret_cast<const float*>(sB + Cfg::B_BYTES);
+
+            // Software pipeline over the wave's MFMA rows: the block products of
+            // row i are issued while row i-1 is promoted, so no FMA waits on
+            // the MFMA it depends on.
+            float sa[SM];
+#pragma unroll
+            for (int i = 0; i < SM; i += 4) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(sS + wm * Cfg::WTM + SM * (lane & 15) + i);
+                sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
+            }
             i32x8 bfrag[SN];
 #pragma unroll
             for (int j = 0; j < SN; ++j)
                 bfrag[j] = lds_fragment(sB, wn * Cfg::WTN + 16 * j, lane);
+            i32x8 afrag = lds_fragment_row(sA, wm * Cfg::WTM + SM * (lane & 15), lane);
+            f32x4 pend[SN];
 #pragma unroll
             for (int i = 0; i < SM; ++i) {
-                const i32x8 afrag = lds_fragment(sA, wm * Cfg::WTM + 16 * i, lane);
+                i32x8 anext;
+                if (i + 1 < SM)
+                    anext = lds_fragment_row(sA, wm * Cfg::WTM + SM * (lane & 15) + i + 1, lane);
+                f32x4 pcur[SN];
+#pragma unroll
+                for (int j = 0; j < SN; ++j) pcur[j] = mfma_e4m3_block(bfrag[j], afrag);
+                if (i > 0) {
+                    const float s = sa[i - 1] * sb;
+#pragma unroll
+                    for (int j = 0; j < SN; ++j) {
+                        acc[i - 1][j].x = __builtin_fmaf(pend[j].x, s, acc[i - 1][j].x);
+                        acc[i - 1][j].y = __builtin_fmaf(pend[j].y, s, acc[i - 1][j].y);
+                        acc[i - 1][j].z = __builtin_fmaf(pend[j].z, s, acc[i - 1][j].z);
+                        acc[i - 1][j].w = __builtin_fmaf(pend[j].w, s, acc[i - 1][j].w);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < SN; ++j) pend[j] = pcur[j];
+                if (i + 1 < SM) afrag = anext;
+                // Issue order inside the segment: the next A fragment's LDS reads
+                // first (a whole segment ahead of their use), then each block
+                // product followed by a share of the previous row's promotion.
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // 2 DS reads
 #pragma unroll
                 for (int j = 0; j < SN; ++j) {
-                    const f32x4 pblk = mfma_e4m3_block(bfrag[j], afrag);
-                    const float s = sa_cur[i] * sb_cur[j];
-                    acc[i][j].x = __builtin_fmaf(pblk.x, s, acc[i][j].x);
-                    acc[i][j].y = __builtin_fmaf(pblk.y, s, acc[i][j].y);
-                    acc[i][j].z = __builtin_fmaf(pblk.z, s, acc[i][j].z);
-                    acc[i][j].w = __builtin_fmaf(pblk.w, s, acc[i][j].w);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // 5 VALU
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            {
+                const float s = sa[SM - 1] * sb;
+#pragma unroll
+                for (int j = 0; j < SN; ++j) {
+                    acc[SM - 1][j].x = __builtin_fmaf(pend[j].x, s, acc[SM - 1][j].x);
+                    acc[SM - 1][j].y = __builtin_fmaf(pend[j].y, s, acc[SM - 1][j].y);
+                    acc[SM - 1][j].z = __builtin_fmaf(pend[j].z, s, acc[SM - 1][j].z);
+                    acc[SM - 1][j].w = __builtin_fmaf(pend[j].w, s, acc[SM - 1][j].w);
                 }
             }
-
-            if (more) {
-                uint8_t* nxt = smem + (cur ^ 1) * Cfg::STAGE_BYTES;
-#pragma unroll
-                for (int i = 0; i < A_LD; ++i)
-                    *reinterpret_cast<i32x4*>(nxt + la_off[i]) = ra[i];
-#pragma unroll
-                for (int i = 0; i < B_LD; ++i)
-                    *reinterpret_cast<i32x4*>(nxt + lb_off[i]) = rb[i];
-            }
-            __syncthreads();
+            // The B scale is a uniform (scalar-cache) load; issuing it after the
+            // LDS reads keeps it from forcing full LDS-counter waits above.
+            __builtin_amdgcn_sched_barrier(0);
+            sb_nxt = sfb_t[sb_row + kn];
         }
+        // every wave is past its last LDS read before the next tile's copies
+        lds_barrier();
 
         // ---- epilogue: (+C), convert once, masked store ---------------------------
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
-            const int m = r0 + wm * Cfg::WTM + 16 * i + (lane & 15);
+            const int m = m_lane0 + i;
             bool row_ok = m < store_rows;
             if (FORM == kContiguous && row_ok) row_ok = p.m_indices[m] == e;
             if (!row_ok) continue;
@@ -269,8 +292,6 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
                 }
             }
         }
-        // The next tile's prologue rewrites stage 0; every wave is past its last
-        // read of either stage because the K loop ends with a barrier.
     }
 }
 
@@ -309,16 +330,32 @@ hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     return hipGetLastError();
 }
 
+using Cfg256x256 = NtCfg<256, 256, 2, 4>;
 using Cfg128x128 = NtCfg<128, 128, 2, 2>;
 using Cfg64x128 = NtCfg<64, 128, 1, 4>;
 
+using Cfg128x256 = NtCfg<128, 256, 2, 4>;
+
+// Tile choice: 256 x 256 (8 waves of 128 x 64) for large dense problems,
+// 128 x 256 for contiguous groups (a tile may not straddle two 128-row expert
+// blocks), 128 x 128 for mid-size rows, 64 x 128 for decode-size groups.
+enum NtTile { kT64x128, kT128x128, kT128x256, kT256x256 };
+
+NtTile choose_tile(const NtProblem& pr) {
+    if (pr.form == kContiguous) return kT128x256;
+    if (pr.rows <= 64) return kT64x128;
+    if (pr.form == kDense && pr.rows >= 1024 && pr.N >= 1024) return kT256x256;
+    return kT128x128;
+}
+
 template <int FORM, bool OUT_F32>
 hipError_t dispatch_tiles(const NtProblem& pr, int cu_cap, hipStream_t stream) {
-    // Rows per group decide the M tile: small-M (decode-like) problems use
-    // 64-row tiles so fewer rows of MFMA work are wasted.
-    const bool small_m = (FORM == kMasked) ? pr.rows <= 64 : (FORM == kDense && pr.rows <= 64);
-    if (small_m) return launch_cfg<Cfg64x128, FORM, OUT_F32>(pr, cu_cap, stream);
-    return launch_cfg<Cfg128x128, FORM, OUT_F32>(pr, cu_cap, stream);
+    switch (choose_tile(pr)) {
+    case kT64x128: return launch_cfg<Cfg64x128, FORM, OUT_F32>(pr, cu_cap, stream);
+    case kT128x256: return launch_cfg<Cfg128x256, FORM, OUT_F32>(pr, cu_cap, stream);
+    case kT256x256: return launch_cfg<Cfg256x256, FORM, OUT_F32>(pr, cu_cap, stream);
+    default: return launch_cfg<Cfg128x128, FORM, OUT_F32>(pr, cu_cap, stream);
+    }
 }
 
 }  // namespace
@@ -338,10 +375,11 @@ hipError_t launch_nt(const NtProblem& pr, int cu_cap, hipStream_t stream) {
 
 const char* describe_nt_config(const NtProblem& pr) {
     static thread_local char buf[160];
-    const bool small_m = (pr.form == kMasked) ? pr.rows <= 64 : (pr.form == kDense && pr.rows <= 64);
+    static const char* names[] = {"64x128 (1x4 waves)", "128x128 (2x2 waves)",
+                                  "128x256 (2x4 waves)", "256x256 (2x4 waves)"};
     snprintf(buf, sizeof buf, "nt form=%d rows=%lld N=%lld K=%lld G=%lld tile=%s", (int)pr.form,
              (long long)pr.rows, (long long)pr.N, (long long)pr.K, (long long)pr.G,
-             small_m ? "64x128 (1x4 waves)" : "128x128 (2x2 waves)");
+             names[choose_tile(pr)]);
     return buf;
 }
 

@@ -11,13 +11,16 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 constexpr int kKBlk = 128;   // K extent of one scale block = one MFMA K step
 
 // LDS tiles hold 128-byte rows (one 128-wide K block of one row of A or B).
 // A row is eight 16-byte chunks; chunk c of row r lives at position
-// c ^ swz(r).  Eight consecutive rows therefore spread one chunk index over
-// all eight positions (conflict-free fragment reads), and rows eight apart
-// are permuted too (conflict-light transposed writes in the TN kernel).
+// c ^ swz(r).  Eight consecutive rows spread one chunk index over all eight
+// positions, and so do rows eight apart (conflict-free fragment reads for
+// both the plain and the strided row maps, and conflict-light transposed
+// writes in the TN kernel).
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 __device__ __forceinline__ int lds_chunk_off(int row, int chunk) {
@@ -39,9 +42,9 @@ __device__ __forceinline__ f32x4 mfma_e4m3_block(const i32x8& rows, const i32x8&
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rows, cols, zero, 0, 0, 0, 0, 0, 0);
 }
 
-// Fragment of 16 consecutive LDS rows starting at row0 (see the layout above).
-__device__ __forceinline__ i32x8 lds_fragment(const uint8_t* tile, int row0, int lane) {
-    const int row = row0 + (lane & 15);
+// Fragment whose lane l takes LDS row `row` (callers pass the row of their
+// lane) and the 32 K bytes [32 * (l >> 4), +32) of it.
+__device__ __forceinline__ i32x8 lds_fragment_row(const uint8_t* tile, int row, int lane) {
     const int c0 = (lane >> 4) * 2;
     const i32x4 lo = *reinterpret_cast<const i32x4*>(tile + lds_chunk_off(row, c0));
     const i32x4 hi = *reinterpret_cast<const i32x4*>(tile + lds_chunk_off(row, c0 + 1));
@@ -49,6 +52,11 @@ __device__ __forceinline__ i32x8 lds_fragment(const uint8_t* tile, int row0, int
     r.s0 = lo.x; r.s1 = lo.y; r.s2 = lo.z; r.s3 = lo.w;
     r.s4 = hi.x; r.s5 = hi.y; r.s6 = hi.z; r.s7 = hi.w;
     return r;
+}
+
+// Fragment of 16 consecutive LDS rows starting at row0.
+__device__ __forceinline__ i32x8 lds_fragment(const uint8_t* tile, int row0, int lane) {
+    return lds_fragment_row(tile, row0 + (lane & 15), lane);
 }
 
 // Round-to-nearest-even fp32 -> bf16 of four values, packed as two dwords
@@ -66,6 +74,50 @@ __device__ __forceinline__ i32x2 pack_bf16x4(float x0, float x1, float x2, float
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
     return __uint_as_float(h16 << 16);
+}
+
+// LDS address (byte offset in the workgroup's LDS) of a pointer into a
+// __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(p)));
+}
+
+// Direct global -> LDS copies (global_load_lds_dwordx4 / _dword).  Lane l's
+// 16 (or 4) bytes at base + voff land at LDS byte lds + 16 * l (or 4 * l), so
+// one wave instruction fills 1024 (or 256) consecutive LDS bytes.  `base` and
+// `lds` must be wave-uniform.  Written as inline asm so the compiler does not
+// treat the in-flight copies as aliasing every LDS read (which would drain
+// the vector-memory counter before each fragment read); the kernels wait for
+// the copies explicitly (vm_drain_barrier).  Extra outstanding loads the
+// compiler does not know about only make its own vmcnt waits stricter.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+
+// Wait for this wave's outstanding vector-memory loads (including the LDS
+// DMA above), then a workgroup barrier.  The asm memory clobber keeps the
+// compiler from moving LDS or global accesses across it.
+__device__ __forceinline__ void vm_drain_barrier() {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void vm_lgkm_drain_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 }  // namespace dg
