@@ -36,6 +36,18 @@ PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (published)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
 MACHINE_BALANCE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # FLOP per byte
 
+# The rocprofv3 runs behind the profiles/ summaries (repository root, one GPU).
+PROFILE_COMMANDS = [
+    "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o run -- "
+    "python3 bench.py --steps 5 --warmup 1 --no-detail --no-cpu --json-out gpurun_out/bench_prof.json",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o run -- "
+    "python3 bench.py --steps 1 --warmup 0 --no-detail --no-cpu --copy-calibration",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o run -- "
+    "python3 bench.py --steps 1 --warmup 0 --no-detail --no-cpu --copy-calibration",
+    "python3 bench.py --summarize-profiles gpurun_out/prof_trace gpurun_out/prof_fetch "
+    "gpurun_out/prof_write gpurun_out/bench_prof.json profiles/<kernel>__dense_sweep.md",
+]
+
 
 def dense_bytes(M, N, K, d_bytes=2):
     return M * K + N * K + 4 * (K // 128) * M + 4 * ((N + 127) // 128) * (K // 128) + d_bytes * M * N
@@ -50,12 +62,21 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device copy before the GEMMs (a kernel of known "
+                         "traffic, to scale hardware byte counters)")
+    ap.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE_DIR", "FETCH_DIR",
+                                                              "WRITE_DIR", "BENCH_JSON", "OUT_MD"),
+                    help="write a profiles/ summary from rocprofv3 CSV output and exit")
     args = ap.parse_args()
 
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, commands=PROFILE_COMMANDS)
+        return
+
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the kernels are single-GPU; see the sharding notes in the design document)",
-              file=sys.stderr)
+        print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported (the kernels run on "
+              "one GPU's shard; the multi-GPU exchange is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -81,10 +102,19 @@ def main():
         a, sa, b, sb = up(x.a), up(x.sfa), up(x.b), up(x.sfb)
         d = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
         ops.append(dict(shape=(M, N, K), args=((a, sa), (b, sb), d), flop=2.0 * M * N * K,
-                        bytes=dense_bytes(M, N, K)))
+                        bytes=dense_bytes(M, N, K),
+                        kernel=dg.kernel_config_name(dg.FORM_DENSE, M, N, K)))
         del x
     gen_s = time.time() - t0
     print(f"[bench] generated dense sweep in {gen_s:.1f}s", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(events=None):
         for i, op in enumerate(ops):
@@ -114,25 +144,41 @@ def main():
     value = flop_step * args.steps / elapsed / 1e12
     ms_per_step = elapsed * 1e3 / args.steps
 
-    dom = int(np.argmax(avg_ms))
-    dop = ops[dom]
-    M, N, K = dop["shape"]
-    intensity = dop["flop"] / dop["bytes"]
+    # Dominant kernel: the kernel instance (tile configuration) with the largest
+    # share of the step's time.  Several shapes may share one instance, so its
+    # per-launch figures are averages over the launches of that instance in
+    # the timed region -- the same average a kernel-trace profile reports for
+    # that kernel name.
+    groups = {}
+    for i, op in enumerate(ops):
+        groups.setdefault(op["kernel"], []).append(i)
+    dom_name = max(groups, key=lambda k: sum(avg_ms[i] for i in groups[k]))
+    idx = groups[dom_name]
+    launch_ms = float(np.mean([avg_ms[i] for i in idx]))
+    launch_flop = float(np.mean([ops[i]["flop"] for i in idx]))
+    launch_bytes = float(np.mean([ops[i]["bytes"] for i in idx]))
+    intensity = launch_flop / launch_bytes
     if intensity >= MACHINE_BALANCE:
-        achieved = dop["flop"] / (avg_ms[dom] * 1e-3) / 1e12
+        achieved = launch_flop / (launch_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_FP8_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / PEAK_FP8_TFLOPS, 4), traffic=None)
     else:
-        achieved = dop["bytes"] / (avg_ms[dom] * 1e-3) / 1e9
+        achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None)
-    roof["kernel"] = f"nt_fp8_kernel dense {M}x{N}x{K}"
-    roof["avg_launch_us"] = round(avg_ms[dom] * 1e3, 2)
+    roof["traffic"] = measured_traffic(dom_name)
+    roof["kernel"] = dom_name
+    roof["launches_per_step"] = len(idx)
+    roof["shapes"] = ["x".join(map(str, ops[i]["shape"])) for i in idx]
+    roof["avg_launch_us"] = round(launch_ms * 1e3, 2)
+    roof["alg_flop_per_launch"] = launch_flop
+    roof["alg_bytes_per_launch"] = launch_bytes
+    M, N, K = ops[max(idx, key=lambda i: avg_ms[i])]["shape"]
 
     per_shape = []
     for op, t in zip(ops, avg_ms):
         m, n, k = op["shape"]
-        per_shape.append(dict(M=m, N=n, K=k, us=round(t * 1e3, 2),
+        per_shape.append(dict(M=m, N=n, K=k, kernel=op["kernel"], us=round(t * 1e3, 2),
                               tflops=round(op["flop"] / (t * 1e-3) / 1e12, 1),
                               gbs=round(op["bytes"] / (t * 1e-3) / 1e9, 1)))
     print(f"[bench] step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
@@ -175,6 +221,103 @@ def main():
     if args.json_out:
         with open(args.json_out, "w") as f:
             f.write(line + "\n")
+
+
+# ------------------------------------------------------------------------------
+# rocprofv3 summaries (profiles/) and the measured-traffic lookup
+# ------------------------------------------------------------------------------
+
+KERNEL_SOURCES = {
+    "nt": ["fp8_fine_grained_e4m3_amd/csrc/nt_kernel.hip",
+           "fp8_fine_grained_e4m3_amd/csrc/tile_common.h",
+           "fp8_fine_grained_e4m3_amd/csrc/dg_internal.h"],
+    "tn": ["fp8_fine_grained_e4m3_amd/csrc/tn_kernel.hip",
+           "fp8_fine_grained_e4m3_amd/csrc/tile_common.h",
+           "fp8_fine_grained_e4m3_amd/csrc/dg_internal.h"],
+}
+
+
+def source_hash(family: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[family]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config_name: str):
+    """HBM-side bytes per launch recorded in profiles/ for this kernel instance,
+    or None when there is no record or the kernel sources changed since."""
+    import glob
+    import re
+    fam = config_name.split("_")[0]
+    for path in glob.glob(os.path.join(ROOT, "profiles", f"{config_name}__*.md")):
+        text = open(path).read()
+        m = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)", text)
+        h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+        if m and h and fam in KERNEL_SOURCES and h.group(1) == source_hash(fam):
+            return float(m.group(1))
+    return None
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, bench_json, out_path, commands):
+    """Write the profiles/ summary of one kernel instance from rocprofv3 CSVs."""
+    import csv
+    res = json.load(open(bench_json))
+    roof = res["roofline"]
+    name = roof["kernel"]
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+
+    def counters(d, counter):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        return [(r["Kernel_Name"], float(r["Counter_Value"]), int(r["Grid_Size"])) for r in rows
+                if r["Counter_Name"] == counter]
+
+    fetch = counters(fetch_dir, "FETCH_SIZE")
+    write = counters(write_dir, "WRITE_SIZE")
+    copy_bytes = float(1 << 30)
+    fetch_copy = max(v for k, v, g in fetch if "copyBuffer" in k) * 1024.0
+    write_copy = max(v for k, v, g in write if "copyBuffer" in k) * 1024.0
+    f_scale, w_scale = copy_bytes / fetch_copy, copy_bytes / write_copy
+    tag = {"256x256": "NtCfg<256, 256, 2, 4>", "128x256": "NtCfg<128, 256, 2, 4>",
+           "128x128": "NtCfg<128, 128, 2, 2>", "64x128": "NtCfg<64, 128, 1, 4>"}[name.split("_")[-1]]
+    f_k = [v for k, v, g in fetch if tag in k]
+    w_k = [v for k, v, g in write if tag in k]
+    fetch_b = float(np.mean(f_k)) * 1024.0 * f_scale
+    write_b = float(np.mean(w_k)) * 1024.0 * w_scale
+    lines = [f"# {name} -- dense FP8 NT sweep (M=4096 shapes), rocprofv3", "",
+             "Commands (run from the repository root on one MI355X):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "## Kernel trace (--kernel-trace --stats)", "",
+              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:80]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
+    avg_us = [float(r["AverageNs"]) / 1e3 for r in stats if tag in r["Name"]][0]
+    lines += ["", f"Dominant instance `{tag}` = `{name}`: rocprofv3 average {avg_us:.2f} us per "
+              f"launch; bench.py's HIP-event average over its timed region {roof['avg_launch_us']} us.",
+              f"Launches of this instance per step: {roof['launches_per_step']} "
+              f"({', '.join(roof['shapes'])}).",
+              f"Algorithmic work per launch (mean over those shapes): "
+              f"{roof['alg_flop_per_launch'] / 1e9:.2f} GFLOP, {roof['alg_bytes_per_launch'] / 1e6:.2f} MB.",
+              "", "## Traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
+              f"Calibration: a 1 GiB device copy (`__amd_rocclr_copyBuffer`) reads FETCH_SIZE "
+              f"{fetch_copy / 1024:.0f} KiB and WRITE_SIZE {write_copy / 1024:.0f} KiB, so the "
+              f"scale factors are {f_scale:.4f} (fetch) and {w_scale:.4f} (write).",
+              "", "| dispatch of this instance | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|"]
+    for i, (fv, wv) in enumerate(zip(f_k, w_k)):
+        lines.append(f"| {i} | {fv:.1f} | {wv:.1f} |")
+    lines += ["", f"Scaled per launch: fetch {fetch_b / 1e6:.1f} MB + write {write_b / 1e6:.1f} MB "
+              f"= {(fetch_b + write_b) / 1e6:.1f} MB, {(fetch_b + write_b) / roof['alg_bytes_per_launch']:.2f}x "
+              f"the algorithmic bytes.",
+              "", "Machine-readable:", "",
+              f"    traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+              f"    kernel_source_sha256_16: {source_hash(name.split('_')[0])}",
+              f"    bench_value_tflops: {res['value']}", ""]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines))
+    print(out_path)
 
 
 def bench_grouped(dg, gen, up, dev, stream, args):

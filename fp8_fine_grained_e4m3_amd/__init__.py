@@ -35,6 +35,7 @@ EXPORTED = (
     "dg_get_num_cus",
     "dg_set_num_cus",
     "dg_get_mk_alignment_for_contiguous_layout",
+    "dg_kernel_config_name",
 )
 
 _lib = None
@@ -71,6 +72,8 @@ def load_library(path: Optional[str] = None):
     lib.dg_set_num_cus.restype = I
     lib.dg_get_mk_alignment_for_contiguous_layout.argtypes = []
     lib.dg_get_mk_alignment_for_contiguous_layout.restype = I
+    lib.dg_kernel_config_name.argtypes = [I, I64, I64, I64, I]
+    lib.dg_kernel_config_name.restype = ctypes.c_char_p
     if path is None:
         _lib = lib
     return lib
@@ -229,6 +232,14 @@ def set_num_cus(n: int) -> None:
 
 def get_mk_alignment_for_contiguous_layout() -> int:
     return load_library().dg_get_mk_alignment_for_contiguous_layout()
+
+
+FORM_DENSE, FORM_CONTIGUOUS, FORM_MASKED, FORM_K_GROUPED = 0, 1, 2, 3
+
+
+def kernel_config_name(form: int, rows: int, N: int, K: int, out_f32: bool = False) -> str:
+    """Kernel instance (tile configuration) a call with these sizes launches."""
+    return load_library().dg_kernel_config_name(form, rows, N, K, int(out_f32)).decode()
 
 
 def to_mn_major_sf(sf: torch.Tensor) -> torch.Tensor:

@@ -278,4 +278,20 @@ dg_status dg_set_num_cus(int n) {
 
 int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }
 
+const char* dg_kernel_config_name(int form, int64_t rows, int64_t N, int64_t K, int out_f32) {
+    if (form >= 0 && form <= 2) {
+        dg::NtProblem p{};
+        p.form = static_cast<dg::NtForm>(form);
+        p.rows = rows; p.N = N; p.K = K; p.G = 1;
+        p.out_f32 = form == 0 && out_f32 != 0;
+        return dg::nt_config_name(p);
+    }
+    if (form == 3) {
+        dg::TnProblem p{};
+        p.M = rows; p.N = N; p.K_tot = K; p.G = 1;
+        return dg::tn_config_name(p);
+    }
+    return "";
+}
+
 }  // extern "C"

@@ -43,8 +43,10 @@ hipError_t launch_nt(const NtProblem& p, int cu_cap, hipStream_t stream);
 hipError_t launch_tn(const TnProblem& p, int cu_cap, hipStream_t stream);
 
 // Short description of the tile configuration chosen for a problem (for
-// DG_PRINT_CONFIGS).
+// DG_PRINT_CONFIGS), and the stable name of the kernel instance it launches.
 const char* describe_nt_config(const NtProblem& p);
 const char* describe_tn_config(const TnProblem& p);
+const char* nt_config_name(const NtProblem& p);
+const char* tn_config_name(const TnProblem& p);
 
 }  // namespace dg

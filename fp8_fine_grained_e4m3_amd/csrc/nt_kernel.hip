@@ -373,13 +373,19 @@ hipError_t launch_nt(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
+const char* nt_config_name(const NtProblem& pr) {
+    static const char* tiles[] = {"64x128", "128x128", "128x256", "256x256"};
+    static const char* forms[] = {"dense", "contiguous", "masked"};
+    static thread_local char buf[64];
+    snprintf(buf, sizeof buf, "nt_%s_%s_%s", forms[(int)pr.form],
+             pr.out_f32 ? "f32" : "bf16", tiles[choose_tile(pr)]);
+    return buf;
+}
+
 const char* describe_nt_config(const NtProblem& pr) {
-    static thread_local char buf[160];
-    static const char* names[] = {"64x128 (1x4 waves)", "128x128 (2x2 waves)",
-                                  "128x256 (2x4 waves)", "256x256 (2x4 waves)"};
-    snprintf(buf, sizeof buf, "nt form=%d rows=%lld N=%lld K=%lld G=%lld tile=%s", (int)pr.form,
-             (long long)pr.rows, (long long)pr.N, (long long)pr.K, (long long)pr.G,
-             names[choose_tile(pr)]);
+    static thread_local char buf[192];
+    snprintf(buf, sizeof buf, "%s rows=%lld N=%lld K=%lld G=%lld", nt_config_name(pr),
+             (long long)pr.rows, (long long)pr.N, (long long)pr.K, (long long)pr.G);
     return buf;
 }
 

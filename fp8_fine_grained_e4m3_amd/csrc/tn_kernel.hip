@@ -306,9 +306,11 @@ hipError_t launch_tn(const TnProblem& pr, int cu_cap, hipStream_t stream) {
     return launch_tn_cfg<TnCfg128>(pr, cu_cap, stream);
 }
 
+const char* tn_config_name(const TnProblem&) { return "tn_kgrouped_f32_128x128"; }
+
 const char* describe_tn_config(const TnProblem& pr) {
-    static thread_local char buf[160];
-    snprintf(buf, sizeof buf, "tn G=%lld M=%lld N=%lld K_tot=%lld tile=128x128 (2x2 waves)",
+    static thread_local char buf[192];
+    snprintf(buf, sizeof buf, "%s G=%lld M=%lld N=%lld K_tot=%lld", tn_config_name(pr),
              (long long)pr.G, (long long)pr.M, (long long)pr.N, (long long)pr.K_tot);
     return buf;
 }

@@ -165,6 +165,17 @@ const char* dg_last_error(void);
 int dg_get_num_cus(void);
 dg_status dg_set_num_cus(int n);
 
+/*
+ * Name of the kernel instance (tile configuration) a call with these sizes
+ * launches, e.g. "nt_dense_bf16_256x256", for profiling and tuning (the
+ * configuration report of DeepGEMM Documentation, section 6, variable
+ * DG_PRINT_CONFIGS; setting DG_PRINT_CONFIGS=1 also prints it per call).
+ *   form: 0 dense, 1 M-grouped contiguous, 2 M-grouped masked (rows = M,
+ *   M_tot or M_max), 3 K-grouped TN (rows = M).  out_f32: dense output dtype.
+ * Returns a static string; "" for an unknown form.  No HIP call is made.
+ */
+const char* dg_kernel_config_name(int form, int64_t rows, int64_t N, int64_t K, int out_f32);
+
 /* Row alignment of every expert segment in the contiguous layout: 128
  * (DeepGEMM Documentation, section 9, and section 10's alignment getter). */
 int dg_get_mk_alignment_for_contiguous_layout(void);
