@@ -64,24 +64,41 @@ struct NtCfg {
     static constexpr int A_BYTES = BM * kKBlk;
     static constexpr int B_BYTES = BN * kKBlk;
     static constexpr int SA_BYTES = BM * 4;    // this tile's A scales for the stage's K block
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES;
+    static constexpr int SB_BYTES = 256;       // B scales of the tile's 128-column blocks
+    static constexpr int SA_OFF = A_BYTES + B_BYTES;
+    static constexpr int SB_OFF = SA_OFF + SA_BYTES;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
     static constexpr int SA_DMA = BM / 64;     // 256-byte (64-float) wave copies per stage
     static constexpr int A_DMA = BM / 8;       // 1 KiB (8-row) wave copies per stage for A
     static constexpr int B_DMA = BN / 8;
     static constexpr int DMA_PER_WAVE = (A_DMA + B_DMA) / WAVES;
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert((A_DMA + B_DMA) % WAVES == 0, "stage copies must split evenly over waves");
-    static_assert(SA_DMA >= 1 && SA_DMA <= WAVES, "one scale copy per wave at most");
+    static_assert(SA_DMA >= 1 && SA_DMA < WAVES, "one scale copy per wave, and a wave left for B");
+    static_assert(BN % kKBlk == 0, "tiles cover whole 128-column B scale blocks");
     static_assert(SM % 4 == 0, "a lane reads its A scales as float4s");
     static_assert(kKBlk % WTN == 0 && (BN % kKBlk == 0 || kKBlk % BN == 0),
                   "a wave's columns must sit inside one 128-column B scale block");
 };
 
-// Rows of a wave tile are dealt to lanes so that lane l owns the SM
-// consecutive rows SM * (l & 15) + i, i = 0..SM-1 (MFMA tile i takes row
-// SM * r + i as its r-th column).  A lane's A scales are then SM consecutive
-// floats.  Columns follow the MFMA layout: tile j, lane l owns the four
-// columns 16 j + 4 (l >> 4) + {0, 1, 2, 3}.
+// Row and LDS maps.
+//  * Lane l (r = l & 15) of a wave owns the SM consecutive rows SM r .. SM r +
+//    SM - 1 of its wave tile; MFMA tile i of the lane reads row SM r + (i ^ (r & 1))
+//    (odd lanes swap neighbouring rows), so any 16 lanes read rows of both
+//    parities.  A lane's A scales are SM consecutive LDS floats, stored
+//    pre-swapped the same way.  Columns follow the MFMA layout: tile j, lane l
+//    owns the four columns 16 j + 4 (l >> 4) + {0, 1, 2, 3}.
+//  * LDS holds 128-byte rows (one K block of one row); chunk c of row `row`
+//    sits at 16-byte position c ^ f(row), with f_A(row) = (row / 2SM) & 7 for
+//    the A tile and f_B(row) = (row / 2) & 7 for the B tile.  LDS serves a
+//    ds_read_b128 16 lanes at a time from 64 four-byte banks; with these maps
+//    every 16-lane group of every fragment read hits 16 distinct 16-byte bank
+//    groups, and the per-fragment address is a per-lane base plus an
+//    immediate (i * 128 for A, j * 2048 for B).
+template <int SM>
+__device__ __forceinline__ int pos_a(int row) { return (row / (2 * SM)) & 7; }
+__device__ __forceinline__ int pos_b(int row) { return (row >> 1) & 7; }
+
 template <class Cfg, int FORM, bool OUT_F32>
 __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN;
@@ -129,22 +146,27 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
         const float* __restrict__ sfb_t = p.sfb + (int64_t)e * NB * KB;
 
         // Stage copies: wave copy u (uniform) moves 8 rows x 128 bytes; lane l
-        // fetches chunk (l & 7) ^ swz(row) of row 8 u' + (l >> 3) so that the
-        // LDS image is the swizzled layout.  Rows past the edge re-read the
-        // last row (never stored).
+        // fetches chunk (l & 7) ^ f(row) of row 8 u' + (l >> 3), so LDS
+        // position p of a row holds chunk p ^ f(row).  Rows past the edge re-read
+        // the last row (never stored).
         uint32_t goff[Cfg::DMA_PER_WAVE];
 #pragma unroll
         for (int q = 0; q < Cfg::DMA_PER_WAVE; ++q) {
             const int u = wave * Cfg::DMA_PER_WAVE + q;
             const bool is_a = u < Cfg::A_DMA;
             const int lrow = 8 * (is_a ? u : u - Cfg::A_DMA) + (lane >> 3);
-            const int chunk = (lane & 7) ^ swz(lrow);
+            const int chunk = (lane & 7) ^ (is_a ? pos_a<SM>(lrow) : pos_b(lrow));
             const int row = is_a ? min(r0 + lrow, grp_rows - 1) : min(n0 + lrow, p.N - 1);
             goff[q] = (uint32_t)row * (uint32_t)p.K + (uint32_t)(chunk * 16);
         }
-        // A scales: wave w < SA_DMA copies floats [64 w, 64 w + 64) of this
-        // tile's rows for the K block (one float per lane, rows clamped).
-        const uint32_t sa_off = 4u * (uint32_t)min(r0 + 64 * wave + lane, grp_rows - 1);
+        // Scales.  Wave w < SA_DMA copies A-scale slots [64 w, 64 w + 64): slot s
+        // holds the scale of tile row s ^ ((s / SM) & 1) (the pair swap of the
+        // row map).  The last wave copies the B scales of the tile's 128-column
+        // blocks (lanes past the last block repeat it).
+        const int sa_slot = 64 * wave + lane;
+        const uint32_t sa_off =
+            4u * (uint32_t)min(r0 + (sa_slot ^ ((sa_slot / SM) & 1)), grp_rows - 1);
+        const uint32_t sb_off = 4u * (uint32_t)(min(n0 / kKBlk + lane, NB - 1) * KB);
         const uint32_t lds0 = lds_addr(smem);
         auto issue_stage = [&](int kb, int stage) {
             const uint32_t dst = lds0 + stage * Cfg::STAGE_BYTES;
@@ -155,12 +177,24 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
                 dma16(src, goff[q], dst + u * 1024);
             }
             if (wave < Cfg::SA_DMA)
-                dma4(sfa_t + (size_t)kb * grp_rows, sa_off,
-                     dst + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256);
+                dma4(sfa_t + (size_t)kb * grp_rows, sa_off, dst + Cfg::SA_OFF + wave * 256);
+            if (wave == Cfg::WAVES - 1)
+                dma4(sfb_t + kb, sb_off, dst + Cfg::SB_OFF);
         };
 
-        const int m_lane0 = r0 + wm * Cfg::WTM + SM * (lane & 15);
-        const int sb_row = min((n0 + wn * Cfg::WTN) / kKBlk, NB - 1) * KB;
+        const int r16 = lane & 15;
+        const int m_lane0 = r0 + wm * Cfg::WTM + SM * r16;   // first of the lane's SM rows
+        // per-lane LDS byte offsets inside a stage (fragment i / j adds an immediate)
+        const int c0 = (lane >> 4) * 2;
+        const int pa = pos_a<SM>(wm * Cfg::WTM + SM * r16);
+        const int a_even = (wm * Cfg::WTM + SM * r16 + (r16 & 1)) * kKBlk;
+        const int a_odd = (wm * Cfg::WTM + SM * r16 - (r16 & 1)) * kKBlk;
+        const int a_lo = (c0 ^ pa) << 4, a_hi = ((c0 + 1) ^ pa) << 4;
+        const int pb = pos_b(wn * Cfg::WTN + r16);
+        const int b_row = Cfg::A_BYTES + (wn * Cfg::WTN + r16) * kKBlk;
+        const int b_lo = b_row + ((c0 ^ pb) << 4), b_hi = b_row + (((c0 + 1) ^ pb) << 4);
+        const int s_a = Cfg::SA_OFF + 4 * (wm * Cfg::WTM + SM * r16);
+        const int s_b = Cfg::SB_OFF + 4 * ((wn * Cfg::WTN) / kKBlk);
 
         f32x4 acc[SM][SN];
 #pragma unroll
@@ -169,28 +203,13 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             for (int j = 0; j < SN; ++j)
                 acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        float sb_nxt = 0.f;
-        if (KB > 0) {
-            issue_stage(0, 0);
-            sb_nxt = sfb_t[sb_row];
-        }
+        if (KB > 0) issue_stage(0, 0);
         for (int kb = 0; kb < KB; ++kb) {
             // stage kb has landed for every wave, and every wave is done with
             // the stage the next copies overwrite
             vm_lgkm_drain_barrier();
-            // Take the B scale (loaded last iteration, so already here) into a
-            // scalar register now: the compiler's wait for it must come before
-            // the copies below, or it would also wait for them.
-            int sb_bits = __builtin_amdgcn_readfirstlane(__float_as_int(sb_nxt));
-            asm volatile("" : "+s"(sb_bits));
-            const float sb = __int_as_float(sb_bits);
-            // The copy for block kb+1 goes to the other stage (a branch here,
-            // ahead of the compute, leaves the compute one basic block).
-            const int kn = kb + 1 < KB ? kb + 1 : kb;
-            if (kb + 1 < KB) issue_stage(kn, (kb + 1) & 1);
-            const uint8_t* sA = smem + (kb & 1) * Cfg::STAGE_BYTES;
-            const uint8_t* sB = sA + Cfg::A_BYTES;
-            const float* sS = reinterpret_cast<const float*>(sB + Cfg::B_BYTES);
+            if (kb + 1 < KB) issue_stage(kb + 1, (kb + 1) & 1);
+            const uint8_t* st = smem + (kb & 1) * Cfg::STAGE_BYTES;
 
             // Software pipeline over the wave's MFMA rows: the block products of
             // row i are issued while row i-1 is promoted, so no FMA waits on
@@ -198,20 +217,33 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             float sa[SM];
 #pragma unroll
             for (int i = 0; i < SM; i += 4) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(sS + wm * Cfg::WTM + SM * (lane & 15) + i);
+                const f32x4 v = *reinterpret_cast<const f32x4*>(st + s_a + 4 * i);
                 sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
             }
+            const float sb = *reinterpret_cast<const float*>(st + s_b);
+            auto afrag_at = [&](int i) {
+                const uint8_t* rowp = st + ((i & 1) ? a_odd : a_even) + i * kKBlk;
+                const i32x4 lo = *reinterpret_cast<const i32x4*>(rowp + a_lo);
+                const i32x4 hi = *reinterpret_cast<const i32x4*>(rowp + a_hi);
+                i32x8 r;
+                r.s0 = lo.x; r.s1 = lo.y; r.s2 = lo.z; r.s3 = lo.w;
+                r.s4 = hi.x; r.s5 = hi.y; r.s6 = hi.z; r.s7 = hi.w;
+                return r;
+            };
             i32x8 bfrag[SN];
 #pragma unroll
-            for (int j = 0; j < SN; ++j)
-                bfrag[j] = lds_fragment(sB, wn * Cfg::WTN + 16 * j, lane);
-            i32x8 afrag = lds_fragment_row(sA, wm * Cfg::WTM + SM * (lane & 15), lane);
+            for (int j = 0; j < SN; ++j) {
+                const i32x4 lo = *reinterpret_cast<const i32x4*>(st + b_lo + j * 16 * kKBlk);
+                const i32x4 hi = *reinterpret_cast<const i32x4*>(st + b_hi + j * 16 * kKBlk);
+                bfrag[j].s0 = lo.x; bfrag[j].s1 = lo.y; bfrag[j].s2 = lo.z; bfrag[j].s3 = lo.w;
+                bfrag[j].s4 = hi.x; bfrag[j].s5 = hi.y; bfrag[j].s6 = hi.z; bfrag[j].s7 = hi.w;
+            }
+            i32x8 afrag = afrag_at(0);
             f32x4 pend[SN];
 #pragma unroll
             for (int i = 0; i < SM; ++i) {
                 i32x8 anext;
-                if (i + 1 < SM)
-                    anext = lds_fragment_row(sA, wm * Cfg::WTM + SM * (lane & 15) + i + 1, lane);
+                if (i + 1 < SM) anext = afrag_at(i + 1);
                 f32x4 pcur[SN];
 #pragma unroll
                 for (int j = 0; j < SN; ++j) pcur[j] = mfma_e4m3_block(bfrag[j], afrag);
@@ -249,10 +281,6 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
                     acc[SM - 1][j].w = __builtin_fmaf(pend[j].w, s, acc[SM - 1][j].w);
                 }
             }
-            // The B scale is a uniform (scalar-cache) load; issuing it after the
-            // LDS reads keeps it from forcing full LDS-counter waits above.
-            __builtin_amdgcn_sched_barrier(0);
-            sb_nxt = sfb_t[sb_row + kn];
         }
         // every wave is past its last LDS read before the next tile's copies
         lds_barrier();
@@ -260,7 +288,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
         // ---- epilogue: (+C), convert once, masked store ---------------------------
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
-            const int m = m_lane0 + i;
+            const int m = m_lane0 + (i ^ (r16 & 1));
             bool row_ok = m < store_rows;
             if (FORM == kContiguous && row_ok) row_ok = p.m_indices[m] == e;
             if (!row_ok) continue;

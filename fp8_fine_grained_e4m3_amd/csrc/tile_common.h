@@ -86,23 +86,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Direct global -> LDS copies (global_load_lds_dwordx4 / _dword).  Lane l's
 // 16 (or 4) bytes at base + voff land at LDS byte lds + 16 * l (or 4 * l), so
 // one wave instruction fills 1024 (or 256) consecutive LDS bytes.  `base` and
-// `lds` must be wave-uniform.  Written as inline asm so the compiler does not
-// treat the in-flight copies as aliasing every LDS read (which would drain
-// the vector-memory counter before each fragment read); the kernels wait for
-// the copies explicitly (vm_drain_barrier).  Extra outstanding loads the
-// compiler does not know about only make its own vmcnt waits stricter.
+// `lds` must be wave-uniform; `lds` travels in M0, which the compiler loads
+// (the "{m0}" operand).  The leading s_nop is the one wait state the gfx9
+// family needs between an SALU write of M0 and an LDS DMA that reads it
+// (the hazard recognizer does not look inside inline asm).
+// Written as inline asm so the compiler does not treat the in-flight copies
+// as aliasing every LDS read (which would drain the vector-memory counter
+// before each fragment read); the kernels wait for the copies explicitly
+// (vm_drain_barrier).  Extra outstanding loads the compiler does not know
+// about only make its own vmcnt waits stricter.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(voff), "s"(base), "s"(lds)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(base), "{m0}"(lds)
+                 : "memory");
 }
 
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1"
                  :
-                 : "v"(voff), "s"(base), "s"(lds)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(base), "{m0}"(lds)
+                 : "memory");
 }
 
 // Wait for this wave's outstanding vector-memory loads (including the LDS
