@@ -51,10 +51,11 @@ struct NtArgs {
     int num_tiles;     // enumerated tiles (masked: G * tiles_m * tiles_n)
 };
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
 struct NtCfg {
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int STAGES = STAGES_;     // LDS stages (STAGES - 1 K blocks in flight)
     static constexpr int WAVES = WAVES_M * WAVES_N;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int WTM = BM / WAVES_M;   // wave tile rows (m)
@@ -64,7 +65,7 @@ struct NtCfg {
     static constexpr int A_BYTES = BM * kKBlk;
     static constexpr int B_BYTES = BN * kKBlk;
     static constexpr int SA_BYTES = BM * 4;    // this tile's A scales for the stage's K block
-    static constexpr int SB_BYTES = 256;       // B scales of the tile's 128-column blocks
+    static constexpr int SB_BYTES = 256 * WAVES;   // one copy of the tile's B scales per wave
     static constexpr int SA_OFF = A_BYTES + B_BYTES;
     static constexpr int SB_OFF = SA_OFF + SA_BYTES;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
@@ -72,10 +73,12 @@ struct NtCfg {
     static constexpr int A_DMA = BM / 8;       // 1 KiB (8-row) wave copies per stage for A
     static constexpr int B_DMA = BN / 8;
     static constexpr int DMA_PER_WAVE = (A_DMA + B_DMA) / WAVES;
+    static constexpr int VM_PER_STAGE = DMA_PER_WAVE + 1;   // copies a wave issues per stage
+    static_assert(STAGES >= 2 && (STAGES - 2) * VM_PER_STAGE <= 63, "vmcnt range");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert((A_DMA + B_DMA) % WAVES == 0, "stage copies must split evenly over waves");
-    static_assert(SA_DMA >= 1 && SA_DMA < WAVES, "one scale copy per wave, and a wave left for B");
-    static_assert(BN % kKBlk == 0, "tiles cover whole 128-column B scale blocks");
+    static_assert(SA_DMA >= 1 && SA_DMA <= WAVES, "one scale copy per wave at most");
+    static_assert(BN % kKBlk == 0 || kKBlk % BN == 0, "tiles align with 128-column B scale blocks");
     static_assert(SM % 4 == 0, "a lane reads its A scales as float4s");
     static_assert(kKBlk % WTN == 0 && (BN % kKBlk == 0 || kKBlk % BN == 0),
                   "a wave's columns must sit inside one 128-column B scale block");
@@ -103,7 +106,7 @@ template <class Cfg, int FORM, bool OUT_F32>
 __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN;
     constexpr int SM = Cfg::SM, SN = Cfg::SN;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * Cfg::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::STAGES * Cfg::STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -159,10 +162,12 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             const int row = is_a ? min(r0 + lrow, grp_rows - 1) : min(n0 + lrow, p.N - 1);
             goff[q] = (uint32_t)row * (uint32_t)p.K + (uint32_t)(chunk * 16);
         }
-        // Scales.  Wave w < SA_DMA copies A-scale slots [64 w, 64 w + 64): slot s
-        // holds the scale of tile row s ^ ((s / SM) & 1) (the pair swap of the
-        // row map).  The last wave copies the B scales of the tile's 128-column
-        // blocks (lanes past the last block repeat it).
+        // Scales.  Every wave issues exactly one scale copy per stage (so all
+        // waves count the same number of copies in flight): wave w < SA_DMA
+        // copies A-scale slots [64 w, 64 w + 64), slot s holding the scale of
+        // tile row s ^ ((s / SM) & 1) (the pair swap of the row map); every
+        // other wave copies the B scales of the tile's 128-column blocks into
+        // its own 256-byte slot (lanes past the last block repeat it).
         const int sa_slot = 64 * wave + lane;
         const uint32_t sa_off =
             4u * (uint32_t)min(r0 + (sa_slot ^ ((sa_slot / SM) & 1)), grp_rows - 1);
@@ -178,8 +183,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             }
             if (wave < Cfg::SA_DMA)
                 dma4(sfa_t + (size_t)kb * grp_rows, sa_off, dst + Cfg::SA_OFF + wave * 256);
-            if (wave == Cfg::WAVES - 1)
-                dma4(sfb_t + kb, sb_off, dst + Cfg::SB_OFF);
+            else
+                dma4(sfb_t + kb, sb_off, dst + Cfg::SB_OFF + wave * 256);
         };
 
         const int r16 = lane & 15;
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
         const int b_row = Cfg::A_BYTES + (wn * Cfg::WTN + r16) * kKBlk;
         const int b_lo = b_row + ((c0 ^ pb) << 4), b_hi = b_row + (((c0 + 1) ^ pb) << 4);
         const int s_a = Cfg::SA_OFF + 4 * (wm * Cfg::WTM + SM * r16);
-        const int s_b = Cfg::SB_OFF + 4 * ((wn * Cfg::WTN) / kKBlk);
+        const int s_b = Cfg::SB_OFF + 256 * (Cfg::WAVES - 1) + 4 * ((wn * Cfg::WTN) / kKBlk);
 
         f32x4 acc[SM][SN];
 #pragma unroll
@@ -203,13 +208,27 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             for (int j = 0; j < SN; ++j)
                 acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        if (KB > 0) issue_stage(0, 0);
-        for (int kb = 0; kb < KB; ++kb) {
-            // stage kb has landed for every wave, and every wave is done with
-            // the stage the next copies overwrite
-            vm_lgkm_drain_barrier();
-            if (kb + 1 < KB) issue_stage(kb + 1, (kb + 1) & 1);
-            const uint8_t* st = smem + (kb & 1) * Cfg::STAGE_BYTES;
+        const int kb_lo = 0, nkb = KB;
+        // Prologue: the first STAGES - 1 K blocks go in flight.
+#pragma unroll
+        for (int q = 0; q < Cfg::STAGES - 1; ++q)
+            if (q < nkb) issue_stage(kb_lo + q, q);
+        int stage = 0;   // stage holding block kb
+        for (int it = 0; it < nkb; ++it) {
+            // Block kb_lo + it has landed for this wave once at most `ahead` later
+            // stages' copies are outstanding; the barrier then makes every wave's
+            // copies visible and guarantees every wave is done with the stage the
+            // next copy overwrites (read in the previous iteration).
+            const int ahead = min(Cfg::STAGES - 2, nkb - 1 - it);
+            wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(ahead);
+            lgkm_drain_barrier();
+            if (it + Cfg::STAGES - 1 < nkb) {
+                int nst = stage + Cfg::STAGES - 1;
+                nst -= nst >= Cfg::STAGES ? Cfg::STAGES : 0;
+                issue_stage(kb_lo + it + Cfg::STAGES - 1, nst);
+            }
+            const uint8_t* st = smem + stage * Cfg::STAGE_BYTES;
+            stage = stage + 1 == Cfg::STAGES ? 0 : stage + 1;
 
             // Software pipeline over the wave's MFMA rows: the block products of
             // row i are issued while row i-1 is promoted, so no FMA waits on
@@ -358,20 +377,25 @@ hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     return hipGetLastError();
 }
 
-using Cfg256x256 = NtCfg<256, 256, 2, 4>;
-using Cfg128x128 = NtCfg<128, 128, 2, 2>;
-using Cfg64x128 = NtCfg<64, 128, 1, 4>;
+using Cfg256x256 = NtCfg<256, 256, 2, 4, 2>;
+using Cfg128x128 = NtCfg<128, 128, 2, 2, 2>;
+using Cfg128x64 = NtCfg<128, 64, 2, 2, 3>;
+using Cfg64x64 = NtCfg<64, 64, 1, 4, 4>;
 
-using Cfg128x256 = NtCfg<128, 256, 2, 4>;
+using Cfg128x256 = NtCfg<128, 256, 2, 4, 2>;
 
 // Tile choice: 256 x 256 (8 waves of 128 x 64) for large dense problems,
 // 128 x 256 for contiguous groups (a tile may not straddle two 128-row expert
-// blocks), 128 x 128 for mid-size rows, 64 x 128 for decode-size groups.
-enum NtTile { kT64x128, kT128x128, kT128x256, kT256x256 };
+// blocks), 128 x 128 for mid-size rows, and for decode-size rows (HBM-bound:
+// every B byte is used once) narrow 64-column tiles with deeper pipelines, so
+// more workgroups stream B with more bytes in flight each.
+enum NtTile { kT64x64, kT128x64, kT128x128, kT128x256, kT256x256 };
 
 NtTile choose_tile(const NtProblem& pr) {
     if (pr.form == kContiguous) return kT128x256;
-    if (pr.rows <= 64) return kT64x128;
+    if (pr.form == kDense && pr.rows <= 64) return kT64x64;
+    if (pr.form == kDense && pr.rows <= 128) return kT128x64;
+    if (pr.rows <= 64) return kT64x64;
     if (pr.form == kDense && pr.rows >= 1024 && pr.N >= 1024) return kT256x256;
     return kT128x128;
 }
@@ -379,7 +403,8 @@ NtTile choose_tile(const NtProblem& pr) {
 template <int FORM, bool OUT_F32>
 hipError_t dispatch_tiles(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     switch (choose_tile(pr)) {
-    case kT64x128: return launch_cfg<Cfg64x128, FORM, OUT_F32>(pr, cu_cap, stream);
+    case kT64x64: return launch_cfg<Cfg64x64, FORM, OUT_F32>(pr, cu_cap, stream);
+    case kT128x64: return launch_cfg<Cfg128x64, FORM, OUT_F32>(pr, cu_cap, stream);
     case kT128x256: return launch_cfg<Cfg128x256, FORM, OUT_F32>(pr, cu_cap, stream);
     case kT256x256: return launch_cfg<Cfg256x256, FORM, OUT_F32>(pr, cu_cap, stream);
     default: return launch_cfg<Cfg128x128, FORM, OUT_F32>(pr, cu_cap, stream);
@@ -402,7 +427,7 @@ hipError_t launch_nt(const NtProblem& pr, int cu_cap, hipStream_t stream) {
 }
 
 const char* nt_config_name(const NtProblem& pr) {
-    static const char* tiles[] = {"64x128", "128x128", "128x256", "256x256"};
+    static const char* tiles[] = {"64x64", "128x64", "128x128", "128x256", "256x256"};
     static const char* forms[] = {"dense", "contiguous", "masked"};
     static thread_local char buf[64];
     snprintf(buf, sizeof buf, "nt_%s_%s_%s", forms[(int)pr.form],

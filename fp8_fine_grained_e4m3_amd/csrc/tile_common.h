@@ -87,23 +87,26 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 16 (or 4) bytes at base + voff land at LDS byte lds + 16 * l (or 4 * l), so
 // one wave instruction fills 1024 (or 256) consecutive LDS bytes.  `base` and
 // `lds` must be wave-uniform; `lds` travels in M0, which the compiler loads
-// (the "{m0}" operand).  The leading s_nop is the one wait state the gfx9
-// family needs between an SALU write of M0 and an LDS DMA that reads it
-// (the hazard recognizer does not look inside inline asm).
+// (the "{m0}" operand).  The hazard recognizer does not look inside inline
+// asm, so the asm pads itself: s_nop 4 gives the five wait states the gfx9
+// family needs between a VALU write of an SGPR (v_readlane of a spilled
+// SGPR, v_readfirstlane) and a VMEM instruction reading it as its address
+// base, which also covers the one wait state between a write of M0 and an
+// LDS DMA reading it.
 // Written as inline asm so the compiler does not treat the in-flight copies
 // as aliasing every LDS read (which would drain the vector-memory counter
 // before each fragment read); the kernels wait for the copies explicitly
 // (vm_drain_barrier).  Extra outstanding loads the compiler does not know
 // about only make its own vmcnt waits stricter.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(voff), "s"(base), "{m0}"(lds)
                  : "memory");
 }
 
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1"
+    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1"
                  :
                  : "v"(voff), "s"(base), "{m0}"(lds)
                  : "memory");
@@ -118,6 +121,28 @@ __device__ __forceinline__ void vm_drain_barrier() {
 
 __device__ __forceinline__ void vm_lgkm_drain_barrier() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most ahead * PER copies of this wave are outstanding
+// (ahead in [0, MAXA]); copies retire in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+template <int MAXA, int PER>
+__device__ __forceinline__ void wait_stage_copies(int ahead) {
+    if constexpr (MAXA >= 6) { if (ahead >= 6) { wait_vmcnt<6 * PER>(); return; } }
+    if constexpr (MAXA >= 5) { if (ahead == 5) { wait_vmcnt<5 * PER>(); return; } }
+    if constexpr (MAXA >= 4) { if (ahead == 4) { wait_vmcnt<4 * PER>(); return; } }
+    if constexpr (MAXA >= 3) { if (ahead == 3) { wait_vmcnt<3 * PER>(); return; } }
+    if constexpr (MAXA >= 2) { if (ahead == 2) { wait_vmcnt<2 * PER>(); return; } }
+    if constexpr (MAXA >= 1) { if (ahead == 1) { wait_vmcnt<1 * PER>(); return; } }
+    wait_vmcnt<0>();
+}
+
+__device__ __forceinline__ void lgkm_drain_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ void lds_barrier() {

@@ -406,3 +406,66 @@ def test_c5_k_grouped_full_size():
     got = d[torch.from_numpy(groups).cuda(), torch.from_numpy(rows).cuda()].cpu().numpy()
     ref = oracle.k_grouped_tn(x.a, x.sfa, x.b, x.sfb, x.k_sizes, x.c, groups=groups, rows=rows)
     print(check_close(got.astype(np.float64), ref, "C5"))
+
+
+# ------------------------------------------------------------------------------
+# small-M dense (narrow tiles, deep pipelines) and graph capture
+# ------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (128, 4096, 2048), (33, 528, 4096),
+                                   (96, 208, 1280)])
+def test_small_m_matches_oracle_and_is_reproducible(M, N, K):
+    """Decode-size rows take the narrow-tile, multi-stage path; results match the
+    oracle and are bitwise reproducible, also under a CU cap."""
+    announce(f"small-M {M}x{N}x{K}")
+    x = gen.gen_dense(M, N, K, seed=M + N)
+    d1 = run_dense(x)
+    check_close(to64(d1), oracle.gemm_nt(x.a, x.sfa, x.b, x.sfb), "small-M")
+    d2 = run_dense(x)
+    assert torch.equal(d1, d2)
+    dg.set_num_cus(5)
+    try:
+        d3 = run_dense(x)
+    finally:
+        dg.set_num_cus(0)
+    assert torch.equal(d1, d3)
+
+
+def test_graph_capture_replays_dense_and_masked():
+    """Dense and masked calls captured into a HIP graph replay correctly several
+    times, with eager work in between; the masked replay reads masked_m from
+    device memory at replay time."""
+    announce("graph capture dense + masked")
+    x = gen.gen_dense(64, 1024, 2048, seed=77)
+    a, sa, b, sb = dev(x.a), dev(x.sfa), dev(x.b), dev(x.sfb)
+    eager = torch.empty(64, 1024, dtype=torch.bfloat16, device="cuda")
+    dg.fp8_gemm_nt((a, sa), (b, sb), eager)
+    torch.cuda.synchronize()
+    mi = gen.gen_masked(G=4, M_max=128, N=256, K=512, masked_m=np.array([128, 5, 0, 77]), seed=78)
+    ma, msa, mb, msb = dev(mi.a), dev(mi.sfa), dev(mi.b), dev(mi.sfb)
+    mm = dev(mi.masked_m)
+    out = torch.empty(64, 1024, dtype=torch.bfloat16, device="cuda")
+    mout = Guarded((4, 128, 256), torch.bfloat16)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dg.fp8_gemm_nt((a, sa), (b, sb), out)        # warm-up on the capture stream
+        dg.m_grouped_fp8_gemm_nt_masked((ma, msa), (mb, msb), mout.view, mm)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        dg.fp8_gemm_nt((a, sa), (b, sb), out)
+        dg.m_grouped_fp8_gemm_nt_masked((ma, msa), (mb, msb), mout.view, mm)
+    for rep, counts in enumerate([[128, 5, 0, 77], [3, 128, 64, 0], [0, 0, 1, 128]]):
+        out.zero_()
+        mout.raw.fill_(mout.bits)
+        mm.copy_(torch.tensor(counts, dtype=torch.int32))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"dense replay {rep}"
+        ref = oracle.m_grouped_masked(mi.a, mi.sfa, mi.b, mi.sfb, np.array(counts, np.int32))
+        check_close(to64(mout.view), ref, f"masked replay {rep}")
+        check_masked_rows_untouched(mout, counts, 128)
+        assert mout.intact()
