@@ -49,6 +49,7 @@ struct NtArgs {
     int tiles_m;       // per group
     int tiles_n;
     int num_tiles;     // enumerated tiles (masked: G * tiles_m * tiles_n)
+    int band_m;        // grouped rasterisation: bands of band_m M tiles
 };
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
@@ -119,14 +120,28 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
 
     for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
         // ---- tile scheduling (uniform over the workgroup) ------------------
-        int g = 0, e = 0, local = t;
+        int g = 0, e = 0, local = t, half = 0;
         if (FORM == kMasked) {
             g = t / per_group;
             local = t - g * per_group;
             e = g;
+        } else if (FORM == kContiguous) {
+            // Tiles of BM = 256 rows span two 128-row expert blocks: the tile is
+            // listed twice, pass `half` computing it with the expert of block
+            // `half` (pass 1 only when that expert differs from block 0's).
+            half = t / per_group;
+            local = t - half * per_group;
         }
-        const int tm = local % p.tiles_m;
-        const int tn = local / p.tiles_m;
+        // Grouped rasterisation: tiles run in bands of band_m M tiles; inside a
+        // band N advances after every M tile of the band, so the tiles in
+        // flight share a few A row panels and a few B column panels.
+        const int band_tiles = p.band_m * p.tiles_n;
+        const int band = local / band_tiles;
+        const int in_band = local - band * band_tiles;
+        const int first_m = band * p.band_m;
+        const int rows_in_band = min(p.tiles_m - first_m, p.band_m);
+        const int tm = first_m + in_band % rows_in_band;
+        const int tn = in_band / rows_in_band;
         const int r0 = tm * BM;        // first row of the tile, relative to its group
         const int n0 = tn * BN;
         const int grp_rows = p.rows;   // rows that exist in memory for this group
@@ -139,8 +154,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             grp_row0 = (int64_t)g * p.rows;
             if (r0 >= mm) continue;
         } else if (FORM == kContiguous) {
-            e = p.m_indices[r0];
+            const int rb = r0 + half * kKBlk;   // first row of the block whose expert is used
+            if (rb >= p.rows) continue;
+            e = p.m_indices[rb];
             if (e < 0 || e >= p.G) continue;
+            if (half == 1 && p.m_indices[r0] == e) continue;   // pass 0 already covers it
         }
 
         const uint8_t* __restrict__ a_t = p.a + grp_row0 * p.K;
@@ -348,6 +366,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
 
 namespace {
 
+constexpr int kBandM = 8;   // M tiles per rasterisation band
+
 template <class Cfg, int FORM, bool OUT_F32>
 hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     NtArgs a;
@@ -356,7 +376,11 @@ hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     a.rows = (int)pr.rows; a.N = (int)pr.N; a.K = (int)pr.K; a.G = (int)pr.G;
     a.tiles_m = (int)((pr.rows + Cfg::BM - 1) / Cfg::BM);
     a.tiles_n = (int)((pr.N + Cfg::BN - 1) / Cfg::BN);
-    const int64_t groups = (FORM == kMasked) ? pr.G : 1;
+    // Dense runs M-fastest over all M tiles (one band); contiguous groups use
+    // narrow bands so the tiles in flight share few expert weight panels.
+    a.band_m = (FORM == kContiguous && a.tiles_m > kBandM) ? kBandM : a.tiles_m;
+    static_assert(FORM != kContiguous || Cfg::BM == 2 * kKBlk, "contiguous tiles span two blocks");
+    const int64_t groups = (FORM == kMasked) ? pr.G : (FORM == kContiguous ? 2 : 1);
     const int64_t tiles = groups * a.tiles_m * a.tiles_n;
     if (tiles <= 0) return hipSuccess;
     a.num_tiles = (int)tiles;
@@ -382,17 +406,16 @@ using Cfg128x128 = NtCfg<128, 128, 2, 2, 2>;
 using Cfg128x64 = NtCfg<128, 64, 2, 2, 3>;
 using Cfg64x64 = NtCfg<64, 64, 1, 4, 4>;
 
-using Cfg128x256 = NtCfg<128, 256, 2, 4, 2>;
 
-// Tile choice: 256 x 256 (8 waves of 128 x 64) for large dense problems,
-// 128 x 256 for contiguous groups (a tile may not straddle two 128-row expert
-// blocks), 128 x 128 for mid-size rows, and for decode-size rows (HBM-bound:
+// Tile choice: 256 x 256 (8 waves of 128 x 64) for large dense problems and
+// for contiguous groups (a 256-row tile runs once per distinct expert of its
+// two 128-row blocks), 128 x 128 for mid-size rows, and for decode-size rows (HBM-bound:
 // every B byte is used once) narrow 64-column tiles with deeper pipelines, so
 // more workgroups stream B with more bytes in flight each.
-enum NtTile { kT64x64, kT128x64, kT128x128, kT128x256, kT256x256 };
+enum NtTile { kT64x64, kT128x64, kT128x128, kT256x256 };
 
 NtTile choose_tile(const NtProblem& pr) {
-    if (pr.form == kContiguous) return kT128x256;
+    if (pr.form == kContiguous) return kT256x256;
     if (pr.form == kDense && pr.rows <= 64) return kT64x64;
     if (pr.form == kDense && pr.rows <= 128) return kT128x64;
     if (pr.rows <= 64) return kT64x64;
@@ -402,12 +425,15 @@ NtTile choose_tile(const NtProblem& pr) {
 
 template <int FORM, bool OUT_F32>
 hipError_t dispatch_tiles(const NtProblem& pr, int cu_cap, hipStream_t stream) {
+    if constexpr (FORM == kContiguous) {
+        return launch_cfg<Cfg256x256, FORM, OUT_F32>(pr, cu_cap, stream);
+    } else {
     switch (choose_tile(pr)) {
     case kT64x64: return launch_cfg<Cfg64x64, FORM, OUT_F32>(pr, cu_cap, stream);
     case kT128x64: return launch_cfg<Cfg128x64, FORM, OUT_F32>(pr, cu_cap, stream);
-    case kT128x256: return launch_cfg<Cfg128x256, FORM, OUT_F32>(pr, cu_cap, stream);
     case kT256x256: return launch_cfg<Cfg256x256, FORM, OUT_F32>(pr, cu_cap, stream);
     default: return launch_cfg<Cfg128x128, FORM, OUT_F32>(pr, cu_cap, stream);
+    }
     }
 }
 
@@ -427,7 +453,7 @@ hipError_t launch_nt(const NtProblem& pr, int cu_cap, hipStream_t stream) {
 }
 
 const char* nt_config_name(const NtProblem& pr) {
-    static const char* tiles[] = {"64x64", "128x64", "128x128", "128x256", "256x256"};
+    static const char* tiles[] = {"64x64", "128x64", "128x128", "256x256"};
     static const char* forms[] = {"dense", "contiguous", "masked"};
     static thread_local char buf[64];
     snprintf(buf, sizeof buf, "nt_%s_%s_%s", forms[(int)pr.form],
