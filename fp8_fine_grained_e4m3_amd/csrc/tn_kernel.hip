@@ -12,13 +12,26 @@
 // scale sa[m] * sb[n] (news article "Deepseek AI Libera Deepgemm ...", section
 // "Details and technical benefits": two-level accumulation).
 //
-// The MFMA wants 32 K-consecutive bytes of one row per lane, while memory
-// holds M (or N) consecutive bytes of one K row.  Each thread loads an 8 x 8
-// byte block (8 K rows x 8 columns, coalesced along the columns), transposes
-// it in registers with byte permutes, and writes 8 K-consecutive bytes per
-// column into the same swizzled K-major LDS layout the NT kernel uses.  From
-// there on the block product, promotion and epilogue mirror the NT kernel,
-// with fp32 C read and fp32 D written.
+// Staging: per 128-row K block, the A tile [128 k x BM] and the B tile
+// [128 k x BN] are copied global -> LDS as they lie in memory (one LDS row per
+// K row; 16-byte chunk c of row k at position c ^ f(k)), together with the
+// block's scales, by global_load_lds; STAGES - 1 blocks are in flight.
+//
+// Fragments: the MFMA wants, per lane, 32 K-consecutive bytes of one column
+// (one m or one n).  gfx950's transposing LDS read ds_read_b64_tr_b8 produces
+// them from the MN-major tile: within each 16-lane group, lane k names 8 bytes
+// (chunk C_k) and lane i + 8h (i < 8) receives byte i of C_{2j+h} as its
+// byte j.  Lane k of a group names K row kbase + (k >> 1) at column offset
+// 8 (k & 1) of a 16-column chunk, so lane r of the group receives column r's
+// K values kbase .. kbase + 7; four reads (kbase = 32 g + 8 q for the lane's
+// K quarter g, q = 0..3) make the lane's 32 bytes.  The chunk swizzle f(k)
+// keeps each 32-lane half of a read on 32 distinct 8-byte bank slots.
+//
+// The block product runs on the MFMA unit (the B fragment as row operand, A as
+// column operand: a lane's 4 results share one m and cover 4 consecutive n),
+// the promotion acc += P * (sa[m] * sb[n]) on the VALU, software-pipelined two
+// block products behind.  The accumulator starts from C (its loads overlap the first
+// copies), so the epilogue is a plain fp32 store.
 //
 // Scheduling: the host passes each group's K-block range and a processing
 // order (largest K first, so the longest tiles start first); the persistent
@@ -47,68 +60,67 @@ struct TnArgs {
     int32_t kb_count[kMaxTnGroups];   // number of 128-K blocks of group g
 };
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
 struct TnCfg {
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int WAVES = WAVES_M * WAVES_N;
     static constexpr int THREADS = 64 * WAVES;
+    static constexpr int STAGES = STAGES_;
     static constexpr int WTM = BM / WAVES_M;
     static constexpr int WTN = BN / WAVES_N;
     static constexpr int SM = WTM / 16;
     static constexpr int SN = WTN / 16;
-    static constexpr int A_BYTES = BM * kKBlk;
-    static constexpr int B_BYTES = BN * kKBlk;
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int A_BLK = (kKBlk / 8) * (BM / 8) / THREADS;   // 8x8 blocks per thread
-    static constexpr int B_BLK = (kKBlk / 8) * (BN / 8) / THREADS;
-    static_assert(A_BLK * THREADS == (kKBlk / 8) * (BM / 8), "A tile must split evenly");
-    static_assert(B_BLK * THREADS == (kKBlk / 8) * (BN / 8), "B tile must split evenly");
+    static constexpr int A_BYTES = kKBlk * BM;
+    static constexpr int B_BYTES = kKBlk * BN;
+    static constexpr int SA_OFF = A_BYTES + B_BYTES;
+    static constexpr int SB_OFF = SA_OFF + 4 * BM;
+    static constexpr int STAGE_BYTES = SB_OFF + 4 * BN;
+    static constexpr int A_DMA = A_BYTES / 1024;   // 1 KiB wave copies per stage
+    static constexpr int B_DMA = B_BYTES / 1024;
+    static constexpr int SA_DMA = BM / 64;         // 256-byte (64-float) wave copies
+    static constexpr int SB_DMA = BN / 64;
+    static constexpr int DMA_PER_WAVE = (A_DMA + B_DMA) / WAVES;
+    static constexpr int VM_PER_STAGE = DMA_PER_WAVE + 1;
+    static_assert((A_DMA + B_DMA) % WAVES == 0, "tile copies must split evenly over waves");
+    static_assert(SA_DMA + SB_DMA <= WAVES, "at most one scale copy per wave");
+    static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "row widths");
+    static_assert(WTM % 64 == 0 && WTN % 16 == 0, "wave tile");
+    static_assert(STAGES >= 2 && (STAGES - 2) * VM_PER_STAGE <= 63, "vmcnt range");
 };
 
-// 4 x 4 byte transpose: out[j] byte i = in[i] byte j.
-__device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
-                                             uint32_t& c0, uint32_t& c1, uint32_t& c2,
-                                             uint32_t& c3) {
-    // __builtin_amdgcn_perm(hi, lo, sel): selector bytes 0..3 pick from lo, 4..7 from hi
-    const uint32_t t0 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);   // r0.0 r1.0 r0.1 r1.1
-    const uint32_t t1 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);   // r0.2 r1.2 r0.3 r1.3
-    const uint32_t t2 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
-    const uint32_t t3 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
-    c0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);                  // t0.0 t0.1 t2.0 t2.1
-    c1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);                  // t0.2 t0.3 t2.2 t2.3
-    c2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-    c3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
-}
-
-// rows[i] = 8 bytes (columns 0..7) of K row i; out[j] = 8 bytes (K rows 0..7) of column j.
-__device__ __forceinline__ void transpose8x8(const i32x2 rows[8], i32x2 out[8]) {
-    uint32_t c0, c1, c2, c3;
-    // columns 0..3, K 0..3 -> low dwords
-    transpose4x4(rows[0].x, rows[1].x, rows[2].x, rows[3].x, c0, c1, c2, c3);
-    out[0].x = c0; out[1].x = c1; out[2].x = c2; out[3].x = c3;
-    // columns 0..3, K 4..7 -> high dwords
-    transpose4x4(rows[4].x, rows[5].x, rows[6].x, rows[7].x, c0, c1, c2, c3);
-    out[0].y = c0; out[1].y = c1; out[2].y = c2; out[3].y = c3;
-    // columns 4..7
-    transpose4x4(rows[0].y, rows[1].y, rows[2].y, rows[3].y, c0, c1, c2, c3);
-    out[4].x = c0; out[5].x = c1; out[6].x = c2; out[7].x = c3;
-    transpose4x4(rows[4].y, rows[5].y, rows[6].y, rows[7].y, c0, c1, c2, c3);
-    out[4].y = c0; out[5].y = c1; out[6].y = c2; out[7].y = c3;
+// Swizzle of an MN-major LDS tile with W-byte rows: 16-byte chunk c of K row
+// `row` sits at chunk position c ^ tn_swz<W>(row).  A transposing read touches
+// rows 32 g + 8 q + 0..7 (g = 0, 1 in one 32-lane half); the low bits spread
+// those 8 rows, bit 5 of the row moves the second group to the other half of
+// the banks.
+template <int W>
+__device__ __forceinline__ int tn_swz(int row) {
+    if constexpr (W == 128) return ((row >> 1) & 3) | (((row >> 5) & 1) << 2);
+    else return (row & 7) | (((row >> 5) & 1) << 3);
 }
 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, THREADS = Cfg::THREADS;
-    constexpr int SM = Cfg::SM, SN = Cfg::SN, A_BLK = Cfg::A_BLK, B_BLK = Cfg::B_BLK;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Cfg::STAGE_BYTES];
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, SM = Cfg::SM, SN = Cfg::SN;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::STAGES * Cfg::STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / Cfg::WAVES_N;
     const int wn = wave % Cfg::WAVES_N;
     const int per_group = p.tiles_m * p.tiles_n;
+    const uint32_t lds0 = lds_addr(smem);
+    const int r16 = lane & 15;
+
+    // Per-lane part of the transposing fragment reads: K row 32 g + (k >> 1)
+    // (+ 8 q), column offset 8 (k & 1), for lane (g, k) = (lane >> 4, lane & 15).
+    const int tr_row = 32 * (lane >> 4) + (r16 >> 1);
+    const int a_lane = tr_row * BM + 8 * (r16 & 1);
+    const int b_lane = Cfg::A_BYTES + tr_row * BN + 8 * (r16 & 1);
+    const int a_x = tn_swz<BM>(tr_row);
+    const int b_x = tn_swz<BN>(tr_row);
 
     for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
         const int gi = t / per_group;
@@ -118,142 +130,167 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         const int tn = local / p.tiles_m;
         const int m0 = tm * BM, n0 = tn * BN;
         const int kb0 = p.kb_start[g];
-        const int KBg = p.kb_count[g];
+        const int nkb = p.kb_count[g];
+        const int64_t gbase = (int64_t)g * p.M * p.N;
 
-        // Per-thread 8x8 block coordinates; columns clamped so loads stay in bounds.
-        uint32_t ga_off[A_BLK], gb_off[B_BLK];
+        // Copy offsets.  Copy u of A moves 1024 / BM K rows: lane l fills LDS
+        // chunk position l % (BM / 16) of row u * (1024 / BM) + l / (BM / 16),
+        // i.e. loads the chunk that the swizzle places there.  Chunks past the
+        // M (or N) edge re-read the last chunk; their columns are never stored.
+        uint32_t goff[Cfg::DMA_PER_WAVE];
 #pragma unroll
-        for (int q = 0; q < A_BLK; ++q) {
-            const int blk = tid + q * THREADS;
-            const int cq = blk % (BM / 8), kq = blk / (BM / 8);
-            const int col = min(m0 + cq * 8, p.M - 8);
-            ga_off[q] = (uint32_t)(kq * 8) * (uint32_t)p.M + (uint32_t)col;
+        for (int q = 0; q < Cfg::DMA_PER_WAVE; ++q) {
+            const int u = wave * Cfg::DMA_PER_WAVE + q;
+            if (u < Cfg::A_DMA) {
+                const int row = u * (1024 / BM) + lane / (BM / 16);
+                const int ch = (lane % (BM / 16)) ^ tn_swz<BM>(row);
+                goff[q] = (uint32_t)row * (uint32_t)p.M + (uint32_t)min(m0 + 16 * ch, p.M - 16);
+            } else {
+                const int uu = u - Cfg::A_DMA;
+                const int row = uu * (1024 / BN) + lane / (BN / 16);
+                const int ch = (lane % (BN / 16)) ^ tn_swz<BN>(row);
+                goff[q] = (uint32_t)row * (uint32_t)p.N + (uint32_t)min(n0 + 16 * ch, p.N - 16);
+            }
         }
-#pragma unroll
-        for (int q = 0; q < B_BLK; ++q) {
-            const int blk = tid + q * THREADS;
-            const int cq = blk % (BN / 8), kq = blk / (BN / 8);
-            const int col = min(n0 + cq * 8, p.N - 8);
-            gb_off[q] = (uint32_t)(kq * 8) * (uint32_t)p.N + (uint32_t)col;
+        // Scale copies, one per wave: copies [0, SA_DMA) fill A-scale slots,
+        // the next SB_DMA fill B-scale slots, surplus waves repeat one (same
+        // bytes to the same place).  A slot wm*WTM + r*SM + i holds the scale of
+        // column wm*WTM + 16 i + r, so a lane's SM scales are consecutive.
+        const int scopy = wave % (Cfg::SA_DMA + Cfg::SB_DMA);
+        const bool s_is_a = scopy < Cfg::SA_DMA;
+        uint32_t s_off, s_lds;
+        if (s_is_a) {
+            const int slot = 64 * scopy + lane;
+            const int wms = slot / Cfg::WTM, rem = slot % Cfg::WTM;
+            const int col = wms * Cfg::WTM + 16 * (rem % SM) + rem / SM;
+            s_off = 4u * (uint32_t)min(m0 + col, p.M - 1);
+            s_lds = Cfg::SA_OFF + 256 * scopy;
+        } else {
+            const int slot = 64 * (scopy - Cfg::SA_DMA) + lane;
+            s_off = 4u * (uint32_t)min(n0 + slot, p.N - 1);
+            s_lds = Cfg::SB_OFF + 256 * (scopy - Cfg::SA_DMA);
         }
-        int sa_idx[SM];
-#pragma unroll
-        for (int i = 0; i < SM; ++i)
-            sa_idx[i] = min(m0 + wm * Cfg::WTM + 16 * i + (lane & 15), p.M - 1);
-        int sb_idx[SN];
-#pragma unroll
-        for (int j = 0; j < SN; ++j)
-            sb_idx[j] = min(n0 + wn * Cfg::WTN + 16 * j + 4 * (lane >> 4), p.N - 4);
-
-        f32x4 acc[SM][SN];
-#pragma unroll
-        for (int i = 0; i < SM; ++i)
-#pragma unroll
-            for (int j = 0; j < SN; ++j)
-                acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        i32x2 ra[A_BLK][8], rb[B_BLK][8];
-        float sa_cur[SM], sa_nxt[SM];
-        f32x4 sb_cur[SN], sb_nxt[SN];
-
-        auto gload = [&](int kb) {
+        auto issue_stage = [&](int kb, int stage) {
+            const uint32_t dst = lds0 + stage * Cfg::STAGE_BYTES;
             const uint8_t* ak = p.a + (int64_t)kb * kKBlk * p.M;
             const uint8_t* bk = p.b + (int64_t)kb * kKBlk * p.N;
 #pragma unroll
-            for (int q = 0; q < A_BLK; ++q)
+            for (int q = 0; q < Cfg::DMA_PER_WAVE; ++q) {
+                const int u = wave * Cfg::DMA_PER_WAVE + q;
+                dma16(u < Cfg::A_DMA ? ak : bk, goff[q], dst + u * 1024);
+            }
+            const float* sk = s_is_a ? p.sfa + (int64_t)kb * p.M : p.sfb + (int64_t)kb * p.N;
+            dma4(sk, s_off, dst + s_lds);
+        };
+
+        // The accumulators start from C; its loads overlap the first copies.
+        f32x4 acc[SM][SN];
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    ra[q][i] = *reinterpret_cast<const i32x2*>(ak + ga_off[q] + i * p.M);
+        for (int i = 0; i < SM; ++i) {
+            const int m = min(m0 + wm * Cfg::WTM + 16 * i + r16, p.M - 1);
 #pragma unroll
-            for (int q = 0; q < B_BLK; ++q)
+            for (int j = 0; j < SN; ++j) {
+                const int n = min(n0 + wn * Cfg::WTN + 16 * j + 4 * (lane >> 4), p.N - 4);
+                acc[i][j] = p.c ? *reinterpret_cast<const f32x4*>(p.c + gbase + (int64_t)m * p.N + n)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    rb[q][i] = *reinterpret_cast<const i32x2*>(bk + gb_off[q] + i * p.N);
+        for (int q = 0; q < Cfg::STAGES - 1; ++q)
+            if (q < nkb) issue_stage(kb0 + q, q);
+        int stage = 0;
+        for (int it = 0; it < nkb; ++it) {
+            const int ahead = min(Cfg::STAGES - 2, nkb - 1 - it);
+            wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(ahead);
+            lgkm_drain_barrier();
+            if (it + Cfg::STAGES - 1 < nkb) {
+                int nst = stage + Cfg::STAGES - 1;
+                nst -= nst >= Cfg::STAGES ? Cfg::STAGES : 0;
+                issue_stage(kb0 + it + Cfg::STAGES - 1, nst);
+            }
+            const uint8_t* st = smem + stage * Cfg::STAGE_BYTES;
+            stage = stage + 1 == Cfg::STAGES ? 0 : stage + 1;
+
+            // 16 columns x 128 K of the tile whose LDS rows are `row_bytes` wide,
+            // columns 16 * chunk .. 16 * chunk + 15.
+            auto tr_frag = [&](int lane_off, int chunk, int x, int row_bytes) {
+                const uint8_t* base = st + lane_off + ((chunk ^ x) << 4);
+                i32x8 r;
 #pragma unroll
-            for (int i = 0; i < SM; ++i) sa_nxt[i] = p.sfa[(int64_t)kb * p.M + sa_idx[i]];
+                for (int q = 0; q < 4; ++q) {
+                    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) i32x2*)(base + q * 8 * row_bytes));
+                    r[2 * q] = v.x;
+                    r[2 * q + 1] = v.y;
+                }
+                return r;
+            };
+            float sa[SM];
+#pragma unroll
+            for (int i = 0; i < SM; i += 4) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(
+                    st + Cfg::SA_OFF + 4 * (wm * Cfg::WTM + SM * r16 + i));
+                sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
+            }
+            f32x4 sb[SN];
 #pragma unroll
             for (int j = 0; j < SN; ++j)
-                sb_nxt[j] = *reinterpret_cast<const f32x4*>(p.sfb + (int64_t)kb * p.N + sb_idx[j]);
-        };
-        auto lstore = [&](int stage) {
-            uint8_t* sA = smem + stage * Cfg::STAGE_BYTES;
-            uint8_t* sB = sA + Cfg::A_BYTES;
-#pragma unroll
-            for (int q = 0; q < A_BLK; ++q) {
-                i32x2 cols[8];
-                transpose8x8(ra[q], cols);
-                const int blk = tid + q * THREADS;
-                const int cq = blk % (BM / 8), kq = blk / (BM / 8);
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    *reinterpret_cast<i32x2*>(sA + lds_chunk_off(cq * 8 + j, kq >> 1) +
-                                              (kq & 1) * 8) = cols[j];
-            }
-#pragma unroll
-            for (int q = 0; q < B_BLK; ++q) {
-                i32x2 cols[8];
-                transpose8x8(rb[q], cols);
-                const int blk = tid + q * THREADS;
-                const int cq = blk % (BN / 8), kq = blk / (BN / 8);
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    *reinterpret_cast<i32x2*>(sB + lds_chunk_off(cq * 8 + j, kq >> 1) +
-                                              (kq & 1) * 8) = cols[j];
-            }
-        };
-
-        if (KBg > 0) {
-            gload(kb0);
-            lstore(0);
-        }
-        __syncthreads();
-
-        for (int it = 0; it < KBg; ++it) {
-            const int cur = it & 1;
-#pragma unroll
-            for (int i = 0; i < SM; ++i) sa_cur[i] = sa_nxt[i];
-#pragma unroll
-            for (int j = 0; j < SN; ++j) sb_cur[j] = sb_nxt[j];
-            const bool more = it + 1 < KBg;
-            if (more) gload(kb0 + it + 1);
-
-            const uint8_t* sA = smem + cur * Cfg::STAGE_BYTES;
-            const uint8_t* sB = sA + Cfg::A_BYTES;
+                sb[j] = *reinterpret_cast<const f32x4*>(
+                    st + Cfg::SB_OFF + 4 * (wn * Cfg::WTN + 16 * j + 4 * (lane >> 4)));
             i32x8 bfrag[SN];
 #pragma unroll
             for (int j = 0; j < SN; ++j)
-                bfrag[j] = lds_fragment(sB, wn * Cfg::WTN + 16 * j, lane);
+                bfrag[j] = tr_frag(b_lane, (wn * Cfg::WTN) / 16 + j, b_x, BN);
+            i32x8 afrag = tr_frag(a_lane, (wm * Cfg::WTM) / 16, a_x, BM);
+            // Block products t = SN * i + j in order; the promotion of product t
+            // runs after product t + 2 is issued (three results in flight).
+            auto promote = [&](const f32x4& pr, int i, int j) {
+                const float s = sa[i];
+                acc[i][j].x = __builtin_fmaf(pr.x, s * sb[j].x, acc[i][j].x);
+                acc[i][j].y = __builtin_fmaf(pr.y, s * sb[j].y, acc[i][j].y);
+                acc[i][j].z = __builtin_fmaf(pr.z, s * sb[j].z, acc[i][j].z);
+                acc[i][j].w = __builtin_fmaf(pr.w, s * sb[j].w, acc[i][j].w);
+            };
+            f32x4 pbuf[3];
 #pragma unroll
             for (int i = 0; i < SM; ++i) {
-                const i32x8 afrag = lds_fragment(sA, wm * Cfg::WTM + 16 * i, lane);
+                i32x8 anext;
+                if (i + 1 < SM) anext = tr_frag(a_lane, (wm * Cfg::WTM) / 16 + i + 1, a_x, BM);
 #pragma unroll
                 for (int j = 0; j < SN; ++j) {
-                    const f32x4 pblk = mfma_e4m3_block(bfrag[j], afrag);
-                    const float sa = sa_cur[i];
-                    acc[i][j].x = __builtin_fmaf(pblk.x, sa * sb_cur[j].x, acc[i][j].x);
-                    acc[i][j].y = __builtin_fmaf(pblk.y, sa * sb_cur[j].y, acc[i][j].y);
-                    acc[i][j].z = __builtin_fmaf(pblk.z, sa * sb_cur[j].z, acc[i][j].z);
-                    acc[i][j].w = __builtin_fmaf(pblk.w, sa * sb_cur[j].w, acc[i][j].w);
+                    const int t = SN * i + j;
+                    pbuf[t % 3] = mfma_e4m3_block(bfrag[j], afrag);
+                    if (t >= 2) promote(pbuf[(t - 2) % 3], (t - 2) / SN, (t - 2) % SN);
                 }
+                if (i + 1 < SM) afrag = anext;
+                // Issue order: the next A fragment's reads, then each block
+                // product followed by the promotion of the product two back.
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // 4 DS reads
+#pragma unroll
+                for (int j = 0; j < SN; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (more) lstore(cur ^ 1);
-            __syncthreads();
+            constexpr int T = SM * SN;
+            promote(pbuf[(T - 2) % 3], (T - 2) / SN, (T - 2) % SN);
+            promote(pbuf[(T - 1) % 3], (T - 1) / SN, (T - 1) % SN);
         }
+        // every wave is past its last LDS read before the next tile's copies
+        lds_barrier();
 
-        // epilogue: D[g] = C[g] + acc, fp32, rows/cols inside [M, N]
-        const int64_t gbase = (int64_t)g * p.M * p.N;
+        // epilogue: D[g] = acc (C already included), fp32, inside [M, N]
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
-            const int m = m0 + wm * Cfg::WTM + 16 * i + (lane & 15);
+            const int m = m0 + wm * Cfg::WTM + 16 * i + r16;
             if (m >= p.M) continue;
 #pragma unroll
             for (int j = 0; j < SN; ++j) {
                 const int n = n0 + wn * Cfg::WTN + 16 * j + 4 * (lane >> 4);
                 if (n >= p.N) continue;
-                const int64_t off = gbase + (int64_t)m * p.N + n;
-                f32x4 v = acc[i][j];
-                if (p.c) v += *reinterpret_cast<const f32x4*>(p.c + off);
-                *reinterpret_cast<f32x4*>(p.d + off) = v;
+                *reinterpret_cast<f32x4*>(p.d + gbase + (int64_t)m * p.N + n) = acc[i][j];
             }
         }
     }
@@ -261,7 +298,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
 
 namespace {
 
-using TnCfg128 = TnCfg<128, 128, 2, 2>;
+using TnCfg256 = TnCfg<256, 256, 2, 4, 2>;
 
 template <class Cfg>
 hipError_t launch_tn_cfg(const TnProblem& pr, int cu_cap, hipStream_t stream) {
@@ -303,10 +340,10 @@ hipError_t launch_tn_cfg(const TnProblem& pr, int cu_cap, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_tn(const TnProblem& pr, int cu_cap, hipStream_t stream) {
-    return launch_tn_cfg<TnCfg128>(pr, cu_cap, stream);
+    return launch_tn_cfg<TnCfg256>(pr, cu_cap, stream);
 }
 
-const char* tn_config_name(const TnProblem&) { return "tn_kgrouped_f32_128x128"; }
+const char* tn_config_name(const TnProblem&) { return "tn_kgrouped_f32_256x256"; }
 
 const char* describe_tn_config(const TnProblem& pr) {
     static thread_local char buf[192];

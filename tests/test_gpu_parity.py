@@ -395,6 +395,46 @@ def test_k_grouped_power_of_two_is_bit_exact():
     assert np.array_equal(got, oracle.k_grouped_tn(a, sfa, b, sfb, ks))
 
 
+@pytest.mark.parametrize("M,N,ks", [(16, 16, [128, 0, 256]), (272, 528, [1280, 384]),
+                                    (256, 256, [2560]), (512, 144, [128] * 7)])
+def test_k_grouped_shapes(M, N, ks):
+    """Tiles smaller than, equal to and ragged against the 256x256 tile; one
+    long group (many K blocks through the stage ring); many short groups."""
+    announce(f"k-grouped shapes M={M} N={N} ks={ks}")
+    ks = np.array(ks, np.int32)
+    x = gen.gen_k_grouped(G=len(ks), M=M, N=N, K_tot=int(ks.sum()), k_sizes=ks, seed=M + N)
+    d = run_tn(x, c=x.c)
+    ref = oracle.k_grouped_tn(x.a, x.sfa, x.b, x.sfb, x.k_sizes, x.c)
+    check_close(d.cpu().numpy().astype(np.float64), ref, f"tn {M}x{N}")
+
+
+def test_k_grouped_one_hot_k_mapping_is_bit_exact():
+    """Column m of A and column n of B each hold a single 1.0 at a random K
+    index inside the group; D[g][m, n] = 1 exactly where the two indices meet,
+    which pins which K row every lane's transposed fragment reads."""
+    announce("k-grouped one-hot K map")
+    ks = np.array([256, 384], np.int32)
+    K_tot, M, N = 640, 272, 528
+    rng = np.random.default_rng(77)
+    a = np.zeros((K_tot, M), np.uint8)
+    b = np.zeros((K_tot, N), np.uint8)
+    off = 0
+    for kg in ks:
+        # few distinct K indices so that matches are frequent
+        ka = off + rng.integers(0, 8, M) * (kg // 8) + rng.integers(0, 2, M)
+        kb = off + rng.integers(0, 8, N) * (kg // 8) + rng.integers(0, 2, N)
+        a[ka, np.arange(M)] = 0x38
+        b[kb, np.arange(N)] = 0x38
+        off += int(kg)
+    sfa = np.ones((K_tot // 128, M), np.float32)
+    sfb = np.ones((K_tot // 128, N), np.float32)
+    x = gen.KGroupedInputs(a, sfa, b, sfb, ks, ks.astype(np.int64), None, 2, M, N, K_tot)
+    got = run_tn(x).cpu().numpy().astype(np.float64)
+    ref = oracle.k_grouped_tn(a, sfa, b, sfb, ks)
+    assert ref.sum() > 100
+    assert np.array_equal(got, ref)
+
+
 def test_c5_k_grouped_full_size():
     announce("k-grouped C5 32 groups M=2048 N=4096 K_tot=49152 seed0")
     x = gen.gen_k_grouped(seed=0)

@@ -30,7 +30,7 @@ def device_asm(src, tmp_path):
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-@pytest.mark.parametrize("src", ["nt_kernel.hip"])
+@pytest.mark.parametrize("src", ["nt_kernel.hip", "tn_kernel.hip"])
 def test_every_lds_dma_is_padded(src, tmp_path):
     lines = device_asm(os.path.join(CSRC, src), tmp_path)
     n = 0
