@@ -261,6 +261,21 @@ def measured_traffic(config_name: str):
     return None
 
 
+def instance_matcher(name):
+    """Predicate on demangled kernel names selecting the template instance
+    behind a config name such as nt_dense_bf16_256x256 or
+    tn_kgrouped_f32_256x256; also returns a readable tag."""
+    kind, form, out, tile = name.split("_")
+    bm, bn = tile.split("x")
+    if kind == "tn":
+        tag = f"TnCfg<{bm}, {bn},"
+        return (lambda k: "tn_fp8_kernel" in k and tag in k), tag + " ...>"
+    form_id = {"dense": 0, "contiguous": 1, "masked": 2}[form]
+    tail = f", {form_id}, {'true' if out == 'f32' else 'false'}>"
+    tag = f"NtCfg<{bm}, {bn},"
+    return (lambda k: "nt_fp8_kernel" in k and tag in k and tail in k), tag + " ...>" + tail
+
+
 def summarize_profiles(trace_dir, fetch_dir, write_dir, bench_json, out_path, commands):
     """Write the profiles/ summary of one kernel instance from rocprofv3 CSVs."""
     import csv
@@ -280,10 +295,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, bench_json, out_path, co
     fetch_copy = max(v for k, v, g in fetch if "copyBuffer" in k) * 1024.0
     write_copy = max(v for k, v, g in write if "copyBuffer" in k) * 1024.0
     f_scale, w_scale = copy_bytes / fetch_copy, copy_bytes / write_copy
-    tag = {"256x256": "NtCfg<256, 256, 2, 4>", "128x256": "NtCfg<128, 256, 2, 4>",
-           "128x128": "NtCfg<128, 128, 2, 2>", "64x128": "NtCfg<64, 128, 1, 4>"}[name.split("_")[-1]]
-    f_k = [v for k, v, g in fetch if tag in k]
-    w_k = [v for k, v, g in write if tag in k]
+    match, tag = instance_matcher(name)
+    f_k = [v for k, v, g in fetch if match(k)]
+    w_k = [v for k, v, g in write if match(k)]
     fetch_b = float(np.mean(f_k)) * 1024.0 * f_scale
     write_b = float(np.mean(w_k)) * 1024.0 * w_scale
     lines = [f"# {name} -- dense FP8 NT sweep (M=4096 shapes), rocprofv3", "",
@@ -294,7 +308,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, bench_json, out_path, co
     for r in stats:
         lines.append(f"| `{r['Name'][:80]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
-    avg_us = [float(r["AverageNs"]) / 1e3 for r in stats if tag in r["Name"]][0]
+    avg_us = [float(r["AverageNs"]) / 1e3 for r in stats if match(r["Name"])][0]
     lines += ["", f"Dominant instance `{tag}` = `{name}`: rocprofv3 average {avg_us:.2f} us per "
               f"launch; bench.py's HIP-event average over its timed region {roof['avg_launch_us']} us.",
               f"Launches of this instance per step: {roof['launches_per_step']} "

@@ -50,6 +50,7 @@ struct NtArgs {
     int tiles_n;
     int num_tiles;     // enumerated tiles (masked: G * tiles_m * tiles_n)
     int band_m;        // grouped rasterisation: bands of band_m M tiles
+    int xcd_remap;     // 1: give each XCD a contiguous run of the tile order
 };
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
@@ -131,6 +132,15 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             // `half` (pass 1 only when that expert differs from block 0's).
             half = t / per_group;
             local = t - half * per_group;
+        }
+        // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so
+        // with a grid that is a multiple of 8, tile t runs on XCD t % 8.  The
+        // remap gives each XCD one contiguous run of the raster order, so the
+        // tiles an XCD has in flight together share A and B panels in its L2.
+        if (FORM == kDense && p.xcd_remap) {
+            const int per = p.num_tiles >> 3, extra = p.num_tiles & 7;
+            const int x = t & 7;
+            local = x * per + min(x, extra) + (t >> 3);
         }
         // Grouped rasterisation: tiles run in bands of band_m M tiles; inside a
         // band N advances after every M tile of the band, so the tiles in
@@ -226,99 +236,129 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             for (int j = 0; j < SN; ++j)
                 acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        const int kb_lo = 0, nkb = KB;
-        // Prologue: the first STAGES - 1 K blocks go in flight.
+        const int nkb = KB;
+        // Stage ring: block kb lives in stage kb % STAGES.  The prologue puts
+        // blocks 0 .. STAGES-1 in flight (the last one once block 0 has landed
+        // and the barrier has passed); iteration it, once every wave is done
+        // reading block it, refills its stage with block it + STAGES.
 #pragma unroll
         for (int q = 0; q < Cfg::STAGES - 1; ++q)
-            if (q < nkb) issue_stage(kb_lo + q, q);
-        int stage = 0;   // stage holding block kb
-        for (int it = 0; it < nkb; ++it) {
-            // Block kb_lo + it has landed for this wave once at most `ahead` later
-            // stages' copies are outstanding; the barrier then makes every wave's
-            // copies visible and guarantees every wave is done with the stage the
-            // next copy overwrites (read in the previous iteration).
-            const int ahead = min(Cfg::STAGES - 2, nkb - 1 - it);
-            wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(ahead);
-            lgkm_drain_barrier();
-            if (it + Cfg::STAGES - 1 < nkb) {
-                int nst = stage + Cfg::STAGES - 1;
-                nst -= nst >= Cfg::STAGES ? Cfg::STAGES : 0;
-                issue_stage(kb_lo + it + Cfg::STAGES - 1, nst);
-            }
-            const uint8_t* st = smem + stage * Cfg::STAGE_BYTES;
-            stage = stage + 1 == Cfg::STAGES ? 0 : stage + 1;
+            if (q < nkb) issue_stage(q, q);
+        wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(min(Cfg::STAGES - 2, nkb - 1));
+        lgkm_drain_barrier();
+        if (Cfg::STAGES - 1 < nkb) issue_stage(Cfg::STAGES - 1, Cfg::STAGES - 1);
 
-            // Software pipeline over the wave's MFMA rows: the block products of
-            // row i are issued while row i-1 is promoted, so no FMA waits on
-            // the MFMA it depends on.
-            float sa[SM];
+        // Operand reads from one stage: scales, B fragments, A fragment i.
+        auto load_scales = [&](const uint8_t* st, float (&sa)[SM], float& sb) {
 #pragma unroll
             for (int i = 0; i < SM; i += 4) {
                 const f32x4 v = *reinterpret_cast<const f32x4*>(st + s_a + 4 * i);
                 sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
             }
-            const float sb = *reinterpret_cast<const float*>(st + s_b);
-            auto afrag_at = [&](int i) {
-                const uint8_t* rowp = st + ((i & 1) ? a_odd : a_even) + i * kKBlk;
-                const i32x4 lo = *reinterpret_cast<const i32x4*>(rowp + a_lo);
-                const i32x4 hi = *reinterpret_cast<const i32x4*>(rowp + a_hi);
-                i32x8 r;
-                r.s0 = lo.x; r.s1 = lo.y; r.s2 = lo.z; r.s3 = lo.w;
-                r.s4 = hi.x; r.s5 = hi.y; r.s6 = hi.z; r.s7 = hi.w;
-                return r;
-            };
-            i32x8 bfrag[SN];
+            sb = *reinterpret_cast<const float*>(st + s_b);
+        };
+        auto bfrag_at = [&](const uint8_t* st, int j) {
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(st + b_lo + j * 16 * kKBlk);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(st + b_hi + j * 16 * kKBlk);
+            i32x8 r;
+            r.s0 = lo.x; r.s1 = lo.y; r.s2 = lo.z; r.s3 = lo.w;
+            r.s4 = hi.x; r.s5 = hi.y; r.s6 = hi.z; r.s7 = hi.w;
+            return r;
+        };
+        auto afrag_at = [&](const uint8_t* st, int i) {
+            const uint8_t* rowp = st + ((i & 1) ? a_odd : a_even) + i * kKBlk;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(rowp + a_lo);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(rowp + a_hi);
+            i32x8 r;
+            r.s0 = lo.x; r.s1 = lo.y; r.s2 = lo.z; r.s3 = lo.w;
+            r.s4 = hi.x; r.s5 = hi.y; r.s6 = hi.z; r.s7 = hi.w;
+            return r;
+        };
+        // acc[i][j] += pr * s for one MFMA result.  The empty asm pins the
+        // result at this point of the instruction stream: without it the
+        // compiler sinks the promotions past the stage-refill branch, where
+        // they pile up and the products they wait on spill.
+        auto promote1 = [&](int i, int j, const f32x4& pr, float s) {
+            acc[i][j].x = __builtin_fmaf(pr.x, s, acc[i][j].x);
+            acc[i][j].y = __builtin_fmaf(pr.y, s, acc[i][j].y);
+            acc[i][j].z = __builtin_fmaf(pr.z, s, acc[i][j].z);
+            acc[i][j].w = __builtin_fmaf(pr.w, s, acc[i][j].w);
+            asm volatile("" : "+v"(acc[i][j]));
+        };
+
+        float sa[SM], sb;
+        i32x8 bfrag[SN];
+        load_scales(smem, sa, sb);
 #pragma unroll
-            for (int j = 0; j < SN; ++j) {
-                const i32x4 lo = *reinterpret_cast<const i32x4*>(st + b_lo + j * 16 * kKBlk);
-                const i32x4 hi = *reinterpret_cast<const i32x4*>(st + b_hi + j * 16 * kKBlk);
-                bfrag[j].s0 = lo.x; bfrag[j].s1 = lo.y; bfrag[j].s2 = lo.z; bfrag[j].s3 = lo.w;
-                bfrag[j].s4 = hi.x; bfrag[j].s5 = hi.y; bfrag[j].s6 = hi.z; bfrag[j].s7 = hi.w;
-            }
-            i32x8 afrag = afrag_at(0);
-            f32x4 pend[SN];
+        for (int j = 0; j < SN; ++j) bfrag[j] = bfrag_at(smem, j);
+        i32x8 afrag = afrag_at(smem, 0);
+
+        // The promotion runs one MFMA row behind, across K blocks too: row 0 of
+        // block kb promotes row SM-1 of block kb-1 (with that block's scale
+        // s_prev).  Before the first block there is nothing to promote:
+        // pend = 0 and s_prev = 0 leave acc unchanged.
+        f32x4 pend[SN];
 #pragma unroll
-            for (int i = 0; i < SM; ++i) {
+        for (int j = 0; j < SN; ++j) pend[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float s_prev = 0.f;
+
+        int stage = 0;   // stage holding block it
+        for (int it = 0; it < nkb; ++it) {
+            const uint8_t* st = smem + stage * Cfg::STAGE_BYTES;
+            const int next = stage + 1 == Cfg::STAGES ? 0 : stage + 1;
+            const uint8_t* st_next = smem + next * Cfg::STAGE_BYTES;
+
+            // Rows 0 .. SM-2.  Step (i, j) issues block product (i, j) and
+            // promotes (i-1, j); row i+1's A fragment is requested at step
+            // (i, 0).  The scheduling fences keep exactly this order, so every
+            // FMA reads an MFMA result issued SN steps earlier and no more than
+            // two rows of products are live.
+#pragma unroll
+            for (int i = 0; i + 1 < SM; ++i) {
+                const float s = i == 0 ? s_prev : sa[i - 1] * sb;
+                const int ip = i == 0 ? SM - 1 : i - 1;
                 i32x8 anext;
-                if (i + 1 < SM) anext = afrag_at(i + 1);
                 f32x4 pcur[SN];
 #pragma unroll
-                for (int j = 0; j < SN; ++j) pcur[j] = mfma_e4m3_block(bfrag[j], afrag);
-                if (i > 0) {
-                    const float s = sa[i - 1] * sb;
-#pragma unroll
-                    for (int j = 0; j < SN; ++j) {
-                        acc[i - 1][j].x = __builtin_fmaf(pend[j].x, s, acc[i - 1][j].x);
-                        acc[i - 1][j].y = __builtin_fmaf(pend[j].y, s, acc[i - 1][j].y);
-                        acc[i - 1][j].z = __builtin_fmaf(pend[j].z, s, acc[i - 1][j].z);
-                        acc[i - 1][j].w = __builtin_fmaf(pend[j].w, s, acc[i - 1][j].w);
-                    }
+                for (int j = 0; j < SN; ++j) {
+                    pcur[j] = mfma_e4m3_block(bfrag[j], afrag);
+                    if (j == 0) anext = afrag_at(st, i + 1);
+                    promote1(ip, j, pend[j], s);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
                 for (int j = 0; j < SN; ++j) pend[j] = pcur[j];
-                if (i + 1 < SM) afrag = anext;
-                // Issue order inside the segment: the next A fragment's LDS reads
-                // first (a whole segment ahead of their use), then each block
-                // product followed by a share of the previous row's promotion.
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // 2 DS reads
+                afrag = anext;
+            }
+
+            // Every read of this stage has been issued.  Once they complete and
+            // block it+1 has landed for every wave, the stage is refilled, and
+            // the next block's B and A fragments are read under the last row
+            // (B fragment j right after the last product that uses it).
+            wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(
+                max(0, min(Cfg::STAGES - 2, nkb - 2 - it)));
+            lgkm_drain_barrier();
+            if (it + Cfg::STAGES < nkb) issue_stage(it + Cfg::STAGES, stage);
+            __builtin_amdgcn_sched_barrier(0);
+
+            f32x4 plast[SN];
+            const float s = sa[SM - 2] * sb;
 #pragma unroll
-                for (int j = 0; j < SN; ++j) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // 5 VALU
-                }
+            for (int j = 0; j < SN; ++j) {
+                plast[j] = mfma_e4m3_block(bfrag[j], afrag);
+                bfrag[j] = bfrag_at(st_next, j);
+                promote1(SM - 2, j, pend[j], s);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            {
-                const float s = sa[SM - 1] * sb;
+            afrag = afrag_at(st_next, 0);
+            s_prev = sa[SM - 1] * sb;
+            load_scales(st_next, sa, sb);
 #pragma unroll
-                for (int j = 0; j < SN; ++j) {
-                    acc[SM - 1][j].x = __builtin_fmaf(pend[j].x, s, acc[SM - 1][j].x);
-                    acc[SM - 1][j].y = __builtin_fmaf(pend[j].y, s, acc[SM - 1][j].y);
-                    acc[SM - 1][j].z = __builtin_fmaf(pend[j].z, s, acc[SM - 1][j].z);
-                    acc[SM - 1][j].w = __builtin_fmaf(pend[j].w, s, acc[SM - 1][j].w);
-                }
-            }
+            for (int j = 0; j < SN; ++j) pend[j] = plast[j];
+            stage = next;
         }
+#pragma unroll
+        for (int j = 0; j < SN; ++j) promote1(SM - 1, j, pend[j], s_prev);
         // every wave is past its last LDS read before the next tile's copies
         lds_barrier();
 
@@ -376,9 +416,10 @@ hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     a.rows = (int)pr.rows; a.N = (int)pr.N; a.K = (int)pr.K; a.G = (int)pr.G;
     a.tiles_m = (int)((pr.rows + Cfg::BM - 1) / Cfg::BM);
     a.tiles_n = (int)((pr.N + Cfg::BN - 1) / Cfg::BN);
-    // Dense runs M-fastest over all M tiles (one band); contiguous groups use
-    // narrow bands so the tiles in flight share few expert weight panels.
-    a.band_m = (FORM == kContiguous && a.tiles_m > kBandM) ? kBandM : a.tiles_m;
+    // Bands of kBandM M tiles: the tiles in flight share few A row panels and
+    // few B column panels (for contiguous groups: few expert weight panels).
+    a.band_m = (FORM != kMasked && a.tiles_m > kBandM) ? kBandM : a.tiles_m;
+    a.xcd_remap = FORM == kDense ? 1 : 0;
     static_assert(FORM != kContiguous || Cfg::BM == 2 * kKBlk, "contiguous tiles span two blocks");
     const int64_t groups = (FORM == kMasked) ? pr.G : (FORM == kContiguous ? 2 : 1);
     const int64_t tiles = groups * a.tiles_m * a.tiles_n;
