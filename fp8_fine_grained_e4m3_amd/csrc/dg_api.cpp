@@ -10,8 +10,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
+#include <utility>
 
 namespace {
 
@@ -105,11 +107,22 @@ bool print_configs() {
     return v == 1;
 }
 
-dg_status run_nt(const dg::NtProblem& p, void* stream) {
+// ---- split-K workspace ------------------------------------------------------------
+
+struct Workspace {
+    float* part = nullptr;
+    int32_t* counters = nullptr;
+    size_t part_floats = 0, n_counters = 0;
+};
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::mutex g_ws_mutex;
+
+dg_status run_nt(dg::NtProblem p, void* stream) {
     int dev = 0;
     DeviceInfo info;
     dg_status st = current_device(dev, info);
     if (st != DG_OK) return st;
+    p.device_cus = info.cus;
     if (print_configs()) fprintf(stderr, "[dg] %s\n", dg::describe_nt_config(p));
     hipError_t e = dg::launch_nt(p, cu_cap_for(info), reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
@@ -117,6 +130,49 @@ dg_status run_nt(const dg::NtProblem& p, void* stream) {
 }
 
 }  // namespace
+
+namespace dg {
+
+bool split_workspace(hipStream_t stream, size_t part_floats, size_t n_counters,
+                     SplitWorkspace* ws) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& w = g_ws[{dev, stream}];
+    if (w.part_floats < part_floats || w.n_counters < n_counters) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+            return false;
+        // grow to cover this request and every earlier one
+        const size_t pf = part_floats > w.part_floats ? part_floats : w.part_floats;
+        const size_t nc = n_counters > w.n_counters ? n_counters : w.n_counters;
+        // the old buffers may still be in use by work queued on this stream
+        if (w.part || w.counters) {
+            if (hipStreamSynchronize(stream) != hipSuccess) return false;
+            (void)hipFree(w.part);
+            (void)hipFree(w.counters);
+            w = Workspace{};
+        }
+        float* part = nullptr;
+        int32_t* counters = nullptr;
+        if (hipMalloc(&part, pf * sizeof(float)) != hipSuccess) return false;
+        if (hipMalloc(&counters, nc * sizeof(int32_t)) != hipSuccess ||
+            hipMemsetAsync(counters, 0, nc * sizeof(int32_t), stream) != hipSuccess) {
+            (void)hipFree(part);
+            if (counters) (void)hipFree(counters);
+            return false;
+        }
+        w.part = part;
+        w.counters = counters;
+        w.part_floats = pf;
+        w.n_counters = nc;
+    }
+    ws->part = w.part;
+    ws->counters = w.counters;
+    return true;
+}
+
+}  // namespace dg
 
 extern "C" {
 

@@ -22,6 +22,7 @@ struct NtProblem {
     int64_t rows;             // dense: M, contiguous: M_tot, masked: M_max
     int64_t N, K, G;
     bool out_f32;
+    int device_cus;           // CUs of the device (not the cap): sizes the K split
 };
 
 struct TnProblem {
@@ -36,6 +37,20 @@ struct TnProblem {
 };
 
 constexpr int kMaxTnGroups = 256;
+
+// Device memory for split-K partial tiles, one buffer per (device, stream),
+// grown on demand and kept until the process ends.  `counters` are zero
+// whenever no kernel using them is running (each launch leaves them zero).
+struct SplitWorkspace {
+    float* part = nullptr;
+    int32_t* counters = nullptr;
+};
+// Provide at least part_floats floats and n_counters counters for kernels on
+// `stream`.  Returns false when that is not possible (allocation failure, or
+// the buffer would have to grow while the stream is being captured); the
+// caller then runs without splitting K.
+bool split_workspace(hipStream_t stream, size_t part_floats, size_t n_counters,
+                     SplitWorkspace* ws);
 
 // Launch on `stream`; `cu_cap` bounds the persistent grid.  Return the HIP
 // status of the launch.  Shapes have already been validated.

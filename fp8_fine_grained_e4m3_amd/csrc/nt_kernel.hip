@@ -51,6 +51,11 @@ struct NtArgs {
     int num_tiles;     // enumerated tiles (masked: G * tiles_m * tiles_n)
     int band_m;        // grouped rasterisation: bands of band_m M tiles
     int xcd_remap;     // 1: give each XCD a contiguous run of the tile order
+    // Split K (dense only): each output tile is computed as `splits` partial
+    // sums over consecutive K-block ranges; see the epilogue.
+    int splits;
+    float* part;       // [tiles][splits][SM * SN * 4][THREADS] fp32 partials
+    int32_t* counters; // [tiles], zero between launches
 };
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
@@ -82,6 +87,9 @@ struct NtCfg {
     static_assert(SA_DMA >= 1 && SA_DMA <= WAVES, "one scale copy per wave at most");
     static_assert(BN % kKBlk == 0 || kKBlk % BN == 0, "tiles align with 128-column B scale blocks");
     static_assert(SM % 4 == 0, "a lane reads its A scales as float4s");
+    // Split K is compiled in for tiles whose partial sums fit the batched
+    // reduction in registers (up to 16 MFMA tiles per lane).
+    static constexpr bool SPLIT_OK = SM * SN <= 16;
     static_assert(kKBlk % WTN == 0 && (BN % kKBlk == 0 || kKBlk % BN == 0),
                   "a wave's columns must sit inside one 128-column B scale block");
 };
@@ -121,7 +129,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
 
     for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
         // ---- tile scheduling (uniform over the workgroup) ------------------
-        int g = 0, e = 0, local = t, half = 0;
+        int g = 0, e = 0, local = t, half = 0, split = 0;
         if (FORM == kMasked) {
             g = t / per_group;
             local = t - g * per_group;
@@ -142,6 +150,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             const int x = t & 7;
             local = x * per + min(x, extra) + (t >> 3);
         }
+        if (FORM == kDense) {
+            split = local % p.splits;
+            local /= p.splits;
+        }
+        const int tile_id = local;
         // Grouped rasterisation: tiles run in bands of band_m M tiles; inside a
         // band N advances after every M tile of the band, so the tiles in
         // flight share a few A row panels and a few B column panels.
@@ -171,6 +184,9 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             if (half == 1 && p.m_indices[r0] == e) continue;   // pass 0 already covers it
         }
 
+        // K blocks [kb_lo, kb_lo + nkb) of this work unit (all of K unless split)
+        const int kb_lo = (int)(((int64_t)split * KB) / p.splits);
+        const int nkb = (int)(((int64_t)(split + 1) * KB) / p.splits) - kb_lo;
         const uint8_t* __restrict__ a_t = p.a + grp_row0 * p.K;
         const uint8_t* __restrict__ b_t = p.b + (int64_t)e * p.N * p.K;
         const float* __restrict__ sfa_t = p.sfa + (FORM == kMasked ? (int64_t)g * KB * p.rows : 0);
@@ -201,7 +217,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             4u * (uint32_t)min(r0 + (sa_slot ^ ((sa_slot / SM) & 1)), grp_rows - 1);
         const uint32_t sb_off = 4u * (uint32_t)(min(n0 / kKBlk + lane, NB - 1) * KB);
         const uint32_t lds0 = lds_addr(smem);
-        auto issue_stage = [&](int kb, int stage) {
+        auto issue_stage = [&](int kbr, int stage) {
+            const int kb = kb_lo + kbr;
             const uint32_t dst = lds0 + stage * Cfg::STAGE_BYTES;
 #pragma unroll
             for (int q = 0; q < Cfg::DMA_PER_WAVE; ++q) {
@@ -236,7 +253,6 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             for (int j = 0; j < SN; ++j)
                 acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        const int nkb = KB;
         // Stage ring: block kb lives in stage kb % STAGES.  The prologue puts
         // blocks 0 .. STAGES-1 in flight (the last one once block 0 has landed
         // and the barrier has passed); iteration it, once every wave is done
@@ -362,6 +378,83 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
         // every wave is past its last LDS read before the next tile's copies
         lds_barrier();
 
+        // ---- split K: partial sums meet in the workgroup that finishes last ----
+        // Each work unit stores its fp32 partial tile (lane-private layout, as
+        // device-scope stores, which are written through to the point where
+        // all XCDs see them), waits for the stores, then bumps the tile's
+        // counter.  The unit that brings the counter to splits-1 adds the
+        // partials in split order 0, 1, ... (so the result does not depend on
+        // which unit finishes last), resets the counter for the next launch,
+        // and runs the epilogue; the others are done with the tile.
+        if constexpr (FORM == kDense && Cfg::SPLIT_OK) if (p.splits > 1) {
+            constexpr int PER_UNIT = Cfg::THREADS * SM * SN * 4;
+            float* mine = p.part + ((int64_t)tile_id * p.splits + split) * PER_UNIT;
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+#pragma unroll
+                for (int j = 0; j < SN; ++j) {
+                    // component c of MFMA tile (i, j) of thread tid at
+                    // ((i SN + j) 4 + c) THREADS + tid: each store instruction
+                    // writes 256 contiguous bytes
+                    float* q = mine + (i * SN + j) * 4 * Cfg::THREADS + tid;
+                    __hip_atomic_store(q + 0 * Cfg::THREADS, acc[i][j].x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(q + 1 * Cfg::THREADS, acc[i][j].y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(q + 2 * Cfg::THREADS, acc[i][j].z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(q + 3 * Cfg::THREADS, acc[i][j].w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            // every wave's partial stores have completed before the count
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+            __shared__ int last_flag;
+            if (tid == 0) {
+                const int prior = __hip_atomic_fetch_add(p.counters + tile_id, 1, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+                last_flag = prior == p.splits - 1;
+            }
+            __syncthreads();
+            const bool last = last_flag;
+            __syncthreads();   // last_flag is rewritten by the next tile
+            if (!last) continue;
+            // All partials (this unit's too, read back) are added in split
+            // order.  Loads go in batches of at most 128 floats per lane, all
+            // in flight together: GCH MFMA tiles of BATCH partials at a time.
+            const float* all = p.part + (int64_t)tile_id * p.splits * PER_UNIT + tid;
+            constexpr int NT = SM * SN;                      // MFMA tiles per lane
+            constexpr int GCH = NT < 8 ? NT : 8;
+            constexpr int BATCH = 32 / GCH;
+            static_assert(NT % GCH == 0, "MFMA tiles split into equal groups");
+#pragma unroll
+            for (int g0 = 0; g0 < NT; g0 += GCH) {
+                f32x4 sum[GCH];
+#pragma unroll
+                for (int g = 0; g < GCH; ++g) sum[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int u0 = 0; u0 < p.splits; u0 += BATCH) {
+                    f32x4 buf[BATCH][GCH];
+#pragma unroll
+                    for (int bi = 0; bi < BATCH; ++bi) {
+                        const float* q = all + (int64_t)min(u0 + bi, p.splits - 1) * PER_UNIT;
+#pragma unroll
+                        for (int g = 0; g < GCH; ++g) {
+                            const float* e = q + (g0 + g) * 4 * Cfg::THREADS;
+                            buf[bi][g].x = __hip_atomic_load(e + 0 * Cfg::THREADS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            buf[bi][g].y = __hip_atomic_load(e + 1 * Cfg::THREADS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            buf[bi][g].z = __hip_atomic_load(e + 2 * Cfg::THREADS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            buf[bi][g].w = __hip_atomic_load(e + 3 * Cfg::THREADS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        }
+                    }
+#pragma unroll
+                    for (int bi = 0; bi < BATCH; ++bi)
+                        if (u0 + bi < p.splits) {
+#pragma unroll
+                            for (int g = 0; g < GCH; ++g) sum[g] += buf[bi][g];
+                        }
+                }
+#pragma unroll
+                for (int g = 0; g < GCH; ++g) acc[(g0 + g) / SN][(g0 + g) % SN] = sum[g];
+            }
+            if (tid == 0)
+                __hip_atomic_store(p.counters + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+
         // ---- epilogue: (+C), convert once, masked store ---------------------------
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
@@ -408,6 +501,37 @@ namespace {
 
 constexpr int kBandM = 8;   // M tiles per rasterisation band
 
+constexpr int kMinSplitBlocks = 8;   // K blocks per split work unit, at least
+constexpr int kMaxSplits = 8;
+
+template <class Cfg, int FORM, bool OUT_F32>
+int occupancy_of() {
+    static int occupancy = -1;   // workgroups per CU for this instance
+    if (occupancy < 0) {
+        int occ = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &occ, reinterpret_cast<const void*>(&nt_fp8_kernel<Cfg, FORM, OUT_F32>),
+                Cfg::THREADS, 0) != hipSuccess || occ < 1)
+            occ = 1;
+        occupancy = occ;
+    }
+    return occupancy;
+}
+
+// K split for a dense problem with too few output tiles to give every
+// resident workgroup slot of the device work: as many splits as fill the
+// slots, each split keeping at least kMinSplitBlocks K blocks.  It depends on
+// the shape and the device's CU count only (not on the CU cap), so results
+// are the same under any cap.
+int split_count(int64_t tiles, int KB, int device_cus, int occupancy) {
+    const int64_t slots = (int64_t)device_cus * occupancy;
+    if (tiles <= 0 || tiles * 2 > slots || KB < 2 * kMinSplitBlocks) return 1;
+    int64_t sp = slots / tiles;
+    if (sp > KB / kMinSplitBlocks) sp = KB / kMinSplitBlocks;
+    if (sp > kMaxSplits) sp = kMaxSplits;
+    return sp < 1 ? 1 : (int)sp;
+}
+
 template <class Cfg, int FORM, bool OUT_F32>
 hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     NtArgs a;
@@ -424,19 +548,25 @@ hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     const int64_t groups = (FORM == kMasked) ? pr.G : (FORM == kContiguous ? 2 : 1);
     const int64_t tiles = groups * a.tiles_m * a.tiles_n;
     if (tiles <= 0) return hipSuccess;
-    a.num_tiles = (int)tiles;
+    const int occupancy = occupancy_of<Cfg, FORM, OUT_F32>();
 
-    static int occupancy = -1;   // workgroups per CU for this instance
-    if (occupancy < 0) {
-        int occ = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &occ, reinterpret_cast<const void*>(&nt_fp8_kernel<Cfg, FORM, OUT_F32>),
-                Cfg::THREADS, 0) != hipSuccess || occ < 1)
-            occ = 1;
-        occupancy = occ;
+    a.splits = 1;
+    a.part = nullptr;
+    a.counters = nullptr;
+    if (FORM == kDense && Cfg::SPLIT_OK) {
+        const int sp = split_count(tiles, (int)(pr.K / kKBlk), pr.device_cus, occupancy);
+        SplitWorkspace ws;
+        if (sp > 1 && split_workspace(stream, (size_t)tiles * sp * Cfg::BM * Cfg::BN,
+                                      (size_t)tiles, &ws)) {
+            a.splits = sp;
+            a.part = ws.part;
+            a.counters = ws.counters;
+        }
     }
+    a.num_tiles = (int)(tiles * a.splits);
+
     const int64_t resident = (int64_t)cu_cap * occupancy;
-    const int grid = (int)(tiles < resident ? tiles : resident);
+    const int grid = (int)(a.num_tiles < resident ? a.num_tiles : resident);
     hipLaunchKernelGGL((nt_fp8_kernel<Cfg, FORM, OUT_F32>), dim3(grid), dim3(Cfg::THREADS), 0,
                        stream, a);
     return hipGetLastError();
@@ -454,13 +584,18 @@ using Cfg64x64 = NtCfg<64, 64, 1, 4, 4>;
 // every B byte is used once) narrow 64-column tiles with deeper pipelines, so
 // more workgroups stream B with more bytes in flight each.
 enum NtTile { kT64x64, kT128x64, kT128x128, kT256x256 };
+constexpr int64_t kRefCus = 256;   // MI355X CU count: the tile choice is a function of the shape
 
 NtTile choose_tile(const NtProblem& pr) {
     if (pr.form == kContiguous) return kT256x256;
     if (pr.form == kDense && pr.rows <= 64) return kT64x64;
     if (pr.form == kDense && pr.rows <= 128) return kT128x64;
     if (pr.rows <= 64) return kT64x64;
-    if (pr.form == kDense && pr.rows >= 1024 && pr.N >= 1024) return kT256x256;
+    // 256 x 256 tiles when they give at least half a tile per CU; smaller
+    // problems take 128 x 128 tiles (4x as many, split along K if still few).
+    if (pr.form == kDense && pr.rows >= 1024 && pr.N >= 1024 &&
+        ((pr.rows + 255) / 256) * ((pr.N + 255) / 256) * 2 >= (int64_t)kRefCus)
+        return kT256x256;
     return kT128x128;
 }
 

@@ -83,6 +83,37 @@ def test_dense_with_c_and_in_place(out):
     assert torch.equal(d, out)
 
 
+@pytest.mark.parametrize("M,N,K,out", [(64, 256, 4096, "bf16"), (96, 1024, 4096, "f32"),
+                                       (200, 384, 2048, "f32"), (1024, 1024, 8192, "bf16")])
+def test_dense_split_k_with_c_in_place_and_reproducible(M, N, K, out):
+    """Shapes with far fewer output tiles than workgroup slots run with K split
+    over several workgroups (64x64, 128x64 and 128x128 tiles here).  With C,
+    in place, both output types: parity with the oracle, bitwise identical
+    across runs (the partial sums are added in a fixed order), in place equal
+    to out of place, and unchanged under a CU cap."""
+    announce(f"dense split-K {M}x{N}x{K} {out}")
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    x = gen.gen_dense(M, N, K, seed=M + K, with_c=True)
+    c = dev(x.c).to(dt)
+    rows = sample_rows(M, 24, np.random.default_rng(3)) if M > 256 else None
+    ref = oracle.gemm_nt(x.a, x.sfa, x.b, x.sfb, c=to64(c), rows=rows)
+    d1 = run_dense(x, dt, c=c)
+    got = to64(d1) if rows is None else to64(d1[torch.from_numpy(rows).cuda()])
+    check_close(got, ref, "split-K")
+    d2 = run_dense(x, dt, c=c)
+    assert torch.equal(d1, d2)
+    d = c.clone()
+    dg.fp8_gemm_nt((dev(x.a), dev(x.sfa)), (dev(x.b), dev(x.sfb)), d, c=d)
+    torch.cuda.synchronize()
+    assert torch.equal(d, d1)
+    dg.set_num_cus(7)
+    try:
+        d3 = run_dense(x, dt, c=c)
+    finally:
+        dg.set_num_cus(0)
+    assert torch.equal(d1, d3)
+
+
 def test_dense_k_zero_gives_c():
     announce("dense K=0")
     M, N = 32, 64
