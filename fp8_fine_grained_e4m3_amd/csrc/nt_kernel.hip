@@ -116,7 +116,9 @@ template <class Cfg, int FORM, bool OUT_F32>
 __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN;
     constexpr int SM = Cfg::SM, SN = Cfg::SN;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::STAGES * Cfg::STAGE_BYTES];
+    // stages, then one 256-byte slot per wave that absorbs placeholder copies
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::STAGES * Cfg::STAGE_BYTES +
+                                                           256 * Cfg::WAVES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -127,12 +129,31 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
     const int NB = (p.N + kKBlk - 1) / kKBlk;
     const int per_group = p.tiles_m * p.tiles_n;
 
-    for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
+    // Masked groups: only the tiles holding valid rows are enumerated.  Group
+    // g has ceil(masked_m[g] / BM) * tiles_n of them; every workgroup reads
+    // the counts (device memory, so a captured graph sees the values of each
+    // replay) and walks the live tiles round-robin, which balances the work.
+    int num_work = p.num_tiles;
+    if (FORM == kMasked) {
+        num_work = 0;
+        for (int gg = 0; gg < p.G; ++gg) {
+            const int mm = min(max(p.masked_m[gg], 0), p.rows);
+            num_work += ((mm + BM - 1) / BM) * p.tiles_n;
+        }
+    }
+
+    for (int t = blockIdx.x; t < num_work; t += gridDim.x) {
         // ---- tile scheduling (uniform over the workgroup) ------------------
         int g = 0, e = 0, local = t, half = 0, split = 0;
+        int mtiles = 0;   // masked: live M tiles of group g
         if (FORM == kMasked) {
-            g = t / per_group;
-            local = t - g * per_group;
+            for (g = 0; g < p.G; ++g) {
+                const int mm = min(max(p.masked_m[g], 0), p.rows);
+                mtiles = (mm + BM - 1) / BM;
+                const int cnt = mtiles * p.tiles_n;
+                if (local < cnt) break;
+                local -= cnt;
+            }
             e = g;
         } else if (FORM == kContiguous) {
             // Tiles of BM = 256 rows span two 128-row expert blocks: the tile is
@@ -155,16 +176,34 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             local /= p.splits;
         }
         const int tile_id = local;
-        // Grouped rasterisation: tiles run in bands of band_m M tiles; inside a
-        // band N advances after every M tile of the band, so the tiles in
-        // flight share a few A row panels and a few B column panels.
-        const int band_tiles = p.band_m * p.tiles_n;
-        const int band = local / band_tiles;
-        const int in_band = local - band * band_tiles;
-        const int first_m = band * p.band_m;
-        const int rows_in_band = min(p.tiles_m - first_m, p.band_m);
-        const int tm = first_m + in_band % rows_in_band;
-        const int tn = in_band / rows_in_band;
+        int tm, tn;
+        if (FORM == kMasked) {
+            // Runs of 8 N tiles x all live M tiles: the M tiles that share a
+            // B panel are 8 apart in t, hence on one XCD (t % 8) and in flight
+            // together, so the panel comes from HBM once.
+            const int run = 8 * mtiles;
+            const int nfull = p.tiles_n >> 3;
+            if (local < nfull * run) {
+                const int blk = local / run, r = local - blk * run;
+                tm = r >> 3;
+                tn = blk * 8 + (r & 7);
+            } else {
+                const int r = local - nfull * run, w = p.tiles_n - nfull * 8;
+                tm = r / w;
+                tn = nfull * 8 + r % w;
+            }
+        } else {
+            // Grouped rasterisation: tiles run in bands of band_m M tiles;
+            // inside a band N advances after every M tile of the band, so the
+            // tiles in flight share a few A row panels and B column panels.
+            const int band_tiles = p.band_m * p.tiles_n;
+            const int band = local / band_tiles;
+            const int in_band = local - band * band_tiles;
+            const int first_m = band * p.band_m;
+            const int rows_in_band = min(p.tiles_m - first_m, p.band_m);
+            tm = first_m + in_band % rows_in_band;
+            tn = in_band / rows_in_band;
+        }
         const int r0 = tm * BM;        // first row of the tile, relative to its group
         const int n0 = tn * BN;
         const int grp_rows = p.rows;   // rows that exist in memory for this group
@@ -175,7 +214,6 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             mm = mm < 0 ? 0 : (mm > p.rows ? p.rows : mm);
             store_rows = mm;
             grp_row0 = (int64_t)g * p.rows;
-            if (r0 >= mm) continue;
         } else if (FORM == kContiguous) {
             const int rb = r0 + half * kKBlk;   // first row of the block whose expert is used
             if (rb >= p.rows) continue;
@@ -224,7 +262,14 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             for (int q = 0; q < Cfg::DMA_PER_WAVE; ++q) {
                 const int u = wave * Cfg::DMA_PER_WAVE + q;
                 const uint8_t* src = (u < Cfg::A_DMA ? a_t : b_t) + (size_t)kb * kKBlk;
-                dma16(src, goff[q], dst + u * 1024);
+                // Masked groups: A rows at or past masked_m are never stored,
+                // so their copy shrinks to a 256-byte placeholder (every wave
+                // keeps the same number of copies per stage, which the waits
+                // count on).
+                if (FORM == kMasked && u < Cfg::A_DMA && r0 + 8 * u >= store_rows)
+                    dma4(src, 0, lds0 + Cfg::STAGES * Cfg::STAGE_BYTES + wave * 256);
+                else
+                    dma16(src, goff[q], dst + u * 1024);
             }
             if (wave < Cfg::SA_DMA)
                 dma4(sfa_t + (size_t)kb * grp_rows, sa_off, dst + Cfg::SA_OFF + wave * 256);
@@ -591,6 +636,10 @@ NtTile choose_tile(const NtProblem& pr) {
     if (pr.form == kDense && pr.rows <= 64) return kT64x64;
     if (pr.form == kDense && pr.rows <= 128) return kT128x64;
     if (pr.rows <= 64) return kT64x64;
+    // Masked groups of more than 128 rows: 256 x 256 tiles, so each A row
+    // loaded serves 256 columns (the A rows are re-read once per N tile) and
+    // rows past masked_m cost placeholder copies only.
+    if (pr.form == kMasked && pr.rows > 128) return kT256x256;
     // 256 x 256 tiles when they give at least half a tile per CU; smaller
     // problems take 128 x 128 tiles (4x as many, split along K if still few).
     if (pr.form == kDense && pr.rows >= 1024 && pr.N >= 1024 &&

@@ -30,11 +30,24 @@
  *
  * Conventions for every GEMM entry point:
  *   - All pointers are DEVICE pointers unless the name ends in _host.  The
- *     caller owns every buffer; the library keeps no pointer after it returns
- *     and allocates nothing.
+ *     caller owns every buffer; the library keeps no pointer to them after
+ *     it returns.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Each call
- *     enqueues one kernel on it and returns; there is no host synchronisation,
- *     so the masked form may be captured into a HIP graph.
+ *     enqueues one kernel on it and returns; there is no host synchronisation
+ *     in the steady state, so calls may be captured into a HIP graph.
+ *   - Workspace (dg_fp8_gemm_nt only): a dense problem with too few output
+ *     tiles to occupy the device splits K over several workgroups, whose fp32
+ *     partial tiles meet in a device buffer the library owns, one per (device,
+ *     stream), kept until the process ends.  It is allocated, or grown, by
+ *     the first call on that stream that needs more than it has (that call
+ *     synchronises the stream once).  During stream capture the library never
+ *     allocates: a capture that would need a larger workspace runs that call
+ *     without splitting K (same result up to the order of the K-block sums).
+ *     A captured graph keeps the workspace of its capture stream; do not
+ *     replay it concurrently with other work that uses that stream's
+ *     workspace.  The split depends only on the shape and the device's CU
+ *     count (not on dg_set_num_cus), and the partial sums are added in a
+ *     fixed order, so results are bitwise reproducible.
  *   - FP8 operands are raw e4m3 bytes (uint8_t).  Scale factors are fp32.
  *   - Outputs: bf16 is stored as uint16_t bit patterns (round to nearest
  *     even, once, from the fp32 accumulator); fp32 as float.
@@ -46,8 +59,9 @@
  *   - Device-side metadata cannot be checked without a synchronisation, so it
  *     gets fixed readings instead: masked_m values are clamped to [0, M_max];
  *     m_indices values outside [0, G) mark padding rows.
- *   - Results are deterministic: the same inputs and launch give bitwise
- *     identical outputs (no atomics, fixed summation order).
+ *   - Results are deterministic: the same inputs give bitwise identical
+ *     outputs on a given device, whatever the CU cap (fixed summation order;
+ *     the only atomics are split-K arrival counters, never sums).
  */
 #ifndef DG_H
 #define DG_H

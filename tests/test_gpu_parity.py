@@ -333,6 +333,18 @@ def test_masked_edge_counts():
     check_masked_rows_untouched(d, mm, 256)
 
 
+def test_masked_two_m_tiles_per_group():
+    """M_max = 384: groups span one or two 256-row tiles; A rows past
+    masked_m are replaced by placeholder copies and must not reach D."""
+    mm = np.array([384, 300, 256, 255, 200, 8, 0], np.int32)
+    announce(f"masked M_max=384 {mm.tolist()}")
+    x = gen.gen_masked(G=7, M_max=384, N=528, K=640, masked_m=mm, seed=24)
+    d = run_masked(x)
+    ref = oracle.m_grouped_masked(x.a, x.sfa, x.b, x.sfb, mm)
+    check_close(to64(d.view), ref, "masked 384")
+    check_masked_rows_untouched(d, mm, 384)
+
+
 def test_masked_all_zero_writes_nothing():
     announce("masked all zero")
     x = gen.gen_masked(G=3, M_max=64, N=128, K=256, masked_m=np.zeros(3, np.int32), seed=22)
