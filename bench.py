@@ -37,6 +37,13 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
 MACHINE_BALANCE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # FLOP per byte
 
 # The rocprofv3 runs behind the profiles/ summaries (repository root, one GPU).
+GROUPED_PROFILE_COMMANDS = [
+    "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_grouped -o run -- "
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu --json-out gpurun_out/bench_grouped.json",
+    "python3 bench.py --summarize-grouped gpurun_out/prof_grouped gpurun_out/bench_grouped.json "
+    "profiles/grouped_moe__contiguous_masked_kgrouped.md",
+]
+
 PROFILE_COMMANDS = [
     "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o run -- "
     "python3 bench.py --steps 5 --warmup 1 --no-detail --no-cpu --json-out gpurun_out/bench_prof.json",
@@ -68,10 +75,15 @@ def main():
     ap.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE_DIR", "FETCH_DIR",
                                                               "WRITE_DIR", "BENCH_JSON", "OUT_MD"),
                     help="write a profiles/ summary from rocprofv3 CSV output and exit")
+    ap.add_argument("--summarize-grouped", nargs=3, metavar=("TRACE_DIR", "BENCH_JSON", "OUT_MD"),
+                    help="write the profiles/ summary of the grouped-workload kernel trace and exit")
     args = ap.parse_args()
 
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, commands=PROFILE_COMMANDS)
+        return
+    if args.summarize_grouped:
+        summarize_grouped(*args.summarize_grouped)
         return
 
     if args.gpus != 1:
@@ -329,6 +341,37 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, bench_json, out_path, co
               f"    traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
               f"    kernel_source_sha256_16: {source_hash(name.split('_')[0])}",
               f"    bench_value_tflops: {res['value']}", ""]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines))
+    print(out_path)
+
+
+def summarize_grouped(trace_dir, bench_json, out_path):
+    """profiles/ summary of the grouped MoE workloads (contiguous, masked,
+    K-grouped): rocprofv3 per-kernel averages next to bench.py's own
+    HIP-event timings of the same run."""
+    import csv
+    res = json.load(open(bench_json))
+    grouped = res["detail"]["grouped"]
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    lines = ["# Grouped MoE workloads (contiguous, masked, K-grouped) -- rocprofv3 kernel trace", "",
+             "Commands (run from the repository root on one MI355X):", ""]
+    lines += [f"    {c}" for c in GROUPED_PROFILE_COMMANDS]
+    lines += ["", "One bench.py run times the dense sweep and then each grouped workload (detail);",
+              "the trace below covers all of them.  Grouped kernels: form 1 = contiguous,",
+              "form 2 = masked (second template argument), `tn_fp8_kernel` = K-grouped.", "",
+              "## Kernel trace (--kernel-trace --stats)", "",
+              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", "## bench.py HIP-event timings of the grouped workloads (same run)", "",
+              "| workload | us | TFLOP/s | GB/s (algorithmic) | fraction of roof |", "|---|---|---|---|---|"]
+    for name, v in grouped.items():
+        frac = v.get("frac_mfma", v.get("frac_hbm"))
+        roof = "MFMA" if "frac_mfma" in v else "HBM"
+        lines.append(f"| {name} | {v['us']} | {v['tflops']} | {v['gbs']} | {frac} ({roof}) |")
+    lines += ["", f"    kernel_source_sha256_16: nt {source_hash('nt')}, tn {source_hash('tn')}", ""]
     with open(out_path, "w") as f:
         f.write("\n".join(lines))
     print(out_path)
