@@ -90,6 +90,12 @@ struct NtCfg {
     // Split K is compiled in for tiles whose partial sums fit the batched
     // reduction in registers (up to 16 MFMA tiles per lane).
     static constexpr bool SPLIT_OK = SM * SN <= 16;
+    // Early B refill (two stages): when every wave copies only A rows with the
+    // A scales, or only B rows with the B scales, the B half of a stage is
+    // refilled as soon as its fragments are in registers (one barrier earlier
+    // than the A half), so B copies have about two K blocks to land.
+    static constexpr bool EARLY_B =
+        STAGES == 2 && A_DMA % DMA_PER_WAVE == 0 && SA_DMA * DMA_PER_WAVE == A_DMA;
     static_assert(kKBlk % WTN == 0 && (BN % kKBlk == 0 || kKBlk % BN == 0),
                   "a wave's columns must sit inside one 128-column B scale block");
 };
@@ -302,12 +308,24 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
         // blocks 0 .. STAGES-1 in flight (the last one once block 0 has landed
         // and the barrier has passed); iteration it, once every wave is done
         // reading block it, refills its stage with block it + STAGES.
+        const bool a_wave = wave < Cfg::SA_DMA;   // EARLY_B: this wave copies A (else B)
+        if constexpr (Cfg::EARLY_B) {
+            // blocks 0 (A and B) and 1 (B) in flight; once block 0 has landed,
+            // block 1's A
+            if (nkb > 0) issue_stage(0, 0);
+            if (!a_wave && nkb > 1) issue_stage(1, 1);
+            if (!a_wave && nkb > 1) wait_vmcnt<Cfg::VM_PER_STAGE>();
+            else wait_vmcnt<0>();
+            lgkm_drain_barrier();
+            if (a_wave && nkb > 1) issue_stage(1, 1);
+        } else {
 #pragma unroll
-        for (int q = 0; q < Cfg::STAGES - 1; ++q)
-            if (q < nkb) issue_stage(q, q);
-        wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(min(Cfg::STAGES - 2, nkb - 1));
-        lgkm_drain_barrier();
-        if (Cfg::STAGES - 1 < nkb) issue_stage(Cfg::STAGES - 1, Cfg::STAGES - 1);
+            for (int q = 0; q < Cfg::STAGES - 1; ++q)
+                if (q < nkb) issue_stage(q, q);
+            wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(min(Cfg::STAGES - 2, nkb - 1));
+            lgkm_drain_barrier();
+            if (Cfg::STAGES - 1 < nkb) issue_stage(Cfg::STAGES - 1, Cfg::STAGES - 1);
+        }
 
         // Operand reads from one stage: scales, B fragments, A fragment i.
         auto load_scales = [&](const uint8_t* st, float (&sa)[SM], float& sb) {
@@ -368,6 +386,13 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             const uint8_t* st = smem + stage * Cfg::STAGE_BYTES;
             const int next = stage + 1 == Cfg::STAGES ? 0 : stage + 1;
             const uint8_t* st_next = smem + next * Cfg::STAGE_BYTES;
+            if constexpr (Cfg::EARLY_B) {
+                // every wave's reads of this block's B fragments and scales
+                // (made under the previous block's last row) are complete
+                lgkm_drain_barrier();
+                if (!a_wave && it + 2 < nkb) issue_stage(it + 2, stage);
+                __builtin_amdgcn_sched_barrier(0);
+            }
 
             // Rows 0 .. SM-2.  Step (i, j) issues block product (i, j) and
             // promotes (i-1, j); row i+1's A fragment is requested at step
@@ -396,10 +421,19 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             // block it+1 has landed for every wave, the stage is refilled, and
             // the next block's B and A fragments are read under the last row
             // (B fragment j right after the last product that uses it).
-            wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(
-                max(0, min(Cfg::STAGES - 2, nkb - 2 - it)));
-            lgkm_drain_barrier();
-            if (it + Cfg::STAGES < nkb) issue_stage(it + Cfg::STAGES, stage);
+            if constexpr (Cfg::EARLY_B) {
+                // block it+1 landed: A copies were the last this wave issued;
+                // a B wave may have block it+2's B copies in flight behind it
+                if (!a_wave && it + 2 < nkb) wait_vmcnt<Cfg::VM_PER_STAGE>();
+                else wait_vmcnt<0>();
+                lgkm_drain_barrier();
+                if (a_wave && it + 2 < nkb) issue_stage(it + 2, stage);
+            } else {
+                wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(
+                    max(0, min(Cfg::STAGES - 2, nkb - 2 - it)));
+                lgkm_drain_barrier();
+                if (it + Cfg::STAGES < nkb) issue_stage(it + Cfg::STAGES, stage);
+            }
             __builtin_amdgcn_sched_barrier(0);
 
             f32x4 plast[SN];
