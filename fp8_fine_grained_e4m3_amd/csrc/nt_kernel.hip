@@ -103,17 +103,25 @@ struct NtCfg {
 // Row and LDS maps.
 //  * Lane l (r = l & 15) of a wave owns the SM consecutive rows SM r .. SM r +
 //    SM - 1 of its wave tile; MFMA tile i of the lane reads row SM r + (i ^ (r & 1))
-//    (odd lanes swap neighbouring rows), so any 16 lanes read rows of both
-//    parities.  A lane's A scales are SM consecutive LDS floats, stored
-//    pre-swapped the same way.  Columns follow the MFMA layout: tile j, lane l
-//    owns the four columns 16 j + 4 (l >> 4) + {0, 1, 2, 3}.
+//    (odd lanes swap neighbouring rows), so the 16 rows of a fragment cover
+//    both parities.  Columns follow the MFMA layout: tile j, lane l owns the
+//    four columns 16 j + 4 (l >> 4) + {0, 1, 2, 3}.
 //  * LDS holds 128-byte rows (one K block of one row); chunk c of row `row`
-//    sits at 16-byte position c ^ f(row), with f_A(row) = (row / 2SM) & 7 for
-//    the A tile and f_B(row) = (row / 2) & 7 for the B tile.  LDS serves a
-//    ds_read_b128 16 lanes at a time from 64 four-byte banks; with these maps
-//    every 16-lane group of every fragment read hits 16 distinct 16-byte bank
-//    groups, and the per-fragment address is a per-lane base plus an
-//    immediate (i * 128 for A, j * 2048 for B).
+//    sits at 16-byte position sigma(c) ^ f(row), with f_A(row) = (row / 2SM) & 7
+//    for the A tile, f_B(row) = (row / 2) & 7 for the B tile, and sigma swapping
+//    bits 0 and 1 of c.
+//  * Bank rule (measured on gfx950): a ds_read_b128 is served in four groups
+//    of 16 lanes, lane l in group 2 * bit5(l) + (bit2 ^ bit3 ^ bit4)(l), and a
+//    group is conflict-free when its lanes hit 16 distinct 16-byte slots modulo
+//    256 bytes.  A group holds each fragment row r once, half of them reading
+//    chunk 2q (+1) and half chunk 2q + 2 (+1); sigma makes those two chunks
+//    differ in position bit 0 only, so row parity, f and that bit together
+//    give 16 distinct slots.  Every fragment address is a per-lane base plus
+//    an immediate (i * 128 for A, j * 2048 for B).
+//  * A scales: the lane's scale for fragment i sits at float
+//    (i / 4) * 64 + 4 r + i % 4 of its wave's block, so each float4 read of a
+//    16-lane group covers 256 contiguous bytes.
+__device__ __forceinline__ int sigma(int c) { return ((c >> 1) & 1) | ((c & 1) << 1) | (c & 4); }
 template <int SM>
 __device__ __forceinline__ int pos_a(int row) { return (row / (2 * SM)) & 7; }
 __device__ __forceinline__ int pos_b(int row) { return (row >> 1) & 7; }
@@ -246,7 +254,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             const int u = wave * Cfg::DMA_PER_WAVE + q;
             const bool is_a = u < Cfg::A_DMA;
             const int lrow = 8 * (is_a ? u : u - Cfg::A_DMA) + (lane >> 3);
-            const int chunk = (lane & 7) ^ (is_a ? pos_a<SM>(lrow) : pos_b(lrow));
+            const int chunk = sigma((lane & 7) ^ (is_a ? pos_a<SM>(lrow) : pos_b(lrow)));
             const int row = is_a ? min(r0 + lrow, grp_rows - 1) : min(n0 + lrow, p.N - 1);
             goff[q] = (uint32_t)row * (uint32_t)p.K + (uint32_t)(chunk * 16);
         }
@@ -256,9 +264,14 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
         // tile row s ^ ((s / SM) & 1) (the pair swap of the row map); every
         // other wave copies the B scales of the tile's 128-column blocks into
         // its own 256-byte slot (lanes past the last block repeat it).
+        // A-scale slot t of the stage holds the scale of the row that lane
+        // r = (u % 64) / 4 of wave-row wm reads as fragment i = 4 (u / 64) + u % 4
+        // (u = t % WTM, wm = t / WTM)
         const int sa_slot = 64 * wave + lane;
-        const uint32_t sa_off =
-            4u * (uint32_t)min(r0 + (sa_slot ^ ((sa_slot / SM) & 1)), grp_rows - 1);
+        const int sa_u = sa_slot % Cfg::WTM, sa_r = (sa_u % 64) / 4;
+        const int sa_row = (sa_slot / Cfg::WTM) * Cfg::WTM + SM * sa_r +
+                           ((4 * (sa_u / 64) + (sa_u % 4)) ^ (sa_r & 1));
+        const uint32_t sa_off = 4u * (uint32_t)min(r0 + sa_row, grp_rows - 1);
         const uint32_t sb_off = 4u * (uint32_t)(min(n0 / kKBlk + lane, NB - 1) * KB);
         const uint32_t lds0 = lds_addr(smem);
         auto issue_stage = [&](int kbr, int stage) {
@@ -290,11 +303,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
         const int pa = pos_a<SM>(wm * Cfg::WTM + SM * r16);
         const int a_even = (wm * Cfg::WTM + SM * r16 + (r16 & 1)) * kKBlk;
         const int a_odd = (wm * Cfg::WTM + SM * r16 - (r16 & 1)) * kKBlk;
-        const int a_lo = (c0 ^ pa) << 4, a_hi = ((c0 + 1) ^ pa) << 4;
+        const int a_lo = (sigma(c0) ^ pa) << 4, a_hi = (sigma(c0 + 1) ^ pa) << 4;
         const int pb = pos_b(wn * Cfg::WTN + r16);
         const int b_row = Cfg::A_BYTES + (wn * Cfg::WTN + r16) * kKBlk;
-        const int b_lo = b_row + ((c0 ^ pb) << 4), b_hi = b_row + (((c0 + 1) ^ pb) << 4);
-        const int s_a = Cfg::SA_OFF + 4 * (wm * Cfg::WTM + SM * r16);
+        const int b_lo = b_row + ((sigma(c0) ^ pb) << 4), b_hi = b_row + ((sigma(c0 + 1) ^ pb) << 4);
+        const int s_a = Cfg::SA_OFF + 4 * (wm * Cfg::WTM + 4 * r16);
         const int s_b = Cfg::SB_OFF + 256 * (Cfg::WAVES - 1) + 4 * ((wn * Cfg::WTN) / kKBlk);
 
         f32x4 acc[SM][SN];
@@ -331,7 +344,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
         auto load_scales = [&](const uint8_t* st, float (&sa)[SM], float& sb) {
 #pragma unroll
             for (int i = 0; i < SM; i += 4) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(st + s_a + 4 * i);
+                const f32x4 v = *reinterpret_cast<const f32x4*>(st + s_a + 4 * 64 * (i / 4));
                 sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
             }
             sb = *reinterpret_cast<const float*>(st + s_b);

@@ -154,15 +154,17 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         }
         // Scale copies, one per wave: copies [0, SA_DMA) fill A-scale slots,
         // the next SB_DMA fill B-scale slots, surplus waves repeat one (same
-        // bytes to the same place).  A slot wm*WTM + r*SM + i holds the scale of
-        // column wm*WTM + 16 i + r, so a lane's SM scales are consecutive.
+        // bytes to the same place).  A slot wm*WTM + 64 (i / 4) + 4 r + i % 4
+        // holds the scale of column wm*WTM + 16 i + r: lane r reads its scales
+        // as float4s and each float4 read of 16 lanes covers 256 contiguous
+        // bytes (no bank conflicts).
         const int scopy = wave % (Cfg::SA_DMA + Cfg::SB_DMA);
         const bool s_is_a = scopy < Cfg::SA_DMA;
         uint32_t s_off, s_lds;
         if (s_is_a) {
             const int slot = 64 * scopy + lane;
-            const int wms = slot / Cfg::WTM, rem = slot % Cfg::WTM;
-            const int col = wms * Cfg::WTM + 16 * (rem % SM) + rem / SM;
+            const int wms = slot / Cfg::WTM, u = slot % Cfg::WTM;
+            const int col = wms * Cfg::WTM + 16 * (4 * (u / 64) + u % 4) + (u % 64) / 4;
             s_off = 4u * (uint32_t)min(m0 + col, p.M - 1);
             s_lds = Cfg::SA_OFF + 256 * scopy;
         } else {
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
 #pragma unroll
             for (int i = 0; i < SM; i += 4) {
                 const f32x4 v = *reinterpret_cast<const f32x4*>(
-                    st + Cfg::SA_OFF + 4 * (wm * Cfg::WTM + SM * r16 + i));
+                    st + Cfg::SA_OFF + 4 * (wm * Cfg::WTM + 64 * (i / 4) + 4 * r16));
                 sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
             }
             f32x4 sb[SN];
