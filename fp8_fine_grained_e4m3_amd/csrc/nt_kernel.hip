@@ -272,7 +272,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
         const int sa_row = (sa_slot / Cfg::WTM) * Cfg::WTM + SM * sa_r +
                            ((4 * (sa_u / 64) + (sa_u % 4)) ^ (sa_r & 1));
         const uint32_t sa_off = 4u * (uint32_t)min(r0 + sa_row, grp_rows - 1);
-        const uint32_t sb_off = 4u * (uint32_t)(min(n0 / kKBlk + lane, NB - 1) * KB);
+        const int nb_last = min(NB - 1, (n0 + BN - 1) / kKBlk);   // the tile's last B-scale block
+        const uint32_t sb_off = 4u * (uint32_t)(min(n0 / kKBlk + lane, nb_last) * KB);
         const uint32_t lds0 = lds_addr(smem);
         auto issue_stage = [&](int kbr, int stage) {
             const int kb = kb_lo + kbr;
