@@ -98,6 +98,13 @@ struct NtCfg {
         STAGES == 2 && A_DMA % DMA_PER_WAVE == 0 && SA_DMA * DMA_PER_WAVE == A_DMA;
     static_assert(kKBlk % WTN == 0 && (BN % kKBlk == 0 || kKBlk % BN == 0),
                   "a wave's columns must sit inside one 128-column B scale block");
+    // Whole-block prefetch (wave tiles of at most 8 MFMA tiles): with so few
+    // products per K block, a row-by-row fragment pipeline leaves the MFMA
+    // unit waiting on LDS latency and barriers.  Instead every operand of
+    // block kb + 1 is read into a second register set while block kb's
+    // products run, one barrier per block.
+    static constexpr bool FULL_PREFETCH = SM * SN <= 8;
+    static_assert(!(FULL_PREFETCH && EARLY_B), "whole-block prefetch uses the plain stage ring");
 };
 
 // Row and LDS maps.
@@ -127,7 +134,7 @@ __device__ __forceinline__ int pos_a(int row) { return (row / (2 * SM)) & 7; }
 __device__ __forceinline__ int pos_b(int row) { return (row >> 1) & 7; }
 
 template <class Cfg, int FORM, bool OUT_F32>
-__global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
+__global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void nt_fp8_kernel(NtArgs p) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN;
     constexpr int SM = Cfg::SM, SN = Cfg::SN;
     // stages, then one 256-byte slot per wave that absorbs placeholder copies
@@ -379,6 +386,61 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
             asm volatile("" : "+v"(acc[i][j]));
         };
 
+        if constexpr (Cfg::FULL_PREFETCH) {
+            // Block it's operands (cur) were requested during block it-1; the
+            // barrier at the top of iteration it also covers block it+1 having
+            // landed, so its operands (nxt) are requested before block it's
+            // products, which hide their latency.  Products t = i * SN + j run in
+            // order; each is promoted two products later (a two-entry ring), so
+            // the last two of a block are promoted under the next block's first
+            // two, with the scale of the block they came from.
+            constexpr int T = SM * SN;
+            static_assert(T % 2 == 0, "the product ring alternates between two slots");
+            struct Ops {
+                i32x8 a[SM];
+                i32x8 b[SN];
+                float sa[SM];
+                float sb;
+            };
+            auto read_ops = [&](const uint8_t* st, Ops& o) {
+                load_scales(st, o.sa, o.sb);
+#pragma unroll
+                for (int j = 0; j < SN; ++j) o.b[j] = bfrag_at(st, j);
+#pragma unroll
+                for (int i = 0; i < SM; ++i) o.a[i] = afrag_at(st, i);
+            };
+            Ops cur, nxt;
+            read_ops(smem, cur);
+            // nothing is pending before block 0: zero products with zero scale
+            f32x4 ring[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            float ring_s[2] = {0.f, 0.f};
+            int stage = 0;   // stage holding block it
+            for (int it = 0; it < nkb; ++it) {
+                const int next = stage + 1 == Cfg::STAGES ? 0 : stage + 1;
+                // block it+1 has landed for every wave, and every wave's reads of
+                // block it (cur) are complete
+                wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(
+                    max(0, min(Cfg::STAGES - 2, nkb - 2 - it)));
+                lgkm_drain_barrier();
+                if (it + Cfg::STAGES < nkb) issue_stage(it + Cfg::STAGES, stage);
+                if (it + 1 < nkb) read_ops(smem + next * Cfg::STAGE_BYTES, nxt);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const int i = t / SN, j = t % SN;
+                    const f32x4 pr = mfma_e4m3_block(cur.b[j], cur.a[i]);
+                    const int tp = t >= 2 ? t - 2 : T + t - 2;   // tile of the pending product
+                    promote1(tp / SN, tp % SN, ring[t & 1], ring_s[t & 1]);
+                    ring[t & 1] = pr;
+                    ring_s[t & 1] = cur.sa[i] * cur.sb;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                cur = nxt;
+                stage = next;
+            }
+            promote1((T - 2) / SN, (T - 2) % SN, ring[0], ring_s[0]);
+            promote1((T - 1) / SN, (T - 1) % SN, ring[1], ring_s[1]);
+        } else {
         float sa[SM], sb;
         i32x8 bfrag[SN];
         load_scales(smem, sa, sb);
@@ -468,6 +530,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void nt_fp8_kernel(NtArgs p) {
         }
 #pragma unroll
         for (int j = 0; j < SN; ++j) promote1(SM - 1, j, pend[j], s_prev);
+        }
         // every wave is past its last LDS read before the next tile's copies
         lds_barrier();
 
