@@ -128,45 +128,60 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(events=None):
+    def step(events=None, only=None):
         for i, op in enumerate(ops):
-            if events is not None:
+            rec = events is not None and (only is None or op["kernel"] == only)
+            if rec:
                 events[i][0].record(stream)
             dg.fp8_gemm_nt(*op["args"])
-            if events is not None:
+            if rec:
                 events[i][1].record(stream)
+
+    def new_events(n):
+        return [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in ops] for _ in range(n)]
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly K steps ---------------------------------------------
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in ops] for _ in range(args.steps)]
+    # ---- per-launch pass (untimed): an event pair around every launch ------------
+    # gives the per-shape detail and picks the dominant kernel: the kernel
+    # instance (tile configuration) with the largest share of the step's time.
+    # Several shapes may share one instance.
+    probe_steps = 3
+    ev = new_events(probe_steps)
+    for s_ in range(probe_steps):
+        step(ev[s_])
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for s in range(args.steps):
-        step(ev[s])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    per_launch_ms = np.array([[ev[s][i][0].elapsed_time(ev[s][i][1]) for i in range(len(ops))]
-                              for s in range(args.steps)])
-    avg_ms = per_launch_ms.mean(axis=0)
-    flop_step = sum(op["flop"] for op in ops)
-    value = flop_step * args.steps / elapsed / 1e12
-    ms_per_step = elapsed * 1e3 / args.steps
-
-    # Dominant kernel: the kernel instance (tile configuration) with the largest
-    # share of the step's time.  Several shapes may share one instance, so its
-    # per-launch figures are averages over the launches of that instance in
-    # the timed region -- the same average a kernel-trace profile reports for
-    # that kernel name.
+    avg_ms = np.array([[ev[s_][i][0].elapsed_time(ev[s_][i][1]) for i in range(len(ops))]
+                       for s_ in range(probe_steps)]).mean(axis=0)
     groups = {}
     for i, op in enumerate(ops):
         groups.setdefault(op["kernel"], []).append(i)
     dom_name = max(groups, key=lambda k: sum(avg_ms[i] for i in groups[k]))
     idx = groups[dom_name]
-    launch_ms = float(np.mean([avg_ms[i] for i in idx]))
+
+    # ---- timed region: exactly K steps ---------------------------------------------
+    # Event pairs only around the dominant instance's launches (an event pair
+    # around every launch adds several microseconds per launch to the step).
+    ev = new_events(args.steps)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s_ in range(args.steps):
+        step(ev[s_], only=dom_name)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    dom_ms = np.array([[ev[s_][i][0].elapsed_time(ev[s_][i][1]) for i in idx]
+                       for s_ in range(args.steps)])
+    flop_step = sum(op["flop"] for op in ops)
+    value = flop_step * args.steps / elapsed / 1e12
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # Per-launch figures of the dominant instance: averages over its launches
+    # in the timed region -- the same average a kernel-trace profile reports
+    # for that kernel name.
+    launch_ms = float(dom_ms.mean())
     launch_flop = float(np.mean([ops[i]["flop"] for i in idx]))
     launch_bytes = float(np.mean([ops[i]["bytes"] for i in idx]))
     intensity = launch_flop / launch_bytes
@@ -187,7 +202,7 @@ def main():
     roof["alg_bytes_per_launch"] = launch_bytes
     M, N, K = ops[max(idx, key=lambda i: avg_ms[i])]["shape"]
 
-    per_shape = []
+    per_shape = []   # from the per-launch pass
     for op, t in zip(ops, avg_ms):
         m, n, k = op["shape"]
         per_shape.append(dict(M=m, N=n, K=k, kernel=op["kernel"], us=round(t * 1e3, 2),

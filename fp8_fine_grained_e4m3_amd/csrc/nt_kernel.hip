@@ -441,95 +441,97 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
             promote1((T - 2) / SN, (T - 2) % SN, ring[0], ring_s[0]);
             promote1((T - 1) / SN, (T - 1) % SN, ring[1], ring_s[1]);
         } else {
-        float sa[SM], sb;
-        i32x8 bfrag[SN];
-        load_scales(smem, sa, sb);
+            // Row pipeline.  Products t = i * SN + j run row by row; A fragment
+            // i + 2 is requested at the start of row i (a four-entry ring, two
+            // rows of LDS latency hidden), and each product is promoted two
+            // products later through a two-entry ring, so a block's last two
+            // products are promoted under the next block's first two, with the
+            // scale of the block they came from.  The mid-block barrier comes
+            // after row SM - 3, once every A read of the block has been issued:
+            // past it, rows SM - 2 and SM - 1 request the next block's scales,
+            // its first two A fragments and (after the last product that uses
+            // each) its B fragments.
+            constexpr int T = SM * SN;
+            static_assert(SM % 4 == 0 && T % 2 == 0, "A ring of four rows, product ring of two");
+            i32x8 af[4];
+            i32x8 bfr[SN];
+            float sa[SM], sb, sa_n[SM], sb_n;
+            f32x4 ring[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            float ring_s[2] = {0.f, 0.f};   // nothing pending before block 0
+            load_scales(smem, sa, sb);
 #pragma unroll
-        for (int j = 0; j < SN; ++j) bfrag[j] = bfrag_at(smem, j);
-        i32x8 afrag = afrag_at(smem, 0);
+            for (int j = 0; j < SN; ++j) bfr[j] = bfrag_at(smem, j);
+            af[0] = afrag_at(smem, 0);
+            af[1] = afrag_at(smem, 1);
 
-        // The promotion runs one MFMA row behind, across K blocks too: row 0 of
-        // block kb promotes row SM-1 of block kb-1 (with that block's scale
-        // s_prev).  Before the first block there is nothing to promote:
-        // pend = 0 and s_prev = 0 leave acc unchanged.
-        f32x4 pend[SN];
-#pragma unroll
-        for (int j = 0; j < SN; ++j) pend[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float s_prev = 0.f;
+            // one product step: block product (i, j), promotion of the product
+            // two steps back, optional operand request
+            auto step = [&](int i, int j, float s_row) {
+                const int t = i * SN + j;
+                const f32x4 pr = mfma_e4m3_block(bfr[j], af[i & 3]);
+                const int tp = t >= 2 ? t - 2 : T + t - 2;   // tile of the pending product
+                promote1(tp / SN, tp % SN, ring[t & 1], ring_s[t & 1]);
+                ring[t & 1] = pr;
+                ring_s[t & 1] = s_row;
+            };
 
-        int stage = 0;   // stage holding block it
-        for (int it = 0; it < nkb; ++it) {
-            const uint8_t* st = smem + stage * Cfg::STAGE_BYTES;
-            const int next = stage + 1 == Cfg::STAGES ? 0 : stage + 1;
-            const uint8_t* st_next = smem + next * Cfg::STAGE_BYTES;
-            if constexpr (Cfg::EARLY_B) {
-                // every wave's reads of this block's B fragments and scales
-                // (made under the previous block's last row) are complete
-                lgkm_drain_barrier();
-                if (!a_wave && it + 2 < nkb) issue_stage(it + 2, stage);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-
-            // Rows 0 .. SM-2.  Step (i, j) issues block product (i, j) and
-            // promotes (i-1, j); row i+1's A fragment is requested at step
-            // (i, 0).  The scheduling fences keep exactly this order, so every
-            // FMA reads an MFMA result issued SN steps earlier and no more than
-            // two rows of products are live.
-#pragma unroll
-            for (int i = 0; i + 1 < SM; ++i) {
-                const float s = i == 0 ? s_prev : sa[i - 1] * sb;
-                const int ip = i == 0 ? SM - 1 : i - 1;
-                i32x8 anext;
-                f32x4 pcur[SN];
-#pragma unroll
-                for (int j = 0; j < SN; ++j) {
-                    pcur[j] = mfma_e4m3_block(bfrag[j], afrag);
-                    if (j == 0) anext = afrag_at(st, i + 1);
-                    promote1(ip, j, pend[j], s);
+            int stage = 0;   // stage holding block it
+            for (int it = 0; it < nkb; ++it) {
+                const uint8_t* st = smem + stage * Cfg::STAGE_BYTES;
+                const int next = stage + 1 == Cfg::STAGES ? 0 : stage + 1;
+                const uint8_t* st_next = smem + next * Cfg::STAGE_BYTES;
+                if constexpr (Cfg::EARLY_B) {
+                    // every wave's reads of this block's B fragments and scales
+                    // (made during the previous block) are complete
+                    lgkm_drain_barrier();
+                    if (!a_wave && it + 2 < nkb) issue_stage(it + 2, stage);
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
-                for (int j = 0; j < SN; ++j) pend[j] = pcur[j];
-                afrag = anext;
-            }
-
-            // Every read of this stage has been issued.  Once they complete and
-            // block it+1 has landed for every wave, the stage is refilled, and
-            // the next block's B and A fragments are read under the last row
-            // (B fragment j right after the last product that uses it).
-            if constexpr (Cfg::EARLY_B) {
-                // block it+1 landed: A copies were the last this wave issued;
-                // a B wave may have block it+2's B copies in flight behind it
-                if (!a_wave && it + 2 < nkb) wait_vmcnt<Cfg::VM_PER_STAGE>();
-                else wait_vmcnt<0>();
-                lgkm_drain_barrier();
-                if (a_wave && it + 2 < nkb) issue_stage(it + 2, stage);
-            } else {
-                wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(
-                    max(0, min(Cfg::STAGES - 2, nkb - 2 - it)));
-                lgkm_drain_barrier();
-                if (it + Cfg::STAGES < nkb) issue_stage(it + Cfg::STAGES, stage);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-
-            f32x4 plast[SN];
-            const float s = sa[SM - 2] * sb;
+                for (int i = 0; i + 2 < SM; ++i) {
+                    const float s_row = sa[i] * sb;
 #pragma unroll
-            for (int j = 0; j < SN; ++j) {
-                plast[j] = mfma_e4m3_block(bfrag[j], afrag);
-                bfrag[j] = bfrag_at(st_next, j);
-                promote1(SM - 2, j, pend[j], s);
+                    for (int j = 0; j < SN; ++j) {
+                        step(i, j, s_row);
+                        if (j == 0) af[(i + 2) & 3] = afrag_at(st, i + 2);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                // Block it+1 landed for every wave and every read of block it
+                // done: refill (the A half, with early B refill).
+                if constexpr (Cfg::EARLY_B) {
+                    // a B wave may have block it+2's B copies in flight behind
+                    if (!a_wave && it + 2 < nkb) wait_vmcnt<Cfg::VM_PER_STAGE>();
+                    else wait_vmcnt<0>();
+                    lgkm_drain_barrier();
+                    if (a_wave && it + 2 < nkb) issue_stage(it + 2, stage);
+                } else {
+                    wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(
+                        max(0, min(Cfg::STAGES - 2, nkb - 2 - it)));
+                    lgkm_drain_barrier();
+                    if (it + Cfg::STAGES < nkb) issue_stage(it + Cfg::STAGES, stage);
+                }
                 __builtin_amdgcn_sched_barrier(0);
+                // (after the last block these reads see a stale stage; unused)
+                load_scales(st_next, sa_n, sb_n);
+#pragma unroll
+                for (int i = SM - 2; i < SM; ++i) {
+                    const float s_row = sa[i] * sb;
+#pragma unroll
+                    for (int j = 0; j < SN; ++j) {
+                        step(i, j, s_row);
+                        if (j == 0) af[(i + 2) & 3] = afrag_at(st_next, i + 2 - SM);
+                        if (i == SM - 1) bfr[j] = bfrag_at(st_next, j);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < SM; ++i) sa[i] = sa_n[i];
+                sb = sb_n;
+                stage = next;
             }
-            afrag = afrag_at(st_next, 0);
-            s_prev = sa[SM - 1] * sb;
-            load_scales(st_next, sa, sb);
-#pragma unroll
-            for (int j = 0; j < SN; ++j) pend[j] = plast[j];
-            stage = next;
-        }
-#pragma unroll
-        for (int j = 0; j < SN; ++j) promote1(SM - 1, j, pend[j], s_prev);
+            promote1((T - 2) / SN, (T - 2) % SN, ring[0], ring_s[0]);
+            promote1((T - 1) / SN, (T - 1) % SN, ring[1], ring_s[1]);
         }
         // every wave is past its last LDS read before the next tile's copies
         lds_barrier();
