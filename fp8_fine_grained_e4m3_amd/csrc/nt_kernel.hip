@@ -104,6 +104,13 @@ struct NtCfg {
     // block kb + 1 is read into a second register set while block kb's
     // products run, one barrier per block.
     static constexpr bool FULL_PREFETCH = SM * SN <= 8;
+    // Epilogue staging: wave rows (of WTM tile rows) staged per phase; all of
+    // them when the fp32 tile fits in the stages, else one at a time.
+    static constexpr int EPI_WAVE_ROWS =
+        WAVES_M * WTM * BN * 4 <= STAGES * STAGE_BYTES ? WAVES_M : 1;
+    static_assert(WTM * BN * 4 <= STAGES * STAGE_BYTES, "one wave row of the fp32 tile fits in LDS");
+    static_assert(BN % 16 == 0 && 64 % (BN / 4) == 0 && (WTM * EPI_WAVE_ROWS) % (64 / (BN / 4)) == 0,
+                  "staged rows split evenly into wave instructions");
     static_assert(!(FULL_PREFETCH && EARLY_B), "whole-block prefetch uses the plain stage ring");
 };
 
@@ -613,39 +620,65 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 __hip_atomic_store(p.counters + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 
-        // ---- epilogue: (+C), convert once, masked store ---------------------------
+        // ---- epilogue: staged through LDS, (+C), convert once, masked store ----------
+        // The fp32 tile goes to LDS (the stages are idle now), then every wave
+        // writes whole rows: lane q of a row owns its 16-byte fp32 chunk q, so
+        // each store instruction covers full contiguous rows of D.  Staging
+        // runs in phases of WMP wave rows when the whole tile does not fit.
+        // Chunk c of staged row r sits at position c ^ ((r / SM) & 15), which
+        // keeps both the writes (a lane's SM rows are SM apart) and the row
+        // reads free of LDS bank conflicts.
+        {
+            constexpr int WMP = Cfg::EPI_WAVE_ROWS;          // wave rows per phase
+            constexpr int PH_ROWS = WMP * Cfg::WTM;           // tile rows per phase
+            constexpr int ROW_CHUNKS = BN / 4;                // 16-byte fp32 chunks per row
+            constexpr int RPI = 64 / ROW_CHUNKS;              // rows per wave instruction
+            float* const stg = reinterpret_cast<float*>(smem);
 #pragma unroll
-        for (int i = 0; i < SM; ++i) {
-            const int m = m_lane0 + (i ^ (r16 & 1));
-            bool row_ok = m < store_rows;
-            if (FORM == kContiguous && row_ok) row_ok = p.m_indices[m] == e;
-            if (!row_ok) continue;
-            const int64_t row_off = (grp_row0 + m) * (int64_t)p.N;
+            for (int ph = 0; ph < Cfg::WAVES_M / WMP; ++ph) {
+                if (wm / WMP == ph) {
 #pragma unroll
-            for (int j = 0; j < SN; ++j) {
-                const int n = n0 + wn * Cfg::WTN + 16 * j + 4 * (lane >> 4);
-                if (n >= p.N) continue;
-                f32x4 v = acc[i][j];
-                if (OUT_F32) {
-                    float* dp = reinterpret_cast<float*>(p.d) + row_off + n;
-                    if (p.c) {
-                        const f32x4 cv = *reinterpret_cast<const f32x4*>(
-                            reinterpret_cast<const float*>(p.c) + row_off + n);
-                        v += cv;
+                    for (int i = 0; i < SM; ++i) {
+                        const int rl = (wm % WMP) * Cfg::WTM + SM * r16 + (i ^ (r16 & 1));
+#pragma unroll
+                        for (int j = 0; j < SN; ++j) {
+                            const int ch = (wn * Cfg::WTN + 16 * j) / 4 + (lane >> 4);
+                            *reinterpret_cast<f32x4*>(stg + rl * BN + 4 * (ch ^ ((rl / SM) & 15))) =
+                                acc[i][j];
+                        }
                     }
-                    *reinterpret_cast<f32x4*>(dp) = v;
-                } else {
-                    uint16_t* dp = reinterpret_cast<uint16_t*>(p.d) + row_off + n;
-                    if (p.c) {
-                        const i32x2 cv = *reinterpret_cast<const i32x2*>(
-                            reinterpret_cast<const uint16_t*>(p.c) + row_off + n);
-                        v.x += bf16_bits_to_f32((uint32_t)cv.x & 0xFFFFu);
-                        v.y += bf16_bits_to_f32((uint32_t)cv.x >> 16);
-                        v.z += bf16_bits_to_f32((uint32_t)cv.y & 0xFFFFu);
-                        v.w += bf16_bits_to_f32((uint32_t)cv.y >> 16);
-                    }
-                    *reinterpret_cast<i32x2*>(dp) = pack_bf16x4(v.x, v.y, v.z, v.w);
                 }
+                lds_barrier();
+#pragma unroll 4
+                for (int rr = wave * RPI; rr < PH_ROWS; rr += Cfg::WAVES * RPI) {
+                    const int rl = rr + lane / ROW_CHUNKS;
+                    const int ch = lane % ROW_CHUNKS;
+                    f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * BN + 4 * (ch ^ ((rl / SM) & 15)));
+                    const int m = r0 + ph * PH_ROWS + rl;   // row within the group
+                    const int n = n0 + 4 * ch;
+                    bool ok = m < store_rows && n < p.N;
+                    if (FORM == kContiguous && ok) ok = p.m_indices[m] == e;
+                    if (!ok) continue;
+                    const int64_t off = (grp_row0 + m) * (int64_t)p.N + n;
+                    if (OUT_F32) {
+                        if (p.c) v += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.c) + off);
+                        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.d) + off) = v;
+                    } else {
+                        if (p.c) {
+                            const i32x2 cv = *reinterpret_cast<const i32x2*>(
+                                reinterpret_cast<const uint16_t*>(p.c) + off);
+                            v.x += bf16_bits_to_f32((uint32_t)cv.x & 0xFFFFu);
+                            v.y += bf16_bits_to_f32((uint32_t)cv.x >> 16);
+                            v.z += bf16_bits_to_f32((uint32_t)cv.y & 0xFFFFu);
+                            v.w += bf16_bits_to_f32((uint32_t)cv.y >> 16);
+                        }
+                        *reinterpret_cast<i32x2*>(reinterpret_cast<uint16_t*>(p.d) + off) =
+                            pack_bf16x4(v.x, v.y, v.z, v.w);
+                    }
+                }
+                // every wave is done reading the staged rows before they (or the
+                // next tile's copies) are overwritten
+                lds_barrier();
             }
         }
     }
