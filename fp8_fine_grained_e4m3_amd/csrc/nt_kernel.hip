@@ -487,13 +487,6 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 const uint8_t* st = smem + stage * Cfg::STAGE_BYTES;
                 const int next = stage + 1 == Cfg::STAGES ? 0 : stage + 1;
                 const uint8_t* st_next = smem + next * Cfg::STAGE_BYTES;
-                if constexpr (Cfg::EARLY_B) {
-                    // every wave's reads of this block's B fragments and scales
-                    // (made during the previous block) are complete
-                    lgkm_drain_barrier();
-                    if (!a_wave && it + 2 < nkb) issue_stage(it + 2, stage);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
 #pragma unroll
                 for (int i = 0; i + 2 < SM; ++i) {
                     const float s_row = sa[i] * sb;
@@ -501,6 +494,16 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                     for (int j = 0; j < SN; ++j) {
                         step(i, j, s_row);
                         if (j == 0) af[(i + 2) & 3] = afrag_at(st, i + 2);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if constexpr (Cfg::EARLY_B) if (i == 0) {
+                        // Row 0 has consumed every B fragment and the B scale of
+                        // this block (read during the previous block), so every
+                        // wave past this barrier is done with the stage's B half.
+                        // No LDS drain: the A fragments requested since are
+                        // still in flight and unaffected.
+                        asm volatile("s_barrier" ::: "memory");
+                        if (!a_wave && it + 2 < nkb) issue_stage(it + 2, stage);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
