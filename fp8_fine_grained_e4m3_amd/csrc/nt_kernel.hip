@@ -630,7 +630,9 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
         // runs in phases of WMP wave rows when the whole tile does not fit.
         // Chunk c of staged row r sits at position c ^ ((r / SM) & 15), which
         // keeps both the writes (a lane's SM rows are SM apart) and the row
-        // reads free of LDS bank conflicts.
+        // reads free of LDS bank conflicts.  D is written once and never read
+        // here, so the stores are nontemporal (they do not displace operand
+        // panels from L2).
         {
             constexpr int WMP = Cfg::EPI_WAVE_ROWS;          // wave rows per phase
             constexpr int PH_ROWS = WMP * Cfg::WTM;           // tile rows per phase
@@ -665,7 +667,7 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                     const int64_t off = (grp_row0 + m) * (int64_t)p.N + n;
                     if (OUT_F32) {
                         if (p.c) v += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.c) + off);
-                        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.d) + off) = v;
+                        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.d) + off));
                     } else {
                         if (p.c) {
                             const i32x2 cv = *reinterpret_cast<const i32x2*>(
@@ -675,8 +677,8 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                             v.z += bf16_bits_to_f32((uint32_t)cv.y & 0xFFFFu);
                             v.w += bf16_bits_to_f32((uint32_t)cv.y >> 16);
                         }
-                        *reinterpret_cast<i32x2*>(reinterpret_cast<uint16_t*>(p.d) + off) =
-                            pack_bf16x4(v.x, v.y, v.z, v.w);
+                        __builtin_nontemporal_store(pack_bf16x4(v.x, v.y, v.z, v.w),
+                            reinterpret_cast<i32x2*>(reinterpret_cast<uint16_t*>(p.d) + off));
                     }
                 }
                 // every wave is done reading the staged rows before they (or the
