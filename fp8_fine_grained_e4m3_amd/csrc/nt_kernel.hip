@@ -435,7 +435,9 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
                     const int i = t / SN, j = t % SN;
+                    __builtin_amdgcn_s_setprio(1);
                     const f32x4 pr = mfma_e4m3_block(cur.b[j], cur.a[i]);
+                    __builtin_amdgcn_s_setprio(0);
                     const int tp = t >= 2 ? t - 2 : T + t - 2;   // tile of the pending product
                     promote1(tp / SN, tp % SN, ring[t & 1], ring_s[t & 1]);
                     ring[t & 1] = pr;
@@ -471,11 +473,15 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
             af[0] = afrag_at(smem, 0);
             af[1] = afrag_at(smem, 1);
 
-            // one product step: block product (i, j), promotion of the product
-            // two steps back, optional operand request
+            // one product step: block product (i, j) (issued at raised wave
+            // priority, so a wave with products ready keeps the MFMA unit busy
+            // while its SIMD partner waits on LDS) and the promotion of the
+            // product two steps back
             auto step = [&](int i, int j, float s_row) {
                 const int t = i * SN + j;
+                __builtin_amdgcn_s_setprio(1);
                 const f32x4 pr = mfma_e4m3_block(bfr[j], af[i & 3]);
+                __builtin_amdgcn_s_setprio(0);
                 const int tp = t >= 2 ? t - 2 : T + t - 2;   // tile of the pending product
                 promote1(tp / SN, tp % SN, ring[t & 1], ring_s[t & 1]);
                 ring[t & 1] = pr;
