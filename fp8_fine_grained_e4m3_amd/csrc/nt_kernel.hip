@@ -701,7 +701,8 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
 
 namespace {
 
-constexpr int kBandM = 8;   // M tiles per rasterisation band
+constexpr int kBandMDense = 4;        // M tiles per rasterisation band, dense
+constexpr int kBandMContiguous = 8;   // contiguous groups (expert panels are larger)
 
 constexpr int kMinSplitBlocks = 8;   // K blocks per split work unit, at least
 constexpr int kMaxSplits = 8;
@@ -742,9 +743,10 @@ hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     a.rows = (int)pr.rows; a.N = (int)pr.N; a.K = (int)pr.K; a.G = (int)pr.G;
     a.tiles_m = (int)((pr.rows + Cfg::BM - 1) / Cfg::BM);
     a.tiles_n = (int)((pr.N + Cfg::BN - 1) / Cfg::BN);
-    // Bands of kBandM M tiles: the tiles in flight share few A row panels and
+    // Bands of a few M tiles: the tiles in flight share few A row panels and
     // few B column panels (for contiguous groups: few expert weight panels).
-    a.band_m = (FORM != kMasked && a.tiles_m > kBandM) ? kBandM : a.tiles_m;
+    const int band = FORM == kDense ? kBandMDense : kBandMContiguous;
+    a.band_m = (FORM != kMasked && a.tiles_m > band) ? band : a.tiles_m;
     a.xcd_remap = FORM == kDense ? 1 : 0;
     static_assert(FORM != kContiguous || Cfg::BM == 2 * kKBlk, "contiguous tiles span two blocks");
     const int64_t groups = (FORM == kMasked) ? pr.G : (FORM == kContiguous ? 2 : 1);
