@@ -249,6 +249,16 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
             if (e < 0 || e >= p.G) continue;
             if (half == 1 && p.m_indices[r0] == e) continue;   // pass 0 already covers it
         }
+        // Contiguous groups: the expert of every row this wave stores in the
+        // epilogue, requested now so its latency hides under the K loop.  With
+        // one row per store instruction, wave w stores tile rows w + 8 j
+        // (j = 0 .. 31 over both phases); lane j holds that row's expert.
+        int row_expert = -1;
+        if constexpr (FORM == kContiguous && BN == 256) {
+            static_assert(Cfg::WAVES == 8 && BM == 256, "row map of the contiguous epilogue");
+            const int row = r0 + wave + 8 * (lane & 31);
+            if (row < p.rows) row_expert = p.m_indices[row];
+        }
 
         // K blocks [kb_lo, kb_lo + nkb) of this work unit (all of K unless split)
         const int kb_lo = (int)(((int64_t)split * KB) / p.splits);
@@ -668,7 +678,13 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                     const int m = r0 + ph * PH_ROWS + rl;   // row within the group
                     const int n = n0 + 4 * ch;
                     bool ok = m < store_rows && n < p.N;
-                    if (FORM == kContiguous && ok) ok = p.m_indices[m] == e;
+                    if constexpr (FORM == kContiguous && BN == 256) {
+                        // one row per instruction: row step j of this wave
+                        if (ok) ok = __builtin_amdgcn_readlane(
+                                         row_expert, (ph * PH_ROWS + rl - wave) / 8) == e;
+                    } else if (FORM == kContiguous && ok) {
+                        ok = p.m_indices[m] == e;
+                    }
                     if (!ok) continue;
                     const int64_t off = (grp_row0 + m) * (int64_t)p.N + n;
                     if (OUT_F32) {
