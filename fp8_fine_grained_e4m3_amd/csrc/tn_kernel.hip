@@ -30,8 +30,9 @@
 // The block product runs on the MFMA unit (the B fragment as row operand, A as
 // column operand: a lane's 4 results share one m and cover 4 consecutive n),
 // the promotion acc += P * (sa[m] * sb[n]) on the VALU, software-pipelined two
-// block products behind.  The accumulator starts from C (its loads overlap the first
-// copies), so the epilogue is a plain fp32 store.
+// block products behind.  The accumulator starts from C (its loads overlap the
+// first copies), so the epilogue is a plain fp32 store, staged through LDS into
+// whole-row stores.
 //
 // Scheduling: the host passes each group's K-block range and a processing
 // order (largest K first, so the longest tiles start first); the persistent
@@ -283,17 +284,42 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         // every wave is past its last LDS read before the next tile's copies
         lds_barrier();
 
-        // epilogue: D[g] = acc (C already included), fp32, inside [M, N]
+        // Epilogue: D[g] = acc (C already included), fp32, inside [M, N],
+        // staged through LDS one wave row (WTM tile rows) at a time so that
+        // each store instruction writes one whole row (lane q: 16-byte chunk
+        // q).  Chunk c of staged row r sits at position c ^ (r & 15): the 16
+        // lanes that write one chunk column hold 16 consecutive rows, so both
+        // the writes and the row reads hit 16 distinct 16-byte bank slots.
+        // D is written once and never read here: nontemporal stores.
+        float* const stg = reinterpret_cast<float*>(smem);
+        constexpr int ROW_CHUNKS = BN / 4;
+        static_assert(ROW_CHUNKS == 64, "one row per store instruction");
+        static_assert(Cfg::WTM * BN * 4 <= Cfg::STAGES * Cfg::STAGE_BYTES, "a wave row of the tile fits in LDS");
 #pragma unroll
-        for (int i = 0; i < SM; ++i) {
-            const int m = m0 + wm * Cfg::WTM + 16 * i + r16;
-            if (m >= p.M) continue;
+        for (int ph = 0; ph < Cfg::WAVES_M; ++ph) {
+            if (wm == ph) {
 #pragma unroll
-            for (int j = 0; j < SN; ++j) {
-                const int n = n0 + wn * Cfg::WTN + 16 * j + 4 * (lane >> 4);
-                if (n >= p.N) continue;
-                *reinterpret_cast<f32x4*>(p.d + gbase + (int64_t)m * p.N + n) = acc[i][j];
+                for (int i = 0; i < SM; ++i) {
+                    const int rl = 16 * i + r16;
+#pragma unroll
+                    for (int j = 0; j < SN; ++j) {
+                        const int ch = (wn * Cfg::WTN + 16 * j) / 4 + (lane >> 4);
+                        *reinterpret_cast<f32x4*>(stg + rl * BN + 4 * (ch ^ (rl & 15))) = acc[i][j];
+                    }
+                }
             }
+            lds_barrier();
+#pragma unroll 4
+            for (int rl = wave; rl < Cfg::WTM; rl += Cfg::WAVES) {
+                const int m = m0 + ph * Cfg::WTM + rl;
+                const int n = n0 + 4 * lane;
+                if (m >= p.M || n >= p.N) continue;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * BN + 4 * (lane ^ (rl & 15)));
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.d + gbase + (int64_t)m * p.N + n));
+            }
+            // every wave is done reading the staged rows before they (or the
+            // next tile's copies) are overwritten
+            lds_barrier();
         }
     }
 }
