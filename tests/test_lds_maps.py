@@ -89,3 +89,43 @@ def test_tn_transposing_reads_conflict_free():
                     row = 32 * grp + (k16 >> 1) + 8 * q
                     addrs.append(row * W + ((chunk ^ swz(W, row)) << 4) + 8 * (k16 & 1))
                 assert tr8_conflict_free(addrs), (W, chunk, q)
+
+
+def test_epilogue_staging_round_trip_and_banks():
+    """The epilogues stage the fp32 tile through LDS in 16-byte chunks: chunk
+    c of staged row r sits at position c ^ f(r), f(r) = (r / SM) & 15 for the
+    NT row map (a lane owns rows SM r16 + (i ^ (r16 & 1))) and r & 15 for the
+    TN map (rows 16 i + r16).  Every lane's MFMA-layout write must land where
+    the row reads find it, and both the writes (checked with the same 16-lane
+    grouping as the reads) and the row reads must be conflict-free."""
+    cases = [  # (map, SM, SN, WAVES_N, BN)
+        ("nt", 8, 4, 4, 256), ("nt", 4, 4, 2, 128), ("nt", 4, 2, 2, 64), ("nt", 4, 1, 4, 64),
+        ("tn", 8, 4, 4, 256)]
+    for kind, SM, SN, WN, BN in cases:
+        WTM, WTN, RC = 16 * SM, 16 * SN, BN // 4
+        f = (lambda r: (r // SM) & 15) if kind == "nt" else (lambda r: r & 15)
+        lane_row = ((lambda i, r16: SM * r16 + (i ^ (r16 & 1))) if kind == "nt"
+                    else (lambda i, r16: 16 * i + r16))
+        stg = {}
+        for wn in range(WN):
+            for i in range(SM):
+                for j in range(SN):
+                    addrs = []
+                    for l in range(64):
+                        r16 = l & 15
+                        row = lane_row(i, r16)
+                        ch = (wn * WTN + 16 * j) // 4 + (l >> 4)
+                        a = 4 * (row * BN + 4 * (ch ^ f(row)))
+                        addrs.append(a)
+                        assert a not in stg
+                        stg[a] = (row, 4 * ch)          # fp32 values of row, columns 4 ch .. +3
+                    assert b128_conflict_free(addrs), (kind, SM, SN, BN, wn, i, j)
+        assert len(stg) == WTM * BN // 4
+        for base in range(0, WTM, 64 // RC):               # one wave read instruction
+            addrs = []
+            for l in range(64):
+                row, ch = base + l // RC, l % RC
+                a = 4 * (row * BN + 4 * (ch ^ f(row)))
+                addrs.append(a)
+                assert stg[a] == (row, 4 * ch)
+            assert b128_conflict_free(addrs), (kind, SM, SN, BN, base)
