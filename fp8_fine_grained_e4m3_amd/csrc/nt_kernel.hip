@@ -17,9 +17,11 @@
 //   * A workgroup owns a BM x BN output tile and walks K in 128-wide blocks.
 //     The grid is persistent: workgroup w takes tiles w, w + grid, ...
 //   * Per K block the A tile [BM x 128] and B tile [BN x 128] are staged into
-//     LDS (double-buffered: the global loads of block kb+1 are in flight while
-//     block kb is multiplied), rows of 128 bytes with an XOR-swizzled 16-byte
-//     chunk order.
+//     LDS by direct global -> LDS copies (a ring of STAGES stages: the copies
+//     of the next blocks are in flight while block kb is multiplied), rows of
+//     128 bytes with an XOR-swizzled 16-byte chunk order.
+//   * The epilogue stages the fp32 tile through the idle stages and writes D
+//     (+ C, one rounding) in whole-row stores.
 //   * Each wave owns a WTM x WTN sub-tile made of 16 x 16 MFMA tiles.  The MFMA
 //     takes the B fragment as its row operand and the A fragment as its column
 //     operand, so every lane's four results share one m (one A scale) and
