@@ -324,7 +324,6 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
         };
 
         const int r16 = lane & 15;
-        const int m_lane0 = r0 + wm * Cfg::WTM + SM * r16;   // first of the lane's SM rows
         // per-lane LDS byte offsets inside a stage (fragment i / j adds an immediate)
         const int c0 = (lane >> 4) * 2;
         const int pa = pos_a<SM>(wm * Cfg::WTM + SM * r16);
@@ -672,9 +671,10 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                     }
                 }
                 lds_barrier();
+                constexpr int NR = PH_ROWS / (Cfg::WAVES * RPI);   // row steps per wave
 #pragma unroll 4
-                for (int rr = wave * RPI; rr < PH_ROWS; rr += Cfg::WAVES * RPI) {
-                    const int rl = rr + lane / ROW_CHUNKS;
+                for (int k = 0; k < NR; ++k) {
+                    const int rl = wave * RPI + k * Cfg::WAVES * RPI + lane / ROW_CHUNKS;
                     const int ch = lane % ROW_CHUNKS;
                     f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * BN + 4 * (ch ^ ((rl / SM) & 15)));
                     const int m = r0 + ph * PH_ROWS + rl;   // row within the group
