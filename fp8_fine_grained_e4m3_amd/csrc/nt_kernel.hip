@@ -53,6 +53,12 @@ struct NtArgs {
     int num_tiles;     // enumerated tiles (masked: G * tiles_m * tiles_n)
     int band_m;        // grouped rasterisation: bands of band_m M tiles
     int xcd_remap;     // 1: give each XCD a contiguous run of the tile order
+    // Contiguous form: the first xcd_units tiles go in XCD blocks (each XCD
+    // takes xcd_blk_m M tiles x tiles_n / 2 N tiles per round of the grid);
+    // the band order covers the rest, from M tile xcd_m0 on.
+    int xcd_blk_m;
+    int xcd_units;
+    int xcd_m0;
     // Split K (dense only): each output tile is computed as `splits` partial
     // sums over consecutive K-block ranges; see the epilogue.
     int splits;
@@ -222,14 +228,26 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 tm = r / w;
                 tn = nfull * 8 + r % w;
             }
+        } else if (FORM == kContiguous && local < p.xcd_units) {
+            // XCD blocks: one round of the grid (gridDim.x units, a multiple
+            // of 8) covers 4 * xcd_blk_m M tiles x all N tiles; unit u runs on
+            // XCD u % 8, which takes a block of xcd_blk_m M tiles x half the
+            // N tiles (4 x 2 blocks).  Fewer panels per XCD than a band of the
+            // same size: 12 instead of 18 at 32 tiles per XCD and 16 N tiles.
+            const int sb = local / (int)gridDim.x;
+            const int u = local - sb * (int)gridDim.x;
+            const int x = u & 7, j = u >> 3;
+            tm = (sb * 4 + (x & 3)) * p.xcd_blk_m + j % p.xcd_blk_m;
+            tn = (x >> 2) * (p.tiles_n >> 1) + j / p.xcd_blk_m;
         } else {
             // Grouped rasterisation: tiles run in bands of band_m M tiles;
             // inside a band N advances after every M tile of the band, so the
             // tiles in flight share a few A row panels and B column panels.
+            const int rest = local - p.xcd_units;
             const int band_tiles = p.band_m * p.tiles_n;
-            const int band = local / band_tiles;
-            const int in_band = local - band * band_tiles;
-            const int first_m = band * p.band_m;
+            const int band = rest / band_tiles;
+            const int in_band = rest - band * band_tiles;
+            const int first_m = p.xcd_m0 + band * p.band_m;
             const int rows_in_band = min(p.tiles_m - first_m, p.band_m);
             tm = first_m + in_band % rows_in_band;
             tn = in_band / rows_in_band;
@@ -789,6 +807,17 @@ hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
 
     const int64_t resident = (int64_t)cu_cap * occupancy;
     const int grid = (int)(a.num_tiles < resident ? a.num_tiles : resident);
+    a.xcd_blk_m = 0;
+    a.xcd_units = 0;
+    a.xcd_m0 = 0;
+    if (FORM == kContiguous && grid % 8 == 0 && a.tiles_n % 2 == 0 &&
+        (grid / 8) % (a.tiles_n / 2) == 0) {
+        const int blk = (grid / 8) / (a.tiles_n / 2);
+        const int rounds = a.tiles_m / (4 * blk);
+        a.xcd_blk_m = blk;
+        a.xcd_units = rounds * grid;
+        a.xcd_m0 = rounds * 4 * blk;
+    }
     hipLaunchKernelGGL((nt_fp8_kernel<Cfg, FORM, OUT_F32>), dim3(grid), dim3(Cfg::THREADS), 0,
                        stream, a);
     return hipGetLastError();

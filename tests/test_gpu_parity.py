@@ -282,6 +282,25 @@ def test_contiguous_expert_isolation():
     assert not torch.equal(d0[128:256], d1[128:256])
 
 
+def test_contiguous_xcd_blocks_and_band_rest():
+    """N = 4096 (16 N tiles) and 20 M tiles of 256 rows: at 256 workgroups
+    the first 16 M tiles run in XCD blocks, the other 4 in band order.  One
+    random row in each 128-row half of every M tile, all columns, so every
+    (tile, half) pass is checked."""
+    announce("contiguous XCD blocks + band rest, N=4096 K=256")
+    x = gen.gen_contiguous(G=6, N=4096, K=256, counts=np.array([1000, 0, 1500, 777, 1300, 130]), seed=15)
+    assert x.M_tot == 20 * 256
+    d = run_contiguous(x)
+    rng = np.random.default_rng(15)
+    rows = np.arange(0, x.M_tot, 128) + rng.integers(0, 128, x.M_tot // 128)
+    rows = rows[x.m_indices[rows] >= 0]
+    got = to64(d.view[torch.from_numpy(rows).cuda()])
+    ref = oracle.m_grouped_contiguous(x.a, x.sfa, x.b, x.sfb, x.m_indices, rows=rows)
+    print(check_close(got, ref, "contiguous XCD blocks"))
+    pad = np.nonzero(x.m_indices < 0)[0]
+    assert d.untouched(torch.from_numpy(pad).cuda()), "padding rows were written"
+
+
 def test_c3_contiguous_full_size():
     announce("contiguous C3 32 experts N=K=4096 zipf top6 seed0")
     x = gen.gen_contiguous(seed=0)
