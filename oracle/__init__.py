@@ -5,8 +5,10 @@ import this package.  The GPU library never imports, links or calls it, and
 the two share no code.  The arithmetic lives in oracle.c (plain C, built with
 gcc, -ffp-contract=off); this wrapper only marshals numpy arrays.
 
-Every function returns float64 arrays.  Rows with no reference value (padding
-rows of the contiguous layout, rows at or past masked_m) come back as NaN.
+The GEMM functions return float64 arrays.  Rows with no reference value
+(padding rows of the contiguous layout, rows at or past masked_m) come back as
+NaN.  The casting functions (cast_rows, cast_blocks, e4m3_encode) return the
+e4m3 codes and fp32 scales they define, bit for bit.
 """
 from __future__ import annotations
 
@@ -84,6 +86,12 @@ def _bind(lib):
     lib.oracle_m_grouped_masked.restype = ctypes.c_int
     lib.oracle_k_grouped_tn.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P, I, P]
     lib.oracle_k_grouped_tn.restype = ctypes.c_int
+    lib.oracle_e4m3_encode.argtypes = [P, P, I]
+    lib.oracle_e4m3_encode.restype = None
+    lib.oracle_cast_rows.argtypes = [P, I, I, I, ctypes.c_int, P, P]
+    lib.oracle_cast_rows.restype = ctypes.c_int
+    lib.oracle_cast_blocks.argtypes = [P, I, I, I, ctypes.c_int, P, P]
+    lib.oracle_cast_blocks.restype = ctypes.c_int
     return lib
 
 
@@ -193,3 +201,40 @@ def k_grouped_tn(a, sfa, b, sfb, k_sizes, c=None, groups=None, rows=None) -> np.
     if rc:
         raise ValueError("oracle_k_grouped_tn: bad arguments")
     return out.reshape(G, M, N) if full else out
+
+
+def e4m3_encode(values) -> np.ndarray:
+    """Nearest e4m3 codes (ties to even mantissa, |y| >= 448 -> +-448)."""
+    y = _c(values, np.float64)
+    out = np.empty(y.shape, dtype=np.uint8)
+    _load().oracle_e4m3_encode(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+def cast_rows(x, pow2: bool = False):
+    """1 x 128 casting of activations x [R, K] or [G, R, K] (any float dtype
+    exact in fp32).  Returns (codes uint8 like x, sf fp32 [K/128, R] or
+    [G, K/128, R])."""
+    xx = np.asarray(x)
+    batched = xx.ndim == 3
+    x3 = _c(xx if batched else xx[None], np.float32)
+    G, R, K = x3.shape
+    codes = np.empty((G, R, K), dtype=np.uint8)
+    sf = np.empty((G, K // 128, R), dtype=np.float32)
+    if _load().oracle_cast_rows(_ptr(x3), G, R, K, int(pow2), _ptr(codes), _ptr(sf)):
+        raise ValueError("oracle_cast_rows: bad arguments")
+    return (codes, sf) if batched else (codes[0], sf[0])
+
+
+def cast_blocks(w, pow2: bool = False):
+    """128 x 128 casting of weights w [N, K] or [G, N, K].  Returns (codes,
+    sf fp32 [ceil(N/128), K/128] or [G, ceil(N/128), K/128])."""
+    ww = np.asarray(w)
+    batched = ww.ndim == 3
+    w3 = _c(ww if batched else ww[None], np.float32)
+    G, N, K = w3.shape
+    codes = np.empty((G, N, K), dtype=np.uint8)
+    sf = np.empty((G, (N + 127) // 128, K // 128), dtype=np.float32)
+    if _load().oracle_cast_blocks(_ptr(w3), G, N, K, int(pow2), _ptr(codes), _ptr(sf)):
+        raise ValueError("oracle_cast_blocks: bad arguments")
+    return (codes, sf) if batched else (codes[0], sf[0])

@@ -233,3 +233,133 @@ int oracle_k_grouped_tn(const uint8_t* a, const float* sfa, const uint8_t* b, co
     }
     return bad;
 }
+
+/* ---------------------------------------------------------------------------
+ * FP8 casting: the step before the GEMM.  The "DeepGEMM" README ("Interfaces",
+ * "Notices") leaves casting to the caller and suggests fusing it into the
+ * producing kernel; the granularities are the ones the GEMM consumes.  The
+ * pages give no formula; the reading is the one the workloads are built with:
+ *
+ *   amax = max |x| over the block (1 x 128 for activations, 128 x 128 for
+ *          weights; a weight block at the N tail covers the rows that exist)
+ *   s    = amax / 448 in fp32 (correctly rounded); s = 1 when amax == 0;
+ *          with pow2, s is then rounded up to a power of two (the UE8M0 scale
+ *          format the README's "Notices" names for its newer path)
+ *   q    = the e4m3 code nearest to clamp(x / s, -448, 448), the quotient
+ *          taken in fp32 (correctly rounded), ties to the code whose mantissa
+ *          is even; a negative value that rounds to zero keeps its sign (0x80)
+ *
+ * x is fp32 (bf16 inputs are exact in it).
+ * ------------------------------------------------------------------------- */
+
+/* Nearest e4m3 code to y, ties to even mantissa; |y| >= 448 gives +-448. */
+static uint8_t e4m3_encode(double y)
+{
+    const uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    const double a = fabs(y);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    /* codes 0x00 .. 0x7E hold increasing values; find lo with
+     * value(lo) <= a < value(lo + 1) */
+    int lo = 0, hi = 0x7E;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (e4m3_value((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const double below = a - e4m3_value((uint8_t)lo);
+    const double above = e4m3_value((uint8_t)hi) - a;
+    int code;
+    if (below < above)
+        code = lo;
+    else if (above < below)
+        code = hi;
+    else
+        code = (lo % 2 == 0) ? lo : hi;   /* tie: the even mantissa */
+    return sign | (uint8_t)code;
+}
+
+void oracle_e4m3_encode(const double* y, uint8_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = e4m3_encode(y[i]);
+}
+
+static float cast_scale(float amax, int pow2)
+{
+    if (amax == 0.0f)
+        return 1.0f;
+    float s = amax / 448.0f;
+    if (pow2) {
+        int e;
+        const double f = frexp((double)s, &e);   /* s = f * 2^e, 0.5 <= f < 1 */
+        if (f != 0.5)
+            s = (float)ldexp(1.0, e);
+    }
+    return s;
+}
+
+static uint8_t cast_one(float x, float s)
+{
+    float q = x / s;
+    if (q > 448.0f)
+        q = 448.0f;
+    if (q < -448.0f)
+        q = -448.0f;
+    return e4m3_encode((double)q);
+}
+
+/* Activations, 1 x 128: x [G, R, K] -> codes [G, R, K], sf [G, K/128, R]. */
+int oracle_cast_rows(const float* x, int64_t G, int64_t R, int64_t K, int pow2,
+                     uint8_t* codes, float* sf)
+{
+    if (K % KBLK != 0 || G < 0 || R < 0)
+        return 1;
+    build_table();
+    const int64_t KB = K / KBLK;
+#pragma omp parallel for schedule(static)
+    for (int64_t gr = 0; gr < G * R; ++gr) {
+        const int64_t g = gr / R, r = gr % R;
+        const float* xr = x + gr * K;
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            float amax = 0.0f;
+            for (int64_t k = kb * KBLK; k < (kb + 1) * KBLK; ++k)
+                if (fabsf(xr[k]) > amax)
+                    amax = fabsf(xr[k]);
+            const float s = cast_scale(amax, pow2);
+            sf[(g * KB + kb) * R + r] = s;
+            for (int64_t k = kb * KBLK; k < (kb + 1) * KBLK; ++k)
+                codes[gr * K + k] = cast_one(xr[k], s);
+        }
+    }
+    return 0;
+}
+
+/* Weights, 128 x 128: w [G, N, K] -> codes [G, N, K], sf [G, ceil(N/128), K/128]. */
+int oracle_cast_blocks(const float* w, int64_t G, int64_t N, int64_t K, int pow2,
+                       uint8_t* codes, float* sf)
+{
+    if (K % KBLK != 0 || G < 0 || N < 0)
+        return 1;
+    build_table();
+    const int64_t KB = K / KBLK, NB = (N + KBLK - 1) / KBLK;
+#pragma omp parallel for schedule(static)
+    for (int64_t gb = 0; gb < G * NB * KB; ++gb) {
+        const int64_t g = gb / (NB * KB), nb = (gb / KB) % NB, kb = gb % KB;
+        const int64_t n1 = (nb + 1) * KBLK < N ? (nb + 1) * KBLK : N;
+        const float* wg = w + g * N * K;
+        float amax = 0.0f;
+        for (int64_t n = nb * KBLK; n < n1; ++n)
+            for (int64_t k = kb * KBLK; k < (kb + 1) * KBLK; ++k)
+                if (fabsf(wg[n * K + k]) > amax)
+                    amax = fabsf(wg[n * K + k]);
+        const float s = cast_scale(amax, pow2);
+        sf[gb] = s;
+        for (int64_t n = nb * KBLK; n < n1; ++n)
+            for (int64_t k = kb * KBLK; k < (kb + 1) * KBLK; ++k)
+                codes[g * N * K + n * K + k] = cast_one(wg[n * K + k], s);
+    }
+    return 0;
+}

@@ -10,6 +10,7 @@ library.
 import pytest
 
 import oracle
+from tests import test_oracle_cast_pins as cast_pins
 from tests import test_oracle_pins as pins
 
 MUTANTS = {
@@ -43,6 +44,18 @@ MUTANTS = {
                        "for (int64_t kb = 0; kb < k1 / KBLK; ++kb) {"),
     "tn_c_dropped": ("out[i * N + n] = acc + (c ? (double)c[(g * M + m) * N + n] : 0.0);",
                      "out[i * N + n] = acc;"),
+    # FP8 casting
+    "cast_fnuz_max": ("float s = amax / 448.0f;", "float s = amax / 240.0f;"),
+    "cast_ties_away": ("code = (lo % 2 == 0) ? lo : hi;", "code = hi;"),
+    "cast_truncates": ("if (below < above)", "if (below < above || 1)"),
+    "cast_zero_unsigned": ("const uint8_t sign = signbit(y) ? 0x80 : 0x00;",
+                           "const uint8_t sign = y < 0 ? 0x80 : 0x00;"),
+    "cast_sf_row_major": ("sf[(g * KB + kb) * R + r] = s;", "sf[(g * R + r) * KB + kb] = s;"),
+    "cast_multiply_by_reciprocal": ("float q = x / s;", "float q = x * (1.0f / s);"),
+    "cast_pow2_rounds_down": ("s = (float)ldexp(1.0, e);", "s = (float)ldexp(1.0, e - 1);"),
+    "cast_blocks_drop_tail_rows": ("const int64_t n1 = (nb + 1) * KBLK < N ? (nb + 1) * KBLK : N;",
+                                   "const int64_t n1 = (nb + 1) * KBLK < N ? (nb + 1) * KBLK : N - 1;"),
+    "cast_zero_scale": ("if (amax == 0.0f)\n        return 1.0f;", "if (amax == 0.0f)\n        return 0.5f;"),
 }
 
 
@@ -64,6 +77,17 @@ def _pin_suite():
         ("contiguous", pins.test_contiguous_matches_exact_rationals),
         ("masked", pins.test_masked_matches_exact_rationals_and_masks_rows),
         ("k_grouped", pins.test_k_grouped_matches_exact_rationals_with_empty_group),
+        ("encode_codes", cast_pins.test_encode_round_trips_every_finite_code),
+        ("encode_midpoints", cast_pins.test_encode_midpoints_tie_to_even_and_neighbours_round_to_nearest),
+        ("encode_torch", cast_pins.test_encode_matches_torch_cast),
+        ("cast_golden", cast_pins.test_cast_rows_hand_worked_golden),
+        ("cast_nearest", cast_pins.test_cast_rows_is_the_nearest_code_of_the_fp32_quotient),
+        ("cast_layout", cast_pins.test_cast_rows_scale_layout_and_block_max),
+        ("cast_zero", cast_pins.test_cast_rows_zero_block),
+        ("cast_gen_rows", cast_pins.test_cast_rows_matches_generator_quantiser),
+        ("cast_pow2", cast_pins.test_cast_rows_pow2_scales),
+        ("cast_gen_blocks", cast_pins.test_cast_blocks_matches_generator_quantiser_with_ragged_n),
+        ("cast_blocks_nearest", cast_pins.test_cast_blocks_is_the_nearest_code_of_the_fp32_quotient),
     ]
     failed = []
     for name, fn in checks:
