@@ -13,8 +13,9 @@ Also reported on the same JSON line:
                   MFMA (fp8 dense 5.0 PFLOP/s) or HBM (8 TB/s) roof, whichever
                   bounds its arithmetic intensity;
   cpu_baseline -- the fp64 CPU oracle on a bounded sample of that shape's rows;
-  detail       -- per-shape times, and the three grouped MoE workloads
-                  (contiguous, masked, K-grouped) timed the same way.
+  detail       -- per-shape times, the three grouped MoE workloads
+                  (contiguous, masked, K-grouped) timed the same way, and the
+                  FP8 casting kernels on bf16 operands of those shapes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-detail]
                        [--no-cpu] [--json-out PATH]
@@ -75,12 +76,17 @@ def main():
     ap.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE_DIR", "FETCH_DIR",
                                                               "WRITE_DIR", "BENCH_JSON", "OUT_MD"),
                     help="write a profiles/ summary from rocprofv3 CSV output and exit")
+    ap.add_argument("--summarize-cast", nargs=3, metavar=("TRACE_DIR", "BENCH_JSON", "OUT_MD"),
+                    help="write the profiles/ summary of the casting kernels")
     ap.add_argument("--summarize-grouped", nargs=3, metavar=("TRACE_DIR", "BENCH_JSON", "OUT_MD"),
                     help="write the profiles/ summary of the grouped-workload kernel trace and exit")
     args = ap.parse_args()
 
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, commands=PROFILE_COMMANDS)
+        return
+    if args.summarize_cast:
+        summarize_cast(*args.summarize_cast)
         return
     if args.summarize_grouped:
         summarize_grouped(*args.summarize_grouped)
@@ -211,11 +217,12 @@ def main():
     print(f"[bench] step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     # ---- grouped workloads (detail, timed the same way) ------------------------------
-    grouped = {}
+    grouped, cast = {}, {}
     if not args.no_detail:
         del ops
         torch.cuda.empty_cache()
         grouped = bench_grouped(dg, gen, up, dev, stream, args)
+        cast = bench_cast(dg, dev, stream, args)
 
     # ---- CPU baseline: the oracle on a bounded sample ----------------------------------
     cpu = None
@@ -241,7 +248,7 @@ def main():
                    "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "detail": {"dense": per_shape, "grouped": grouped},
+        "detail": {"dense": per_shape, "grouped": grouped, "cast": cast},
     }
     line = json.dumps(result)
     print(line, flush=True)
@@ -261,6 +268,8 @@ KERNEL_SOURCES = {
     "tn": ["fp8_fine_grained_e4m3_amd/csrc/tn_kernel.hip",
            "fp8_fine_grained_e4m3_amd/csrc/tile_common.h",
            "fp8_fine_grained_e4m3_amd/csrc/dg_internal.h"],
+    "cast": ["fp8_fine_grained_e4m3_amd/csrc/cast_kernel.hip",
+             "fp8_fine_grained_e4m3_amd/csrc/dg_internal.h"],
 }
 
 
@@ -453,6 +462,90 @@ def bench_grouped(dg, gen, up, dev, stream, args):
     del a, sa, b, sb, c, d, x
     torch.cuda.empty_cache()
     return out
+
+
+# FP8 casting workloads: the operands of the GEMM workloads above, unquantised
+# (bf16), cast by the casting kernels.  name -> (per_block, shape)
+CAST_WORKLOADS = {
+    "per_token_4096x7168": (False, (4096, 7168)),          # dense M = 4096 A operand
+    "per_token_51200x4096": (False, (51200, 4096)),        # contiguous MoE A operand
+    "per_token_32x256x2048": (False, (32, 256, 2048)),     # masked MoE A operand
+    "per_block_7168x16384": (True, (7168, 16384)),         # dense B operand
+    "per_block_32x4096x4096": (True, (32, 4096, 4096)),    # MoE expert weights
+}
+
+
+def cast_bytes(per_block, shape):
+    """Algorithmic HBM bytes: bf16 in, e4m3 out, fp32 scales out."""
+    n = int(np.prod(shape))
+    K = shape[-1]
+    rows = int(np.prod(shape[:-1]))
+    if per_block:
+        G = shape[0] if len(shape) == 3 else 1
+        n_sf = G * ((shape[-2] + 127) // 128) * (K // 128)
+    else:
+        n_sf = rows * (K // 128)
+    return 2 * n + n + 4 * n_sf
+
+
+def bench_cast(dg, dev, stream, args):
+    """HIP-event times of the casting kernels on bf16 operands of the GEMM
+    workloads' shapes (inputs resident in HBM), against the HBM roof."""
+    import torch
+    out = {}
+    reps = max(3, min(args.steps, 10))
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    for name, (per_block, shape) in CAST_WORKLOADS.items():
+        x = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        fn = dg.per_block_cast_to_fp8 if per_block else dg.per_token_cast_to_fp8
+        codes, sf = fn(x)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn(x, out=(codes, sf))
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+        byts = cast_bytes(per_block, shape)
+        out[name] = dict(us=round(ms * 1e3, 1), gbs=round(byts / ms / 1e6, 1),
+                         frac_hbm=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4), bytes=byts)
+        del x, codes, sf
+        torch.cuda.empty_cache()
+    return out
+
+
+def summarize_cast(trace_dir, bench_json, out_path):
+    """profiles/ summary of the casting kernels: rocprofv3 per-kernel averages
+    next to bench.py's HIP-event timings of the same run."""
+    import csv
+    res = json.load(open(bench_json))
+    cast = res["detail"]["cast"]
+    stats = [r for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv")))
+             if "cast_kernel" in r["Name"]]
+    lines = ["# FP8 casting kernels (per token 1x128, per block 128x128) -- rocprofv3 kernel trace",
+             "", "Commands (run from the repository root on one MI355X):", ""]
+    lines += [f"    {c}" for c in GROUPED_PROFILE_COMMANDS[:1]]
+    lines += [f"    python3 bench.py --summarize-cast gpurun_out/prof_grouped "
+              f"gpurun_out/bench_grouped.json {os.path.relpath(out_path, ROOT)}"]
+    lines += ["", "Template arguments: input type (`unsigned short` = bf16 bits), rows per wave,",
+              "per-block flag (true = 128 x 128 weights).", "",
+              "## Kernel trace (--kernel-trace --stats)", "",
+              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", "## bench.py HIP-event timings (same run; bf16 in, e4m3 + fp32 scales out)", "",
+              "| workload | us | algorithmic MB | GB/s | fraction of HBM roof (8 TB/s) |",
+              "|---|---|---|---|---|"]
+    for name, v in cast.items():
+        lines.append(f"| {name} | {v['us']} | {v['bytes'] / 1e6:.1f} | {v['gbs']} | {v['frac_hbm']} |")
+    lines += ["", f"    kernel_source_sha256_16: cast {source_hash('cast')}", ""]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines))
+    print(out_path)
 
 
 def cpu_baseline(gen, shape, target_s):

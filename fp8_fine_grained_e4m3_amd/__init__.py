@@ -1,7 +1,8 @@
 """Python binding of libdg.so, the MI355X (gfx950) fine-grained FP8 e4m3 GEMM.
 
-Argument marshalling only: every step of every GEMM runs in the HIP kernels
-behind the C ABI declared in include/dg.h.  PyTorch supplies device memory and
+Argument marshalling only: every step of every GEMM, and of the FP8 casting
+that prepares its operands, runs in the HIP kernels behind the C ABI declared
+in include/dg.h.  PyTorch supplies device memory and
 the current stream.  There is no fallback path: if libdg.so is missing or a
 call fails, an exception is raised.
 
@@ -36,7 +37,10 @@ EXPORTED = (
     "dg_set_num_cus",
     "dg_get_mk_alignment_for_contiguous_layout",
     "dg_kernel_config_name",
+    "dg_per_token_cast_to_fp8",
+    "dg_per_block_cast_to_fp8",
 )
+DG_CAST_POW2_SCALE = 1
 
 _lib = None
 
@@ -74,6 +78,9 @@ def load_library(path: Optional[str] = None):
     lib.dg_get_mk_alignment_for_contiguous_layout.restype = I
     lib.dg_kernel_config_name.argtypes = [I, I64, I64, I64, I]
     lib.dg_kernel_config_name.restype = ctypes.c_char_p
+    for name in ("dg_per_token_cast_to_fp8", "dg_per_block_cast_to_fp8"):
+        getattr(lib, name).argtypes = [P, I, P, P, I64, I64, I64, I, P]
+        getattr(lib, name).restype = I
     if path is None:
         _lib = lib
     return lib
@@ -246,3 +253,48 @@ def to_mn_major_sf(sf: torch.Tensor) -> torch.Tensor:
     """[rows, K/128] per-row scales -> the MN-major [K/128, rows] layout the
     A-side scale factors use (a transpose + copy; layout only)."""
     return sf.transpose(-1, -2).contiguous()
+
+
+def _cast(fn: str, x: torch.Tensor, block_scale: bool, pow2_scale: bool,
+          out: Optional[Tuple[torch.Tensor, torch.Tensor]]):
+    x = _dev(x, "x")
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    if x.dim() not in (2, 3):
+        raise ValueError("x must be [rows, K] or [G, rows, K]")
+    batched = x.dim() == 3
+    G, R, K = x.shape if batched else (1,) + tuple(x.shape)
+    if K % 128:
+        raise ValueError(f"K={K} is not a multiple of 128")
+    sf_shape = (G, (R + 127) // 128, K // 128) if block_scale else (G, K // 128, R)
+    if not batched:
+        sf_shape = sf_shape[1:]
+    if out is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        sf = torch.empty(sf_shape, dtype=torch.float32, device=x.device)
+    else:
+        codes, sf = _fp8(out[0], "codes"), _f32(out[1], "sf")
+        if tuple(codes.shape) != tuple(x.shape) or tuple(sf.shape) != sf_shape:
+            raise ValueError(f"out shapes: codes {tuple(codes.shape)} sf {tuple(sf.shape)}, "
+                             f"want {tuple(x.shape)} and {sf_shape}")
+    with torch.cuda.device(x.device):
+        _check(getattr(load_library(), fn)(
+            _ptr(x), DG_F32 if x.dtype == torch.float32 else DG_BF16, _ptr(codes), _ptr(sf),
+            G, R, K, DG_CAST_POW2_SCALE if pow2_scale else 0, _stream(x)))
+    return codes, sf
+
+
+def per_token_cast_to_fp8(x: torch.Tensor, pow2_scale: bool = False,
+                          out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """1 x 128 casting of activations x [R, K] or [G, R, K] (bf16 or fp32).
+    Returns (codes uint8 like x, sf fp32 [K/128, R] or [G, K/128, R]): the A
+    operand and its MN-major scales for the GEMM calls above."""
+    return _cast("dg_per_token_cast_to_fp8", x, False, pow2_scale, out)
+
+
+def per_block_cast_to_fp8(w: torch.Tensor, pow2_scale: bool = False,
+                          out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """128 x 128 casting of weights w [N, K] or [G, N, K] (bf16 or fp32).
+    Returns (codes uint8 like w, sf fp32 [ceil(N/128), K/128] or
+    [G, ceil(N/128), K/128]): the B operand and its scales."""
+    return _cast("dg_per_block_cast_to_fp8", w, True, pow2_scale, out)

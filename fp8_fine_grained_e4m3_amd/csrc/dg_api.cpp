@@ -308,6 +308,55 @@ dg_status dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t* a, const float* sfa
     return ok();
 }
 
+static dg_status run_cast(const void* x, dg_dtype dtype, uint8_t* codes, float* sf, int64_t G,
+                          int64_t R, int64_t K, int flags, bool block_scale, void* stream) {
+    REQUIRE(G >= 0 && R >= 0 && K >= 0, "negative size (G=%lld rows=%lld K=%lld)", (long long)G,
+            (long long)R, (long long)K);
+    REQUIRE(K % 128 == 0, "K=%lld is not a multiple of 128", (long long)K);
+    REQUIRE(dtype == DG_BF16 || dtype == DG_F32, "input dtype must be DG_BF16 or DG_F32");
+    REQUIRE(flags == 0 || flags == DG_CAST_POW2_SCALE, "flags must be 0 or DG_CAST_POW2_SCALE");
+    if (G == 0 || R == 0 || K == 0) return ok();
+    REQUIRE_PTR(x, 16);
+    REQUIRE_PTR(codes, 16);
+    REQUIRE_PTR(sf, 4);
+    REQUIRE(R <= kOffsetLimit && K <= kOffsetLimit, "size too large");
+    REQUIRE(G <= kOffsetLimit && R <= kOffsetLimit / K, "rows*K must stay below 2^31");
+    const int64_t n = G * R * K;   // < 2^62
+    const int64_t in_bytes = n * (dtype == DG_F32 ? 4 : 2);
+    const int64_t kb = K / 128;
+    const int64_t sf_count = block_scale ? G * ((R + 127) / 128) * kb : G * kb * R;
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), c0 = reinterpret_cast<uintptr_t>(codes),
+                    s0 = reinterpret_cast<uintptr_t>(sf);
+    auto disjoint = [](uintptr_t a, int64_t na, uintptr_t b, int64_t nb) {
+        return a + (uintptr_t)na <= b || b + (uintptr_t)nb <= a;
+    };
+    REQUIRE(disjoint(x0, in_bytes, c0, n) && disjoint(x0, in_bytes, s0, sf_count * 4) &&
+                disjoint(c0, n, s0, sf_count * 4),
+            "input, codes and sf must not overlap");
+    dg::CastProblem p{};
+    p.x = x; p.in_f32 = dtype == DG_F32; p.block_scale = block_scale;
+    p.pow2 = flags == DG_CAST_POW2_SCALE;
+    p.codes = codes; p.sf = sf; p.G = G; p.R = R; p.K = K;
+    REQUIRE(dg::cast_grid(p) <= INT_MAX, "too many blocks");
+    int dev = 0;
+    DeviceInfo info;
+    dg_status st = current_device(dev, info);
+    if (st != DG_OK) return st;
+    hipError_t e = dg::launch_cast(p, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+dg_status dg_per_token_cast_to_fp8(const void* x, dg_dtype x_dtype, uint8_t* codes, float* sf,
+                                   int64_t G, int64_t R, int64_t K, int flags, void* stream) {
+    return run_cast(x, x_dtype, codes, sf, G, R, K, flags, false, stream);
+}
+
+dg_status dg_per_block_cast_to_fp8(const void* w, dg_dtype w_dtype, uint8_t* codes, float* sf,
+                                   int64_t G, int64_t N, int64_t K, int flags, void* stream) {
+    return run_cast(w, w_dtype, codes, sf, G, N, K, flags, true, stream);
+}
+
 const char* dg_last_error(void) { return g_last_error.c_str(); }
 
 int dg_get_num_cus(void) {

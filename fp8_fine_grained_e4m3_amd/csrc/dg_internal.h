@@ -38,6 +38,18 @@ struct TnProblem {
 
 constexpr int kMaxTnGroups = 256;
 
+// FP8 casting: x [G, R, K] (bf16 bits or fp32) -> codes [G, R, K] and either
+// per-token scales sf [G, K/128, R] or per-block scales sf [G, ceil(R/128), K/128].
+struct CastProblem {
+    const void* x;
+    bool in_f32;
+    bool block_scale;   // false: 1 x 128 (per token), true: 128 x 128 (per block)
+    bool pow2;          // round each scale up to a power of two
+    uint8_t* codes;
+    float* sf;
+    int64_t G, R, K;
+};
+
 // Device memory for split-K partial tiles, one buffer per (device, stream),
 // grown on demand and kept until the process ends.  `counters` are zero
 // whenever no kernel using them is running (each launch leaves them zero).
@@ -56,6 +68,8 @@ bool split_workspace(hipStream_t stream, size_t part_floats, size_t n_counters,
 // status of the launch.  Shapes have already been validated.
 hipError_t launch_nt(const NtProblem& p, int cu_cap, hipStream_t stream);
 hipError_t launch_tn(const TnProblem& p, int cu_cap, hipStream_t stream);
+hipError_t launch_cast(const CastProblem& p, hipStream_t stream);
+int64_t cast_grid(const CastProblem& p);   // workgroups launch_cast would start
 
 // Short description of the tile configuration chosen for a problem (for
 // DG_PRINT_CONFIGS), and the stable name of the kernel instance it launches.

@@ -166,6 +166,45 @@ dg_status dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t* a, const float* sfa
                                               int64_t G, int64_t M, int64_t N, int64_t K_tot,
                                               void* stream);
 
+/*
+ * FP8 casting, the step before the GEMM (the "DeepGEMM" README, "Interfaces",
+ * "Notices", leaves casting to the caller and suggests fusing it into the
+ * producer; these kernels write exactly the operand layouts the GEMM entry
+ * points above take).  For every block of 128 consecutive K columns and
+ *   - 1 row  (dg_per_token_cast_to_fp8: activations, the A operand), or
+ *   - 128 rows (dg_per_block_cast_to_fp8: weights, the B operand; the last
+ *     block of a group covers the rows that exist):
+ *   amax  = max |x| over the block
+ *   s     = amax / 448 in fp32, correctly rounded; 1 when amax == 0; with
+ *           DG_CAST_POW2_SCALE, s is then rounded up to a power of two
+ *   code  = the e4m3 (OCP E4M3FN) value nearest to clamp(x / s, -448, 448),
+ *           x / s the correctly rounded fp32 quotient, ties to the even
+ *           mantissa; negative values that round to zero give 0x80
+ * These are the casting rules the GEMM workloads are defined with; the pages
+ * give the granularities' names only ("fine-grained").
+ *
+ * dg_per_token_cast_to_fp8:
+ *   x      [G, R, K]  DG_BF16 (uint16_t bit patterns) or DG_F32, row-major;
+ *                     values must be finite
+ *   codes  [G, R, K]  e4m3 bytes
+ *   sf     [G, K/128, R] fp32, MN-major: with G == 1 this is the sfa of
+ *                     dg_fp8_gemm_nt / the contiguous form, with G groups of
+ *                     R = M_max rows the sfa of the masked form
+ * dg_per_block_cast_to_fp8:
+ *   w      [G, N, K]  DG_BF16 or DG_F32 (finite)
+ *   codes  [G, N, K]  e4m3 bytes
+ *   sf     [G, ceil(N/128), K/128] fp32 (the sfb of the GEMM entry points)
+ * Rules: K % 128 == 0; G, R / N >= 0; x / w and codes 16-byte aligned, sf
+ * 4-byte aligned; flags is 0 or DG_CAST_POW2_SCALE; outputs must not overlap
+ * the input.  One kernel launch on `stream`, no synchronisation, no
+ * workspace.  Results are deterministic and bit-exact (no rounding freedom).
+ */
+#define DG_CAST_POW2_SCALE 1
+dg_status dg_per_token_cast_to_fp8(const void* x, dg_dtype x_dtype, uint8_t* codes, float* sf,
+                                   int64_t G, int64_t R, int64_t K, int flags, void* stream);
+dg_status dg_per_block_cast_to_fp8(const void* w, dg_dtype w_dtype, uint8_t* codes, float* sf,
+                                   int64_t G, int64_t N, int64_t K, int flags, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* dg_last_error(void);
 

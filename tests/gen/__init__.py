@@ -330,3 +330,32 @@ def gen_config(i: int, seed: int = 0):
     if i == 5:
         return gen_k_grouped(seed=seed)
     raise ValueError(i)
+
+
+# --------------------------------------------------------------------------
+# Unquantised operands for the casting kernels
+# --------------------------------------------------------------------------
+
+def to_bf16_values(x: np.ndarray) -> np.ndarray:
+    """fp32 array rounded (RNE) to bf16-representable values, kept as fp32."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def gen_activations(shape, seed: int = 0, bf16: bool = True) -> np.ndarray:
+    """Activation-like values: N(0,1) times a per-row magnitude exp(N(0, 1.5)),
+    one outlier (x 30) per row, a few exact zeros and negative zeros, and in
+    the last row a block of bf16 subnormals (its amax is subnormal).  Returned
+    as fp32; with bf16, every value is bf16-representable."""
+    rng = _rng(seed)
+    x = _normal(rng, shape)
+    rows = int(np.prod(shape[:-1]))
+    K = shape[-1]
+    flat = x.reshape(rows, K)
+    flat *= np.exp(rng.normal(0, 1.5, size=(rows, 1))).astype(np.float32)
+    out_col = rng.integers(0, K, size=rows)
+    flat[np.arange(rows), out_col] *= np.float32(30)
+    flat[:, 3] = 0.0
+    flat[:, 7] = -0.0
+    if K >= 128 and rows > 1:
+        flat[-1, :128] = (rng.integers(-120, 121, size=128) * 2.0 ** -133).astype(np.float32)
+    return to_bf16_values(x) if bf16 else x

@@ -127,6 +127,23 @@ def test_k_grouped_rejects(lib):
     assert call([128, 0], M=0) == dg.DG_OK
 
 
+def test_cast_rejects(lib):
+    for f in (lib.dg_per_token_cast_to_fp8, lib.dg_per_block_cast_to_fp8):
+        def call(x=P16, dt=dg.DG_BF16, codes=P16b, sf=P16c, G=1, R=64, K=256, flags=0):
+            return f(x, dt, codes, sf, G, R, K, flags, None)
+        assert call(K=200) == dg.DG_ERR_INVALID_ARG and "K=200" in err(lib)
+        assert call(R=-1) == dg.DG_ERR_INVALID_ARG and "negative" in err(lib)
+        assert call(dt=9) == dg.DG_ERR_INVALID_ARG and "dtype" in err(lib)
+        assert call(flags=2) == dg.DG_ERR_INVALID_ARG and "flags" in err(lib)
+        assert call(x=BAD) == dg.DG_ERR_INVALID_ARG and "16-byte" in err(lib)
+        assert call(codes=NULL) == dg.DG_ERR_INVALID_ARG and "codes is NULL" in err(lib)
+        assert call(codes=ctypes.c_void_p(0x10000 + 64 * 256)) == dg.DG_ERR_INVALID_ARG
+        assert "overlap" in err(lib)
+        assert call(R=1 << 24, K=1024) == dg.DG_ERR_INVALID_ARG and "2^31" in err(lib)
+        assert call(R=0, x=NULL) == dg.DG_OK and call(G=0, x=NULL) == dg.DG_OK
+        assert call(K=0, x=NULL) == dg.DG_OK
+
+
 def test_valid_call_without_gpu_fails_cleanly(lib):
     """With valid arguments the library asks HIP for the device; with no GPU
     that fails with a HIP or unsupported-device status, never a crash."""
