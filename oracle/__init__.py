@@ -92,6 +92,10 @@ def _bind(lib):
     lib.oracle_cast_rows.restype = ctypes.c_int
     lib.oracle_cast_blocks.argtypes = [P, I, I, I, ctypes.c_int, P, P]
     lib.oracle_cast_blocks.restype = ctypes.c_int
+    lib.oracle_gemm_nt_ue8m0.argtypes = [P, P, P, P, P, I, I, I, P, I, P]
+    lib.oracle_gemm_nt_ue8m0.restype = ctypes.c_int
+    lib.oracle_pack_ue8m0.argtypes = [P, ctypes.c_int, I, I, P]
+    lib.oracle_pack_ue8m0.restype = ctypes.c_int
     return lib
 
 
@@ -238,3 +242,31 @@ def cast_blocks(w, pow2: bool = False):
     if _load().oracle_cast_blocks(_ptr(w3), G, N, K, int(pow2), _ptr(codes), _ptr(sf)):
         raise ValueError("oracle_cast_blocks: bad arguments")
     return (codes, sf) if batched else (codes[0], sf[0])
+
+
+def gemm_nt_ue8m0(a, sfa_packed, b, sfb_packed, c=None, rows=None) -> np.ndarray:
+    """D[rows] of D = C + A @ B^T with packed UE8M0 per-row scales:
+    sfa_packed int32 [ceil(K/512), M], sfb_packed int32 [ceil(K/512), N]."""
+    a = _c(a, np.uint8); b = _c(b, np.uint8)
+    sa = _c(sfa_packed, np.int32); sb = _c(sfb_packed, np.int32)
+    M, K = a.shape
+    N = b.shape[0]
+    K4 = (K // 128 + 3) // 4
+    assert b.shape[1] == K and sa.shape == (K4, M) and sb.shape == (K4, N)
+    cc = None if c is None else _c(c, np.float32)
+    r = np.arange(M, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    out = np.empty((len(r), N), dtype=np.float64)
+    if _load().oracle_gemm_nt_ue8m0(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(cc), M, N, K,
+                                    _ptr(r), len(r), _ptr(out)):
+        raise ValueError("oracle_gemm_nt_ue8m0: bad arguments")
+    return out
+
+
+def pack_ue8m0(sf, per_block: bool, MN: int, K: int) -> np.ndarray:
+    """Power-of-two fp32 scales -> packed UE8M0 int32 [ceil(K/512), MN].
+    per_block=False: sf [K/128, MN]; True: sf [ceil(MN/128), K/128]."""
+    s = _c(sf, np.float32)
+    out = np.empty(((K // 128 + 3) // 4, MN), dtype=np.int32)
+    if _load().oracle_pack_ue8m0(_ptr(s), int(per_block), MN, K, _ptr(out)):
+        raise ValueError("oracle_pack_ue8m0: bad arguments or a scale that is not a power of two")
+    return out

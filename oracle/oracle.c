@@ -363,3 +363,77 @@ int oracle_cast_blocks(const float* w, int64_t G, int64_t N, int64_t K, int pow2
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Power-of-two (UE8M0) scales.  The "DeepGEMM" README ("Interfaces",
+ * "Notices") gives its newer path scale factors as UE8M0 exponents packed
+ * four to a 32-bit integer.  Reading: byte i of word [k4][mn] is the exponent
+ * e of the scale 2^(e - 127) of K block 4 k4 + i for row mn (MN-major, K
+ * blocks packed little-end first); bytes past the last K block are 0.  Both
+ * operands carry per-row scales in this form (a 128 x 128 weight scale is
+ * given to each of its 128 rows).  The GEMM is the same definition as above
+ * with those scales:
+ *   D[m,n] = C[m,n] + sum_kb 2^(ea(m,kb) - 127) * 2^(eb(n,kb) - 127) * P_kb[m,n]
+ * ------------------------------------------------------------------------- */
+
+static double ue8m0_scale(const int32_t* packed, int64_t MN, int64_t mn, int64_t kb)
+{
+    const uint32_t w = (uint32_t)packed[(kb / 4) * MN + mn];
+    const int e = (int)((w >> (8 * (kb % 4))) & 0xFF);
+    return e == 0xFF ? NAN : ldexp(1.0, e - 127);
+}
+
+int oracle_gemm_nt_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
+                         const int32_t* sfb, const float* c, int64_t M, int64_t N, int64_t K,
+                         const int64_t* rows, int64_t n_rows, double* out)
+{
+    if (K % KBLK != 0)
+        return 1;
+    build_table();
+    const int64_t KB = K / KBLK;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int64_t m = rows[i];
+        if (m < 0 || m >= M) { bad |= 1; continue; }
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t kb = 0; kb < KB; ++kb) {
+                double p = 0.0;                           /* exact block sum */
+                for (int64_t k = kb * KBLK; k < (kb + 1) * KBLK; ++k)
+                    p += g_dec[a[m * K + k]] * g_dec[b[n * K + k]];
+                acc += ue8m0_scale(sfa, M, m, kb) * ue8m0_scale(sfb, N, n, kb) * p;
+            }
+            out[i * N + n] = acc + (c ? (double)c[m * N + n] : 0.0);
+        }
+    }
+    return bad;
+}
+
+/* fp32 power-of-two scales -> packed UE8M0 words [ceil(K/512), MN].
+ * layout 0: sf [K/128, MN], one scale per (row, K block) (the A side);
+ * layout 1: sf [ceil(MN/128), K/128], one per 128 x 128 block, given to each
+ *           of the block's rows (the B side).
+ * A scale that is not a power of two in [2^-127, 2^127] is rejected (1). */
+int oracle_pack_ue8m0(const float* sf, int layout, int64_t MN, int64_t K, int32_t* packed)
+{
+    if (K % KBLK != 0 || (layout != 0 && layout != 1))
+        return 1;
+    const int64_t KB = K / KBLK, K4 = (KB + 3) / 4;
+    for (int64_t k4 = 0; k4 < K4; ++k4)
+        for (int64_t mn = 0; mn < MN; ++mn) {
+            uint32_t w = 0;
+            for (int64_t i = 0; i < 4 && 4 * k4 + i < KB; ++i) {
+                const int64_t kb = 4 * k4 + i;
+                const double s = layout == 0 ? sf[kb * MN + mn] : sf[(mn / KBLK) * KB + kb];
+                int x;
+                const double f = frexp(s, &x);            /* s = f * 2^x */
+                const int e = x - 1 + 127;                /* s = 2^(x-1) when f == 0.5 */
+                if (f != 0.5 || e < 0 || e > 254)
+                    return 1;
+                w |= (uint32_t)e << (8 * i);
+            }
+            packed[k4 * MN + mn] = (int32_t)w;
+        }
+    return 0;
+}

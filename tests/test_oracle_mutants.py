@@ -12,6 +12,7 @@ import pytest
 import oracle
 from tests import test_oracle_cast_pins as cast_pins
 from tests import test_oracle_pins as pins
+from tests import test_oracle_ue8m0_pins as ue8m0_pins
 
 MUTANTS = {
     "exponent_bias": ("mag = ldexp(1.0 + (double)m / 8.0, e - 7);",
@@ -55,6 +56,13 @@ MUTANTS = {
     "cast_pow2_rounds_down": ("s = (float)ldexp(1.0, e);", "s = (float)ldexp(1.0, e - 1);"),
     "cast_blocks_drop_tail_rows": ("const int64_t n1 = (nb + 1) * KBLK < N ? (nb + 1) * KBLK : N;",
                                    "const int64_t n1 = (nb + 1) * KBLK < N ? (nb + 1) * KBLK : N - 1;"),
+    "ue8m0_bias": ("return e == 0xFF ? NAN : ldexp(1.0, e - 127);",
+                   "return e == 0xFF ? NAN : ldexp(1.0, e - 128);"),
+    "ue8m0_byte_order": ("const int e = (int)((w >> (8 * (kb % 4))) & 0xFF);",
+                         "const int e = (int)((w >> (8 * (3 - kb % 4))) & 0xFF);"),
+    "ue8m0_b_per_block": ("ue8m0_scale(sfb, N, n, kb)", "ue8m0_scale(sfb, N, (n / KBLK) * KBLK, kb)"),
+    "ue8m0_pack_offset": ("const int e = x - 1 + 127;", "const int e = x + 127;"),
+    "ue8m0_pack_broadcast": ("sf[(mn / KBLK) * KB + kb]", "sf[kb]"),
     "cast_zero_scale": ("if (amax == 0.0f)\n        return 1.0f;", "if (amax == 0.0f)\n        return 0.5f;"),
 }
 
@@ -88,6 +96,10 @@ def _pin_suite():
         ("cast_pow2", cast_pins.test_cast_rows_pow2_scales),
         ("cast_gen_blocks", cast_pins.test_cast_blocks_matches_generator_quantiser_with_ragged_n),
         ("cast_blocks_nearest", cast_pins.test_cast_blocks_is_the_nearest_code_of_the_fp32_quotient),
+        ("ue8m0_pack", ue8m0_pins.test_pack_matches_frexp_and_byte_order),
+        ("ue8m0_broadcast", ue8m0_pins.test_pack_broadcasts_block_scales_to_rows),
+        ("ue8m0_exact", lambda: ue8m0_pins.test_gemm_ue8m0_matches_exact_rationals(53, 4, 6, 640)),
+        ("ue8m0_vs_fp32", ue8m0_pins.test_gemm_ue8m0_equals_fp32_scale_definition_on_block_constant_b),
     ]
     failed = []
     for name, fn in checks:

@@ -1,0 +1,112 @@
+"""Pins of the oracle's power-of-two (UE8M0) scale path against things other
+than itself.
+
+Reading (the "DeepGEMM" README, "Interfaces", "Notices", names packed UE8M0
+scale factors, four per 32-bit integer, for its newer path): byte i of word
+[k4][mn] is the exponent e of the scale 2^(e - 127) of K block 4 k4 + i for row
+mn; both operands carry per-row scales (a 128 x 128 weight scale is given to
+each of its rows).
+
+* The packer against exponents computed with math.frexp, the byte order, the
+  broadcast of block scales and its refusal of non-powers of two.
+* The GEMM against exact rational arithmetic with every row and column of B
+  on its own exponents, and against the fp32-scale oracle where the two
+  definitions coincide (B exponents constant over 128-row blocks).
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.test_oracle_pins import random_codes, torch_decode
+
+
+def rand_exponents(rng, shape, lo=110, hi=140):
+    return rng.integers(lo, hi, size=shape).astype(np.int64)
+
+
+def pack_bytes(e):
+    """[KB, MN] exponent bytes -> [ceil(KB/4), MN] int32 words (byte i = block 4 k4 + i)."""
+    KB, MN = e.shape
+    K4 = (KB + 3) // 4
+    w = np.zeros((K4, MN), np.uint32)
+    for kb in range(KB):
+        w[kb // 4] |= (e[kb].astype(np.uint32) << np.uint32(8 * (kb % 4)))
+    return w.view(np.int32)
+
+
+def test_pack_matches_frexp_and_byte_order():
+    rng = np.random.default_rng(50)
+    KB, MN = 6, 9
+    e = rand_exponents(rng, (KB, MN), 1, 254)
+    sf = np.ldexp(np.float32(1), (e - 127).astype(np.int32)).astype(np.float32)
+    got = oracle.pack_ue8m0(sf, False, MN, KB * 128).view(np.uint32)
+    assert got.shape == (2, MN)
+    for kb in range(KB):
+        for mn in range(MN):
+            byte = (int(got[kb // 4, mn]) >> (8 * (kb % 4))) & 0xFF
+            m, x = math.frexp(float(sf[kb, mn]))
+            assert m == 0.5 and byte == x - 1 + 127
+    assert np.all(got[1] >> 16 == 0)                   # blocks 6, 7 do not exist
+
+
+def test_pack_broadcasts_block_scales_to_rows():
+    rng = np.random.default_rng(51)
+    N, KB = 300, 5
+    e = rand_exponents(rng, (3, KB))
+    sf = np.ldexp(np.float32(1), (e - 127).astype(np.int32)).astype(np.float32)
+    got = oracle.pack_ue8m0(sf, True, N, KB * 128)
+    want = pack_bytes(np.repeat(e.T, 128, axis=1)[:, :N])
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("bad", [3.0, 0.0, 2.0 ** -130, 1.5])
+def test_pack_rejects_non_powers_of_two(bad):
+    sf = np.ones((1, 4), np.float32)
+    sf[0, 2] = bad
+    with pytest.raises(ValueError):
+        oracle.pack_ue8m0(sf, False, 4, 128)
+
+
+def exact_ue8m0(a, ea, b, eb):
+    """Exact D for tiny shapes: ea [KB, M], eb [KB, N] exponent bytes."""
+    M, K = a.shape
+    N = b.shape[0]
+    da = [[Fraction(float(v)) for v in row] for row in torch_decode(a)]
+    db = [[Fraction(float(v)) for v in row] for row in torch_decode(b)]
+    val = np.zeros((M, N)); bound = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0); mag = Fraction(0)
+            for kb in range(K // 128):
+                p = sum(da[m][k] * db[n][k] for k in range(kb * 128, kb * 128 + 128))
+                s = Fraction(2) ** (int(ea[kb, m]) - 127) * Fraction(2) ** (int(eb[kb, n]) - 127)
+                tot += s * p; mag += abs(s * p)
+            val[m, n] = float(tot)
+            bound[m, n] = float(mag) * (2 * (K // 128) + 2) * 2.0 ** -53 + 1e-300
+    return val, bound
+
+
+@pytest.mark.parametrize("seed,M,N,K", [(52, 3, 5, 128), (53, 4, 6, 640), (54, 2, 17, 1152)])
+def test_gemm_ue8m0_matches_exact_rationals(seed, M, N, K):
+    rng = np.random.default_rng(seed)
+    a = random_codes(rng, (M, K)); b = random_codes(rng, (N, K))
+    ea = rand_exponents(rng, (K // 128, M)); eb = rand_exponents(rng, (K // 128, N))
+    got = oracle.gemm_nt_ue8m0(a, pack_bytes(ea), b, pack_bytes(eb))
+    val, bound = exact_ue8m0(a, ea, b, eb)
+    assert np.all(np.abs(got - val) <= bound)
+
+
+def test_gemm_ue8m0_equals_fp32_scale_definition_on_block_constant_b():
+    rng = np.random.default_rng(55)
+    M, N, K = 5, 256, 640
+    a = random_codes(rng, (M, K)); b = random_codes(rng, (N, K))
+    ea = rand_exponents(rng, (K // 128, M)); eb_blk = rand_exponents(rng, (N // 128, K // 128))
+    sfa = np.ldexp(np.float32(1), (ea - 127).astype(np.int32)).astype(np.float32)
+    sfb = np.ldexp(np.float32(1), (eb_blk - 127).astype(np.int32)).astype(np.float32)
+    ref = oracle.gemm_nt(a, sfa, b, sfb)
+    got = oracle.gemm_nt_ue8m0(a, oracle.pack_ue8m0(sfa, False, M, K), b,
+                               oracle.pack_ue8m0(sfb, True, N, K))
+    assert np.array_equal(got, ref)
