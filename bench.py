@@ -14,8 +14,10 @@ Also reported on the same JSON line:
                   bounds its arithmetic intensity;
   cpu_baseline -- the fp64 CPU oracle on a bounded sample of that shape's rows;
   detail       -- per-shape times, the three grouped MoE workloads
-                  (contiguous, masked, K-grouped) timed the same way, and the
-                  FP8 casting kernels on bf16 operands of those shapes.
+                  (contiguous, masked, K-grouped) timed the same way, the
+                  FP8 casting kernels on bf16 operands of those shapes, and
+                  the power-of-two (packed UE8M0) scale variant of the dense
+                  sweep and the contiguous and masked workloads.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-detail]
                        [--no-cpu] [--json-out PATH]
@@ -217,12 +219,13 @@ def main():
     print(f"[bench] step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     # ---- grouped workloads (detail, timed the same way) ------------------------------
-    grouped, cast = {}, {}
+    grouped, cast, ue8m0 = {}, {}, {}
     if not args.no_detail:
         del ops
         torch.cuda.empty_cache()
         grouped = bench_grouped(dg, gen, up, dev, stream, args)
         cast = bench_cast(dg, dev, stream, args)
+        ue8m0 = bench_ue8m0(dg, gen, up, dev, stream, args)
 
     # ---- CPU baseline: the oracle on a bounded sample ----------------------------------
     cpu = None
@@ -248,7 +251,7 @@ def main():
                    "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "detail": {"dense": per_shape, "grouped": grouped, "cast": cast},
+        "detail": {"dense": per_shape, "grouped": grouped, "cast": cast, "ue8m0": ue8m0},
     }
     line = json.dumps(result)
     print(line, flush=True)
@@ -460,6 +463,75 @@ def bench_grouped(dg, gen, up, dev, stream, args):
                                         gbs=round(byts / ms / 1e6, 1),
                                         frac_hbm=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
     del a, sa, b, sb, c, d, x
+    torch.cuda.empty_cache()
+    return out
+
+
+def median_ms(stream, fn, n):
+    """Median HIP-event time of n launches of fn on `stream` (after one warm-up)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    fn()
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+
+def bench_ue8m0(dg, gen, up, dev, stream, args):
+    """The same workloads with power-of-two scales packed as UE8M0 words (the
+    MFMA applies the scales; no separate promotion): the dense sweep shape by
+    shape, and the contiguous and masked MoE workloads."""
+    import torch
+    reps = max(3, min(args.steps, 10))
+    dense, t_sum, f_sum = [], 0.0, 0.0
+    for (M, N, K) in gen.DENSE_SWEEP:
+        x = gen.gen_dense_ue8m0(M, N, K, seed=0)
+        a, sa, b, sb = up(x.a), up(x.sfa), up(x.b), up(x.sfb)
+        d = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        ms = median_ms(stream, lambda: dg.fp8_gemm_nt((a, sa), (b, sb), d), reps)
+        flop = 2.0 * M * N * K
+        byts = M * K + N * K + 4 * ((K // 128 + 3) // 4) * (M + N) + 2 * M * N
+        dense.append(dict(M=M, N=N, K=K, us=round(ms * 1e3, 2), tflops=round(flop / ms / 1e9, 1),
+                          gbs=round(byts / ms / 1e6, 1)))
+        t_sum += ms
+        f_sum += flop
+        del x, a, sa, b, sb, d
+    out = {"dense": dense,
+           "dense_sweep_sum_of_medians_tflops": round(f_sum / t_sum / 1e9, 1)}
+    torch.cuda.empty_cache()
+
+    x = gen.gen_contiguous(seed=0, pow2=True)
+    wa, wb = gen.to_ue8m0(x.sfa, x.sfb, x.N)
+    a, sa, b, sb, mi = up(x.a), up(wa), up(x.b), up(wb), up(x.m_indices)
+    d = torch.empty(x.M_tot, x.N, dtype=torch.bfloat16, device=dev)
+    ms = median_ms(stream, lambda: dg.m_grouped_fp8_gemm_nt_contiguous((a, sa), (b, sb), d, mi),
+                   reps)
+    flop = 2.0 * int(x.counts.sum()) * x.N * x.K
+    out["contiguous_32x4096x4096"] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
+                                         frac_mfma=round(flop / ms / 1e9 / PEAK_FP8_TFLOPS, 4))
+    del a, sa, b, sb, mi, d, x, wa, wb
+    torch.cuda.empty_cache()
+
+    x = gen.gen_masked(seed=0, pow2=True)
+    wa, wb = gen.to_ue8m0(x.sfa, x.sfb, x.N)
+    a, sa, b, sb, mm = up(x.a), up(wa), up(x.b), up(wb), up(x.masked_m)
+    d = torch.empty(x.G, x.M_max, x.N, dtype=torch.bfloat16, device=dev)
+    ms = median_ms(stream, lambda: dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d, mm), reps)
+    valid = int(x.masked_m.sum())
+    live = int((x.masked_m > 0).sum())
+    k4 = (x.K // 128 + 3) // 4
+    byts = (valid * x.K + valid * 4 * k4 + live * x.N * x.K + live * 4 * k4 * x.N
+            + 2 * valid * x.N + 4 * x.G)
+    out["masked_32x256x4096x2048"] = dict(us=round(ms * 1e3, 1),
+                                         tflops=round(2.0 * valid * x.N * x.K / ms / 1e9, 1),
+                                         gbs=round(byts / ms / 1e6, 1),
+                                         frac_hbm=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
+    del a, sa, b, sb, mm, d, x, wa, wb
     torch.cuda.empty_cache()
     return out
 

@@ -8,8 +8,11 @@ call fails, an exception is raised.
 
 FP8 operands are passed as (data, scale) pairs, data being uint8 (raw e4m3
 bytes) or torch.float8_e4m3fn, scales fp32 (the operand convention of the
-"DeepGEMM" README, yuguo-Jack fork, section "Interfaces").  The caller
-allocates the output and passes it in.
+"DeepGEMM" README, yuguo-Jack fork, section "Interfaces").  For the three NT
+forms the scales may instead be packed UE8M0 words (int32, four power-of-two
+exponents per word, the README's newer-path format): the dtype of the scale
+tensors picks the C entry point.  The caller allocates the output and passes
+it in.
 """
 from __future__ import annotations
 
@@ -39,6 +42,10 @@ EXPORTED = (
     "dg_kernel_config_name",
     "dg_per_token_cast_to_fp8",
     "dg_per_block_cast_to_fp8",
+    "dg_fp8_gemm_nt_ue8m0",
+    "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0",
+    "dg_m_grouped_fp8_gemm_nt_masked_ue8m0",
+    "dg_pack_ue8m0_scales",
 )
 DG_CAST_POW2_SCALE = 1
 
@@ -80,6 +87,14 @@ def load_library(path: Optional[str] = None):
     lib.dg_kernel_config_name.restype = ctypes.c_char_p
     for name in ("dg_per_token_cast_to_fp8", "dg_per_block_cast_to_fp8"):
         getattr(lib, name).argtypes = [P, I, P, P, I64, I64, I64, I, P]
+        getattr(lib, name).restype = I
+    lib.dg_fp8_gemm_nt_ue8m0.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
+    lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0.argtypes = [P, P, P, P, P, P, I64, I64, I64,
+                                                              I64, P]
+    lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
+    lib.dg_pack_ue8m0_scales.argtypes = [P, I, P, I64, I64, I64, P]
+    for name in ("dg_fp8_gemm_nt_ue8m0", "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0",
+                 "dg_m_grouped_fp8_gemm_nt_masked_ue8m0", "dg_pack_ue8m0_scales"):
         getattr(lib, name).restype = I
     if path is None:
         _lib = lib
@@ -123,6 +138,18 @@ def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
     return _dev(t, name)
 
 
+def _scales(sa: torch.Tensor, sb: torch.Tensor):
+    """Both fp32 (-> False) or both packed UE8M0 int32 words (-> True)."""
+    if sa.dtype == torch.int32 and sb.dtype == torch.int32:
+        return _dev(sa, "SFA"), _dev(sb, "SFB"), True
+    return _f32(sa, "SFA"), _f32(sb, "SFB"), False
+
+
+def _k4(K: int) -> int:
+    """Packed UE8M0 words per row: ceil(K / 512)."""
+    return (K // 128 + 3) // 4
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -130,9 +157,10 @@ def _stream(t: torch.Tensor):
 def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, torch.Tensor],
                 d: torch.Tensor, c: Optional[torch.Tensor] = None) -> torch.Tensor:
     """d[M,N] = c + a @ b^T.  a = (A [M,K], SFA [K/128, M]), b = (B [N,K],
-    SFB [ceil(N/128), K/128]); d bf16 or fp32; c None or like d (may be d)."""
-    A, SA = _fp8(a[0], "A"), _f32(a[1], "SFA")
-    B, SB = _fp8(b[0], "B"), _f32(b[1], "SFB")
+    SFB [ceil(N/128), K/128]); d bf16 or fp32; c None or like d (may be d).
+    Packed UE8M0 scales (int32): SFA [ceil(K/512), M], SFB [ceil(K/512), N]."""
+    A, B = _fp8(a[0], "A"), _fp8(b[0], "B")
+    SA, SB, ue8m0 = _scales(a[1], b[1])
     d = _dev(d, "d")
     if d.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("d must be bfloat16 or float32")
@@ -144,10 +172,13 @@ def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, tor
     N = B.shape[0]
     if B.shape[1] != K or tuple(d.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)} B {tuple(B.shape)} d {tuple(d.shape)}")
-    if tuple(SA.shape) != (K // 128, M) or tuple(SB.shape) != ((N + 127) // 128, K // 128):
-        raise ValueError(f"scale shapes: SFA {tuple(SA.shape)} SFB {tuple(SB.shape)}")
+    want = (((_k4(K), M), (_k4(K), N)) if ue8m0
+            else ((K // 128, M), ((N + 127) // 128, K // 128)))
+    if (tuple(SA.shape), tuple(SB.shape)) != want:
+        raise ValueError(f"scale shapes: SFA {tuple(SA.shape)} SFB {tuple(SB.shape)}, want {want}")
+    fn = "dg_fp8_gemm_nt_ue8m0" if ue8m0 else "dg_fp8_gemm_nt"
     with torch.cuda.device(d.device):
-        _check(load_library().dg_fp8_gemm_nt(
+        _check(getattr(load_library(), fn)(
             _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(c), _ptr(d),
             DG_F32 if d.dtype == torch.float32 else DG_BF16, M, N, K, _stream(d)))
     return d
@@ -157,9 +188,10 @@ def m_grouped_fp8_gemm_nt_contiguous(a: Tuple[torch.Tensor, torch.Tensor],
                                      b: Tuple[torch.Tensor, torch.Tensor],
                                      d: torch.Tensor, m_indices: torch.Tensor) -> torch.Tensor:
     """d[r] = a[r] @ b[m_indices[r]]^T; a = (A [M_tot,K], SFA [K/128, M_tot]),
-    b = (B [G,N,K], SFB [G, ceil(N/128), K/128]); d bf16 [M_tot, N]."""
-    A, SA = _fp8(a[0], "A"), _f32(a[1], "SFA")
-    B, SB = _fp8(b[0], "B"), _f32(b[1], "SFB")
+    b = (B [G,N,K], SFB [G, ceil(N/128), K/128]); d bf16 [M_tot, N].
+    Packed UE8M0 scales (int32): SFA [ceil(K/512), M_tot], SFB [G, ceil(K/512), N]."""
+    A, B = _fp8(a[0], "A"), _fp8(b[0], "B")
+    SA, SB, ue8m0 = _scales(a[1], b[1])
     d, mi = _dev(d, "d"), _i32(m_indices, "m_indices")
     if d.dtype != torch.bfloat16:
         raise TypeError("d must be bfloat16")
@@ -167,10 +199,14 @@ def m_grouped_fp8_gemm_nt_contiguous(a: Tuple[torch.Tensor, torch.Tensor],
     G, N, Kb = B.shape
     if Kb != K or tuple(d.shape) != (M_tot, N) or tuple(mi.shape) != (M_tot,):
         raise ValueError("shape mismatch")
-    if tuple(SA.shape) != (K // 128, M_tot) or tuple(SB.shape) != (G, (N + 127) // 128, K // 128):
-        raise ValueError("scale shape mismatch")
+    want = (((_k4(K), M_tot), (G, _k4(K), N)) if ue8m0
+            else ((K // 128, M_tot), (G, (N + 127) // 128, K // 128)))
+    if (tuple(SA.shape), tuple(SB.shape)) != want:
+        raise ValueError(f"scale shapes: SFA {tuple(SA.shape)} SFB {tuple(SB.shape)}, want {want}")
+    fn = ("dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0" if ue8m0
+          else "dg_m_grouped_fp8_gemm_nt_contiguous")
     with torch.cuda.device(d.device):
-        _check(load_library().dg_m_grouped_fp8_gemm_nt_contiguous(
+        _check(getattr(load_library(), fn)(
             _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(mi), _ptr(d), M_tot, N, K, G, _stream(d)))
     return d
 
@@ -179,9 +215,10 @@ def m_grouped_fp8_gemm_nt_masked(a: Tuple[torch.Tensor, torch.Tensor],
                                  b: Tuple[torch.Tensor, torch.Tensor],
                                  d: torch.Tensor, masked_m: torch.Tensor) -> torch.Tensor:
     """d[g, r] = a[g, r] @ b[g]^T for r < masked_m[g]; other rows untouched.
-    a = (A [G,M_max,K], SFA [G, K/128, M_max]), b = (B [G,N,K], SFB [G,NB,KB])."""
-    A, SA = _fp8(a[0], "A"), _f32(a[1], "SFA")
-    B, SB = _fp8(b[0], "B"), _f32(b[1], "SFB")
+    a = (A [G,M_max,K], SFA [G, K/128, M_max]), b = (B [G,N,K], SFB [G,NB,KB]).
+    Packed UE8M0 scales (int32): SFA [G, ceil(K/512), M_max], SFB [G, ceil(K/512), N]."""
+    A, B = _fp8(a[0], "A"), _fp8(b[0], "B")
+    SA, SB, ue8m0 = _scales(a[1], b[1])
     d, mm = _dev(d, "d"), _i32(masked_m, "masked_m")
     if d.dtype != torch.bfloat16:
         raise TypeError("d must be bfloat16")
@@ -189,10 +226,13 @@ def m_grouped_fp8_gemm_nt_masked(a: Tuple[torch.Tensor, torch.Tensor],
     N = B.shape[1]
     if tuple(B.shape) != (G, N, K) or tuple(d.shape) != (G, M_max, N) or tuple(mm.shape) != (G,):
         raise ValueError("shape mismatch")
-    if tuple(SA.shape) != (G, K // 128, M_max) or tuple(SB.shape) != (G, (N + 127) // 128, K // 128):
-        raise ValueError("scale shape mismatch")
+    want = (((G, _k4(K), M_max), (G, _k4(K), N)) if ue8m0
+            else ((G, K // 128, M_max), (G, (N + 127) // 128, K // 128)))
+    if (tuple(SA.shape), tuple(SB.shape)) != want:
+        raise ValueError(f"scale shapes: SFA {tuple(SA.shape)} SFB {tuple(SB.shape)}, want {want}")
+    fn = "dg_m_grouped_fp8_gemm_nt_masked_ue8m0" if ue8m0 else "dg_m_grouped_fp8_gemm_nt_masked"
     with torch.cuda.device(d.device):
-        _check(load_library().dg_m_grouped_fp8_gemm_nt_masked(
+        _check(getattr(load_library(), fn)(
             _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(mm), _ptr(d), G, M_max, N, K, _stream(d)))
     return d
 
@@ -298,3 +338,35 @@ def per_block_cast_to_fp8(w: torch.Tensor, pow2_scale: bool = False,
     Returns (codes uint8 like w, sf fp32 [ceil(N/128), K/128] or
     [G, ceil(N/128), K/128]): the B operand and its scales."""
     return _cast("dg_per_block_cast_to_fp8", w, True, pow2_scale, out)
+
+
+def pack_ue8m0_scales(sf: torch.Tensor, mn: Optional[int] = None,
+                      per_block: bool = False) -> torch.Tensor:
+    """fp32 power-of-two scales -> packed UE8M0 int32 words [.., ceil(K/512), MN].
+
+    per_block False: sf [K/128, MN] or [G, K/128, MN] (A-side, MN-major);
+    per_block True: sf [ceil(MN/128), K/128] or [G, ..] (128 x 128 weight
+    blocks, each given to its rows; pass mn = N).  Byte i of word k4 holds
+    the exponent of K block 4 k4 + i (the layout the *_ue8m0 GEMMs take)."""
+    sf = _f32(sf, "sf")
+    if sf.dim() not in (2, 3):
+        raise ValueError("sf must be 2-D or 3-D")
+    batched = sf.dim() == 3
+    sf3 = sf if batched else sf.unsqueeze(0)
+    G = sf3.shape[0]
+    if per_block:
+        if mn is None:
+            raise ValueError("per_block packing needs mn (the row count N)")
+        KB = sf3.shape[2]
+        if sf3.shape[1] != (mn + 127) // 128:
+            raise ValueError(f"sf {tuple(sf.shape)} does not cover {mn} rows")
+    else:
+        KB, MN = sf3.shape[1], sf3.shape[2]
+        if mn is not None and mn != MN:
+            raise ValueError(f"mn={mn} but sf has {MN} rows")
+        mn = MN
+    out = torch.empty((G, (KB + 3) // 4, mn), dtype=torch.int32, device=sf.device)
+    with torch.cuda.device(sf.device):
+        _check(load_library().dg_pack_ue8m0_scales(_ptr(sf3), int(per_block), _ptr(out), G, mn,
+                                                   KB * 128, _stream(sf)))
+    return out if batched else out[0]

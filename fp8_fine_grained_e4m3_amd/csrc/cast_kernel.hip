@@ -210,7 +210,45 @@ hipError_t launch_cast(const CastProblem& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Packed UE8M0 scale words: thread t writes word t of packed [G, K4, MN]
+// (row mn fastest, so reads of MN-major scales and the writes are coalesced).
+// Byte i of word k4 is the 8-bit exponent field of the fp32 scale of K block
+// 4 k4 + i, which for a power of two 2^x (x >= -126) is x + 127, the UE8M0
+// code of that scale; bytes past the last K block are 0.
+__global__ __launch_bounds__(256) void pack_ue8m0_kernel(const float* __restrict__ sf,
+                                                         int per_block, int64_t total, int MN,
+                                                         int KB, int K4,
+                                                         int32_t* __restrict__ packed) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= total) return;
+    const int mn = (int)(t % MN);
+    const int64_t rest = t / MN;
+    const int k4 = (int)(rest % K4);
+    const int64_t g = rest / K4;
+    const int row_blocks = (MN + kBlk - 1) / kBlk;
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int kb = 4 * k4 + i;
+        if (kb >= KB) break;
+        const float s = per_block ? sf[(g * row_blocks + mn / kBlk) * KB + kb]
+                                  : sf[(g * KB + kb) * MN + mn];
+        w |= ((__float_as_uint(s) >> 23) & 0xFFu) << (8 * i);
+    }
+    packed[t] = (int32_t)w;
+}
+
 }  // namespace
+
+hipError_t launch_pack_ue8m0(const PackProblem& p, hipStream_t stream) {
+    const int K4 = (int)((p.KB + 3) / 4);
+    const int64_t total = p.G * K4 * p.MN;
+    if (total == 0) return hipSuccess;
+    const int64_t grid = (total + 255) / 256;
+    hipLaunchKernelGGL(pack_ue8m0_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p.sf,
+                       p.per_block ? 1 : 0, total, (int)p.MN, (int)p.KB, K4, p.packed);
+    return hipGetLastError();
+}
 
 int64_t cast_grid(const CastProblem& p) {
     const int64_t wg_rows = p.block_scale ? 128 : 64;

@@ -174,11 +174,15 @@ bool split_workspace(hipStream_t stream, size_t part_floats, size_t n_counters,
 
 }  // namespace dg
 
-extern "C" {
+namespace {
 
-dg_status dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
-                         const void* c, void* d, dg_dtype d_dtype, int64_t M, int64_t N,
-                         int64_t K, void* stream) {
+// The three NT forms take either fp32 scales or packed UE8M0 words; both are
+// 4-byte elements, passed through as raw pointers.
+dg_status gemm_nt(const uint8_t* a, const void* sfa_, const uint8_t* b, const void* sfb_,
+                  const void* c, void* d, dg_dtype d_dtype, int64_t M, int64_t N, int64_t K,
+                  bool ue8m0, void* stream) {
+    const float* sfa = static_cast<const float*>(sfa_);
+    const float* sfb = static_cast<const float*>(sfb_);
     REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size (M=%lld N=%lld K=%lld)", (long long)M,
             (long long)N, (long long)K);
     REQUIRE(K % 128 == 0, "K=%lld is not a multiple of 128", (long long)K);
@@ -203,13 +207,15 @@ dg_status dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, c
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.c = c; p.d = d;
     p.rows = M; p.N = N; p.K = K; p.G = 1;
     p.out_f32 = d_dtype == DG_F32;
+    p.ue8m0 = ue8m0;
     return run_nt(p, stream);
 }
 
-dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa,
-                                              const uint8_t* b, const float* sfb,
-                                              const int32_t* m_indices, void* d, int64_t M_tot,
-                                              int64_t N, int64_t K, int64_t G, void* stream) {
+dg_status gemm_nt_contiguous(const uint8_t* a, const void* sfa_, const uint8_t* b,
+                             const void* sfb_, const int32_t* m_indices, void* d, int64_t M_tot,
+                             int64_t N, int64_t K, int64_t G, bool ue8m0, void* stream) {
+    const float* sfa = static_cast<const float*>(sfa_);
+    const float* sfb = static_cast<const float*>(sfb_);
     REQUIRE(M_tot >= 0 && N >= 0 && K >= 0, "negative size");
     REQUIRE(G >= 1, "G=%lld must be >= 1", (long long)G);
     REQUIRE(M_tot % 128 == 0, "M_tot=%lld is not a multiple of 128 (the contiguous-layout alignment)",
@@ -232,13 +238,15 @@ dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa
     p.m_indices = m_indices;
     p.rows = M_tot; p.N = N; p.K = K; p.G = G;
     p.out_f32 = false;
+    p.ue8m0 = ue8m0;
     return run_nt(p, stream);
 }
 
-dg_status dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
-                                          const float* sfb, const int32_t* masked_m, void* d,
-                                          int64_t G, int64_t M_max, int64_t N, int64_t K,
-                                          void* stream) {
+dg_status gemm_nt_masked(const uint8_t* a, const void* sfa_, const uint8_t* b, const void* sfb_,
+                         const int32_t* masked_m, void* d, int64_t G, int64_t M_max, int64_t N,
+                         int64_t K, bool ue8m0, void* stream) {
+    const float* sfa = static_cast<const float*>(sfa_);
+    const float* sfb = static_cast<const float*>(sfb_);
     REQUIRE(G >= 0 && M_max >= 0 && N >= 0 && K >= 0, "negative size");
     REQUIRE(K % 128 == 0, "K=%lld is not a multiple of 128", (long long)K);
     REQUIRE(N % 16 == 0, "N=%lld is not a multiple of 16", (long long)N);
@@ -258,7 +266,82 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, co
     p.masked_m = masked_m;
     p.rows = M_max; p.N = N; p.K = K; p.G = G;
     p.out_f32 = false;
+    p.ue8m0 = ue8m0;
     return run_nt(p, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                         const void* c, void* d, dg_dtype d_dtype, int64_t M, int64_t N,
+                         int64_t K, void* stream) {
+    return gemm_nt(a, sfa, b, sfb, c, d, d_dtype, M, N, K, false, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa,
+                                              const uint8_t* b, const float* sfb,
+                                              const int32_t* m_indices, void* d, int64_t M_tot,
+                                              int64_t N, int64_t K, int64_t G, void* stream) {
+    return gemm_nt_contiguous(a, sfa, b, sfb, m_indices, d, M_tot, N, K, G, false, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                          const float* sfb, const int32_t* masked_m, void* d,
+                                          int64_t G, int64_t M_max, int64_t N, int64_t K,
+                                          void* stream) {
+    return gemm_nt_masked(a, sfa, b, sfb, masked_m, d, G, M_max, N, K, false, stream);
+}
+
+dg_status dg_fp8_gemm_nt_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
+                               const int32_t* sfb, const void* c, void* d, dg_dtype d_dtype,
+                               int64_t M, int64_t N, int64_t K, void* stream) {
+    return gemm_nt(a, sfa, b, sfb, c, d, d_dtype, M, N, K, true, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const uint8_t* a, const int32_t* sfa,
+                                                    const uint8_t* b, const int32_t* sfb,
+                                                    const int32_t* m_indices, void* d,
+                                                    int64_t M_tot, int64_t N, int64_t K,
+                                                    int64_t G, void* stream) {
+    return gemm_nt_contiguous(a, sfa, b, sfb, m_indices, d, M_tot, N, K, G, true, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t* a, const int32_t* sfa,
+                                                const uint8_t* b, const int32_t* sfb,
+                                                const int32_t* masked_m, void* d, int64_t G,
+                                                int64_t M_max, int64_t N, int64_t K,
+                                                void* stream) {
+    return gemm_nt_masked(a, sfa, b, sfb, masked_m, d, G, M_max, N, K, true, stream);
+}
+
+dg_status dg_pack_ue8m0_scales(const float* sf, int per_block, int32_t* packed, int64_t G,
+                               int64_t MN, int64_t K, void* stream) {
+    REQUIRE(G >= 0 && MN >= 0 && K >= 0, "negative size (G=%lld MN=%lld K=%lld)", (long long)G,
+            (long long)MN, (long long)K);
+    REQUIRE(K % 128 == 0, "K=%lld is not a multiple of 128", (long long)K);
+    REQUIRE(per_block == 0 || per_block == 1, "per_block must be 0 or 1");
+    if (G == 0 || MN == 0 || K == 0) return ok();
+    REQUIRE_PTR(sf, 4);
+    REQUIRE_PTR(packed, 4);
+    const int64_t kb = K / 128, k4 = (kb + 3) / 4;
+    REQUIRE(MN <= INT_MAX && G <= kOffsetLimit / k4 && G * k4 <= kOffsetLimit / MN,
+            "G*ceil(K/512)*MN must stay below 2^31");
+    const int64_t sf_count = per_block ? G * ((MN + 127) / 128) * kb : G * kb * MN;
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(sf), p0 = reinterpret_cast<uintptr_t>(packed);
+    REQUIRE(s0 + (uintptr_t)(sf_count * 4) <= p0 || p0 + (uintptr_t)(G * k4 * MN * 4) <= s0,
+            "sf and packed must not overlap");
+    dg::PackProblem p{};
+    p.sf = sf; p.per_block = per_block != 0; p.packed = packed;
+    p.G = G; p.MN = MN; p.KB = kb;
+    int dev = 0;
+    DeviceInfo info;
+    dg_status st = current_device(dev, info);
+    if (st != DG_OK) return st;
+    hipError_t e = dg::launch_pack_ue8m0(p, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
 }
 
 dg_status dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t* a, const float* sfa,

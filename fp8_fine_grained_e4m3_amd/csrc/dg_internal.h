@@ -22,6 +22,11 @@ struct NtProblem {
     int64_t rows;             // dense: M, contiguous: M_tot, masked: M_max
     int64_t N, K, G;
     bool out_f32;
+    // false: fp32 scales, sfa [KB, rows] (masked: per group), sfb [G, ceil(N/128), KB].
+    // true: packed UE8M0 words (int32; byte i of word k4 = exponent of K block
+    // 4 k4 + i), sfa [K4, rows] (masked: [G, K4, M_max]), sfb [G, K4, N],
+    // K4 = ceil(KB / 4).
+    bool ue8m0;
     int device_cus;           // CUs of the device (not the cap): sizes the K split
 };
 
@@ -49,6 +54,18 @@ struct CastProblem {
     float* sf;
     int64_t G, R, K;
 };
+
+// fp32 power-of-two scales -> packed UE8M0 words packed [G, ceil(KB/4), MN]:
+// per_block false: sf [G, KB, MN] (one scale per row and K block, MN-major);
+// true: sf [G, ceil(MN/128), KB] (one per 128 x 128 block, given to each of
+// its rows).
+struct PackProblem {
+    const float* sf;
+    bool per_block;
+    int32_t* packed;
+    int64_t G, MN, KB;
+};
+hipError_t launch_pack_ue8m0(const PackProblem& p, hipStream_t stream);
 
 // Device memory for split-K partial tiles, one buffer per (device, stream),
 // grown on demand and kept until the process ends.  `counters` are zero

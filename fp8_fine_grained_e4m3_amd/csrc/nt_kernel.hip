@@ -148,10 +148,13 @@ template <int SM>
 __device__ __forceinline__ int pos_a(int row) { return (row / (2 * SM)) & 7; }
 __device__ __forceinline__ int pos_b(int row) { return (row >> 1) & 7; }
 
-template <class Cfg, int FORM, bool OUT_F32>
+template <class Cfg, int FORM, bool OUT_F32, bool UE8M0>
 __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void nt_fp8_kernel(NtArgs p) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN;
     constexpr int SM = Cfg::SM, SN = Cfg::SN;
+    // UE8M0: the B-scale words of a stage, one per tile column, fill the
+    // 256-byte slots of the waves that do not copy A scales.
+    static_assert(!UE8M0 || BN <= 64 * (Cfg::WAVES - Cfg::SA_DMA), "B-scale words fit the slots");
     // stages, then one 256-byte slot per wave that absorbs placeholder copies
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::STAGES * Cfg::STAGE_BYTES +
                                                            256 * Cfg::WAVES];
@@ -163,6 +166,7 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
     const int wn = wave % Cfg::WAVES_N;
     const int KB = p.K / kKBlk;
     const int NB = (p.N + kKBlk - 1) / kKBlk;
+    const int K4 = (KB + 3) / 4;   // UE8M0: packed scale words per row
     const int per_group = p.tiles_m * p.tiles_n;
 
     // Masked groups: only the tiles holding valid rows are enumerated.  Group
@@ -285,8 +289,11 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
         const int nkb = (int)(((int64_t)(split + 1) * KB) / p.splits) - kb_lo;
         const uint8_t* __restrict__ a_t = p.a + grp_row0 * p.K;
         const uint8_t* __restrict__ b_t = p.b + (int64_t)e * p.N * p.K;
-        const float* __restrict__ sfa_t = p.sfa + (FORM == kMasked ? (int64_t)g * KB * p.rows : 0);
-        const float* __restrict__ sfb_t = p.sfb + (int64_t)e * NB * KB;
+        // scale rows per group: KB fp32 scales, or K4 packed UE8M0 words
+        const int sf_k = UE8M0 ? K4 : KB;
+        const float* __restrict__ sfa_t = p.sfa + (FORM == kMasked ? (int64_t)g * sf_k * p.rows : 0);
+        const float* __restrict__ sfb_t =
+            p.sfb + (int64_t)e * (UE8M0 ? (int64_t)K4 * p.N : (int64_t)NB * KB);
 
         // Stage copies: wave copy u (uniform) moves 8 rows x 128 bytes; lane l
         // fetches chunk (l & 7) ^ f(row) of row 8 u' + (l >> 3), so LDS
@@ -317,7 +324,11 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                            ((4 * (sa_u / 64) + (sa_u % 4)) ^ (sa_r & 1));
         const uint32_t sa_off = 4u * (uint32_t)min(r0 + sa_row, grp_rows - 1);
         const int nb_last = min(NB - 1, (n0 + BN - 1) / kKBlk);   // the tile's last B-scale block
-        const uint32_t sb_off = 4u * (uint32_t)(min(n0 / kKBlk + lane, nb_last) * KB);
+        // UE8M0: wave w >= SA_DMA copies the words of tile columns
+        // 64 (w - SA_DMA) + lane (clamped to the last column) into slot w - SA_DMA
+        const uint32_t sb_off =
+            UE8M0 ? 4u * (uint32_t)min(n0 + 64 * max(wave - Cfg::SA_DMA, 0) + lane, p.N - 1)
+                  : 4u * (uint32_t)(min(n0 / kKBlk + lane, nb_last) * KB);
         const uint32_t lds0 = lds_addr(smem);
         auto issue_stage = [&](int kbr, int stage) {
             const int kb = kb_lo + kbr;
@@ -335,10 +346,19 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 else
                     dma16(src, goff[q], dst + u * 1024);
             }
-            if (wave < Cfg::SA_DMA)
-                dma4(sfa_t + (size_t)kb * grp_rows, sa_off, dst + Cfg::SA_OFF + wave * 256);
-            else
-                dma4(sfb_t + kb, sb_off, dst + Cfg::SB_OFF + wave * 256);
+            if constexpr (UE8M0) {
+                // word kb / 4 of each row holds block kb's exponent in byte kb % 4
+                if (wave < Cfg::SA_DMA)
+                    dma4(sfa_t + (size_t)(kb >> 2) * grp_rows, sa_off, dst + Cfg::SA_OFF + wave * 256);
+                else
+                    dma4(sfb_t + (size_t)(kb >> 2) * p.N, sb_off,
+                         dst + Cfg::SB_OFF + (wave - Cfg::SA_DMA) * 256);
+            } else {
+                if (wave < Cfg::SA_DMA)
+                    dma4(sfa_t + (size_t)kb * grp_rows, sa_off, dst + Cfg::SA_OFF + wave * 256);
+                else
+                    dma4(sfb_t + kb, sb_off, dst + Cfg::SB_OFF + wave * 256);
+            }
         };
 
         const int r16 = lane & 15;
@@ -353,6 +373,7 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
         const int b_lo = b_row + ((sigma(c0) ^ pb) << 4), b_hi = b_row + ((sigma(c0 + 1) ^ pb) << 4);
         const int s_a = Cfg::SA_OFF + 4 * (wm * Cfg::WTM + 4 * r16);
         const int s_b = Cfg::SB_OFF + 256 * (Cfg::WAVES - 1) + 4 * ((wn * Cfg::WTN) / kKBlk);
+        const int s_be = Cfg::SB_OFF + 4 * (wn * Cfg::WTN + r16);   // UE8M0: word of B fragment 0
 
         f32x4 acc[SM][SN];
 #pragma unroll
@@ -392,6 +413,21 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
             }
             sb = *reinterpret_cast<const float*>(st + s_b);
+        };
+        // UE8M0: the exponent bytes of K block kb (held by the stage `st`) for
+        // the lane's SM A rows (same slots as the fp32 A scales) and its SN B
+        // fragment rows.
+        auto load_exps = [&](const uint8_t* st, int kb, int (&ea)[SM], int (&eb)[SN]) {
+            const int sh = 8 * (kb & 3);
+#pragma unroll
+            for (int i = 0; i < SM; i += 4) {
+                const i32x4 v = *reinterpret_cast<const i32x4*>(st + s_a + 4 * 64 * (i / 4));
+                ea[i] = (v.x >> sh) & 0xFF; ea[i + 1] = (v.y >> sh) & 0xFF;
+                ea[i + 2] = (v.z >> sh) & 0xFF; ea[i + 3] = (v.w >> sh) & 0xFF;
+            }
+#pragma unroll
+            for (int j = 0; j < SN; ++j)
+                eb[j] = (*reinterpret_cast<const int*>(st + s_be + 64 * j) >> sh) & 0xFF;
         };
         auto bfrag_at = [&](const uint8_t* st, int j) {
             const i32x4 lo = *reinterpret_cast<const i32x4*>(st + b_lo + j * 16 * kKBlk);
@@ -437,16 +473,19 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 i32x8 b[SN];
                 float sa[SM];
                 float sb;
+                int ea[SM];   // UE8M0 exponents
+                int eb[SN];
             };
-            auto read_ops = [&](const uint8_t* st, Ops& o) {
-                load_scales(st, o.sa, o.sb);
+            auto read_ops = [&](const uint8_t* st, int kb, Ops& o) {
+                if constexpr (UE8M0) load_exps(st, kb, o.ea, o.eb);
+                else load_scales(st, o.sa, o.sb);
 #pragma unroll
                 for (int j = 0; j < SN; ++j) o.b[j] = bfrag_at(st, j);
 #pragma unroll
                 for (int i = 0; i < SM; ++i) o.a[i] = afrag_at(st, i);
             };
             Ops cur, nxt;
-            read_ops(smem, cur);
+            read_ops(smem, kb_lo, cur);
             // nothing is pending before block 0: zero products with zero scale
             f32x4 ring[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
             float ring_s[2] = {0.f, 0.f};
@@ -459,25 +498,35 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                     max(0, min(Cfg::STAGES - 2, nkb - 2 - it)));
                 lgkm_drain_barrier();
                 if (it + Cfg::STAGES < nkb) issue_stage(it + Cfg::STAGES, stage);
-                if (it + 1 < nkb) read_ops(smem + next * Cfg::STAGE_BYTES, nxt);
+                if (it + 1 < nkb) read_ops(smem + next * Cfg::STAGE_BYTES, kb_lo + it + 1, nxt);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
                     const int i = t / SN, j = t % SN;
-                    __builtin_amdgcn_s_setprio(1);
-                    const f32x4 pr = mfma_e4m3_block(cur.b[j], cur.a[i]);
-                    __builtin_amdgcn_s_setprio(0);
-                    const int tp = t >= 2 ? t - 2 : T + t - 2;   // tile of the pending product
-                    promote1(tp / SN, tp % SN, ring[t & 1], ring_s[t & 1]);
-                    ring[t & 1] = pr;
-                    ring_s[t & 1] = cur.sa[i] * cur.sb;
+                    if constexpr (UE8M0) {
+                        __builtin_amdgcn_s_setprio(1);
+                        acc[i][j] = mfma_e4m3_block_ue8m0(cur.b[j], cur.a[i], acc[i][j], cur.eb[j],
+                                                          cur.ea[i]);
+                        asm volatile("" : "+v"(acc[i][j]));   // keep the product in place
+                        __builtin_amdgcn_s_setprio(0);
+                    } else {
+                        __builtin_amdgcn_s_setprio(1);
+                        const f32x4 pr = mfma_e4m3_block(cur.b[j], cur.a[i]);
+                        __builtin_amdgcn_s_setprio(0);
+                        const int tp = t >= 2 ? t - 2 : T + t - 2;   // tile of the pending product
+                        promote1(tp / SN, tp % SN, ring[t & 1], ring_s[t & 1]);
+                        ring[t & 1] = pr;
+                        ring_s[t & 1] = cur.sa[i] * cur.sb;
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 cur = nxt;
                 stage = next;
             }
-            promote1((T - 2) / SN, (T - 2) % SN, ring[0], ring_s[0]);
-            promote1((T - 1) / SN, (T - 1) % SN, ring[1], ring_s[1]);
+            if constexpr (!UE8M0) {
+                promote1((T - 2) / SN, (T - 2) % SN, ring[0], ring_s[0]);
+                promote1((T - 1) / SN, (T - 1) % SN, ring[1], ring_s[1]);
+            }
         } else {
             // Row pipeline.  Products t = i * SN + j run row by row; A fragment
             // i + 2 is requested at the start of row i (a four-entry ring, two
@@ -494,9 +543,11 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
             i32x8 af[4];
             i32x8 bfr[SN];
             float sa[SM], sb, sa_n[SM], sb_n;
+            int ea[SM], eb[SN], ea_n[SM], eb_n[SN];   // UE8M0 exponents
             f32x4 ring[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
             float ring_s[2] = {0.f, 0.f};   // nothing pending before block 0
-            load_scales(smem, sa, sb);
+            if constexpr (UE8M0) load_exps(smem, kb_lo, ea, eb);
+            else load_scales(smem, sa, sb);
 #pragma unroll
             for (int j = 0; j < SN; ++j) bfr[j] = bfrag_at(smem, j);
             af[0] = afrag_at(smem, 0);
@@ -506,15 +557,26 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
             // priority, so a wave with products ready keeps the MFMA unit busy
             // while its SIMD partner waits on LDS) and the promotion of the
             // product two steps back
+            // (UE8M0: the MFMA applies the exponents and accumulates itself)
             auto step = [&](int i, int j, float s_row) {
-                const int t = i * SN + j;
-                __builtin_amdgcn_s_setprio(1);
-                const f32x4 pr = mfma_e4m3_block(bfr[j], af[i & 3]);
-                __builtin_amdgcn_s_setprio(0);
-                const int tp = t >= 2 ? t - 2 : T + t - 2;   // tile of the pending product
-                promote1(tp / SN, tp % SN, ring[t & 1], ring_s[t & 1]);
-                ring[t & 1] = pr;
-                ring_s[t & 1] = s_row;
+                if constexpr (UE8M0) {
+                    __builtin_amdgcn_s_setprio(1);
+                    acc[i][j] = mfma_e4m3_block_ue8m0(bfr[j], af[i & 3], acc[i][j], eb[j], ea[i]);
+                    // pins the product here: with nothing reading acc until the
+                    // epilogue, the compiler would otherwise sink every product of
+                    // the block past the LDS reads it is meant to overlap
+                    asm volatile("" : "+v"(acc[i][j]));
+                    __builtin_amdgcn_s_setprio(0);
+                } else {
+                    const int t = i * SN + j;
+                    __builtin_amdgcn_s_setprio(1);
+                    const f32x4 pr = mfma_e4m3_block(bfr[j], af[i & 3]);
+                    __builtin_amdgcn_s_setprio(0);
+                    const int tp = t >= 2 ? t - 2 : T + t - 2;   // tile of the pending product
+                    promote1(tp / SN, tp % SN, ring[t & 1], ring_s[t & 1]);
+                    ring[t & 1] = pr;
+                    ring_s[t & 1] = s_row;
+                }
             };
 
             int stage = 0;   // stage holding block it
@@ -524,7 +586,7 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 const uint8_t* st_next = smem + next * Cfg::STAGE_BYTES;
 #pragma unroll
                 for (int i = 0; i + 2 < SM; ++i) {
-                    const float s_row = sa[i] * sb;
+                    const float s_row = UE8M0 ? 0.f : sa[i] * sb;
 #pragma unroll
                     for (int j = 0; j < SN; ++j) {
                         step(i, j, s_row);
@@ -558,10 +620,11 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 // (after the last block these reads see a stale stage; unused)
-                load_scales(st_next, sa_n, sb_n);
+                if constexpr (UE8M0) load_exps(st_next, kb_lo + it + 1, ea_n, eb_n);
+                else load_scales(st_next, sa_n, sb_n);
 #pragma unroll
                 for (int i = SM - 2; i < SM; ++i) {
-                    const float s_row = sa[i] * sb;
+                    const float s_row = UE8M0 ? 0.f : sa[i] * sb;
 #pragma unroll
                     for (int j = 0; j < SN; ++j) {
                         step(i, j, s_row);
@@ -570,13 +633,22 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
+                if constexpr (UE8M0) {
 #pragma unroll
-                for (int i = 0; i < SM; ++i) sa[i] = sa_n[i];
-                sb = sb_n;
+                    for (int i = 0; i < SM; ++i) ea[i] = ea_n[i];
+#pragma unroll
+                    for (int j = 0; j < SN; ++j) eb[j] = eb_n[j];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < SM; ++i) sa[i] = sa_n[i];
+                    sb = sb_n;
+                }
                 stage = next;
             }
-            promote1((T - 2) / SN, (T - 2) % SN, ring[0], ring_s[0]);
-            promote1((T - 1) / SN, (T - 1) % SN, ring[1], ring_s[1]);
+            if constexpr (!UE8M0) {
+                promote1((T - 2) / SN, (T - 2) % SN, ring[0], ring_s[0]);
+                promote1((T - 1) / SN, (T - 1) % SN, ring[1], ring_s[1]);
+            }
         }
         // every wave is past its last LDS read before the next tile's copies
         lds_barrier();
@@ -743,13 +815,13 @@ constexpr int kBandMContiguous = 8;   // contiguous groups (expert panels are la
 constexpr int kMinSplitBlocks = 8;   // K blocks per split work unit, at least
 constexpr int kMaxSplits = 8;
 
-template <class Cfg, int FORM, bool OUT_F32>
+template <class Cfg, int FORM, bool OUT_F32, bool UE8M0>
 int occupancy_of() {
     static int occupancy = -1;   // workgroups per CU for this instance
     if (occupancy < 0) {
         int occ = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &occ, reinterpret_cast<const void*>(&nt_fp8_kernel<Cfg, FORM, OUT_F32>),
+                &occ, reinterpret_cast<const void*>(&nt_fp8_kernel<Cfg, FORM, OUT_F32, UE8M0>),
                 Cfg::THREADS, 0) != hipSuccess || occ < 1)
             occ = 1;
         occupancy = occ;
@@ -771,7 +843,7 @@ int split_count(int64_t tiles, int KB, int device_cus, int occupancy) {
     return sp < 1 ? 1 : (int)sp;
 }
 
-template <class Cfg, int FORM, bool OUT_F32>
+template <class Cfg, int FORM, bool OUT_F32, bool UE8M0>
 hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     NtArgs a;
     a.a = pr.a; a.sfa = pr.sfa; a.b = pr.b; a.sfb = pr.sfb; a.c = pr.c; a.d = pr.d;
@@ -788,7 +860,7 @@ hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     const int64_t groups = (FORM == kMasked) ? pr.G : (FORM == kContiguous ? 2 : 1);
     const int64_t tiles = groups * a.tiles_m * a.tiles_n;
     if (tiles <= 0) return hipSuccess;
-    const int occupancy = occupancy_of<Cfg, FORM, OUT_F32>();
+    const int occupancy = occupancy_of<Cfg, FORM, OUT_F32, UE8M0>();
 
     a.splits = 1;
     a.part = nullptr;
@@ -818,7 +890,7 @@ hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
         a.xcd_units = rounds * grid;
         a.xcd_m0 = rounds * 4 * blk;
     }
-    hipLaunchKernelGGL((nt_fp8_kernel<Cfg, FORM, OUT_F32>), dim3(grid), dim3(Cfg::THREADS), 0,
+    hipLaunchKernelGGL((nt_fp8_kernel<Cfg, FORM, OUT_F32, UE8M0>), dim3(grid), dim3(Cfg::THREADS), 0,
                        stream, a);
     return hipGetLastError();
 }
@@ -854,41 +926,51 @@ NtTile choose_tile(const NtProblem& pr) {
     return kT128x128;
 }
 
-template <int FORM, bool OUT_F32>
+template <int FORM, bool OUT_F32, bool UE8M0>
 hipError_t dispatch_tiles(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     if constexpr (FORM == kContiguous) {
-        return launch_cfg<Cfg256x256, FORM, OUT_F32>(pr, cu_cap, stream);
+        return launch_cfg<Cfg256x256, FORM, OUT_F32, UE8M0>(pr, cu_cap, stream);
     } else {
     switch (choose_tile(pr)) {
-    case kT64x64: return launch_cfg<Cfg64x64, FORM, OUT_F32>(pr, cu_cap, stream);
-    case kT128x64: return launch_cfg<Cfg128x64, FORM, OUT_F32>(pr, cu_cap, stream);
-    case kT256x256: return launch_cfg<Cfg256x256, FORM, OUT_F32>(pr, cu_cap, stream);
-    default: return launch_cfg<Cfg128x128, FORM, OUT_F32>(pr, cu_cap, stream);
+    case kT64x64: return launch_cfg<Cfg64x64, FORM, OUT_F32, UE8M0>(pr, cu_cap, stream);
+    case kT128x64:
+        if constexpr (FORM == kDense)
+            return launch_cfg<Cfg128x64, FORM, OUT_F32, UE8M0>(pr, cu_cap, stream);
+        else
+            return hipErrorInvalidValue;   // chosen for dense problems only
+    case kT256x256: return launch_cfg<Cfg256x256, FORM, OUT_F32, UE8M0>(pr, cu_cap, stream);
+    default: return launch_cfg<Cfg128x128, FORM, OUT_F32, UE8M0>(pr, cu_cap, stream);
     }
     }
+}
+
+template <bool UE8M0>
+hipError_t dispatch_forms(const NtProblem& pr, int cu_cap, hipStream_t stream) {
+    switch (pr.form) {
+    case kDense:
+        return pr.out_f32 ? dispatch_tiles<kDense, true, UE8M0>(pr, cu_cap, stream)
+                          : dispatch_tiles<kDense, false, UE8M0>(pr, cu_cap, stream);
+    case kContiguous:
+        return dispatch_tiles<kContiguous, false, UE8M0>(pr, cu_cap, stream);
+    case kMasked:
+        return dispatch_tiles<kMasked, false, UE8M0>(pr, cu_cap, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_nt(const NtProblem& pr, int cu_cap, hipStream_t stream) {
-    switch (pr.form) {
-    case kDense:
-        return pr.out_f32 ? dispatch_tiles<kDense, true>(pr, cu_cap, stream)
-                          : dispatch_tiles<kDense, false>(pr, cu_cap, stream);
-    case kContiguous:
-        return dispatch_tiles<kContiguous, false>(pr, cu_cap, stream);
-    case kMasked:
-        return dispatch_tiles<kMasked, false>(pr, cu_cap, stream);
-    }
-    return hipErrorInvalidValue;
+    return pr.ue8m0 ? dispatch_forms<true>(pr, cu_cap, stream)
+                    : dispatch_forms<false>(pr, cu_cap, stream);
 }
 
 const char* nt_config_name(const NtProblem& pr) {
     static const char* tiles[] = {"64x64", "128x64", "128x128", "256x256"};
     static const char* forms[] = {"dense", "contiguous", "masked"};
     static thread_local char buf[64];
-    snprintf(buf, sizeof buf, "nt_%s_%s_%s", forms[(int)pr.form],
-             pr.out_f32 ? "f32" : "bf16", tiles[choose_tile(pr)]);
+    snprintf(buf, sizeof buf, "nt_%s_%s%s_%s", forms[(int)pr.form],
+             pr.out_f32 ? "f32" : "bf16", pr.ue8m0 ? "_ue8m0" : "", tiles[choose_tile(pr)]);
     return buf;
 }
 

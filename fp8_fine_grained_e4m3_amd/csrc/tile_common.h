@@ -42,6 +42,18 @@ __device__ __forceinline__ f32x4 mfma_e4m3_block(const i32x8& rows, const i32x8&
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rows, cols, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// The same block product with power-of-two scales applied inside the MFMA
+// and accumulated into `acc`: v_mfma_scale_f32_16x16x128_f8f6f4, where lane l
+// passes, in bits 7..0 of e_rows / e_cols, the UE8M0 exponent e (scale
+// 2^(e - 127)) of the 32 K values it holds for its row of each operand.  The
+// scales are powers of two, so scaling the products is exact and the sum over
+// K blocks needs no separate promotion step.
+__device__ __forceinline__ f32x4 mfma_e4m3_block_ue8m0(const i32x8& rows, const i32x8& cols,
+                                                       const f32x4& acc, int e_rows, int e_cols) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rows, cols, acc, 0, 0, 0, e_rows, 0,
+                                                            e_cols);
+}
+
 // Fragment whose lane l takes LDS row `row` (callers pass the row of their
 // lane) and the 32 K bytes [32 * (l >> 4), +32) of it.
 __device__ __forceinline__ i32x8 lds_fragment_row(const uint8_t* tile, int row, int lane) {

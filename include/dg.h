@@ -205,6 +205,69 @@ dg_status dg_per_token_cast_to_fp8(const void* x, dg_dtype x_dtype, uint8_t* cod
 dg_status dg_per_block_cast_to_fp8(const void* w, dg_dtype w_dtype, uint8_t* codes, float* sf,
                                    int64_t G, int64_t N, int64_t K, int flags, void* stream);
 
+/*
+ * Power-of-two (UE8M0) scale factors, packed four to a 32-bit integer.
+ * Source: "DeepGEMM" README, "Interfaces", "Notices" (the newer path takes
+ * its scale factors as UE8M0 values packed four per int instead of fp32),
+ * and DeepGEMM Documentation, section 10 (a utility packs fp32 scales into
+ * that MN-major layout).  Reading of the layout:
+ *   word [k4][mn] (int32, MN-major, row mn fastest) holds in byte i (bits
+ *   8i .. 8i+7) the exponent e of the scale 2^(e - 127) of K block 4 k4 + i
+ *   of row mn; K4 = ceil(K/512) words per row; bytes past the last K block
+ *   are ignored (the packer writes 0).  Both operands carry one scale per
+ *   row per 128-K block in this form (a 128 x 128 weight scale is given to
+ *   each of its 128 rows).  e = 255 (NaN) is not supported.
+ * The GEMM is the definition at the top of this file with those scales:
+ *   D[m,n] = C[m,n] + sum_kb 2^(ea(m,kb) - 127) * 2^(eb(n,kb) - 127) * P_kb[m,n]
+ * Scaling by a power of two is exact, so the MFMA applies the scales to the
+ * FP8 products itself and accumulates every K block into the fp32
+ * accumulator; there is no separate promotion step.
+ *
+ * The three entry points take exactly the arguments, rules, error behaviour
+ * and output conventions of their fp32-scale counterparts above, except:
+ *   dg_fp8_gemm_nt_ue8m0:                   sfa [K4, M],  sfb [K4, N]
+ *   dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0: sfa [K4, M_tot], sfb [G, K4, N]
+ *   dg_m_grouped_fp8_gemm_nt_masked_ue8m0:  sfa [G, K4, M_max], sfb [G, K4, N]
+ * (int32 words, 4-byte aligned).  The dense form splits K over workgroups
+ * like dg_fp8_gemm_nt (same workspace rules).
+ */
+dg_status dg_fp8_gemm_nt_ue8m0(const uint8_t* a, const int32_t* sfa,
+                               const uint8_t* b, const int32_t* sfb,
+                               const void* c, void* d, dg_dtype d_dtype,
+                               int64_t M, int64_t N, int64_t K, void* stream);
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const uint8_t* a, const int32_t* sfa,
+                                                    const uint8_t* b, const int32_t* sfb,
+                                                    const int32_t* m_indices, void* d,
+                                                    int64_t M_tot, int64_t N, int64_t K,
+                                                    int64_t G, void* stream);
+dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t* a, const int32_t* sfa,
+                                                const uint8_t* b, const int32_t* sfb,
+                                                const int32_t* masked_m, void* d,
+                                                int64_t G, int64_t M_max, int64_t N, int64_t K,
+                                                void* stream);
+
+/*
+ * fp32 power-of-two scales -> packed UE8M0 words (layout above), G batches:
+ *   per_block == 0: sf [G, K/128, MN] fp32, one scale per (row, K block),
+ *                   MN-major (the sfa layout, e.g. from dg_per_token_cast_to_fp8
+ *                   with DG_CAST_POW2_SCALE)
+ *   per_block == 1: sf [G, ceil(MN/128), K/128] fp32, one per 128 x 128 block
+ *                   (the sfb layout, e.g. from dg_per_block_cast_to_fp8 with
+ *                   DG_CAST_POW2_SCALE), given to each of the block's rows
+ *   packed          [G, ceil(K/512), MN] int32
+ * Byte i of a word is the 8-bit exponent field of the fp32 scale of K block
+ * 4 k4 + i, which is its UE8M0 code when the scale is a positive power of two
+ * in [2^-126, 2^127] (the precondition; other values give the exponent field
+ * regardless, i.e. the mantissa and sign are dropped).  Bytes past the last
+ * K block are 0.
+ * Rules: K % 128 == 0; sf and packed 4-byte aligned and not overlapping.
+ * One kernel launch on `stream`; errors as for the GEMMs.
+ * Source: DeepGEMM Documentation, section 10 (the packed-UE8M0 MN-major
+ * layout utility).
+ */
+dg_status dg_pack_ue8m0_scales(const float* sf, int per_block, int32_t* packed, int64_t G,
+                               int64_t MN, int64_t K, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* dg_last_error(void);
 

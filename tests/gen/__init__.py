@@ -44,12 +44,16 @@ def _cast_e4m3(y: torch.Tensor) -> torch.Tensor:
     return y.to(torch.float8_e4m3fn).view(torch.uint8)
 
 
-def _safe_scale(amax: torch.Tensor) -> torch.Tensor:
+def _safe_scale(amax: torch.Tensor, pow2: bool = False) -> torch.Tensor:
     scale = amax / torch.tensor(E4M3_MAX, dtype=torch.float32)
-    return torch.where(amax == 0, torch.ones_like(scale), scale)
+    scale = torch.where(amax == 0, torch.ones_like(scale), scale)
+    if pow2:   # round up to a power of two (the UE8M0-representable scales)
+        m, e = torch.frexp(scale)
+        scale = torch.where(m == 0.5, scale, torch.ldexp(torch.ones_like(scale), e))
+    return scale
 
 
-def quantize_rows(x: np.ndarray | torch.Tensor):
+def quantize_rows(x: np.ndarray | torch.Tensor, pow2: bool = False):
     """Per-row, per-128-K-block quantisation of an activation matrix.
 
     x: fp32 [R, K] with K % 128 == 0.
@@ -61,12 +65,12 @@ def quantize_rows(x: np.ndarray | torch.Tensor):
     assert K % BLOCK == 0
     KB = K // BLOCK
     xb = xt.reshape(R, KB, BLOCK)
-    scale = _safe_scale(xb.abs().amax(dim=2))            # [R, KB]
+    scale = _safe_scale(xb.abs().amax(dim=2), pow2)      # [R, KB]
     codes = _cast_e4m3(xb / scale[:, :, None]).reshape(R, K)
     return codes.numpy(), scale.t().contiguous().numpy()
 
 
-def quantize_blocks(w: np.ndarray | torch.Tensor):
+def quantize_blocks(w: np.ndarray | torch.Tensor, pow2: bool = False):
     """Per-128x128-block quantisation of a weight matrix [N, K].
 
     Partial blocks (N % 128 != 0) take their amax over the rows that exist.
@@ -80,7 +84,7 @@ def quantize_blocks(w: np.ndarray | torch.Tensor):
     pad = NB * BLOCK - N
     wp = torch.nn.functional.pad(wt, (0, 0, 0, pad)) if pad else wt
     blocks = wp.reshape(NB, BLOCK, KB, BLOCK)
-    scale = _safe_scale(blocks.abs().amax(dim=(1, 3)))    # [NB, KB]
+    scale = _safe_scale(blocks.abs().amax(dim=(1, 3)), pow2)   # [NB, KB]
     full = scale[:, None, :, None].expand(NB, BLOCK, KB, BLOCK).reshape(NB * BLOCK, K)[:N]
     codes = _cast_e4m3(wt / full)
     return codes.numpy(), scale.contiguous().numpy()
@@ -100,6 +104,28 @@ def quantize_cols(x: np.ndarray | torch.Tensor):
     scale = _safe_scale(xb.abs().amax(dim=1))             # [KB, C]
     codes = _cast_e4m3(xb / scale[:, None, :]).reshape(Kt, C)
     return codes.numpy(), scale.contiguous().numpy()
+
+
+def ue8m0_words(e: np.ndarray) -> np.ndarray:
+    """Exponent bytes e [..., KB, MN] -> packed UE8M0 words int32 [..., ceil(KB/4), MN]:
+    byte i of word k4 holds block 4 k4 + i (little end first), unused bytes 0."""
+    e = np.asarray(e).astype(np.uint32)
+    KB = e.shape[-2]
+    K4 = (KB + 3) // 4
+    w = np.zeros(e.shape[:-2] + (K4, e.shape[-1]), np.uint32)
+    for kb in range(KB):
+        w[..., kb // 4, :] |= e[..., kb, :] << np.uint32(8 * (kb % 4))
+    return w.view(np.int32)
+
+
+def exponent_bytes(sf: np.ndarray) -> np.ndarray:
+    """8-bit exponent fields of fp32 scales (the UE8M0 code of a power of two)."""
+    return (np.ascontiguousarray(sf, np.float32).view(np.uint32) >> np.uint32(23)) & np.uint32(0xFF)
+
+
+def pow2_scales(e: np.ndarray) -> np.ndarray:
+    """UE8M0 codes -> the fp32 scales 2^(e - 127) (e in [1, 254])."""
+    return np.ldexp(np.float32(1), (np.asarray(e, np.int64) - 127).astype(np.int32)).astype(np.float32)
 
 
 # --------------------------------------------------------------------------
@@ -171,6 +197,19 @@ def _normal(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
     return x
 
 
+@dataclasses.dataclass
+class DenseUe8m0Inputs:
+    a: np.ndarray      # uint8 [M, K]
+    sfa: np.ndarray    # int32 [ceil(K/512), M], packed UE8M0 words
+    b: np.ndarray      # uint8 [N, K]
+    sfb: np.ndarray    # int32 [ceil(K/512), N], one exponent per row of B
+    sfa_f32: np.ndarray   # the same A scales as fp32 [K/128, M]
+    sfb_f32: np.ndarray   # fp32 [ceil(N/128), K/128] (block scales) or None
+    M: int
+    N: int
+    K: int
+
+
 # --------------------------------------------------------------------------
 # Dense NT (workloads 1 and 2)
 # --------------------------------------------------------------------------
@@ -195,6 +234,20 @@ def gen_dense(M: int, N: int, K: int, seed: int = 0, with_c: bool = False) -> De
     if with_c:
         c = torch.from_numpy(_normal(rng, (M, N))).to(torch.bfloat16).float().numpy()
     return DenseInputs(a, sfa, b, sfb, M, N, K, c)
+
+
+def gen_dense_ue8m0(M: int, N: int, K: int, seed: int = 0) -> DenseUe8m0Inputs:
+    """The dense workload with power-of-two scales: A[M,K], B[N,K] ~ N(0,1),
+    quantised 1x128 / 128x128 with each scale rounded up to a power of two,
+    then packed into UE8M0 words (B's block exponents given to each row)."""
+    rng = _rng(seed)
+    a32 = _normal(rng, (M, K))
+    b32 = _normal(rng, (N, K))
+    a, sfa = quantize_rows(a32, pow2=True)
+    b, sfb = quantize_blocks(b32, pow2=True)
+    eb = np.repeat(exponent_bytes(sfb).T, BLOCK, axis=1)[:, :N]        # [KB, N]
+    return DenseUe8m0Inputs(a, ue8m0_words(exponent_bytes(sfa)), b, ue8m0_words(eb),
+                            sfa, sfb, M, N, K)
 
 
 # --------------------------------------------------------------------------
@@ -232,8 +285,9 @@ def contiguous_layout(counts: np.ndarray, align: int = BLOCK):
 
 def gen_contiguous(G: int = 32, N: int = 4096, K: int = 4096, tokens: int = 8192,
                    topk: int = 6, seed: int = 0, counts: Optional[np.ndarray] = None,
-                   zipf_s: float = 1.1) -> ContiguousInputs:
-    """Workload 3 (or a smaller variant).  `counts` overrides the routing."""
+                   zipf_s: float = 1.1, pow2: bool = False) -> ContiguousInputs:
+    """Workload 3 (or a smaller variant).  `counts` overrides the routing;
+    pow2 rounds every scale up to a power of two (see to_ue8m0)."""
     rng = _rng(seed)
     if counts is None:
         counts = route_topk_zipf(rng, tokens, G, topk, zipf_s)
@@ -248,13 +302,13 @@ def gen_contiguous(G: int = 32, N: int = 4096, K: int = 4096, tokens: int = 8192
         a32[offs[e]: offs[e] + c] = valid[r: r + c]
         r += c
     del valid
-    a, sfa = quantize_rows(a32)
+    a, sfa = quantize_rows(a32, pow2)
     del a32
     NB = (N + BLOCK - 1) // BLOCK
     b = np.empty((G, N, K), dtype=np.uint8)
     sfb = np.empty((G, NB, K // BLOCK), dtype=np.float32)
     for e in range(G):
-        b[e], sfb[e] = quantize_blocks(_normal(rng, (N, K)))
+        b[e], sfb[e] = quantize_blocks(_normal(rng, (N, K)), pow2)
     return ContiguousInputs(a, sfa, b, sfb, m_idx, counts, M_tot, N, K, G)
 
 
@@ -263,7 +317,8 @@ def gen_contiguous(G: int = 32, N: int = 4096, K: int = 4096, tokens: int = 8192
 # --------------------------------------------------------------------------
 
 def gen_masked(G: int = 32, M_max: int = 256, N: int = 4096, K: int = 2048,
-               seed: int = 0, masked_m: Optional[np.ndarray] = None) -> MaskedInputs:
+               seed: int = 0, masked_m: Optional[np.ndarray] = None,
+               pow2: bool = False) -> MaskedInputs:
     """masked_m ~ U{0..M_max} per group; A fully drawn (rows past masked_m are
     junk the kernel must never let into D)."""
     rng = _rng(seed)
@@ -273,13 +328,23 @@ def gen_masked(G: int = 32, M_max: int = 256, N: int = 4096, K: int = 2048,
     a = np.empty((G, M_max, K), dtype=np.uint8)
     sfa = np.empty((G, K // BLOCK, M_max), dtype=np.float32)
     for g in range(G):
-        a[g], sfa[g] = quantize_rows(_normal(rng, (M_max, K)))
+        a[g], sfa[g] = quantize_rows(_normal(rng, (M_max, K)), pow2)
     NB = (N + BLOCK - 1) // BLOCK
     b = np.empty((G, N, K), dtype=np.uint8)
     sfb = np.empty((G, NB, K // BLOCK), dtype=np.float32)
     for g in range(G):
-        b[g], sfb[g] = quantize_blocks(_normal(rng, (N, K)))
+        b[g], sfb[g] = quantize_blocks(_normal(rng, (N, K)), pow2)
     return MaskedInputs(a, sfa, b, sfb, masked_m, G, M_max, N, K)
+
+
+def to_ue8m0(sfa: np.ndarray, sfb: np.ndarray, N: int):
+    """Power-of-two fp32 scales of an NT workload -> packed UE8M0 words:
+    sfa [..., KB, rows] -> [..., ceil(KB/4), rows]; sfb [..., ceil(N/128), KB]
+    (block scales) -> [..., ceil(KB/4), N], each row of a block taking the
+    block's exponent."""
+    ea = exponent_bytes(sfa)
+    eb = np.repeat(np.swapaxes(exponent_bytes(sfb), -1, -2), BLOCK, axis=-1)[..., :N]
+    return ue8m0_words(ea), ue8m0_words(eb)
 
 
 # --------------------------------------------------------------------------

@@ -174,3 +174,34 @@ def test_no_oracle_in_product_path():
                 assert "oracle" not in text.lower(), fn
     nm = os.popen(f"nm -D {dg.LIB_PATH}").read()
     assert "oracle" not in nm
+
+
+def test_ue8m0_entry_points_reject(lib):
+    f = lib.dg_fp8_gemm_nt_ue8m0
+    assert f(P16, P16, P16b, P16, NULL, P16c, dg.DG_BF16, 128, 256, 500, None) == dg.DG_ERR_INVALID_ARG
+    assert "K=500" in err(lib)
+    assert f(P16, NULL, P16b, P16, NULL, P16c, dg.DG_BF16, 128, 256, 512, None) == dg.DG_ERR_INVALID_ARG
+    assert "sfa is NULL" in err(lib)
+    assert f(P16, P16, P16b, P16, NULL, P16c, 9, 128, 256, 512, None) == dg.DG_ERR_INVALID_ARG
+    assert f(P16, P16, P16b, P16, NULL, P16c, dg.DG_BF16, 0, 256, 512, None) == dg.DG_OK
+    g = lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0
+    assert g(P16, P16, P16b, P16, P16, P16c, 200, 256, 512, 4, None) == dg.DG_ERR_INVALID_ARG
+    assert "multiple of 128" in err(lib)
+    h = lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0
+    assert h(P16, P16, P16b, P16, NULL, P16c, 4, 256, 256, 512, None) == dg.DG_ERR_INVALID_ARG
+    assert "masked_m is NULL" in err(lib)
+
+
+def test_pack_ue8m0_rejects(lib):
+    f = lib.dg_pack_ue8m0_scales
+
+    def call(sf=P16, per_block=0, packed=P16b, G=1, MN=256, K=512):
+        return f(sf, per_block, packed, G, MN, K, None)
+
+    assert call(K=200) == dg.DG_ERR_INVALID_ARG and "K=200" in err(lib)
+    assert call(per_block=2) == dg.DG_ERR_INVALID_ARG and "per_block" in err(lib)
+    assert call(sf=NULL) == dg.DG_ERR_INVALID_ARG and "sf is NULL" in err(lib)
+    assert call(packed=ctypes.c_void_p(0x10002)) == dg.DG_ERR_INVALID_ARG
+    assert call(packed=ctypes.c_void_p(0x10000 + 64)) == dg.DG_ERR_INVALID_ARG
+    assert "overlap" in err(lib)
+    assert call(MN=0, sf=NULL) == dg.DG_OK and call(K=0, sf=NULL) == dg.DG_OK

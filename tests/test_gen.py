@@ -109,3 +109,39 @@ def test_small_grouped_generators_shapes():
     ki = gen.gen_k_grouped(G=3, M=64, N=32, K_tot=512, k_sizes=np.array([256, 0, 256]))
     assert ki.sfa.shape == (4, 64) and ki.c.shape == (3, 64, 32)
     assert np.all(ki.a[ki.valid_tokens[0]:256] == 0)
+
+
+def test_pow2_quantisers_match_the_oracle_cast():
+    """The generator's power-of-two scales and codes equal the oracle's casts
+    with power-of-two scales (the recipe the UE8M0 inputs are made with)."""
+    import oracle
+    rng = np.random.default_rng(60)
+    x = (rng.standard_normal((70, 384)) * np.exp(rng.uniform(-6, 6, (70, 1)))).astype(np.float32)
+    q, sf = gen.quantize_rows(x, pow2=True)
+    oq, osf = oracle.cast_rows(x, pow2=True)
+    assert np.array_equal(q, oq) and np.array_equal(sf, osf)
+    m, _ = np.frexp(sf)
+    assert np.all(m == 0.5)
+    w = rng.standard_normal((300, 256)).astype(np.float32)
+    q, sf = gen.quantize_blocks(w, pow2=True)
+    oq, osf = oracle.cast_blocks(w, pow2=True)
+    assert np.array_equal(q, oq) and np.array_equal(sf, osf)
+
+
+def test_ue8m0_words_match_the_oracle_packer():
+    import oracle
+    rng = np.random.default_rng(61)
+    for KB, MN in ((1, 7), (4, 16), (5, 33), (9, 130)):
+        e = rng.integers(1, 255, size=(KB, MN))
+        sf = gen.pow2_scales(e)
+        assert np.array_equal(gen.exponent_bytes(sf), e)
+        assert np.array_equal(gen.ue8m0_words(e), oracle.pack_ue8m0(sf, False, MN, KB * 128))
+
+
+def test_gen_dense_ue8m0_layout():
+    import oracle
+    x = gen.gen_dense_ue8m0(64, 300, 640, seed=3)
+    assert x.sfa.dtype == np.int32 and x.sfa.shape == (2, 64)
+    assert x.sfb.shape == (2, 300)
+    assert np.array_equal(x.sfa, oracle.pack_ue8m0(x.sfa_f32, False, 64, 640))
+    assert np.array_equal(x.sfb, oracle.pack_ue8m0(x.sfb_f32, True, 300, 640))
