@@ -96,6 +96,8 @@ def _bind(lib):
     lib.oracle_gemm_nt_ue8m0.restype = ctypes.c_int
     lib.oracle_pack_ue8m0.argtypes = [P, ctypes.c_int, I, I, P]
     lib.oracle_pack_ue8m0.restype = ctypes.c_int
+    lib.oracle_gemm_layout.argtypes = [P, ctypes.c_int, P, P, ctypes.c_int, P, P, I, I, I, P, I, P]
+    lib.oracle_gemm_layout.restype = ctypes.c_int
     return lib
 
 
@@ -269,4 +271,41 @@ def pack_ue8m0(sf, per_block: bool, MN: int, K: int) -> np.ndarray:
     out = np.empty(((K // 128 + 3) // 4, MN), dtype=np.int32)
     if _load().oracle_pack_ue8m0(_ptr(s), int(per_block), MN, K, _ptr(out)):
         raise ValueError("oracle_pack_ue8m0: bad arguments or a scale that is not a power of two")
+    return out
+
+
+def gemm_layout(layout: str, a, sfa, b, sfb, c=None, rows=None) -> np.ndarray:
+    """D[rows] of the GEMM in layout "nn", "tn", "tt" (or "nt" with per-row B
+    scales): A stored [M, K] ("n") or [K, M] ("t"), B stored [K, N] ("n") or
+    [N, K] ("t"); sfa fp32 [K/128, M], sfb fp32 [K/128, N]; c fp32 [M, N]."""
+    assert layout in ("nn", "tn", "tt", "nt")
+    a = _c(a, np.uint8); b = _c(b, np.uint8)
+    sa = _c(sfa, np.float32); sb = _c(sfb, np.float32)
+    a_mk, b_nk = layout[0] == "n", layout[1] == "t"
+    M, K = a.shape if a_mk else a.shape[::-1]
+    N = b.shape[0] if b_nk else b.shape[1]
+    assert (b.shape[1] if b_nk else b.shape[0]) == K
+    assert sa.shape == (K // 128, M) and sb.shape == (K // 128, N)
+    cc = None if c is None else _c(c, np.float32)
+    r = np.arange(M, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    out = np.empty((len(r), N), dtype=np.float64)
+    if _load().oracle_gemm_layout(_ptr(a), int(a_mk), _ptr(sa), _ptr(b), int(b_nk), _ptr(sb),
+                                  _ptr(cc), M, N, K, _ptr(r), len(r), _ptr(out)):
+        raise ValueError("oracle_gemm_layout: bad arguments")
+    return out
+
+
+def m_grouped_nn_contiguous(a, sfa, b, sfb, m_indices, rows=None) -> np.ndarray:
+    """M-grouped contiguous NN: D[r] = A[r] @ B[e_r] with e_r = m_indices[r];
+    A [M_tot, K], sfa [K/128, M_tot], B [G, K, N], sfb [G, K/128, N].  Rows
+    whose index is outside [0, G) have no reference (NaN).  Each expert's
+    rows are the NN definition with that expert's B."""
+    mi = np.asarray(m_indices)
+    G, _, N = b.shape
+    r = np.arange(len(mi), dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    out = np.full((len(r), N), np.nan)
+    for e in range(G):
+        sel = np.nonzero(mi[r] == e)[0]
+        if len(sel):
+            out[sel] = gemm_layout("nn", a, sfa, b[e], sfb[e], rows=r[sel])
     return out

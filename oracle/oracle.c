@@ -437,3 +437,53 @@ int oracle_pack_ue8m0(const float* sf, int layout, int64_t MN, int64_t K, int32_
         }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * The other memory layouts.  The "DeepGEMM" README ("Interfaces", "Notices")
+ * names a GEMM D = C + A @ B by two letters for the layouts of A and B, NT
+ * being A as stored ([M, K]) times B transposed (B stored [N, K]); its newer
+ * path supports all four of NT, TN, NN and TT.  Reading: the first letter is
+ * A's, "N" = A stored [M, K] (K contiguous), "T" = A stored [K, M] (the
+ * operand is its transpose); the second letter is B's, "T" = B stored [N, K]
+ * (the operand is its transpose), "N" = B stored [K, N].  So
+ *   NN: D = C + A @ B        A [M, K],  B [K, N]
+ *   TN: D = C + A^T @ B      A [K, M],  B [K, N]   (the K-grouped form's layout)
+ *   TT: D = C + A^T @ B^T    A [K, M],  B [N, K]
+ * For these layouts each operand carries one fp32 scale per row of the output
+ * side it belongs to (m for A, n for B) per 128-wide K block, stored
+ * MN-major: sfa [K/128, M], sfb [K/128, N] (the per-row scale granularity the
+ * newer path uses for both operands, and the K-grouped form's layout).
+ * The definition is the one at the top of this file with those scales:
+ *   D[m,n] = C[m,n] + sum_kb (sa[kb,m] * sb[kb,n]) * sum_{k in kb} A(m,k) * B(k,n)
+ * where A(m,k) is a[m*K + k] (A stored [M, K]) or a[k*M + m] (stored [K, M]),
+ * and B(k,n) is b[n*K + k] (stored [N, K]) or b[k*N + n] (stored [K, N]).
+ * ------------------------------------------------------------------------- */
+int oracle_gemm_layout(const uint8_t* a, int a_stored_mk, const float* sfa, const uint8_t* b,
+                       int b_stored_nk, const float* sfb, const float* c, int64_t M, int64_t N,
+                       int64_t K, const int64_t* rows, int64_t n_rows, double* out)
+{
+    if (K % KBLK != 0)
+        return 1;
+    build_table();
+    const int64_t KB = K / KBLK;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int64_t m = rows[i];
+        if (m < 0 || m >= M) { bad |= 1; continue; }
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t kb = 0; kb < KB; ++kb) {
+                double p = 0.0;                           /* exact block sum */
+                for (int64_t k = kb * KBLK; k < (kb + 1) * KBLK; ++k) {
+                    const uint8_t av = a_stored_mk ? a[m * K + k] : a[k * M + m];
+                    const uint8_t bv = b_stored_nk ? b[n * K + k] : b[k * N + n];
+                    p += g_dec[av] * g_dec[bv];
+                }
+                acc += ((double)sfa[kb * M + m] * (double)sfb[kb * N + n]) * p;
+            }
+            out[i * N + n] = acc + (c ? (double)c[m * N + n] : 0.0);
+        }
+    }
+    return bad;
+}

@@ -13,6 +13,7 @@ import oracle
 from tests import test_oracle_cast_pins as cast_pins
 from tests import test_oracle_pins as pins
 from tests import test_oracle_ue8m0_pins as ue8m0_pins
+from tests import test_oracle_layout_pins as layout_pins
 
 MUTANTS = {
     "exponent_bias": ("mag = ldexp(1.0 + (double)m / 8.0, e - 7);",
@@ -63,6 +64,16 @@ MUTANTS = {
     "ue8m0_b_per_block": ("ue8m0_scale(sfb, N, n, kb)", "ue8m0_scale(sfb, N, (n / KBLK) * KBLK, kb)"),
     "ue8m0_pack_offset": ("const int e = x - 1 + 127;", "const int e = x + 127;"),
     "ue8m0_pack_broadcast": ("sf[(mn / KBLK) * KB + kb]", "sf[kb]"),
+    "layout_a_ignores_storage": ("const uint8_t av = a_stored_mk ? a[m * K + k] : a[k * M + m];",
+                                 "const uint8_t av = a[m * K + k];"),
+    "layout_b_ignores_storage": ("const uint8_t bv = b_stored_nk ? b[n * K + k] : b[k * N + n];",
+                                 "const uint8_t bv = b[k * N + n];"),
+    "layout_sfa_transposed": ("acc += ((double)sfa[kb * M + m] * (double)sfb[kb * N + n]) * p;",
+                              "acc += ((double)sfa[m * KB + kb] * (double)sfb[kb * N + n]) * p;"),
+    "layout_sfb_transposed": ("acc += ((double)sfa[kb * M + m] * (double)sfb[kb * N + n]) * p;",
+                              "acc += ((double)sfa[kb * M + m] * (double)sfb[n * KB + kb]) * p;"),
+    "layout_drops_c": ("(double)sfb[kb * N + n]) * p;\n            }\n            out[i * N + n] = acc + (c ? (double)c[m * N + n] : 0.0);",
+                       "(double)sfb[kb * N + n]) * p;\n            }\n            out[i * N + n] = acc;"),
     "cast_zero_scale": ("if (amax == 0.0f)\n        return 1.0f;", "if (amax == 0.0f)\n        return 0.5f;"),
 }
 
@@ -100,6 +111,11 @@ def _pin_suite():
         ("ue8m0_broadcast", ue8m0_pins.test_pack_broadcasts_block_scales_to_rows),
         ("ue8m0_exact", lambda: ue8m0_pins.test_gemm_ue8m0_matches_exact_rationals(53, 4, 6, 640)),
         ("ue8m0_vs_fp32", ue8m0_pins.test_gemm_ue8m0_equals_fp32_scale_definition_on_block_constant_b),
+        ("layout_nn_exact", lambda: layout_pins.test_layouts_match_exact_rationals("nn", 71, 4, 3, 384)),
+        ("layout_tt_exact", lambda: layout_pins.test_layouts_match_exact_rationals("tt", 71, 4, 3, 384)),
+        ("layout_tn_exact", lambda: layout_pins.test_layouts_match_exact_rationals("tn", 71, 4, 3, 384)),
+        ("layout_transposes", layout_pins.test_nn_and_tt_are_nt_on_transposed_storage),
+        ("layout_one_hot_nn", lambda: layout_pins.test_one_hot_b_selects_an_element_of_a("nn")),
     ]
     failed = []
     for name, fn in checks:
