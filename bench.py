@@ -304,13 +304,16 @@ def instance_matcher(name):
     """Predicate on demangled kernel names selecting the template instance
     behind a config name such as nt_dense_bf16_256x256 or
     tn_kgrouped_f32_256x256; also returns a readable tag."""
-    kind, form, out, tile = name.split("_")
+    parts = name.split("_")
+    kind, form, out, tile = parts[0], parts[1], parts[2], parts[-1]
+    ue8m0 = "ue8m0" in parts
     bm, bn = tile.split("x")
     if kind == "tn":
         tag = f"TnCfg<{bm}, {bn},"
         return (lambda k: "tn_fp8_kernel" in k and tag in k), tag + " ...>"
     form_id = {"dense": 0, "contiguous": 1, "masked": 2}[form]
-    tail = f", {form_id}, {'true' if out == 'f32' else 'false'}>"
+    tail = (f", {form_id}, {'true' if out == 'f32' else 'false'}, "
+            f"{'true' if ue8m0 else 'false'}>")
     tag = f"NtCfg<{bm}, {bn},"
     return (lambda k: "nt_fp8_kernel" in k and tag in k and tail in k), tag + " ...>" + tail
 
