@@ -46,6 +46,10 @@ EXPORTED = (
     "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0",
     "dg_m_grouped_fp8_gemm_nt_masked_ue8m0",
     "dg_pack_ue8m0_scales",
+    "dg_fp8_gemm_nn",
+    "dg_fp8_gemm_tn",
+    "dg_fp8_gemm_tt",
+    "dg_m_grouped_fp8_gemm_nn_contiguous",
 )
 DG_CAST_POW2_SCALE = 1
 
@@ -93,6 +97,11 @@ def load_library(path: Optional[str] = None):
                                                               I64, P]
     lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
     lib.dg_pack_ue8m0_scales.argtypes = [P, I, P, I64, I64, I64, P]
+    for name in ("dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt"):
+        getattr(lib, name).argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
+        getattr(lib, name).restype = I
+    lib.dg_m_grouped_fp8_gemm_nn_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
+    lib.dg_m_grouped_fp8_gemm_nn_contiguous.restype = I
     for name in ("dg_fp8_gemm_nt_ue8m0", "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0",
                  "dg_m_grouped_fp8_gemm_nt_masked_ue8m0", "dg_pack_ue8m0_scales"):
         getattr(lib, name).restype = I
@@ -282,6 +291,7 @@ def get_mk_alignment_for_contiguous_layout() -> int:
 
 
 FORM_DENSE, FORM_CONTIGUOUS, FORM_MASKED, FORM_K_GROUPED = 0, 1, 2, 3
+FORM_NN, FORM_TN, FORM_TT, FORM_NN_CONTIGUOUS = 4, 5, 6, 7
 
 
 def kernel_config_name(form: int, rows: int, N: int, K: int, out_f32: bool = False) -> str:
@@ -370,3 +380,64 @@ def pack_ue8m0_scales(sf: torch.Tensor, mn: Optional[int] = None,
         _check(load_library().dg_pack_ue8m0_scales(_ptr(sf3), int(per_block), _ptr(out), G, mn,
                                                    KB * 128, _stream(sf)))
     return out if batched else out[0]
+
+
+def _gemm_layout(layout: str, a, b, d, c):
+    """Dense NN / TN / TT: A stored [M, K] ("n") or [K, M] ("t"); B stored
+    [K, N] ("n") or [N, K] ("t"); SFA fp32 [K/128, M], SFB fp32 [K/128, N]."""
+    A, SA = _fp8(a[0], "A"), _f32(a[1], "SFA")
+    B, SB = _fp8(b[0], "B"), _f32(b[1], "SFB")
+    d = _dev(d, "d")
+    if d.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("d must be bfloat16 or float32")
+    if c is not None:
+        c = _dev(c, "c")
+        if c.dtype != d.dtype or c.shape != d.shape:
+            raise ValueError("c must match d in dtype and shape")
+    M, K = A.shape if layout[0] == "n" else A.shape[::-1]
+    N, Kb = B.shape if layout[1] == "t" else B.shape[::-1]
+    if Kb != K or tuple(d.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)} B {tuple(B.shape)} d {tuple(d.shape)}")
+    if tuple(SA.shape) != (K // 128, M) or tuple(SB.shape) != (K // 128, N):
+        raise ValueError(f"scale shapes: SFA {tuple(SA.shape)} SFB {tuple(SB.shape)}, "
+                         f"want {(K // 128, M)} and {(K // 128, N)}")
+    with torch.cuda.device(d.device):
+        _check(getattr(load_library(), f"dg_fp8_gemm_{layout}")(
+            _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(c), _ptr(d),
+            DG_F32 if d.dtype == torch.float32 else DG_BF16, M, N, K, _stream(d)))
+    return d
+
+
+def fp8_gemm_nn(a, b, d, c=None):
+    """d[M,N] = c + A @ B; a = (A [M,K], SFA [K/128, M]), b = (B [K,N], SFB [K/128, N])."""
+    return _gemm_layout("nn", a, b, d, c)
+
+
+def fp8_gemm_tn(a, b, d, c=None):
+    """d[M,N] = c + A^T @ B; a = (A [K,M], SFA [K/128, M]), b = (B [K,N], SFB [K/128, N])."""
+    return _gemm_layout("tn", a, b, d, c)
+
+
+def fp8_gemm_tt(a, b, d, c=None):
+    """d[M,N] = c + A^T @ B^T; a = (A [K,M], SFA [K/128, M]), b = (B [N,K], SFB [K/128, N])."""
+    return _gemm_layout("tt", a, b, d, c)
+
+
+def m_grouped_fp8_gemm_nn_contiguous(a, b, d: torch.Tensor, m_indices: torch.Tensor) -> torch.Tensor:
+    """d[r] = a[r] @ b[m_indices[r]]; a = (A [M_tot,K], SFA [K/128, M_tot]),
+    b = (B [G,K,N], SFB [G, K/128, N]); d bf16 [M_tot, N]."""
+    A, SA = _fp8(a[0], "A"), _f32(a[1], "SFA")
+    B, SB = _fp8(b[0], "B"), _f32(b[1], "SFB")
+    d, mi = _dev(d, "d"), _i32(m_indices, "m_indices")
+    if d.dtype != torch.bfloat16:
+        raise TypeError("d must be bfloat16")
+    M_tot, K = A.shape
+    G, Kb, N = B.shape
+    if Kb != K or tuple(d.shape) != (M_tot, N) or tuple(mi.shape) != (M_tot,):
+        raise ValueError("shape mismatch")
+    if tuple(SA.shape) != (K // 128, M_tot) or tuple(SB.shape) != (G, K // 128, N):
+        raise ValueError("scale shape mismatch")
+    with torch.cuda.device(d.device):
+        _check(load_library().dg_m_grouped_fp8_gemm_nn_contiguous(
+            _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(mi), _ptr(d), M_tot, N, K, G, _stream(d)))
+    return d

@@ -117,6 +117,17 @@ struct Workspace {
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 std::mutex g_ws_mutex;
 
+dg_status run_tn(const dg::TnProblem& p, void* stream) {
+    int dev = 0;
+    DeviceInfo info;
+    dg_status st = current_device(dev, info);
+    if (st != DG_OK) return st;
+    if (print_configs()) fprintf(stderr, "[dg] %s\n", dg::describe_tn_config(p));
+    hipError_t e = dg::launch_tn(p, cu_cap_for(info), reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 dg_status run_nt(dg::NtProblem p, void* stream) {
     int dev = 0;
     DeviceInfo info;
@@ -378,17 +389,90 @@ dg_status dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t* a, const float* sfa
     REQUIRE(G * ((M + 127) / 128) * ((N + 127) / 128) <= INT_MAX, "too many tiles");
     REQUIRE(alias_ok(c, d, G * M * N * 4), "c overlaps d without being equal to it");
     dg::TnProblem p{};
+    p.form = dg::kKGrouped;
+    p.a_mk = false; p.b_nk = false; p.out_f32 = true;
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.k_sizes_host = k_sizes_host;
     p.c = c; p.d = d; p.G = G; p.M = M; p.N = N; p.K_tot = K_tot;
+    return run_tn(p, stream);
+}
 
-    int dev = 0;
-    DeviceInfo info;
-    dg_status st = current_device(dev, info);
-    if (st != DG_OK) return st;
-    if (print_configs()) fprintf(stderr, "[dg] %s\n", dg::describe_tn_config(p));
-    hipError_t e = dg::launch_tn(p, cu_cap_for(info), reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
-    return ok();
+// Dense NN / TN / TT: A stored [M, K] (a_mk) or [K, M]; B stored [N, K] (b_nk)
+// or [K, N]; sfa [K/128, M], sfb [K/128, N]; C like D (may equal it).
+static dg_status gemm_layout(const uint8_t* a, bool a_mk, const float* sfa, const uint8_t* b,
+                             bool b_nk, const float* sfb, const void* c, void* d,
+                             dg_dtype d_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+    REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size (M=%lld N=%lld K=%lld)", (long long)M,
+            (long long)N, (long long)K);
+    REQUIRE(K % 128 == 0, "K=%lld is not a multiple of 128", (long long)K);
+    REQUIRE(N % 16 == 0, "N=%lld is not a multiple of 16", (long long)N);
+    REQUIRE(a_mk || M % 16 == 0, "M=%lld is not a multiple of 16 (A stored [K, M])", (long long)M);
+    REQUIRE(d_dtype == DG_BF16 || d_dtype == DG_F32, "d_dtype must be DG_BF16 or DG_F32");
+    if (M == 0 || N == 0) return ok();
+    REQUIRE_PTR(d, 16);
+    if (c) REQUIRE_PTR(c, 16);
+    if (K > 0) {
+        REQUIRE_PTR(a, 16);
+        REQUIRE_PTR(b, 16);
+        REQUIRE_PTR(sfa, 16);
+        REQUIRE_PTR(sfb, 16);
+    }
+    REQUIRE(M <= kOffsetLimit / (K > 0 ? K : 1) && N <= kOffsetLimit / (K > 0 ? K : 1),
+            "M*K and N*K must stay below 2^31");
+    REQUIRE(((M + 127) / 128) * ((N + 127) / 128) <= INT_MAX, "too many tiles");
+    REQUIRE(alias_ok(c, d, M * N * (d_dtype == DG_F32 ? 4 : 2)),
+            "c overlaps d without being equal to it");
+    dg::TnProblem p{};
+    p.form = dg::kDenseLayout;
+    p.a_mk = a_mk; p.b_nk = b_nk; p.out_f32 = d_dtype == DG_F32;
+    p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.c = c; p.d = d;
+    p.G = 1; p.M = M; p.N = N; p.K_tot = K;
+    return run_tn(p, stream);
+}
+
+dg_status dg_fp8_gemm_nn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                         const void* c, void* d, dg_dtype d_dtype, int64_t M, int64_t N,
+                         int64_t K, void* stream) {
+    return gemm_layout(a, true, sfa, b, false, sfb, c, d, d_dtype, M, N, K, stream);
+}
+
+dg_status dg_fp8_gemm_tn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                         const void* c, void* d, dg_dtype d_dtype, int64_t M, int64_t N,
+                         int64_t K, void* stream) {
+    return gemm_layout(a, false, sfa, b, false, sfb, c, d, d_dtype, M, N, K, stream);
+}
+
+dg_status dg_fp8_gemm_tt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                         const void* c, void* d, dg_dtype d_dtype, int64_t M, int64_t N,
+                         int64_t K, void* stream) {
+    return gemm_layout(a, false, sfa, b, true, sfb, c, d, d_dtype, M, N, K, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nn_contiguous(const uint8_t* a, const float* sfa,
+                                              const uint8_t* b, const float* sfb,
+                                              const int32_t* m_indices, void* d, int64_t M_tot,
+                                              int64_t N, int64_t K, int64_t G, void* stream) {
+    REQUIRE(M_tot >= 0 && N >= 0 && K >= 0, "negative size");
+    REQUIRE(G >= 1, "G=%lld must be >= 1", (long long)G);
+    REQUIRE(M_tot % 128 == 0, "M_tot=%lld is not a multiple of 128 (the contiguous-layout alignment)",
+            (long long)M_tot);
+    REQUIRE(K % 128 == 0, "K=%lld is not a multiple of 128", (long long)K);
+    REQUIRE(N % 16 == 0, "N=%lld is not a multiple of 16", (long long)N);
+    if (M_tot == 0 || N == 0) return ok();
+    REQUIRE_PTR(a, 16);
+    REQUIRE_PTR(b, 16);
+    REQUIRE_PTR(d, 16);
+    REQUIRE_PTR(sfa, 16);
+    REQUIRE_PTR(sfb, 16);
+    REQUIRE_PTR(m_indices, 4);
+    REQUIRE(M_tot <= kOffsetLimit / (K > 0 ? K : 1) && N <= kOffsetLimit / (K > 0 ? K : 1),
+            "M_tot*K and K*N must stay below 2^31");
+    REQUIRE(G <= INT_MAX && (M_tot / 128) * ((N + 255) / 256) <= INT_MAX, "too many tiles");
+    dg::TnProblem p{};
+    p.form = dg::kMGroupedNN;
+    p.a_mk = true; p.b_nk = false; p.out_f32 = false;
+    p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.m_indices = m_indices; p.c = nullptr; p.d = d;
+    p.G = G; p.M = M_tot; p.N = N; p.K_tot = K;
+    return run_tn(p, stream);
 }
 
 static dg_status run_cast(const void* x, dg_dtype dtype, uint8_t* codes, float* sf, int64_t G,
@@ -474,9 +558,13 @@ const char* dg_kernel_config_name(int form, int64_t rows, int64_t N, int64_t K, 
         p.out_f32 = form == 0 && out_f32 != 0;
         return dg::nt_config_name(p);
     }
-    if (form == 3) {
+    if (form >= 3 && form <= 7) {
         dg::TnProblem p{};
         p.M = rows; p.N = N; p.K_tot = K; p.G = 1;
+        p.out_f32 = out_f32 != 0;
+        p.form = form == 3 ? dg::kKGrouped : (form == 7 ? dg::kMGroupedNN : dg::kDenseLayout);
+        p.a_mk = form == 4;           // 4 NN, 5 TN, 6 TT
+        p.b_nk = form == 6;
         return dg::tn_config_name(p);
     }
     return "";

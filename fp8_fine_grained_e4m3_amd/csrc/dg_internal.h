@@ -30,15 +30,26 @@ struct NtProblem {
     int device_cus;           // CUs of the device (not the cap): sizes the K split
 };
 
+// MN-major kernel family: the K-grouped TN form, the dense NN / TN / TT
+// layouts and the M-grouped contiguous NN form.  Both operands carry one fp32
+// scale per output row (m) / column (n) per 128-K block: sfa [KB, M],
+// sfb [KB, N] (grouped NN: sfb [G, KB, N]).
+enum TnForm : int { kKGrouped = 0, kDenseLayout = 1, kMGroupedNN = 2 };
+
 struct TnProblem {
+    TnForm form;
+    bool a_mk;      // A stored [M, K] (K contiguous), else [K, M]
+    bool b_nk;      // B stored [N, K] (K contiguous), else [K, N] (grouped NN: [G, K, N])
+    bool out_f32;   // D (and C) fp32, else bf16
     const uint8_t* a;
     const float* sfa;
     const uint8_t* b;
     const float* sfb;
-    const int32_t* k_sizes_host;
-    const float* c;
-    float* d;
-    int64_t G, M, N, K_tot;
+    const int32_t* k_sizes_host;   // K-grouped
+    const int32_t* m_indices;      // M-grouped NN
+    const void* c;
+    void* d;
+    int64_t G, M, N, K_tot;        // dense / grouped NN: G = experts (1 dense), K_tot = K
 };
 
 constexpr int kMaxTnGroups = 256;

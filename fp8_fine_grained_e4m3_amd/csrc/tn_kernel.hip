@@ -38,6 +38,19 @@
 // order (largest K first, so the longest tiles start first); the persistent
 // grid walks (group, m tile, n tile) in that order.  A group with K = 0 still
 // produces D[g] = C[g] (or 0).
+//
+// The same kernel serves the dense NN, TN and TT layouts (the README's
+// "Notices" lists NT, TN, NN and TT; the first letter is A's, "N" = stored
+// [M, K]; the second is B's, "T" = stored [N, K]) as one group spanning all
+// of K, and the M-grouped contiguous NN form ("Grouped GEMMs (contiguous
+// layout)" names the nt and nn contiguous variants), whose 128-row tiles each
+// take the expert of their first row.  An operand stored with K contiguous
+// (A_MK, B_NK) is staged like the NT kernel's: one 128-byte LDS row per
+// matrix row, 16-byte chunk c at position c ^ swz(row), and read with plain
+// 16-byte LDS loads (lane l: row l & 15 of the fragment, K bytes
+// 32 (l >> 4) .. +31), which is the same register layout the transposing
+// reads produce.  The scales are per output row / column on both sides in
+// every layout, so the promotion is unchanged.
 #include "dg_internal.h"
 #include "tile_common.h"
 
@@ -52,9 +65,11 @@ struct TnArgs {
     const float* sfa;
     const uint8_t* b;
     const float* sfb;
-    const float* c;
-    float* d;
+    const void* c;     // fp32 or bf16 (the output type), may be NULL
+    void* d;
+    const int32_t* m_indices;   // M-grouped NN
     int M, N, G;
+    int K;             // row length of operands stored with K contiguous
     int tiles_m, tiles_n, num_tiles;
     int32_t order[kMaxTnGroups];      // processing order of the groups
     int32_t kb_start[kMaxTnGroups];   // first 128-K block of group g
@@ -101,9 +116,10 @@ __device__ __forceinline__ int tn_swz(int row) {
     else return (row & 7) | (((row >> 5) & 1) << 3);
 }
 
-template <class Cfg>
+template <class Cfg, bool A_MK, bool B_NK, bool OUT_F32, bool GROUPED_M>
 __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, SM = Cfg::SM, SN = Cfg::SN;
+    static_assert(!GROUPED_M || BM == kKBlk, "grouped tiles are one 128-row expert block");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::STAGES * Cfg::STAGE_BYTES];
 
     const int tid = threadIdx.x;
@@ -124,15 +140,24 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
     const int b_x = tn_swz<BN>(tr_row);
 
     for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
-        const int gi = t / per_group;
+        const int gi = GROUPED_M ? 0 : t / per_group;
         const int local = t - gi * per_group;
-        const int g = p.order[gi];
+        const int g = GROUPED_M ? 0 : p.order[gi];
         const int tm = local % p.tiles_m;
         const int tn = local / p.tiles_m;
         const int m0 = tm * BM, n0 = tn * BN;
-        const int kb0 = p.kb_start[g];
-        const int nkb = p.kb_count[g];
+        const int kb0 = GROUPED_M ? 0 : p.kb_start[g];
+        const int nkb = GROUPED_M ? p.K / kKBlk : p.kb_count[g];
         const int64_t gbase = (int64_t)g * p.M * p.N;
+        // M-grouped: the tile's rows are one 128-row block; its expert is the
+        // index of the block's first row (padding blocks are skipped)
+        int e = 0;
+        if constexpr (GROUPED_M) {
+            e = p.m_indices[m0];
+            if (e < 0 || e >= p.G) continue;
+        }
+        const uint8_t* __restrict__ b_e = p.b + (int64_t)e * p.K * p.N;
+        const float* __restrict__ sfb_e = p.sfb + (int64_t)e * (p.K / kKBlk) * p.N;
 
         // Copy offsets.  Copy u of A moves 1024 / BM K rows: lane l fills LDS
         // chunk position l % (BM / 16) of row u * (1024 / BM) + l / (BM / 16),
@@ -143,14 +168,27 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         for (int q = 0; q < Cfg::DMA_PER_WAVE; ++q) {
             const int u = wave * Cfg::DMA_PER_WAVE + q;
             if (u < Cfg::A_DMA) {
-                const int row = u * (1024 / BM) + lane / (BM / 16);
-                const int ch = (lane % (BM / 16)) ^ tn_swz<BM>(row);
-                goff[q] = (uint32_t)row * (uint32_t)p.M + (uint32_t)min(m0 + 16 * ch, p.M - 16);
+                if constexpr (A_MK) {
+                    // 8 matrix rows of 128 K bytes; rows past M re-read the last one
+                    const int row = 8 * u + (lane >> 3);
+                    const int ch = (lane & 7) ^ swz(row);
+                    goff[q] = (uint32_t)min(m0 + row, p.M - 1) * (uint32_t)p.K + (uint32_t)(ch * 16);
+                } else {
+                    const int row = u * (1024 / BM) + lane / (BM / 16);
+                    const int ch = (lane % (BM / 16)) ^ tn_swz<BM>(row);
+                    goff[q] = (uint32_t)row * (uint32_t)p.M + (uint32_t)min(m0 + 16 * ch, p.M - 16);
+                }
             } else {
                 const int uu = u - Cfg::A_DMA;
-                const int row = uu * (1024 / BN) + lane / (BN / 16);
-                const int ch = (lane % (BN / 16)) ^ tn_swz<BN>(row);
-                goff[q] = (uint32_t)row * (uint32_t)p.N + (uint32_t)min(n0 + 16 * ch, p.N - 16);
+                if constexpr (B_NK) {
+                    const int row = 8 * uu + (lane >> 3);
+                    const int ch = (lane & 7) ^ swz(row);
+                    goff[q] = (uint32_t)min(n0 + row, p.N - 1) * (uint32_t)p.K + (uint32_t)(ch * 16);
+                } else {
+                    const int row = uu * (1024 / BN) + lane / (BN / 16);
+                    const int ch = (lane % (BN / 16)) ^ tn_swz<BN>(row);
+                    goff[q] = (uint32_t)row * (uint32_t)p.N + (uint32_t)min(n0 + 16 * ch, p.N - 16);
+                }
             }
         }
         // Scale copies, one per wave: copies [0, SA_DMA) fill A-scale slots,
@@ -175,14 +213,14 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         }
         auto issue_stage = [&](int kb, int stage) {
             const uint32_t dst = lds0 + stage * Cfg::STAGE_BYTES;
-            const uint8_t* ak = p.a + (int64_t)kb * kKBlk * p.M;
-            const uint8_t* bk = p.b + (int64_t)kb * kKBlk * p.N;
+            const uint8_t* ak = p.a + (int64_t)kb * kKBlk * (A_MK ? 1 : p.M);
+            const uint8_t* bk = b_e + (int64_t)kb * kKBlk * (B_NK ? 1 : p.N);
 #pragma unroll
             for (int q = 0; q < Cfg::DMA_PER_WAVE; ++q) {
                 const int u = wave * Cfg::DMA_PER_WAVE + q;
                 dma16(u < Cfg::A_DMA ? ak : bk, goff[q], dst + u * 1024);
             }
-            const float* sk = s_is_a ? p.sfa + (int64_t)kb * p.M : p.sfb + (int64_t)kb * p.N;
+            const float* sk = s_is_a ? p.sfa + (int64_t)kb * p.M : sfb_e + (int64_t)kb * p.N;
             dma4(sk, s_off, dst + s_lds);
         };
 
@@ -194,8 +232,18 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
 #pragma unroll
             for (int j = 0; j < SN; ++j) {
                 const int n = min(n0 + wn * Cfg::WTN + 16 * j + 4 * (lane >> 4), p.N - 4);
-                acc[i][j] = p.c ? *reinterpret_cast<const f32x4*>(p.c + gbase + (int64_t)m * p.N + n)
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
+                const int64_t off = gbase + (int64_t)m * p.N + n;
+                if (!p.c) {
+                    acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                } else if constexpr (OUT_F32) {
+                    acc[i][j] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.c) + off);
+                } else {
+                    const i32x2 cv = *reinterpret_cast<const i32x2*>(static_cast<const uint16_t*>(p.c) + off);
+                    acc[i][j] = f32x4{bf16_bits_to_f32((uint32_t)cv.x & 0xFFFFu),
+                                      bf16_bits_to_f32((uint32_t)cv.x >> 16),
+                                      bf16_bits_to_f32((uint32_t)cv.y & 0xFFFFu),
+                                      bf16_bits_to_f32((uint32_t)cv.y >> 16)};
+                }
             }
         }
 
@@ -241,11 +289,20 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
             for (int j = 0; j < SN; ++j)
                 sb[j] = *reinterpret_cast<const f32x4*>(
                     st + Cfg::SB_OFF + 4 * (wn * Cfg::WTN + 16 * j + 4 * (lane >> 4)));
+            // fragment of 16 columns (tile columns 16 c .. 16 c + 15) of A or B
+            auto a_frag = [&](int c) {
+                if constexpr (A_MK) return lds_fragment_row(st, 16 * c + r16, lane);
+                else return tr_frag(a_lane, c, a_x, BM);
+            };
+            auto b_frag = [&](int c) {
+                if constexpr (B_NK) return lds_fragment_row(st + Cfg::A_BYTES, 16 * c + r16, lane);
+                else return tr_frag(b_lane, c, b_x, BN);
+            };
             i32x8 bfrag[SN];
 #pragma unroll
             for (int j = 0; j < SN; ++j)
-                bfrag[j] = tr_frag(b_lane, (wn * Cfg::WTN) / 16 + j, b_x, BN);
-            i32x8 afrag = tr_frag(a_lane, (wm * Cfg::WTM) / 16, a_x, BM);
+                bfrag[j] = b_frag((wn * Cfg::WTN) / 16 + j);
+            i32x8 afrag = a_frag((wm * Cfg::WTM) / 16);
             // Block products t = SN * i + j in order; the promotion of product t
             // runs after product t + 2 is issued (three results in flight).
             auto promote = [&](const f32x4& pr, int i, int j) {
@@ -259,7 +316,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
 #pragma unroll
             for (int i = 0; i < SM; ++i) {
                 i32x8 anext;
-                if (i + 1 < SM) anext = tr_frag(a_lane, (wm * Cfg::WTM) / 16 + i + 1, a_x, BM);
+                if (i + 1 < SM) anext = a_frag((wm * Cfg::WTM) / 16 + i + 1);
 #pragma unroll
                 for (int j = 0; j < SN; ++j) {
                     const int t = SN * i + j;
@@ -269,7 +326,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
                 if (i + 1 < SM) afrag = anext;
                 // Issue order: the next A fragment's reads, then each block
                 // product followed by the promotion of the product two back.
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // 4 DS reads
+                __builtin_amdgcn_sched_group_barrier(0x100, A_MK ? 2 : 4, 0);   // the A fragment's DS reads
 #pragma unroll
                 for (int j = 0; j < SN; ++j) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
@@ -314,8 +371,16 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
                 const int m = m0 + ph * Cfg::WTM + rl;
                 const int n = n0 + 4 * lane;
                 if (m >= p.M || n >= p.N) continue;
+                if constexpr (GROUPED_M) {
+                    if (p.m_indices[m] != e) continue;   // padding row of the segment
+                }
                 const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * BN + 4 * (lane ^ (rl & 15)));
-                __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.d + gbase + (int64_t)m * p.N + n));
+                const int64_t off = gbase + (int64_t)m * p.N + n;
+                if constexpr (OUT_F32)
+                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(p.d) + off));
+                else
+                    __builtin_nontemporal_store(pack_bf16x4(v.x, v.y, v.z, v.w),
+                                                reinterpret_cast<i32x2*>(static_cast<uint16_t*>(p.d) + off));
             }
             // every wave is done reading the staged rows before they (or the
             // next tile's copies) are overwritten
@@ -327,33 +392,46 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
 namespace {
 
 using TnCfg256 = TnCfg<256, 256, 2, 4, 2>;
+using TnCfg128 = TnCfg<128, 256, 2, 4, 2>;   // M-grouped NN: one 128-row expert block per tile
 
-template <class Cfg>
+template <class Cfg, bool A_MK, bool B_NK, bool OUT_F32, bool GROUPED_M>
 hipError_t launch_tn_cfg(const TnProblem& pr, int cu_cap, hipStream_t stream) {
     TnArgs a;
     a.a = pr.a; a.sfa = pr.sfa; a.b = pr.b; a.sfb = pr.sfb; a.c = pr.c; a.d = pr.d;
+    a.m_indices = pr.m_indices;
     a.M = (int)pr.M; a.N = (int)pr.N; a.G = (int)pr.G;
+    a.K = (int)pr.K_tot;
     a.tiles_m = (int)((pr.M + Cfg::BM - 1) / Cfg::BM);
     a.tiles_n = (int)((pr.N + Cfg::BN - 1) / Cfg::BN);
-    const int64_t tiles = pr.G * a.tiles_m * a.tiles_n;
+    // K-grouped: every group's tiles; dense: one group spanning K; M-grouped:
+    // every 128-row block's tiles (a block's expert is read on the device)
+    const int64_t groups = pr.form == kKGrouped ? pr.G : 1;
+    const int64_t tiles = groups * a.tiles_m * a.tiles_n;
     if (tiles <= 0) return hipSuccess;
     a.num_tiles = (int)tiles;
-    int32_t start = 0;
-    for (int g = 0; g < a.G; ++g) {
-        a.kb_start[g] = start;
-        a.kb_count[g] = pr.k_sizes_host[g] / kKBlk;
-        start += a.kb_count[g];
+    if (pr.form == kKGrouped) {
+        int32_t start = 0;
+        for (int g = 0; g < a.G; ++g) {
+            a.kb_start[g] = start;
+            a.kb_count[g] = pr.k_sizes_host[g] / kKBlk;
+            start += a.kb_count[g];
+        }
+    } else {
+        a.kb_start[0] = 0;
+        a.kb_count[0] = (int32_t)(pr.K_tot / kKBlk);
     }
+    const int n_order = (int)groups;
     // Longest-processing-time order: groups with the most K blocks first.
-    std::iota(a.order, a.order + a.G, 0);
-    std::stable_sort(a.order, a.order + a.G,
+    std::iota(a.order, a.order + n_order, 0);
+    std::stable_sort(a.order, a.order + n_order,
                      [&](int x, int y) { return a.kb_count[x] > a.kb_count[y]; });
 
     static int occupancy = -1;
     if (occupancy < 0) {
         int occ = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &occ, reinterpret_cast<const void*>(&tn_fp8_kernel<Cfg>), Cfg::THREADS, 0) !=
+                &occ, reinterpret_cast<const void*>(&tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M>),
+                Cfg::THREADS, 0) !=
                 hipSuccess ||
             occ < 1)
             occ = 1;
@@ -361,17 +439,43 @@ hipError_t launch_tn_cfg(const TnProblem& pr, int cu_cap, hipStream_t stream) {
     }
     const int64_t resident = (int64_t)cu_cap * occupancy;
     const int grid = (int)(tiles < resident ? tiles : resident);
-    hipLaunchKernelGGL((tn_fp8_kernel<Cfg>), dim3(grid), dim3(Cfg::THREADS), 0, stream, a);
+    hipLaunchKernelGGL((tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M>), dim3(grid),
+                       dim3(Cfg::THREADS), 0, stream, a);
     return hipGetLastError();
+}
+
+template <bool A_MK, bool B_NK>
+hipError_t launch_dense_layout(const TnProblem& pr, int cu_cap, hipStream_t stream) {
+    return pr.out_f32 ? launch_tn_cfg<TnCfg256, A_MK, B_NK, true, false>(pr, cu_cap, stream)
+                      : launch_tn_cfg<TnCfg256, A_MK, B_NK, false, false>(pr, cu_cap, stream);
 }
 
 }  // namespace
 
 hipError_t launch_tn(const TnProblem& pr, int cu_cap, hipStream_t stream) {
-    return launch_tn_cfg<TnCfg256>(pr, cu_cap, stream);
+    switch (pr.form) {
+    case kKGrouped:
+        return launch_tn_cfg<TnCfg256, false, false, true, false>(pr, cu_cap, stream);
+    case kMGroupedNN:
+        return launch_tn_cfg<TnCfg128, true, false, false, true>(pr, cu_cap, stream);
+    case kDenseLayout:
+        if (pr.a_mk && !pr.b_nk) return launch_dense_layout<true, false>(pr, cu_cap, stream);
+        if (!pr.a_mk && !pr.b_nk) return launch_dense_layout<false, false>(pr, cu_cap, stream);
+        if (!pr.a_mk && pr.b_nk) return launch_dense_layout<false, true>(pr, cu_cap, stream);
+        return hipErrorInvalidValue;   // NT is the NT kernel's
+    }
+    return hipErrorInvalidValue;
 }
 
-const char* tn_config_name(const TnProblem&) { return "tn_kgrouped_f32_256x256"; }
+const char* tn_config_name(const TnProblem& pr) {
+    if (pr.form == kKGrouped) return "tn_kgrouped_f32_256x256";
+    if (pr.form == kMGroupedNN) return "nn_contiguous_bf16_128x256";
+    static thread_local char buf[64];
+    snprintf(buf, sizeof buf, "%s_dense_%s_256x256",
+             pr.a_mk ? (pr.b_nk ? "nt" : "nn") : (pr.b_nk ? "tt" : "tn"),
+             pr.out_f32 ? "f32" : "bf16");
+    return buf;
+}
 
 const char* describe_tn_config(const TnProblem& pr) {
     static thread_local char buf[192];

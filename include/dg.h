@@ -1,10 +1,11 @@
 /*
  * dg.h -- C ABI of the MI355X (gfx950) fine-grained FP8 e4m3 GEMM library.
  *
- * The operation, for every entry point, is D = C + A @ B^T on FP8 operands in
- * the OCP E4M3FN encoding, each carrying fp32 scale factors at a fine
- * granularity, with the FP8 partial sums of every 128-wide K block scaled and
- * promoted into an fp32 accumulator:
+ * The operation of every GEMM entry point is D = C + A @ B^T (NT; the other
+ * layouts below transpose the stored operands) on FP8 operands in the OCP
+ * E4M3FN encoding, each carrying scale factors at a fine granularity, with
+ * the FP8 partial sums of every 128-wide K block scaled and promoted into an
+ * fp32 accumulator:
  *
  *   D[m,n] = C[m,n] + sum_kb (sa[kb,m] * sb(n,kb)) * sum_{k in block kb} a[m,k] * b[n,k]
  *
@@ -167,6 +168,63 @@ dg_status dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t* a, const float* sfa
                                               void* stream);
 
 /*
+ * The other memory layouts.  Source: "DeepGEMM" README, "Interfaces",
+ * "Notices" (D = C + A @ B named by two layout letters; the newer path takes
+ * all four of NT, TN, NN and TT) and "Grouped GEMMs (contiguous layout)" (the
+ * nt and nn contiguous variants).  Reading: the first letter is A's, "N" = A
+ * stored [M, K] (K contiguous), "T" = A stored [K, M] (the operand is its
+ * transpose); the second letter is B's, "T" = B stored [N, K], "N" = B stored
+ * [K, N].  In these layouts both operands carry one fp32 scale per output row
+ * (m, for A) or column (n, for B) per 128-K block, MN-major:
+ *   sfa [K/128, M], sfb [K/128, N]
+ * (the per-row granularity of the newer path, and the K-grouped form's
+ * layout; a 128 x 128 weight scale is given to each of its rows).
+ *   D[m,n] = C[m,n] + sum_kb (sa[kb,m] * sb[kb,n]) * sum_{k in kb} A(m,k) * B(k,n)
+ *
+ * dg_fp8_gemm_nn:  D = C + A @ B      a [M, K],  b [K, N]
+ * dg_fp8_gemm_tn:  D = C + A^T @ B    a [K, M],  b [K, N]
+ * dg_fp8_gemm_tt:  D = C + A^T @ B^T  a [K, M],  b [N, K]
+ *   c    NULL (0) or [M, N] of d_dtype; c == d allowed, other overlap rejected
+ *   d    [M, N], DG_BF16 or DG_F32
+ * Rules: K % 128 == 0, N % 16 == 0, and M % 16 == 0 when A is stored [K, M];
+ * every pointer 16-byte aligned.  One kernel launch, no workspace; results
+ * are deterministic.
+ */
+dg_status dg_fp8_gemm_nn(const uint8_t* a, const float* sfa,
+                         const uint8_t* b, const float* sfb,
+                         const void* c, void* d, dg_dtype d_dtype,
+                         int64_t M, int64_t N, int64_t K, void* stream);
+dg_status dg_fp8_gemm_tn(const uint8_t* a, const float* sfa,
+                         const uint8_t* b, const float* sfb,
+                         const void* c, void* d, dg_dtype d_dtype,
+                         int64_t M, int64_t N, int64_t K, void* stream);
+dg_status dg_fp8_gemm_tt(const uint8_t* a, const float* sfa,
+                         const uint8_t* b, const float* sfb,
+                         const void* c, void* d, dg_dtype d_dtype,
+                         int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * M-grouped contiguous NN GEMM: D[r,:] = A[r,:] @ B[e_r], e_r = m_indices[r].
+ *   a         [M_tot, K]     e4m3 (K contiguous); expert segments as in the
+ *                            NT contiguous form (128-row aligned, padding at
+ *                            each segment's tail)
+ *   sfa       [K/128, M_tot] fp32
+ *   b         [G, K, N]      e4m3, one [K, N] matrix per expert (N contiguous)
+ *   sfb       [G, K/128, N]  fp32, one scale per (column n, 128-K block)
+ *   m_indices [M_tot]        int32 expert of each row, -1 for padding
+ *   d         [M_tot, N]     bf16; rows whose index differs from their 128-row
+ *                            block's expert (padding) are not written
+ * Rules: M_tot % 128 == 0, K % 128 == 0, N % 16 == 0, G >= 1; pointers
+ * 16-byte aligned (m_indices 4).  A block whose first index is outside
+ * [0, G) is skipped.
+ */
+dg_status dg_m_grouped_fp8_gemm_nn_contiguous(const uint8_t* a, const float* sfa,
+                                              const uint8_t* b, const float* sfb,
+                                              const int32_t* m_indices, void* d,
+                                              int64_t M_tot, int64_t N, int64_t K, int64_t G,
+                                              void* stream);
+
+/*
  * FP8 casting, the step before the GEMM (the "DeepGEMM" README, "Interfaces",
  * "Notices", leaves casting to the caller and suggests fusing it into the
  * producer; these kernels write exactly the operand layouts the GEMM entry
@@ -287,7 +345,8 @@ dg_status dg_set_num_cus(int n);
  * configuration report of DeepGEMM Documentation, section 6, variable
  * DG_PRINT_CONFIGS; setting DG_PRINT_CONFIGS=1 also prints it per call).
  *   form: 0 dense, 1 M-grouped contiguous, 2 M-grouped masked (rows = M,
- *   M_tot or M_max), 3 K-grouped TN (rows = M).  out_f32: dense output dtype.
+ *   M_tot or M_max), 3 K-grouped TN (rows = M), 4 dense NN, 5 dense TN,
+ *   6 dense TT, 7 M-grouped contiguous NN.  out_f32: dense output dtype.
  * Returns a static string; "" for an unknown form.  No HIP call is made.
  */
 const char* dg_kernel_config_name(int form, int64_t rows, int64_t N, int64_t K, int out_f32);

@@ -424,3 +424,85 @@ def gen_activations(shape, seed: int = 0, bf16: bool = True) -> np.ndarray:
     if K >= 128 and rows > 1:
         flat[-1, :128] = (rng.integers(-120, 121, size=128) * 2.0 ** -133).astype(np.float32)
     return to_bf16_values(x) if bf16 else x
+
+
+# --------------------------------------------------------------------------
+# Other layouts (NN / TN / TT) and the M-grouped contiguous NN form
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LayoutInputs:
+    layout: str        # "nn", "tn" or "tt"
+    a: np.ndarray      # uint8, stored [M, K] ("n") or [K, M] ("t")
+    sfa: np.ndarray    # fp32 [K/128, M]
+    b: np.ndarray      # uint8, stored [K, N] ("n") or [N, K] ("t")
+    sfb: np.ndarray    # fp32 [K/128, N]
+    M: int
+    N: int
+    K: int
+    c: Optional[np.ndarray] = None
+
+
+def gen_layout(layout: str, M: int, N: int, K: int, seed: int = 0,
+               with_c: bool = False) -> LayoutInputs:
+    """A(m,k), B(k,n) ~ N(0,1) fp32, each quantised with one scale per output
+    row / column per 128-K block (1 x 128 along K), then stored in the
+    layout's orientation (a transpose of the codes; the scales are MN-major
+    either way)."""
+    assert layout in ("nn", "tn", "tt")
+    rng = _rng(seed)
+    a32 = _normal(rng, (M, K))
+    bt32 = _normal(rng, (N, K))          # B^T: row n holds B(:, n)
+    a, sfa = quantize_rows(a32)
+    bt, sfb = quantize_rows(bt32)
+    if layout[0] == "t":
+        a = np.ascontiguousarray(a.T)
+    if layout[1] == "n":
+        bt = np.ascontiguousarray(bt.T)
+    c = None
+    if with_c:
+        c = torch.from_numpy(_normal(rng, (M, N))).to(torch.bfloat16).float().numpy()
+    return LayoutInputs(layout, a, sfa, bt, sfb, M, N, K, c)
+
+
+@dataclasses.dataclass
+class NNContiguousInputs:
+    a: np.ndarray          # uint8 [M_tot, K]
+    sfa: np.ndarray        # fp32 [K/128, M_tot]
+    b: np.ndarray          # uint8 [G, K, N]
+    sfb: np.ndarray        # fp32 [G, K/128, N]
+    m_indices: np.ndarray  # int32 [M_tot]
+    counts: np.ndarray
+    M_tot: int
+    N: int
+    K: int
+    G: int
+
+
+def gen_nn_contiguous(G: int = 32, N: int = 4096, K: int = 4096, tokens: int = 8192,
+                      topk: int = 6, seed: int = 0, counts: Optional[np.ndarray] = None,
+                      zipf_s: float = 1.1) -> NNContiguousInputs:
+    """The contiguous MoE workload with each expert's B stored [K, N] and
+    quantised per column n per 128-K block."""
+    rng = _rng(seed)
+    if counts is None:
+        counts = route_topk_zipf(rng, tokens, G, topk, zipf_s)
+    counts = np.asarray(counts, dtype=np.int64)
+    m_idx, offs = contiguous_layout(counts)
+    M_tot = len(m_idx)
+    a32 = np.zeros((M_tot, K), dtype=np.float32)
+    valid = _normal(rng, (int(counts.sum()), K))
+    r = 0
+    for e in range(G):
+        c = int(counts[e])
+        a32[offs[e]: offs[e] + c] = valid[r: r + c]
+        r += c
+    del valid
+    a, sfa = quantize_rows(a32)
+    del a32
+    b = np.empty((G, K, N), dtype=np.uint8)
+    sfb = np.empty((G, K // BLOCK, N), dtype=np.float32)
+    for e in range(G):
+        bt, sfb[e] = quantize_rows(_normal(rng, (N, K)))
+        b[e] = bt.T
+    return NNContiguousInputs(a, sfa, b, sfb, m_idx, counts, M_tot, N, K, G)

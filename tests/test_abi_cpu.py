@@ -205,3 +205,36 @@ def test_pack_ue8m0_rejects(lib):
     assert call(packed=ctypes.c_void_p(0x10000 + 64)) == dg.DG_ERR_INVALID_ARG
     assert "overlap" in err(lib)
     assert call(MN=0, sf=NULL) == dg.DG_OK and call(K=0, sf=NULL) == dg.DG_OK
+
+
+def test_layout_entry_points_reject(lib):
+    for name in ("dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt"):
+        f = getattr(lib, name)
+
+        def call(a=P16, b=P16b, sfa=P16, sfb=P16, c=NULL, d=P16c, dt=dg.DG_BF16, M=128, N=256, K=512):
+            return f(a, sfa, b, sfb, c, d, dt, M, N, K, None)
+
+        assert call(K=300) == dg.DG_ERR_INVALID_ARG and "K=300" in err(lib)
+        assert call(N=100) == dg.DG_ERR_INVALID_ARG and "N=100" in err(lib)
+        assert call(dt=5) == dg.DG_ERR_INVALID_ARG and "d_dtype" in err(lib)
+        assert call(sfb=BAD) == dg.DG_ERR_INVALID_ARG and "sfb" in err(lib)
+        assert call(c=ctypes.c_void_p(0x30000 + 32)) == dg.DG_ERR_INVALID_ARG
+        assert call(M=0, a=NULL) == dg.DG_OK
+        st = call(M=100)       # M % 16 only matters when A is stored [K, M]
+        if name == "dg_fp8_gemm_nn":
+            assert st != dg.DG_ERR_INVALID_ARG
+        else:
+            assert st == dg.DG_ERR_INVALID_ARG and "M=100" in err(lib)
+    g = lib.dg_m_grouped_fp8_gemm_nn_contiguous
+    assert g(P16, P16, P16b, P16, P16, P16c, 200, 256, 512, 4, None) == dg.DG_ERR_INVALID_ARG
+    assert "multiple of 128" in err(lib)
+    assert g(P16, P16, P16b, P16, NULL, P16c, 256, 256, 512, 4, None) == dg.DG_ERR_INVALID_ARG
+    assert g(P16, P16, P16b, P16, P16, P16c, 0, 256, 512, 4, None) == dg.DG_OK
+
+
+def test_layout_config_names(lib):
+    assert dg.kernel_config_name(dg.FORM_NN, 4096, 4096, 4096) == "nn_dense_bf16_256x256"
+    assert dg.kernel_config_name(dg.FORM_TN, 256, 256, 512, True) == "tn_dense_f32_256x256"
+    assert dg.kernel_config_name(dg.FORM_TT, 256, 256, 512) == "tt_dense_bf16_256x256"
+    assert dg.kernel_config_name(dg.FORM_NN_CONTIGUOUS, 256, 256, 512) == "nn_contiguous_bf16_128x256"
+    assert dg.kernel_config_name(dg.FORM_K_GROUPED, 256, 256, 512) == "tn_kgrouped_f32_256x256"
