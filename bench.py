@@ -17,7 +17,8 @@ Also reported on the same JSON line:
                   (contiguous, masked, K-grouped) timed the same way, the
                   FP8 casting kernels on bf16 operands of those shapes, and
                   the power-of-two (packed UE8M0) scale variant of the dense
-                  sweep and the contiguous and masked workloads.
+                  sweep and the contiguous and masked workloads, and the NN /
+                  TN / TT layouts and the M-grouped contiguous NN form.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-detail]
                        [--no-cpu] [--json-out PATH]
@@ -219,13 +220,14 @@ def main():
     print(f"[bench] step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     # ---- grouped workloads (detail, timed the same way) ------------------------------
-    grouped, cast, ue8m0 = {}, {}, {}
+    grouped, cast, ue8m0, layouts = {}, {}, {}, {}
     if not args.no_detail:
         del ops
         torch.cuda.empty_cache()
         grouped = bench_grouped(dg, gen, up, dev, stream, args)
         cast = bench_cast(dg, dev, stream, args)
         ue8m0 = bench_ue8m0(dg, gen, up, dev, stream, args)
+        layouts = bench_layouts(dg, gen, up, dev, stream, args)
 
     # ---- CPU baseline: the oracle on a bounded sample ----------------------------------
     cpu = None
@@ -251,7 +253,8 @@ def main():
                    "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "detail": {"dense": per_shape, "grouped": grouped, "cast": cast, "ue8m0": ue8m0},
+        "detail": {"dense": per_shape, "grouped": grouped, "cast": cast, "ue8m0": ue8m0,
+                   "layouts": layouts},
     }
     line = json.dumps(result)
     print(line, flush=True)
@@ -535,6 +538,41 @@ def bench_ue8m0(dg, gen, up, dev, stream, args):
                                          gbs=round(byts / ms / 1e6, 1),
                                          frac_hbm=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
     del a, sa, b, sb, mm, d, x, wa, wb
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_layouts(dg, gen, up, dev, stream, args):
+    """The NN, TN and TT layouts on the 4096 x 4096 x 7168 shape of the dense
+    sweep (per-row scales on both operands), and the M-grouped contiguous NN
+    form on the contiguous MoE workload (32 experts, N = K = 4096)."""
+    import torch
+    reps = max(3, min(args.steps, 10))
+    out = {}
+    M, N, K = 4096, 4096, 7168
+    fns = {"nn": dg.fp8_gemm_nn, "tn": dg.fp8_gemm_tn, "tt": dg.fp8_gemm_tt}
+    for layout, fn in fns.items():
+        x = gen.gen_layout(layout, M, N, K, seed=0)
+        a, sa, b, sb = up(x.a), up(x.sfa), up(x.b), up(x.sfb)
+        d = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        ms = median_ms(stream, lambda: fn((a, sa), (b, sb), d), reps)
+        flop = 2.0 * M * N * K
+        out[f"{layout}_{M}x{N}x{K}"] = dict(
+            kernel=dg.kernel_config_name({"nn": dg.FORM_NN, "tn": dg.FORM_TN, "tt": dg.FORM_TT}[layout],
+                                         M, N, K),
+            us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
+            frac_mfma=round(flop / ms / 1e9 / PEAK_FP8_TFLOPS, 4))
+        del x, a, sa, b, sb, d
+    torch.cuda.empty_cache()
+    x = gen.gen_nn_contiguous(seed=0)
+    a, sa, b, sb, mi = up(x.a), up(x.sfa), up(x.b), up(x.sfb), up(x.m_indices)
+    d = torch.empty(x.M_tot, x.N, dtype=torch.bfloat16, device=dev)
+    ms = median_ms(stream, lambda: dg.m_grouped_fp8_gemm_nn_contiguous((a, sa), (b, sb), d, mi),
+                   reps)
+    flop = 2.0 * int(x.counts.sum()) * x.N * x.K
+    out["nn_contiguous_32x4096x4096"] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
+                                             frac_mfma=round(flop / ms / 1e9 / PEAK_FP8_TFLOPS, 4))
+    del a, sa, b, sb, mi, d, x
     torch.cuda.empty_cache()
     return out
 

@@ -236,5 +236,5 @@ def test_layout_config_names(lib):
     assert dg.kernel_config_name(dg.FORM_NN, 4096, 4096, 4096) == "nn_dense_bf16_256x256"
     assert dg.kernel_config_name(dg.FORM_TN, 256, 256, 512, True) == "tn_dense_f32_256x256"
     assert dg.kernel_config_name(dg.FORM_TT, 256, 256, 512) == "tt_dense_bf16_256x256"
-    assert dg.kernel_config_name(dg.FORM_NN_CONTIGUOUS, 256, 256, 512) == "nn_contiguous_bf16_128x256"
+    assert dg.kernel_config_name(dg.FORM_NN_CONTIGUOUS, 256, 256, 512) == "nn_contiguous_bf16_256x256"
     assert dg.kernel_config_name(dg.FORM_K_GROUPED, 256, 256, 512) == "tn_kgrouped_f32_256x256"

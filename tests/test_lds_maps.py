@@ -129,3 +129,35 @@ def test_epilogue_staging_round_trip_and_banks():
                 addrs.append(a)
                 assert stg[a] == (row, 4 * ch)
             assert b128_conflict_free(addrs), (kind, SM, SN, BN, base)
+
+
+def test_k_contiguous_staging_of_the_mn_kernel_is_a_bijection_and_conflict_free():
+    """The MN-major kernel's K-contiguous operand staging: chunk c of row r at
+    position sigma(c) ^ ((r >> 1) & 7).  The copy (lane l of copy u fills row
+    8u + l/8, position l % 8) covers every (row, chunk) once, and each 16-lane
+    group of a fragment read (rows 16 c + (l & 15), chunks 2 (l >> 4) (+1))
+    hits 16 distinct 16-byte slots modulo 256 bytes."""
+    def sig(c):
+        return ((c >> 1) & 1) | ((c & 1) << 1) | (c & 4)
+
+    def pos(r, c):
+        return sig(c) ^ ((r >> 1) & 7)
+
+    rows = 256
+    seen = set()
+    for u in range(rows // 8):
+        for l in range(64):
+            r, p = 8 * u + l // 8, l % 8
+            ch = sig(p ^ ((r >> 1) & 7))
+            assert pos(r, ch) == p
+            seen.add((r, ch))
+    assert len(seen) == rows * 8
+    for frag in range(rows // 16):
+        for half in (0, 1):
+            slots = {}
+            for l in range(64):
+                r, c = 16 * frag + (l & 15), 2 * (l >> 4) + half
+                byte = r * 128 + pos(r, c) * 16
+                grp = 2 * ((l >> 5) & 1) + (((l >> 2) ^ (l >> 3) ^ (l >> 4)) & 1)
+                slots.setdefault(grp, set()).add((byte % 256) // 16)
+            assert all(len(v) == 16 for v in slots.values()), (frag, half, slots)
