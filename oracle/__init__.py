@@ -98,6 +98,8 @@ def _bind(lib):
     lib.oracle_pack_ue8m0.restype = ctypes.c_int
     lib.oracle_gemm_layout.argtypes = [P, ctypes.c_int, P, P, ctypes.c_int, P, P, I, I, I, P, I, P]
     lib.oracle_gemm_layout.restype = ctypes.c_int
+    lib.oracle_mqa_logits.argtypes = [P, P, P, P, P, P, I, I, I, I, ctypes.c_int, P, I, P]
+    lib.oracle_mqa_logits.restype = ctypes.c_int
     return lib
 
 
@@ -308,4 +310,23 @@ def m_grouped_nn_contiguous(a, sfa, b, sfb, m_indices, rows=None) -> np.ndarray:
         sel = np.nonzero(mi[r] == e)[0]
         if len(sel):
             out[sel] = gemm_layout("nn", a, sfa, b[e], sfb[e], rows=r[sel])
+    return out
+
+
+def mqa_logits(q, kv, kv_sf, weights, ks, ke, clean: bool = True, rows=None) -> np.ndarray:
+    """out[rows] of the MQA logits: q uint8 [S, H, D], kv uint8 [S_kv, D],
+    kv_sf fp32 [S_kv], weights fp32 [S, H], ks / ke int32 [S]; fp64
+    [len(rows), S_kv] with -inf (clean) or NaN outside each row's range."""
+    q = _c(q, np.uint8); kv = _c(kv, np.uint8)
+    sf = _c(kv_sf, np.float32); w = _c(weights, np.float32)
+    ks = _c(ks, np.int32); ke = _c(ke, np.int32)
+    S, H, D = q.shape
+    S_kv = kv.shape[0]
+    assert kv.shape == (S_kv, D) and sf.shape == (S_kv,) and w.shape == (S, H)
+    assert ks.shape == (S,) and ke.shape == (S,)
+    r = np.arange(S, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    out = np.empty((len(r), S_kv), dtype=np.float64)
+    if _load().oracle_mqa_logits(_ptr(q), _ptr(kv), _ptr(sf), _ptr(w), _ptr(ks), _ptr(ke), S, S_kv,
+                                 H, D, int(clean), _ptr(r), len(r), _ptr(out)):
+        raise ValueError("oracle_mqa_logits: bad arguments")
     return out

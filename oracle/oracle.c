@@ -487,3 +487,51 @@ int oracle_gemm_layout(const uint8_t* a, int a_stored_mk, const float* sfa, cons
     }
     return bad;
 }
+
+/* ---------------------------------------------------------------------------
+ * MQA logits (non-paged), the indexer kernel of the "DeepGEMM" README
+ * ("Interfaces", "V3.2 MQA kernels for the indexer").  Inputs: q e4m3
+ * [S, H, D]; kv e4m3 [S_kv, D] with one fp32 scale per kv token; weights fp32
+ * [S, H]; per query i a kv range [ks[i], ke[i]).  For j in the range:
+ *   kv_j      = kv[j, :] * sf[j]                         (decoded, scaled)
+ *   out[i, j] = sum_h max(0, q[i, h, :] . kv_j) * weights[i, h]
+ * and, with clean set, out[i, j] = -inf outside the range (without it those
+ * entries are not defined here: NaN).  The range is clamped to [0, S_kv]; an
+ * empty range (ks >= ke) selects nothing.  The dot product over D of decoded
+ * e4m3 values is exact in fp64 (as the block sums above); it is multiplied by
+ * sf[j], passed through the ReLU, weighted and summed over h in ascending
+ * order in fp64.
+ * ------------------------------------------------------------------------- */
+int oracle_mqa_logits(const uint8_t* q, const uint8_t* kv, const float* sf, const float* w,
+                      const int32_t* ks, const int32_t* ke, int64_t S, int64_t S_kv, int64_t H,
+                      int64_t D, int clean, const int64_t* rows, int64_t n_rows, double* out)
+{
+    if (S < 0 || S_kv < 0 || H < 0 || D < 0)
+        return 1;
+    build_table();
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t i = rows[r];
+        if (i < 0 || i >= S) { bad |= 1; continue; }
+        int64_t lo = ks[i], hi = ke[i];
+        lo = lo < 0 ? 0 : (lo > S_kv ? S_kv : lo);
+        hi = hi < 0 ? 0 : (hi > S_kv ? S_kv : hi);
+        for (int64_t j = 0; j < S_kv; ++j) {
+            if (j < lo || j >= hi) {
+                out[r * S_kv + j] = clean ? -INFINITY : NAN;
+                continue;
+            }
+            double logit = 0.0;
+            for (int64_t h = 0; h < H; ++h) {
+                double dot = 0.0;                        /* exact */
+                for (int64_t d = 0; d < D; ++d)
+                    dot += g_dec[q[(i * H + h) * D + d]] * g_dec[kv[j * D + d]];
+                const double s = dot * (double)sf[j];
+                logit += (s > 0.0 ? s : 0.0) * (double)w[i * H + h];
+            }
+            out[r * S_kv + j] = logit;
+        }
+    }
+    return bad;
+}

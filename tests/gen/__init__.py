@@ -506,3 +506,54 @@ def gen_nn_contiguous(G: int = 32, N: int = 4096, K: int = 4096, tokens: int = 8
         bt, sfb[e] = quantize_rows(_normal(rng, (N, K)))
         b[e] = bt.T
     return NNContiguousInputs(a, sfa, b, sfb, m_idx, counts, M_tot, N, K, G)
+
+
+# --------------------------------------------------------------------------
+# MQA logits (the indexer kernel)
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class MqaInputs:
+    q: np.ndarray        # uint8 [S, H, D] e4m3 (no scale)
+    kv: np.ndarray       # uint8 [S_kv, D] e4m3
+    kv_sf: np.ndarray    # fp32 [S_kv], one scale per kv token
+    weights: np.ndarray  # fp32 [S, H]
+    ks: np.ndarray       # int32 [S], first kv index of query i's range
+    ke: np.ndarray       # int32 [S], one past the last
+    S: int
+    S_kv: int
+    H: int
+    D: int
+
+
+def causal_ranges(seq_lens, S_kv: Optional[int] = None):
+    """Packed sequences of the given lengths, each query attending to its own
+    sequence's tokens up to and including itself: (ks, ke) int32 [sum(lens)].
+    With S_kv > sum(lens), the kv side holds a shared prefix of S_kv - sum(lens)
+    tokens ahead of the packed sequences that every query also sees."""
+    lens = [int(x) for x in seq_lens]
+    S = sum(lens)
+    prefix = 0 if S_kv is None else S_kv - S
+    ks, ke = np.empty(S, np.int32), np.empty(S, np.int32)
+    i = 0
+    for L in lens:
+        for t in range(L):
+            ks[i] = 0 if prefix else prefix + (i - t)
+            ke[i] = prefix + i + 1
+            i += 1
+    return ks, ke
+
+
+def gen_mqa(S: int, S_kv: int, H: int = 64, D: int = 128, seed: int = 0,
+            seq_lens=None) -> MqaInputs:
+    """q ~ N(0,1) cast to e4m3 (RNE, clamped to +-448; q carries no scale);
+    kv ~ N(0,1) quantised per token (scale = amax / 448 over its D values);
+    weights ~ N(0,1); causal ranges over packed sequences (one sequence of
+    length S by default, S_kv - S shared prefix tokens)."""
+    rng = _rng(seed)
+    q = _cast_e4m3(torch.from_numpy(_normal(rng, (S, H, D)))).numpy()
+    kvc, sf = quantize_rows(_normal(rng, (S_kv, D)))
+    w = _normal(rng, (S, H))
+    ks, ke = causal_ranges([S] if seq_lens is None else seq_lens, S_kv)
+    return MqaInputs(q, kvc, np.ascontiguousarray(sf.reshape(-1)[:S_kv]) if D == BLOCK
+                     else None, w, ks, ke, S, S_kv, H, D)

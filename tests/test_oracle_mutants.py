@@ -14,6 +14,7 @@ from tests import test_oracle_cast_pins as cast_pins
 from tests import test_oracle_pins as pins
 from tests import test_oracle_ue8m0_pins as ue8m0_pins
 from tests import test_oracle_layout_pins as layout_pins
+from tests import test_oracle_mqa_pins as mqa_pins
 
 MUTANTS = {
     "exponent_bias": ("mag = ldexp(1.0 + (double)m / 8.0, e - 7);",
@@ -74,6 +75,13 @@ MUTANTS = {
                               "acc += ((double)sfa[kb * M + m] * (double)sfb[n * KB + kb]) * p;"),
     "layout_drops_c": ("(double)sfb[kb * N + n]) * p;\n            }\n            out[i * N + n] = acc + (c ? (double)c[m * N + n] : 0.0);",
                        "(double)sfb[kb * N + n]) * p;\n            }\n            out[i * N + n] = acc;"),
+    "mqa_no_relu": ("logit += (s > 0.0 ? s : 0.0) * (double)w[i * H + h];",
+                    "logit += s * (double)w[i * H + h];"),
+    "mqa_sf_of_query": ("const double s = dot * (double)sf[j];", "const double s = dot * (double)sf[i % S_kv];"),
+    "mqa_weight_index": ("logit += (s > 0.0 ? s : 0.0) * (double)w[i * H + h];",
+                         "logit += (s > 0.0 ? s : 0.0) * (double)w[(h * S + i) % (S * H)];"),
+    "mqa_range_inclusive": ("if (j < lo || j >= hi) {", "if (j < lo || j > hi) {"),
+    "mqa_clean_zero": ("out[r * S_kv + j] = clean ? -INFINITY : NAN;", "out[r * S_kv + j] = clean ? 0.0 : NAN;"),
     "cast_zero_scale": ("if (amax == 0.0f)\n        return 1.0f;", "if (amax == 0.0f)\n        return 0.5f;"),
 }
 
@@ -116,6 +124,10 @@ def _pin_suite():
         ("layout_tn_exact", lambda: layout_pins.test_layouts_match_exact_rationals("tn", 71, 4, 3, 384)),
         ("layout_transposes", layout_pins.test_nn_and_tt_are_nt_on_transposed_storage),
         ("layout_one_hot_nn", lambda: layout_pins.test_one_hot_b_selects_an_element_of_a("nn")),
+        ("mqa_exact", mqa_pins.test_matches_exact_rationals),
+        ("mqa_numpy", mqa_pins.test_matches_float64_numpy_formula),
+        ("mqa_relu", mqa_pins.test_relu_zeroes_negative_logits_and_one_hot_weights),
+        ("mqa_ranges", mqa_pins.test_ranges_clean_and_unclean_clamped_and_empty),
     ]
     failed = []
     for name, fn in checks:
