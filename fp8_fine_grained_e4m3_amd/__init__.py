@@ -50,6 +50,7 @@ EXPORTED = (
     "dg_fp8_gemm_tn",
     "dg_fp8_gemm_tt",
     "dg_m_grouped_fp8_gemm_nn_contiguous",
+    "dg_fp8_mqa_logits",
 )
 DG_CAST_POW2_SCALE = 1
 
@@ -102,6 +103,8 @@ def load_library(path: Optional[str] = None):
         getattr(lib, name).restype = I
     lib.dg_m_grouped_fp8_gemm_nn_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
     lib.dg_m_grouped_fp8_gemm_nn_contiguous.restype = I
+    lib.dg_fp8_mqa_logits.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I, P]
+    lib.dg_fp8_mqa_logits.restype = I
     for name in ("dg_fp8_gemm_nt_ue8m0", "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0",
                  "dg_m_grouped_fp8_gemm_nt_masked_ue8m0", "dg_pack_ue8m0_scales"):
         getattr(lib, name).restype = I
@@ -441,3 +444,35 @@ def m_grouped_fp8_gemm_nn_contiguous(a, b, d: torch.Tensor, m_indices: torch.Ten
         _check(load_library().dg_m_grouped_fp8_gemm_nn_contiguous(
             _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(mi), _ptr(d), M_tot, N, K, G, _stream(d)))
     return d
+
+
+def fp8_mqa_logits(q: torch.Tensor, kv: Tuple[torch.Tensor, torch.Tensor], weights: torch.Tensor,
+                   cu_seq_len_k_start: torch.Tensor, cu_seq_len_k_end: torch.Tensor,
+                   clean_logits: bool = True, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """logits[i, j] = sum_h relu(q[i, h] . kv[j] * sf[j]) * weights[i, h] for j in
+    [start[i], end[i]) (-inf elsewhere when clean_logits).  q e4m3 [S, H, 128],
+    kv = (e4m3 [S_kv, 128], fp32 [S_kv]), weights fp32 [S, H], ranges int32 [S];
+    returns fp32 [S, S_kv] (or fills `out`)."""
+    Q = _fp8(q, "q")
+    KV, SF = _fp8(kv[0], "kv"), _f32(kv[1], "kv_sf")
+    W = _f32(weights, "weights")
+    ks, ke = _i32(cu_seq_len_k_start, "cu_seq_len_k_start"), _i32(cu_seq_len_k_end, "cu_seq_len_k_end")
+    if Q.dim() != 3:
+        raise ValueError("q must be [seq_len, num_heads, head_dim]")
+    S, H, D = Q.shape
+    S_kv = KV.shape[0]
+    if tuple(KV.shape) != (S_kv, D) or tuple(SF.shape) != (S_kv,) or tuple(W.shape) != (S, H):
+        raise ValueError("shape mismatch")
+    if tuple(ks.shape) != (S,) or tuple(ke.shape) != (S,):
+        raise ValueError("range shape mismatch")
+    if out is None:
+        out = torch.empty(S, S_kv, dtype=torch.float32, device=Q.device)
+    else:
+        out = _f32(out, "out")
+        if tuple(out.shape) != (S, S_kv):
+            raise ValueError("out shape mismatch")
+    with torch.cuda.device(Q.device):
+        _check(load_library().dg_fp8_mqa_logits(
+            _ptr(Q), _ptr(KV), _ptr(SF), _ptr(W), _ptr(ks), _ptr(ke), _ptr(out), S, S_kv, H, D,
+            int(bool(clean_logits)), _stream(out)))
+    return out

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdg.so")
-SOURCES = ["dg_api.cpp", "nt_kernel.hip", "tn_kernel.hip", "cast_kernel.hip"]
+SOURCES = ["dg_api.cpp", "nt_kernel.hip", "tn_kernel.hip", "cast_kernel.hip", "mqa_kernel.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -524,6 +524,36 @@ dg_status dg_per_block_cast_to_fp8(const void* w, dg_dtype w_dtype, uint8_t* cod
     return run_cast(w, w_dtype, codes, sf, G, N, K, flags, true, stream);
 }
 
+dg_status dg_fp8_mqa_logits(const uint8_t* q, const uint8_t* kv, const float* kv_sf,
+                            const float* weights, const int32_t* ks, const int32_t* ke,
+                            float* logits, int64_t S, int64_t S_kv, int64_t H, int64_t D,
+                            int clean_logits, void* stream) {
+    REQUIRE(S >= 0 && S_kv >= 0, "negative size (seq_len=%lld seq_len_kv=%lld)", (long long)S,
+            (long long)S_kv);
+    REQUIRE(D == 128, "head_dim=%lld: only 128 is supported (one MFMA K step)", (long long)D);
+    REQUIRE(H == 16 || H == 32 || H == 64, "num_heads=%lld must be 16, 32 or 64", (long long)H);
+    REQUIRE(clean_logits == 0 || clean_logits == 1, "clean_logits must be 0 or 1");
+    if (S == 0 || S_kv == 0) return ok();
+    REQUIRE_PTR(q, 16);
+    REQUIRE_PTR(kv, 16);
+    REQUIRE_PTR(weights, 16);
+    REQUIRE_PTR(logits, 16);
+    REQUIRE_PTR(kv_sf, 4);
+    REQUIRE_PTR(ks, 4);
+    REQUIRE_PTR(ke, 4);
+    REQUIRE(S <= 65535LL * 16 && S_kv <= INT_MAX, "seq_len must be <= 1048560 and seq_len_kv < 2^31");
+    dg::MqaProblem p{};
+    p.q = q; p.kv = kv; p.kv_sf = kv_sf; p.weights = weights; p.ks = ks; p.ke = ke;
+    p.logits = logits; p.S = S; p.S_kv = S_kv; p.H = H; p.clean = clean_logits != 0;
+    int dev = 0;
+    DeviceInfo info;
+    dg_status st = current_device(dev, info);
+    if (st != DG_OK) return st;
+    hipError_t e = dg::launch_mqa(p, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 const char* dg_last_error(void) { return g_last_error.c_str(); }
 
 int dg_get_num_cus(void) {

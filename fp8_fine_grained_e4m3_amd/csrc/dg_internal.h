@@ -78,6 +78,21 @@ struct PackProblem {
 };
 hipError_t launch_pack_ue8m0(const PackProblem& p, hipStream_t stream);
 
+// MQA logits: q e4m3 [S, H, 128], kv e4m3 [S_kv, 128], kv_sf [S_kv],
+// weights [S, H], ks / ke [S] -> logits fp32 [S, S_kv].
+struct MqaProblem {
+    const uint8_t* q;
+    const uint8_t* kv;
+    const float* kv_sf;
+    const float* weights;
+    const int32_t* ks;
+    const int32_t* ke;
+    float* logits;
+    int64_t S, S_kv, H;
+    bool clean;
+};
+hipError_t launch_mqa(const MqaProblem& p, hipStream_t stream);
+
 // Device memory for split-K partial tiles, one buffer per (device, stream),
 // grown on demand and kept until the process ends.  `counters` are zero
 // whenever no kernel using them is running (each launch leaves them zero).

@@ -326,6 +326,32 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t* a, const int32_t*
 dg_status dg_pack_ue8m0_scales(const float* sf, int per_block, int32_t* packed, int64_t G,
                                int64_t MN, int64_t K, void* stream);
 
+/*
+ * FP8 MQA logits, non-paged (the indexer kernel).  Source: "DeepGEMM" README,
+ * "Interfaces", "V3.2 MQA kernels for the indexer".  For every query i and
+ * every kv token j in [ks[i], ke[i]):
+ *   kv_j        = kv[j, :] * kv_sf[j]
+ *   logits[i,j] = sum_h relu(q[i, h, :] . kv_j) * weights[i, h]
+ * and, when clean_logits is 1, logits[i, j] = -inf for every other j (when
+ * it is 0 those entries are not written).
+ *   q       [S, H, D]  e4m3 (no scale), D = head_dim = 128
+ *   kv      [S_kv, D]  e4m3
+ *   kv_sf   [S_kv]     fp32, one scale per kv token, > 0
+ *   weights [S, H]     fp32
+ *   ks, ke  [S]        int32 device arrays; each range is clamped to
+ *                      [0, S_kv], and ks >= ke selects nothing
+ *   logits  [S, S_kv]  fp32, row-major
+ * Rules: D == 128, H in {16, 32, 64}, S <= 1048560; q, kv, weights and logits
+ * 16-byte aligned, kv_sf / ks / ke 4-byte aligned.  One kernel launch on
+ * `stream`, no workspace, deterministic.  The dot product over D runs on the
+ * MFMA unit in fp32; the kv scale, being positive, is applied once after the
+ * head sum (relu(x * s) = s * relu(x)).
+ */
+dg_status dg_fp8_mqa_logits(const uint8_t* q, const uint8_t* kv, const float* kv_sf,
+                            const float* weights, const int32_t* ks, const int32_t* ke,
+                            float* logits, int64_t S, int64_t S_kv, int64_t H, int64_t D,
+                            int clean_logits, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* dg_last_error(void);
 

@@ -238,3 +238,19 @@ def test_layout_config_names(lib):
     assert dg.kernel_config_name(dg.FORM_TT, 256, 256, 512) == "tt_dense_bf16_256x256"
     assert dg.kernel_config_name(dg.FORM_NN_CONTIGUOUS, 256, 256, 512) == "nn_contiguous_bf16_256x256"
     assert dg.kernel_config_name(dg.FORM_K_GROUPED, 256, 256, 512) == "tn_kgrouped_f32_256x256"
+
+
+def test_mqa_logits_rejects(lib):
+    f = lib.dg_fp8_mqa_logits
+
+    def call(q=P16, kv=P16b, sf=P16, w=P16c, ks=P16, ke=P16, out=P16c, S=64, S_kv=256, H=64,
+             D=128, clean=1):
+        return f(q, kv, sf, w, ks, ke, out, S, S_kv, H, D, clean, None)
+
+    assert call(D=64) == dg.DG_ERR_INVALID_ARG and "head_dim" in err(lib)
+    assert call(H=48) == dg.DG_ERR_INVALID_ARG and "num_heads" in err(lib)
+    assert call(clean=2) == dg.DG_ERR_INVALID_ARG and "clean_logits" in err(lib)
+    assert call(q=BAD) == dg.DG_ERR_INVALID_ARG and "q is not 16-byte" in err(lib)
+    assert call(ke=NULL) == dg.DG_ERR_INVALID_ARG and "ke is NULL" in err(lib)
+    assert call(S=-1) == dg.DG_ERR_INVALID_ARG
+    assert call(S=0, q=NULL) == dg.DG_OK and call(S_kv=0, kv=NULL) == dg.DG_OK

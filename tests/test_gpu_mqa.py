@@ -1,0 +1,111 @@
+"""GPU parity of the FP8 MQA logits kernel (the indexer kernel, non-paged)
+against the CPU oracle (oracle.mqa_logits), through the C ABI.
+
+Definition ("DeepGEMM" README, "Interfaces", "V3.2 MQA kernels for the
+indexer"): logits[i, j] = sum_h relu(q[i, h] . kv[j] * sf[j]) * weights[i, h]
+for j in [ks[i], ke[i]), -inf elsewhere when cleaning.
+
+* Tolerance parity (1 - cos < 1e-5, |err| <= 1e-2 |ref| + 1e-2 rms(ref)) over
+  the in-range entries, for 16, 32 and 64 heads, ragged S and S_kv, causal
+  packed sequences with and without a shared kv prefix, arbitrary ranges
+  (clamped, empty, reversed).
+* Out-of-range entries: exactly -inf with cleaning; untouched (sentinel
+  bytes) without it.
+* Closed forms, bit-exact: all q negative against positive kv gives 0; one
+  head with weight 0.5 and all-ones operands gives 64 sf[j].
+* The 4096 x 4096 x 64-head causal prefill shape on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_fine_grained_e4m3_amd as dg
+import oracle
+from tests import gen
+from tests.parity import announce, check_close, dev
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7FC0DEAD
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dg.load_library()
+    yield
+
+
+def run(x, clean=True):
+    out = torch.full((x.S, x.S_kv), SENTINEL, dtype=torch.int32, device="cuda").view(torch.float32)
+    dg.fp8_mqa_logits(dev(x.q), (dev(x.kv), dev(x.kv_sf)), dev(x.weights), dev(x.ks), dev(x.ke),
+                      clean_logits=clean, out=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def compare(got, ref, clean, what, raw=None):
+    inside = np.isfinite(ref) if clean else ~np.isnan(ref)
+    if inside.any():
+        check_close(got[inside].astype(np.float64), ref[inside], what)
+    if clean:
+        assert np.all(np.isneginf(got[~inside])), f"{what}: out-of-range entries not -inf"
+    else:
+        assert np.all(raw[~inside] == SENTINEL), f"{what}: out-of-range entries written"
+
+
+@pytest.mark.parametrize("H", [16, 32, 64])
+@pytest.mark.parametrize("S,S_kv,lens", [
+    (128, 256, None), (37, 300, None), (200, 200, [70, 130]), (64, 1000, [30, 34]), (1, 5, None),
+])
+def test_mqa_parity(H, S, S_kv, lens):
+    announce(f"mqa H={H} S={S} S_kv={S_kv} lens={lens}")
+    x = gen.gen_mqa(S, S_kv, H=H, seed=S + S_kv + H, seq_lens=lens)
+    ref = oracle.mqa_logits(x.q, x.kv, x.kv_sf, x.weights, x.ks, x.ke, clean=True)
+    compare(run(x, True), ref, True, f"H={H} {S}x{S_kv}")
+
+
+def test_mqa_without_cleaning_leaves_the_rest_untouched():
+    announce("mqa clean=False")
+    x = gen.gen_mqa(70, 520, H=64, seed=3, seq_lens=[40, 30])
+    got = run(x, False)
+    raw = got.view(np.int32)
+    ref = oracle.mqa_logits(x.q, x.kv, x.kv_sf, x.weights, x.ks, x.ke, clean=False)
+    compare(got, ref, False, "unclean", raw=raw)
+
+
+def test_mqa_arbitrary_ranges():
+    announce("mqa arbitrary ranges")
+    x = gen.gen_mqa(40, 700, H=32, seed=4)
+    rng = np.random.default_rng(4)
+    x.ks = rng.integers(-50, 700, size=40).astype(np.int32)
+    x.ke = (x.ks + rng.integers(-20, 400, size=40)).astype(np.int32)
+    x.ke[3] = 10_000; x.ks[5] = 800; x.ke[7] = x.ks[7]        # clamped, empty, empty
+    ref = oracle.mqa_logits(x.q, x.kv, x.kv_sf, x.weights, x.ks, x.ke, clean=True)
+    compare(run(x, True), ref, True, "arbitrary ranges")
+
+
+def test_mqa_closed_forms_bit_exact():
+    announce("mqa closed forms")
+    S, S_kv, H = 20, 300, 64
+    x = gen.gen_mqa(S, S_kv, H=H, seed=5)
+    x.q[:] = 0xB8                            # -1
+    x.kv[:] = 0x38                           # +1
+    x.ks[:] = 0; x.ke[:] = S_kv
+    assert np.all(run(x, True) == 0.0)       # every head negative: relu -> 0
+    x.q[:, 7, :] = 0x38                      # head 7: dot = 128
+    x.weights[:] = 0.0
+    x.weights[:, 7] = 0.5
+    want = (64.0 * x.kv_sf.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(run(x, True), np.broadcast_to(want, (S, S_kv)))
+
+
+def test_mqa_prefill_4096_sampled():
+    """4096 queries x 4096 kv tokens, 64 heads, one causal sequence."""
+    announce("mqa 4096x4096 H=64 causal sampled rows")
+    x = gen.gen_mqa(4096, 4096, H=64, seed=0)
+    got = run(x, True)
+    rows = np.array([0, 1, 255, 256, 1000, 2047, 4095], np.int64)
+    ref = oracle.mqa_logits(x.q, x.kv, x.kv_sf, x.weights, x.ks, x.ke, clean=True, rows=rows)
+    compare(got[rows], ref, True, "prefill 4096")
