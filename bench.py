@@ -18,7 +18,8 @@ Also reported on the same JSON line:
                   FP8 casting kernels on bf16 operands of those shapes, and
                   the power-of-two (packed UE8M0) scale variant of the dense
                   sweep and the contiguous and masked workloads, and the NN /
-                  TN / TT layouts and the M-grouped contiguous NN form.
+                  TN / TT layouts and the M-grouped contiguous NN form, and the
+                  FP8 MQA logits kernel on a 64-head causal prefill.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-detail]
                        [--no-cpu] [--json-out PATH]
@@ -220,7 +221,7 @@ def main():
     print(f"[bench] step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     # ---- grouped workloads (detail, timed the same way) ------------------------------
-    grouped, cast, ue8m0, layouts = {}, {}, {}, {}
+    grouped, cast, ue8m0, layouts, mqa = {}, {}, {}, {}, {}
     if not args.no_detail:
         del ops
         torch.cuda.empty_cache()
@@ -228,6 +229,7 @@ def main():
         cast = bench_cast(dg, dev, stream, args)
         ue8m0 = bench_ue8m0(dg, gen, up, dev, stream, args)
         layouts = bench_layouts(dg, gen, up, dev, stream, args)
+        mqa = bench_mqa(dg, gen, up, dev, stream, args)
 
     # ---- CPU baseline: the oracle on a bounded sample ----------------------------------
     cpu = None
@@ -254,7 +256,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {"dense": per_shape, "grouped": grouped, "cast": cast, "ue8m0": ue8m0,
-                   "layouts": layouts},
+                   "layouts": layouts, "mqa_logits": mqa},
     }
     line = json.dumps(result)
     print(line, flush=True)
@@ -573,6 +575,31 @@ def bench_layouts(dg, gen, up, dev, stream, args):
     out["nn_contiguous_32x4096x4096"] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
                                              frac_mfma=round(flop / ms / 1e9 / PEAK_FP8_TFLOPS, 4))
     del a, sa, b, sb, mi, d, x
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_mqa(dg, gen, up, dev, stream, args):
+    """FP8 MQA logits: 64 heads, head_dim 128, one causal sequence of 4096
+    queries over 4096 kv tokens (and 8 packed sequences of 512), -inf cleaning.
+    Algorithmic FLOP = 2 * H * D per in-range (query, token) pair; bytes =
+    q + kv + kv scales + weights + ranges + the fp32 logits written."""
+    import torch
+    reps = max(3, min(args.steps, 10))
+    out = {}
+    for name, lens in (("causal_4096x4096_h64", None), ("packed_8x512_h64", [512] * 8)):
+        x = gen.gen_mqa(4096, 4096, H=64, seed=0, seq_lens=lens)
+        q, kv, sf, w, ks, ke = up(x.q), up(x.kv), up(x.kv_sf), up(x.weights), up(x.ks), up(x.ke)
+        o = torch.empty(x.S, x.S_kv, dtype=torch.float32, device=dev)
+        ms = median_ms(stream, lambda: dg.fp8_mqa_logits(q, (kv, sf), w, ks, ke, True, out=o), reps)
+        pairs = int(np.clip(x.ke, 0, x.S_kv).astype(np.int64).sum()
+                    - np.clip(x.ks, 0, x.S_kv).astype(np.int64).sum())
+        flop = 2.0 * x.H * x.D * pairs
+        byts = x.q.nbytes + x.kv.nbytes + x.kv_sf.nbytes + x.weights.nbytes + 8 * x.S + 4 * x.S * x.S_kv
+        out[name] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
+                         frac_mfma=round(flop / ms / 1e9 / PEAK_FP8_TFLOPS, 4),
+                         gbs=round(byts / ms / 1e6, 1), pairs=pairs)
+        del x, q, kv, sf, w, ks, ke, o
     torch.cuda.empty_cache()
     return out
 
