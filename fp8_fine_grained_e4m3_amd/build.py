@@ -30,17 +30,41 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libdg.so next to this file; returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
+# Sources compiled on their own with extra flags, then linked in.  The MQA
+# kernel consumes every MFMA result on the VALU at once, so it asks for the
+# MFMA form that writes VGPRs (no accumulator-register reads); the GEMM
+# kernels keep the default.
+SEPARATE = {"mqa_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+OBJ_DIR = os.path.join(HERE, "_build")
+
+
+def _run(cmd, verbose, what):
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libdg.so")
+        raise RuntimeError(f"hipcc failed {what}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (each to its own object, in parallel) and link
+    libdg.so next to this file; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC] + compile_flags + SEPARATE.get(src, []) + [
+            "-c", os.path.join(CSRC, src), "-o", obj]
+        jobs.append((cmd, obj, src))
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "4"))))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose, f"compiling {j[2]}"), jobs))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + [j[1] for j in jobs] + ["-o", tmp],
+         verbose, "linking libdg.so")
     # the host pass warns that it does not know the packed-fp32 feature: harmless
     os.replace(tmp, LIB)
     return LIB
@@ -48,12 +72,12 @@ def build(verbose: bool = False) -> str:
 
 def resource_usage() -> str:
     """Per-kernel VGPR/SGPR/spill/LDS report of the device code (compile only)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES if s.endswith(".hip")]
+    srcs = [s for s in SOURCES if s.endswith(".hip")]
     out = []
     for s in srcs:
-        cmd = [HIPCC] + [f for f in FLAGS if f not in ("-shared",)] + [
-            "--cuda-device-only", "-c", "-Rpass-analysis=kernel-resource-usage", s, "-o",
-            os.devnull]
+        cmd = [HIPCC] + [f for f in FLAGS if f not in ("-shared",)] + SEPARATE.get(s, []) + [
+            "--cuda-device-only", "-c", "-Rpass-analysis=kernel-resource-usage",
+            os.path.join(CSRC, s), "-o", os.devnull]
         res = subprocess.run(cmd, capture_output=True, text=True)
         out.append(res.stderr)
     return "\n".join(out)

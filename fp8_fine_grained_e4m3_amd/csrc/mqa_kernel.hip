@@ -42,6 +42,13 @@ constexpr int kMqaTW = 16 * kMqaTF;  // kv tokens per wave
 constexpr int kMqaTokens = 4 * kMqaTW;   // kv tokens per workgroup
 constexpr int kMqaNBuf = 4;         // LDS buffers of query operands (3 queries ahead)
 
+// max(x, 0) as one integer max on the bit pattern: a negative float (sign
+// bit set) is a negative int32 and becomes +0, a non-negative one is kept.
+// (fmaxf would add a NaN-quieting step; MFMA results are never signalling.)
+__device__ __forceinline__ float relu(float x) {
+    return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
 // K-contiguous row staging (as the MN-major GEMM kernel's): position of
 // chunk c of row `row`; sigma swaps bits 0 and 1 and is its own inverse.
 __device__ __forceinline__ int k_sigma(int c) { return ((c >> 1) & 1) | ((c & 1) << 1) | (c & 4); }
@@ -174,10 +181,10 @@ __global__ __launch_bounds__(256) void mqa_logits_kernel(MqaArgs p) {
 #pragma unroll
                 for (int f = 0; f < F; ++f) {
                     const f32x4 x = mfma_e4m3_block(qf[f], kvf[t]);
-                    acc[t] = __builtin_fmaf(fmaxf(x.x, 0.f), wf[f].x, acc[t]);
-                    acc[t] = __builtin_fmaf(fmaxf(x.y, 0.f), wf[f].y, acc[t]);
-                    acc[t] = __builtin_fmaf(fmaxf(x.z, 0.f), wf[f].z, acc[t]);
-                    acc[t] = __builtin_fmaf(fmaxf(x.w, 0.f), wf[f].w, acc[t]);
+                    acc[t] = __builtin_fmaf(relu(x.x), wf[f].x, acc[t]);
+                    acc[t] = __builtin_fmaf(relu(x.y), wf[f].y, acc[t]);
+                    acc[t] = __builtin_fmaf(relu(x.z), wf[f].z, acc[t]);
+                    acc[t] = __builtin_fmaf(relu(x.w), wf[f].w, acc[t]);
                 }
             }
             // head sum across the four 16-lane groups
