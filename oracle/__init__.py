@@ -100,6 +100,10 @@ def _bind(lib):
     lib.oracle_gemm_layout.restype = ctypes.c_int
     lib.oracle_mqa_logits.argtypes = [P, P, P, P, P, P, I, I, I, I, ctypes.c_int, P, I, P]
     lib.oracle_mqa_logits.restype = ctypes.c_int
+    lib.oracle_k_grouped_tn_ue8m0.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P, I, P]
+    lib.oracle_k_grouped_tn_ue8m0.restype = ctypes.c_int
+    lib.oracle_pack_ue8m0_k_grouped.argtypes = [P, P, I, I, P]
+    lib.oracle_pack_ue8m0_k_grouped.restype = ctypes.c_int
     return lib
 
 
@@ -329,4 +333,45 @@ def mqa_logits(q, kv, kv_sf, weights, ks, ke, clean: bool = True, rows=None) -> 
     if _load().oracle_mqa_logits(_ptr(q), _ptr(kv), _ptr(sf), _ptr(w), _ptr(ks), _ptr(ke), S, S_kv,
                                  H, D, int(clean), _ptr(r), len(r), _ptr(out)):
         raise ValueError("oracle_mqa_logits: bad arguments")
+    return out
+
+
+def k_grouped_word_rows(k_sizes) -> int:
+    """Packed UE8M0 word rows of a K-grouped operand: sum_g ceil(K_g / 512)."""
+    return int(sum((int(k) // 128 + 3) // 4 for k in k_sizes))
+
+
+def k_grouped_tn_ue8m0(a, sfa_packed, b, sfb_packed, k_sizes, c=None, groups=None,
+                       rows=None) -> np.ndarray:
+    """The K-grouped TN form with per-group packed UE8M0 scales
+    (sfa_packed [W, M], sfb_packed [W, N], W = k_grouped_word_rows(k_sizes))."""
+    a = _c(a, np.uint8); b = _c(b, np.uint8)
+    sa = _c(sfa_packed, np.int32); sb = _c(sfb_packed, np.int32)
+    ks = _c(k_sizes, np.int32)
+    K_tot, M = a.shape
+    N = b.shape[1]
+    G = len(ks)
+    W = k_grouped_word_rows(ks)
+    assert sa.shape == (W, M) and sb.shape == (W, N)
+    cc = None if c is None else _c(c, np.float32)
+    full = groups is None
+    if full:
+        groups = np.repeat(np.arange(G), M)
+        rows = np.tile(np.arange(M), G)
+    g = _c(groups, np.int64); r = _c(rows, np.int64)
+    out = np.empty((len(r), N), dtype=np.float64)
+    if _load().oracle_k_grouped_tn_ue8m0(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(ks), _ptr(cc),
+                                         G, M, N, K_tot, _ptr(g), _ptr(r), len(r), _ptr(out)):
+        raise ValueError("oracle_k_grouped_tn_ue8m0: bad arguments")
+    return out.reshape(G, M, N) if full else out
+
+
+def pack_ue8m0_k_grouped(sf, k_sizes) -> np.ndarray:
+    """fp32 power-of-two scales [K_tot/128, MN] -> per-group packed words [W, MN]."""
+    s = _c(sf, np.float32)
+    ks = _c(k_sizes, np.int32)
+    MN = s.shape[1]
+    out = np.zeros((k_grouped_word_rows(ks), MN), dtype=np.int32)
+    if _load().oracle_pack_ue8m0_k_grouped(_ptr(s), _ptr(ks), len(ks), MN, _ptr(out)):
+        raise ValueError("oracle_pack_ue8m0_k_grouped: bad arguments or a non-power-of-two scale")
     return out

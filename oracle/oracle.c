@@ -535,3 +535,92 @@ int oracle_mqa_logits(const uint8_t* q, const uint8_t* kv, const float* sf, cons
     }
     return bad;
 }
+
+/* ---------------------------------------------------------------------------
+ * K-grouped TN with packed UE8M0 scales.  The documentation's section 10
+ * lists a packing utility for the K-grouped GEMM's UE8M0 scales.  Reading:
+ * each group's K blocks are packed on their own, so that a group starts on a
+ * word boundary: group g's KB_g = k_sizes[g] / 128 blocks take ceil(KB_g / 4)
+ * words per column, at word rows w_g = sum_{h < g} ceil(KB_h / 4) ..; byte i
+ * of word [w_g + k4][mn] is the exponent e (scale 2^(e - 127)) of the
+ * group's K block 4 k4 + i for column mn; unused bytes are 0.
+ *   D[g][m,n] = C[g][m,n] + sum over group g's blocks of
+ *               2^(ea - 127) * 2^(eb - 127) * sum_k dec(a[k,m]) * dec(b[k,n])
+ * ------------------------------------------------------------------------- */
+static int k_grouped_word_rows(const int32_t* k_sizes, int64_t G, int64_t g)
+{
+    int64_t w = 0;
+    for (int64_t h = 0; h < g; ++h)
+        w += (k_sizes[h] / KBLK + 3) / 4;
+    return (int)w;
+}
+
+int oracle_k_grouped_tn_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
+                              const int32_t* sfb, const int32_t* k_sizes, const float* c,
+                              int64_t G, int64_t M, int64_t N, int64_t K_tot,
+                              const int64_t* groups, const int64_t* rows, int64_t n_sel,
+                              double* out)
+{
+    build_table();
+    int64_t total = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        if (k_sizes[g] < 0 || k_sizes[g] % KBLK != 0)
+            return 1;
+        total += k_sizes[g];
+    }
+    if (total != K_tot)
+        return 1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t i = 0; i < n_sel; ++i) {
+        int64_t g = groups[i], m = rows[i];
+        if (g < 0 || g >= G || m < 0 || m >= M) { bad |= 1; continue; }
+        int64_t k0 = 0;
+        for (int64_t h = 0; h < g; ++h)
+            k0 += k_sizes[h];
+        const int64_t w0 = k_grouped_word_rows(k_sizes, G, g);
+        const int64_t kb0 = k0 / KBLK, nkb = k_sizes[g] / KBLK;
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < nkb; ++j) {             /* the group's block j */
+                const int64_t kb = kb0 + j;
+                double p = 0.0;                              /* exact block sum */
+                for (int64_t k = kb * KBLK; k < (kb + 1) * KBLK; ++k)
+                    p += g_dec[a[k * M + m]] * g_dec[b[k * N + n]];
+                acc += ue8m0_scale(sfa + (w0 + j / 4) * M, M, m, j % 4)
+                       * ue8m0_scale(sfb + (w0 + j / 4) * N, N, n, j % 4) * p;
+            }
+            out[i * N + n] = acc + (c ? (double)c[(g * M + m) * N + n] : 0.0);
+        }
+    }
+    return bad;
+}
+
+/* fp32 power-of-two scales sf [K_tot/128, MN] -> the per-group packed words
+ * above, [sum_g ceil(KB_g / 4), MN].  Non-powers of two are rejected (1). */
+int oracle_pack_ue8m0_k_grouped(const float* sf, const int32_t* k_sizes, int64_t G, int64_t MN,
+                                int32_t* packed)
+{
+    int64_t kb0 = 0, w = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        if (k_sizes[g] < 0 || k_sizes[g] % KBLK != 0)
+            return 1;
+        const int64_t nkb = k_sizes[g] / KBLK;
+        for (int64_t k4 = 0; k4 < (nkb + 3) / 4; ++k4, ++w)
+            for (int64_t mn = 0; mn < MN; ++mn) {
+                uint32_t word = 0;
+                for (int64_t i = 0; i < 4 && 4 * k4 + i < nkb; ++i) {
+                    const double s = sf[(kb0 + 4 * k4 + i) * MN + mn];
+                    int x;
+                    const double f = frexp(s, &x);
+                    const int e = x - 1 + 127;
+                    if (f != 0.5 || e < 0 || e > 254)
+                        return 1;
+                    word |= (uint32_t)e << (8 * i);
+                }
+                packed[w * MN + mn] = (int32_t)word;
+            }
+        kb0 += nkb;
+    }
+    return 0;
+}

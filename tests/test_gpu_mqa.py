@@ -109,3 +109,33 @@ def test_mqa_prefill_4096_sampled():
     rows = np.array([0, 1, 255, 256, 1000, 2047, 4095], np.int64)
     ref = oracle.mqa_logits(x.q, x.kv, x.kv_sf, x.weights, x.ks, x.ke, clean=True, rows=rows)
     compare(got[rows], ref, True, "prefill 4096")
+
+
+def test_mqa_graph_capture_replays_with_new_ranges():
+    """MQA logits captured into a HIP graph: the ranges live in device memory,
+    so each replay sees the values written before it."""
+    announce("mqa graph capture")
+    x = gen.gen_mqa(96, 700, H=64, seed=8)
+    q, kv, sf, w = dev(x.q), dev(x.kv), dev(x.kv_sf), dev(x.weights)
+    ks, ke = dev(x.ks), dev(x.ke)
+    out = torch.empty(x.S, x.S_kv, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dg.fp8_mqa_logits(q, (kv, sf), w, ks, ke, True, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        dg.fp8_mqa_logits(q, (kv, sf), w, ks, ke, True, out=out)
+    rng = np.random.default_rng(8)
+    for rep in range(3):
+        lo = rng.integers(0, 700, size=96).astype(np.int32)
+        hi = (lo + rng.integers(0, 300, size=96)).astype(np.int32)
+        ks.copy_(torch.from_numpy(lo)); ke.copy_(torch.from_numpy(hi))
+        out.fill_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle.mqa_logits(x.q, x.kv, x.kv_sf, x.weights, lo, hi, clean=True)
+        compare(out.cpu().numpy(), ref, True, f"replay {rep}")

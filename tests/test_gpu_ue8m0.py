@@ -345,3 +345,40 @@ def test_masked_ue8m0_c4_sampled():
             check_close(got[g][rows], ref, f"C4 group {g}")
         if mm < x.M_max:
             assert d.untouched((int(g), slice(mm, None)))
+
+
+def test_graph_capture_replays_masked_ue8m0():
+    """The UE8M0 masked form captured into a HIP graph replays correctly with
+    masked_m changed in device memory between replays (and eager work between
+    them)."""
+    announce("graph capture masked ue8m0")
+    G, M_max, N, K = 4, 256, 528, 1152
+    x = gen.gen_masked(G=G, M_max=M_max, N=N, K=K, masked_m=np.array([256, 5, 0, 77]), seed=41,
+                       pow2=True)
+    wa, wb = gen.to_ue8m0(x.sfa, x.sfb, N)
+    a, sa, b, sb, mm = dev(x.a), dev(wa), dev(x.b), dev(wb), dev(x.masked_m)
+    d = Guarded((G, M_max, N), torch.bfloat16)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d.view, mm)   # warm-up
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d.view, mm)
+    for rep, counts in enumerate([[256, 5, 0, 77], [3, 129, 64, 0], [0, 0, 1, 256]]):
+        d.raw.fill_(d.bits)
+        mm.copy_(torch.tensor(counts, dtype=torch.int32))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = to64(d.view)
+        for gi, c in enumerate(counts):
+            if c:
+                ref = oracle.gemm_nt_ue8m0(x.a[gi], wa[gi], x.b[gi], wb[gi],
+                                           rows=np.arange(c, dtype=np.int64))
+                check_close(got[gi, :c], ref, f"replay {rep} group {gi}")
+            if c < M_max:
+                assert d.untouched((gi, slice(c, None))), f"replay {rep} group {gi}"
+        assert d.intact()

@@ -82,6 +82,12 @@ MUTANTS = {
                          "logit += (s > 0.0 ? s : 0.0) * (double)w[(h * S + i) % (S * H)];"),
     "mqa_range_inclusive": ("if (j < lo || j >= hi) {", "if (j < lo || j > hi) {"),
     "mqa_clean_zero": ("out[r * S_kv + j] = clean ? -INFINITY : NAN;", "out[r * S_kv + j] = clean ? 0.0 : NAN;"),
+    "kgu_global_word_rows": ("acc += ue8m0_scale(sfa + (w0 + j / 4) * M, M, m, j % 4)",
+                             "acc += ue8m0_scale(sfa + (kb / 4) * M, M, m, kb % 4)"),
+    "kgu_b_word_rows": ("* ue8m0_scale(sfb + (w0 + j / 4) * N, N, n, j % 4) * p;",
+                        "* ue8m0_scale(sfb + (j / 4) * N, N, n, j % 4) * p;"),
+    "kgu_pack_drops_group_offset": ("const double s = sf[(kb0 + 4 * k4 + i) * MN + mn];",
+                                    "const double s = sf[(4 * k4 + i) * MN + mn];"),
     "cast_zero_scale": ("if (amax == 0.0f)\n        return 1.0f;", "if (amax == 0.0f)\n        return 0.5f;"),
 }
 
@@ -125,6 +131,8 @@ def _pin_suite():
         ("layout_transposes", layout_pins.test_nn_and_tt_are_nt_on_transposed_storage),
         ("layout_one_hot_nn", lambda: layout_pins.test_one_hot_b_selects_an_element_of_a("nn")),
         ("mqa_exact", mqa_pins.test_matches_exact_rationals),
+        ("kgu_pack", ue8m0_pins.test_k_grouped_pack_layout_and_byte_order),
+        ("kgu_vs_fp32", ue8m0_pins.test_k_grouped_ue8m0_equals_the_fp32_scale_definition),
         ("mqa_numpy", mqa_pins.test_matches_float64_numpy_formula),
         ("mqa_relu", mqa_pins.test_relu_zeroes_negative_logits_and_one_hot_weights),
         ("mqa_ranges", mqa_pins.test_ranges_clean_and_unclean_clamped_and_empty),

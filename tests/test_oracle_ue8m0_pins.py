@@ -110,3 +110,48 @@ def test_gemm_ue8m0_equals_fp32_scale_definition_on_block_constant_b():
     got = oracle.gemm_nt_ue8m0(a, oracle.pack_ue8m0(sfa, False, M, K), b,
                                oracle.pack_ue8m0(sfb, True, N, K))
     assert np.array_equal(got, ref)
+
+
+# --------------------------------------------------------------------------
+# K-grouped TN with per-group packed words
+# --------------------------------------------------------------------------
+
+def test_k_grouped_pack_layout_and_byte_order():
+    """Each group starts on a word boundary: group g's blocks take
+    ceil(KB_g / 4) word rows after the previous groups' rows."""
+    rng = np.random.default_rng(56)
+    k_sizes = np.array([640, 0, 128, 1152], np.int32)      # 5, 0, 1, 9 blocks
+    MN = 7
+    KB = int(k_sizes.sum()) // 128
+    e = rand_exponents(rng, (KB, MN), 1, 254)
+    sf = np.ldexp(np.float32(1), (e - 127).astype(np.int32)).astype(np.float32)
+    got = oracle.pack_ue8m0_k_grouped(sf, k_sizes).view(np.uint32)
+    assert got.shape == (2 + 0 + 1 + 3, MN)
+    kb = 0
+    w = 0
+    for ksz in k_sizes:
+        nkb = int(ksz) // 128
+        want = pack_bytes(e[kb:kb + nkb]).view(np.uint32) if nkb else np.zeros((0, MN), np.uint32)
+        assert np.array_equal(got[w:w + len(want)], want)
+        kb += nkb
+        w += len(want)
+    assert oracle.k_grouped_word_rows(k_sizes) == 6
+
+
+def test_k_grouped_ue8m0_equals_the_fp32_scale_definition():
+    """With power-of-two scales the packed form is the fp32-scale K-grouped
+    oracle, bit for bit (a second, separately pinned route)."""
+    rng = np.random.default_rng(57)
+    M, N = 5, 6
+    k_sizes = np.array([384, 0, 640, 128], np.int32)
+    K_tot = int(k_sizes.sum())
+    a = random_codes(rng, (K_tot, M)); b = random_codes(rng, (K_tot, N))
+    ea = rand_exponents(rng, (K_tot // 128, M)); eb = rand_exponents(rng, (K_tot // 128, N))
+    sfa = np.ldexp(np.float32(1), (ea - 127).astype(np.int32)).astype(np.float32)
+    sfb = np.ldexp(np.float32(1), (eb - 127).astype(np.int32)).astype(np.float32)
+    c = rng.normal(0, 1, (4, M, N)).astype(np.float32)
+    ref = oracle.k_grouped_tn(a, sfa, b, sfb, k_sizes, c)
+    got = oracle.k_grouped_tn_ue8m0(a, oracle.pack_ue8m0_k_grouped(sfa, k_sizes), b,
+                                    oracle.pack_ue8m0_k_grouped(sfb, k_sizes), k_sizes, c)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(got[1], c[1].astype(np.float64))   # empty group: D = C
