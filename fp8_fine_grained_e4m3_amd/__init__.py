@@ -51,6 +51,8 @@ EXPORTED = (
     "dg_fp8_gemm_tt",
     "dg_m_grouped_fp8_gemm_nn_contiguous",
     "dg_fp8_mqa_logits",
+    "dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0",
+    "dg_pack_ue8m0_scales_k_grouped",
 )
 DG_CAST_POW2_SCALE = 1
 
@@ -105,6 +107,11 @@ def load_library(path: Optional[str] = None):
     lib.dg_m_grouped_fp8_gemm_nn_contiguous.restype = I
     lib.dg_fp8_mqa_logits.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I, P]
     lib.dg_fp8_mqa_logits.restype = I
+    lib.dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0.argtypes = [P, P, P, P, P, P, P, I64, I64, I64,
+                                                              I64, P]
+    lib.dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0.restype = I
+    lib.dg_pack_ue8m0_scales_k_grouped.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.dg_pack_ue8m0_scales_k_grouped.restype = I
     for name in ("dg_fp8_gemm_nt_ue8m0", "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0",
                  "dg_m_grouped_fp8_gemm_nt_masked_ue8m0", "dg_pack_ue8m0_scales"):
         getattr(lib, name).restype = I
@@ -255,9 +262,10 @@ def k_grouped_fp8_gemm_tn_contiguous(a: Tuple[torch.Tensor, torch.Tensor],
                                      c: Optional[torch.Tensor] = None) -> torch.Tensor:
     """d[g] = c[g] + a_g^T @ b_g over group g's K rows.  a = (A [K_tot, M],
     SFA [K_tot/128, M]), b = (B [K_tot, N], SFB [K_tot/128, N]); k_sizes is a
-    host sequence; d (and c) fp32 [G, M, N]."""
-    A, SA = _fp8(a[0], "A"), _f32(a[1], "SFA")
-    B, SB = _fp8(b[0], "B"), _f32(b[1], "SFB")
+    host sequence; d (and c) fp32 [G, M, N].  Packed UE8M0 scales (int32):
+    SFA [W, M], SFB [W, N], each group on its own ceil(K_g / 512) word rows."""
+    A, B = _fp8(a[0], "A"), _fp8(b[0], "B")
+    SA, SB, ue8m0 = _scales(a[1], b[1])
     d = _f32(d, "d")
     if c is not None:
         c = _f32(c, "c")
@@ -272,10 +280,13 @@ def k_grouped_fp8_gemm_tn_contiguous(a: Tuple[torch.Tensor, torch.Tensor],
     G = len(ks)
     if B.shape[0] != K_tot or tuple(d.shape) != (G, M, N):
         raise ValueError("shape mismatch")
-    if tuple(SA.shape) != (K_tot // 128, M) or tuple(SB.shape) != (K_tot // 128, N):
+    rows = _k_grouped_words(ks) if ue8m0 else K_tot // 128
+    if tuple(SA.shape) != (rows, M) or tuple(SB.shape) != (rows, N):
         raise ValueError("scale shape mismatch")
+    fn = ("dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0" if ue8m0
+          else "dg_k_grouped_fp8_gemm_tn_contiguous")
     with torch.cuda.device(d.device):
-        _check(load_library().dg_k_grouped_fp8_gemm_tn_contiguous(
+        _check(getattr(load_library(), fn)(
             _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), ks.ctypes.data_as(ctypes.c_void_p), _ptr(c),
             _ptr(d), G, M, N, K_tot, _stream(d)))
     return d
@@ -475,4 +486,22 @@ def fp8_mqa_logits(q: torch.Tensor, kv: Tuple[torch.Tensor, torch.Tensor], weigh
         _check(load_library().dg_fp8_mqa_logits(
             _ptr(Q), _ptr(KV), _ptr(SF), _ptr(W), _ptr(ks), _ptr(ke), _ptr(out), S, S_kv, H, D,
             int(bool(clean_logits)), _stream(out)))
+    return out
+
+
+def _k_grouped_words(k_sizes) -> int:
+    return int(sum((int(k) // 128 + 3) // 4 for k in k_sizes))
+
+
+def pack_ue8m0_scales_k_grouped(sf: torch.Tensor, k_sizes: Sequence[int]) -> torch.Tensor:
+    """fp32 power-of-two scales [K_tot/128, MN] of a K-grouped operand ->
+    packed UE8M0 words [sum_g ceil(K_g / 512), MN], each group on its own rows."""
+    sf = _f32(sf, "sf")
+    ks = np.ascontiguousarray(np.asarray(k_sizes, dtype=np.int32))
+    KB, MN = sf.shape
+    out = torch.empty((_k_grouped_words(ks), MN), dtype=torch.int32, device=sf.device)
+    with torch.cuda.device(sf.device):
+        _check(load_library().dg_pack_ue8m0_scales_k_grouped(
+            _ptr(sf), ks.ctypes.data_as(ctypes.c_void_p), _ptr(out), len(ks), MN, KB * 128,
+            _stream(sf)))
     return out

@@ -238,7 +238,55 @@ __global__ __launch_bounds__(256) void pack_ue8m0_kernel(const float* __restrict
     packed[t] = (int32_t)w;
 }
 
+// K-grouped packing: block (x, w) covers columns 256 x .. of word row w; the
+// row's group is found by a (uniform) scan of the groups' first word rows.
+struct KGroupedPackArgs {
+    const float* sf;
+    int32_t* packed;
+    int MN, G;
+    int32_t w_start[kMaxTnGroups + 1];   // first word row of group g (and the total)
+    int32_t kb_start[kMaxTnGroups];      // first K block of group g
+    int32_t kb_count[kMaxTnGroups];
+};
+
+__global__ __launch_bounds__(256) void pack_ue8m0_k_grouped_kernel(KGroupedPackArgs a) {
+    const int w = blockIdx.y;
+    const int mn = blockIdx.x * 256 + threadIdx.x;
+    if (mn >= a.MN) return;
+    int g = 0;
+    while (g + 1 < a.G && a.w_start[g + 1] <= w) ++g;
+    const int k4 = w - a.w_start[g];
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = 4 * k4 + i;
+        if (j >= a.kb_count[g]) break;
+        const float s = a.sf[(int64_t)(a.kb_start[g] + j) * a.MN + mn];
+        word |= ((__float_as_uint(s) >> 23) & 0xFFu) << (8 * i);
+    }
+    a.packed[(int64_t)w * a.MN + mn] = (int32_t)word;
+}
+
 }  // namespace
+
+hipError_t launch_pack_ue8m0_k_grouped(const float* sf, const int32_t* k_sizes_host, int64_t G,
+                                       int64_t MN, int32_t* packed, hipStream_t stream) {
+    KGroupedPackArgs a;
+    a.sf = sf; a.packed = packed; a.MN = (int)MN; a.G = (int)G;
+    int32_t w = 0, kb = 0;
+    for (int g = 0; g < G; ++g) {
+        a.w_start[g] = w;
+        a.kb_start[g] = kb;
+        a.kb_count[g] = k_sizes_host[g] / kBlk;
+        kb += a.kb_count[g];
+        w += (a.kb_count[g] + 3) / 4;
+    }
+    a.w_start[G] = w;
+    if (w == 0 || MN == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_ue8m0_k_grouped_kernel, dim3((unsigned)((MN + 255) / 256), (unsigned)w),
+                       dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_pack_ue8m0(const PackProblem& p, hipStream_t stream) {
     const int K4 = (int)((p.KB + 3) / 4);

@@ -355,11 +355,67 @@ dg_status dg_pack_ue8m0_scales(const float* sf, int per_block, int32_t* packed, 
     return ok();
 }
 
+static dg_status k_grouped_tn(const uint8_t* a, const void* sfa, const uint8_t* b,
+                              const void* sfb, const int32_t* k_sizes_host, const float* c,
+                              float* d, int64_t G, int64_t M, int64_t N, int64_t K_tot,
+                              bool ue8m0, void* stream);
+
 dg_status dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t* a, const float* sfa,
                                               const uint8_t* b, const float* sfb,
                                               const int32_t* k_sizes_host, const float* c,
                                               float* d, int64_t G, int64_t M, int64_t N,
                                               int64_t K_tot, void* stream) {
+    return k_grouped_tn(a, sfa, b, sfb, k_sizes_host, c, d, G, M, N, K_tot, false, stream);
+}
+
+dg_status dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0(const uint8_t* a, const int32_t* sfa,
+                                                    const uint8_t* b, const int32_t* sfb,
+                                                    const int32_t* k_sizes_host, const float* c,
+                                                    float* d, int64_t G, int64_t M, int64_t N,
+                                                    int64_t K_tot, void* stream) {
+    return k_grouped_tn(a, sfa, b, sfb, k_sizes_host, c, d, G, M, N, K_tot, true, stream);
+}
+
+dg_status dg_pack_ue8m0_scales_k_grouped(const float* sf, const int32_t* k_sizes_host,
+                                         int32_t* packed, int64_t G, int64_t MN, int64_t K_tot,
+                                         void* stream) {
+    REQUIRE(G >= 1 && G <= dg::kMaxTnGroups, "G=%lld must be in [1, %d]", (long long)G,
+            dg::kMaxTnGroups);
+    REQUIRE(MN >= 0 && K_tot >= 0, "negative size");
+    REQUIRE(k_sizes_host != nullptr, "k_sizes_host is NULL");
+    int64_t total = 0, words = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        const int64_t kg = k_sizes_host[g];
+        REQUIRE(kg >= 0 && kg % 128 == 0, "k_sizes_host[%lld]=%lld must be >= 0 and a multiple of 128",
+                (long long)g, (long long)kg);
+        total += kg;
+        words += (kg / 128 + 3) / 4;
+    }
+    REQUIRE(total == K_tot, "sum of k_sizes_host (%lld) != K_tot (%lld)", (long long)total,
+            (long long)K_tot);
+    if (MN == 0 || words == 0) return ok();
+    REQUIRE_PTR(sf, 4);
+    REQUIRE_PTR(packed, 4);
+    REQUIRE(MN <= INT_MAX && words <= 65535, "too many packed word rows");
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(sf), p0 = reinterpret_cast<uintptr_t>(packed);
+    REQUIRE(s0 + (uintptr_t)((K_tot / 128) * MN * 4) <= p0 || p0 + (uintptr_t)(words * MN * 4) <= s0,
+            "sf and packed must not overlap");
+    int dev = 0;
+    DeviceInfo info;
+    dg_status st = current_device(dev, info);
+    if (st != DG_OK) return st;
+    hipError_t e = dg::launch_pack_ue8m0_k_grouped(sf, k_sizes_host, G, MN, packed,
+                                                   reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+static dg_status k_grouped_tn(const uint8_t* a, const void* sfa_, const uint8_t* b,
+                              const void* sfb_, const int32_t* k_sizes_host, const float* c,
+                              float* d, int64_t G, int64_t M, int64_t N, int64_t K_tot,
+                              bool ue8m0, void* stream) {
+    const float* sfa = static_cast<const float*>(sfa_);
+    const float* sfb = static_cast<const float*>(sfb_);
     REQUIRE(M >= 0 && N >= 0 && K_tot >= 0, "negative size");
     REQUIRE(G >= 1 && G <= dg::kMaxTnGroups, "G=%lld must be in [1, %d]", (long long)G,
             dg::kMaxTnGroups);
@@ -390,7 +446,7 @@ dg_status dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t* a, const float* sfa
     REQUIRE(alias_ok(c, d, G * M * N * 4), "c overlaps d without being equal to it");
     dg::TnProblem p{};
     p.form = dg::kKGrouped;
-    p.a_mk = false; p.b_nk = false; p.out_f32 = true;
+    p.a_mk = false; p.b_nk = false; p.out_f32 = true; p.ue8m0 = ue8m0;
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.k_sizes_host = k_sizes_host;
     p.c = c; p.d = d; p.G = G; p.M = M; p.N = N; p.K_tot = K_tot;
     return run_tn(p, stream);

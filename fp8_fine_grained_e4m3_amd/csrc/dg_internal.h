@@ -41,6 +41,7 @@ struct TnProblem {
     bool a_mk;      // A stored [M, K] (K contiguous), else [K, M]
     bool b_nk;      // B stored [N, K] (K contiguous), else [K, N] (grouped NN: [G, K, N])
     bool out_f32;   // D (and C) fp32, else bf16
+    bool ue8m0;     // K-grouped: packed UE8M0 scales, each group on its own word rows
     const uint8_t* a;
     const float* sfa;
     const uint8_t* b;
@@ -77,6 +78,10 @@ struct PackProblem {
     int64_t G, MN, KB;
 };
 hipError_t launch_pack_ue8m0(const PackProblem& p, hipStream_t stream);
+// K-grouped: sf [K_tot/128, MN] -> packed [sum_g ceil(KB_g / 4), MN], each
+// group's blocks on their own word rows.
+hipError_t launch_pack_ue8m0_k_grouped(const float* sf, const int32_t* k_sizes_host, int64_t G,
+                                       int64_t MN, int32_t* packed, hipStream_t stream);
 
 // MQA logits: q e4m3 [S, H, 128], kv e4m3 [S_kv, 128], kv_sf [S_kv],
 // weights [S, H], ks / ke [S] -> logits fp32 [S, S_kv].

@@ -79,6 +79,7 @@ struct TnArgs {
     int32_t order[kMaxTnGroups];      // processing order of the groups
     int32_t kb_start[kMaxTnGroups];   // first 128-K block of group g
     int32_t kb_count[kMaxTnGroups];   // number of 128-K blocks of group g
+    int32_t kw_start[kMaxTnGroups];   // UE8M0: first packed word row of group g
 };
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
@@ -128,7 +129,11 @@ __device__ __forceinline__ int tn_swz(int row) {
 
 constexpr int kGroupedBand = 4;   // M-grouped: 256-row tiles per rasterisation band
 
-template <class Cfg, bool A_MK, bool B_NK, bool OUT_F32, bool GROUPED_M>
+// UE8M0 (K-grouped form): the scales are packed power-of-two exponents, each
+// group's blocks on their own word rows (byte i of word row kw_start[g] + k4
+// holds the group's block 4 k4 + i); v_mfma_scale applies them to the block
+// product and accumulates, so there is no promotion step.
+template <class Cfg, bool A_MK, bool B_NK, bool OUT_F32, bool GROUPED_M, bool UE8M0>
 __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, SM = Cfg::SM, SN = Cfg::SN;
     static_assert(!GROUPED_M || BM == 2 * kKBlk, "grouped tiles span two 128-row expert blocks");
@@ -178,6 +183,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         }
         const int m0 = tm * BM, n0 = tn * BN;
         const int kb0 = GROUPED_M ? 0 : p.kb_start[g];
+        const int kw0 = UE8M0 ? p.kw_start[g] : 0;
         const int nkb = GROUPED_M ? p.K / kKBlk : p.kb_count[g];
         const int64_t gbase = (int64_t)g * p.M * p.N;
         // M-grouped: the expert of block gi is the index of its first row
@@ -254,7 +260,9 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
                 const int u = wave * Cfg::DMA_PER_WAVE + q;
                 dma16(u < Cfg::A_DMA ? ak : bk, goff[q], dst + u * 1024);
             }
-            const float* sk = s_is_a ? p.sfa + (int64_t)kb * p.M : sfb_e + (int64_t)kb * p.N;
+            // fp32: row kb of the scales; UE8M0: the word row holding block kb
+            const int64_t srow = UE8M0 ? kw0 + ((kb - kb0) >> 2) : kb;
+            const float* sk = s_is_a ? p.sfa + srow * p.M : sfb_e + srow * p.N;
             dma4(sk, s_off, dst + s_lds);
         };
 
@@ -312,17 +320,33 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
                 return r;
             };
             float sa[SM];
-#pragma unroll
-            for (int i = 0; i < SM; i += 4) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(
-                    st + Cfg::SA_OFF + 4 * (wm * Cfg::WTM + 64 * (i / 4) + 4 * r16));
-                sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
-            }
             f32x4 sb[SN];
+            int ea[SM], eb[SN];   // UE8M0: the lane's exponents (A column m, B row n of the MFMA)
+            if constexpr (UE8M0) {
+                const int sh = 8 * (it & 3);
 #pragma unroll
-            for (int j = 0; j < SN; ++j)
-                sb[j] = *reinterpret_cast<const f32x4*>(
-                    st + Cfg::SB_OFF + 4 * (wn * Cfg::WTN + 16 * j + 4 * (lane >> 4)));
+                for (int i = 0; i < SM; i += 4) {
+                    const i32x4 v = *reinterpret_cast<const i32x4*>(
+                        st + Cfg::SA_OFF + 4 * (wm * Cfg::WTM + 64 * (i / 4) + 4 * r16));
+                    ea[i] = (v.x >> sh) & 0xFF; ea[i + 1] = (v.y >> sh) & 0xFF;
+                    ea[i + 2] = (v.z >> sh) & 0xFF; ea[i + 3] = (v.w >> sh) & 0xFF;
+                }
+#pragma unroll
+                for (int j = 0; j < SN; ++j)
+                    eb[j] = (*reinterpret_cast<const int*>(
+                                 st + Cfg::SB_OFF + 4 * (wn * Cfg::WTN + 16 * j + r16)) >> sh) & 0xFF;
+            } else {
+#pragma unroll
+                for (int i = 0; i < SM; i += 4) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(
+                        st + Cfg::SA_OFF + 4 * (wm * Cfg::WTM + 64 * (i / 4) + 4 * r16));
+                    sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
+                }
+#pragma unroll
+                for (int j = 0; j < SN; ++j)
+                    sb[j] = *reinterpret_cast<const f32x4*>(
+                        st + Cfg::SB_OFF + 4 * (wn * Cfg::WTN + 16 * j + 4 * (lane >> 4)));
+            }
             // fragment of 16 columns (tile columns 16 c .. 16 c + 15) of A or B
             auto k_frag = [&](const uint8_t* tile, int c) {
                 const i32x4 lo = *reinterpret_cast<const i32x4*>(tile + c * 16 * kKBlk + k_lo);
@@ -359,26 +383,38 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
             for (int i = 0; i < SM; ++i) {
                 i32x8 anext;
                 if (i + 1 < SM) anext = a_frag((wm * Cfg::WTM) / 16 + i + 1);
+                if constexpr (UE8M0) {
 #pragma unroll
-                for (int j = 0; j < SN; ++j) {
-                    const int t = SN * i + j;
-                    pbuf[t % 3] = mfma_e4m3_block(bfrag[j], afrag);
-                    if (t >= 2) promote(pbuf[(t - 2) % 3], (t - 2) / SN, (t - 2) % SN);
-                }
-                if (i + 1 < SM) afrag = anext;
-                // Issue order: the next A fragment's reads, then each block
-                // product followed by the promotion of the product two back.
-                __builtin_amdgcn_sched_group_barrier(0x100, A_MK ? 2 : 4, 0);   // the A fragment's DS reads
+                    for (int j = 0; j < SN; ++j) {
+                        acc[i][j] = mfma_e4m3_block_ue8m0(bfrag[j], afrag, acc[i][j], eb[j], ea[i]);
+                        asm volatile("" : "+v"(acc[i][j]));   // keeps the product in place
+                    }
+                    if (i + 1 < SM) afrag = anext;
+                    __builtin_amdgcn_sched_barrier(0);
+                } else {
 #pragma unroll
-                for (int j = 0; j < SN; ++j) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
+                    for (int j = 0; j < SN; ++j) {
+                        const int t = SN * i + j;
+                        pbuf[t % 3] = mfma_e4m3_block(bfrag[j], afrag);
+                        if (t >= 2) promote(pbuf[(t - 2) % 3], (t - 2) / SN, (t - 2) % SN);
+                    }
+                    if (i + 1 < SM) afrag = anext;
+                    // Issue order: the next A fragment's reads, then each block
+                    // product followed by the promotion of the product two back.
+                    __builtin_amdgcn_sched_group_barrier(0x100, A_MK ? 2 : 4, 0);   // the A fragment's DS reads
+#pragma unroll
+                    for (int j = 0; j < SN; ++j) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
-            constexpr int T = SM * SN;
-            promote(pbuf[(T - 2) % 3], (T - 2) / SN, (T - 2) % SN);
-            promote(pbuf[(T - 1) % 3], (T - 1) / SN, (T - 1) % SN);
+            if constexpr (!UE8M0) {
+                constexpr int T = SM * SN;
+                promote(pbuf[(T - 2) % 3], (T - 2) / SN, (T - 2) % SN);
+                promote(pbuf[(T - 1) % 3], (T - 1) / SN, (T - 1) % SN);
+            }
         }
         // every wave is past its last LDS read before the next tile's copies
         lds_barrier();
@@ -435,7 +471,7 @@ namespace {
 
 using TnCfg256 = TnCfg<256, 256, 2, 4, 2>;
 
-template <class Cfg, bool A_MK, bool B_NK, bool OUT_F32, bool GROUPED_M>
+template <class Cfg, bool A_MK, bool B_NK, bool OUT_F32, bool GROUPED_M, bool UE8M0 = false>
 hipError_t launch_tn_cfg(const TnProblem& pr, int cu_cap, hipStream_t stream) {
     TnArgs a;
     a.a = pr.a; a.sfa = pr.sfa; a.b = pr.b; a.sfb = pr.sfb; a.c = pr.c; a.d = pr.d;
@@ -451,15 +487,18 @@ hipError_t launch_tn_cfg(const TnProblem& pr, int cu_cap, hipStream_t stream) {
     if (tiles <= 0) return hipSuccess;
     a.num_tiles = (int)tiles;
     if (pr.form == kKGrouped) {
-        int32_t start = 0;
+        int32_t start = 0, words = 0;
         for (int g = 0; g < a.G; ++g) {
             a.kb_start[g] = start;
             a.kb_count[g] = pr.k_sizes_host[g] / kKBlk;
+            a.kw_start[g] = words;
             start += a.kb_count[g];
+            words += (a.kb_count[g] + 3) / 4;
         }
     } else {
         a.kb_start[0] = 0;
         a.kb_count[0] = (int32_t)(pr.K_tot / kKBlk);
+        a.kw_start[0] = 0;
     }
     const int n_order = pr.form == kKGrouped ? (int)groups : 1;
     // Longest-processing-time order: groups with the most K blocks first.
@@ -471,7 +510,7 @@ hipError_t launch_tn_cfg(const TnProblem& pr, int cu_cap, hipStream_t stream) {
     if (occupancy < 0) {
         int occ = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &occ, reinterpret_cast<const void*>(&tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M>),
+                &occ, reinterpret_cast<const void*>(&tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M, UE8M0>),
                 Cfg::THREADS, 0) !=
                 hipSuccess ||
             occ < 1)
@@ -480,7 +519,7 @@ hipError_t launch_tn_cfg(const TnProblem& pr, int cu_cap, hipStream_t stream) {
     }
     const int64_t resident = (int64_t)cu_cap * occupancy;
     const int grid = (int)(tiles < resident ? tiles : resident);
-    hipLaunchKernelGGL((tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M>), dim3(grid),
+    hipLaunchKernelGGL((tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M, UE8M0>), dim3(grid),
                        dim3(Cfg::THREADS), 0, stream, a);
     return hipGetLastError();
 }
@@ -496,7 +535,8 @@ hipError_t launch_dense_layout(const TnProblem& pr, int cu_cap, hipStream_t stre
 hipError_t launch_tn(const TnProblem& pr, int cu_cap, hipStream_t stream) {
     switch (pr.form) {
     case kKGrouped:
-        return launch_tn_cfg<TnCfg256, false, false, true, false>(pr, cu_cap, stream);
+        return pr.ue8m0 ? launch_tn_cfg<TnCfg256, false, false, true, false, true>(pr, cu_cap, stream)
+                        : launch_tn_cfg<TnCfg256, false, false, true, false>(pr, cu_cap, stream);
     case kMGroupedNN:
         return launch_tn_cfg<TnCfg256, true, false, false, true>(pr, cu_cap, stream);
     case kDenseLayout:
@@ -509,7 +549,7 @@ hipError_t launch_tn(const TnProblem& pr, int cu_cap, hipStream_t stream) {
 }
 
 const char* tn_config_name(const TnProblem& pr) {
-    if (pr.form == kKGrouped) return "tn_kgrouped_f32_256x256";
+    if (pr.form == kKGrouped) return pr.ue8m0 ? "tn_kgrouped_f32_ue8m0_256x256" : "tn_kgrouped_f32_256x256";
     if (pr.form == kMGroupedNN) return "nn_contiguous_bf16_256x256";
     static thread_local char buf[64];
     snprintf(buf, sizeof buf, "%s_dense_%s_256x256",

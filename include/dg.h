@@ -305,6 +305,32 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t* a, const int32_t*
                                                 void* stream);
 
 /*
+ * K-grouped TN form with packed UE8M0 scales.  Reading of the K-grouped
+ * packed layout (DeepGEMM Documentation, section 10, lists a packing utility
+ * for the K-grouped GEMM): each group's K blocks are packed on their own, so
+ * every group starts on a word boundary.  Group g's KB_g = k_sizes_host[g] / 128
+ * blocks take ceil(KB_g / 4) word rows, after the previous groups' rows; byte
+ * i of word row w_g + k4 holds the exponent of the group's block 4 k4 + i.
+ *   sfa [W, M] int32, sfb [W, N] int32, W = sum_g ceil(KB_g / 4)
+ * Everything else (layouts, C, rules, errors) is dg_k_grouped_fp8_gemm_tn_contiguous's.
+ * The exponents go into the block-scaled MFMA; there is no promotion step.
+ */
+dg_status dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0(const uint8_t* a, const int32_t* sfa,
+                                                    const uint8_t* b, const int32_t* sfb,
+                                                    const int32_t* k_sizes_host,
+                                                    const float* c, float* d,
+                                                    int64_t G, int64_t M, int64_t N, int64_t K_tot,
+                                                    void* stream);
+/* fp32 power-of-two scales sf [K_tot/128, MN] (MN-major, per column per K
+ * block) -> the per-group packed words above, [W, MN] int32.  Byte i of a word
+ * is the fp32 exponent field (the UE8M0 code of a positive power of two in
+ * [2^-126, 2^127]); unused bytes are 0.  Rules as the K-grouped GEMM's for
+ * k_sizes_host; sf and packed 4-byte aligned, not overlapping. */
+dg_status dg_pack_ue8m0_scales_k_grouped(const float* sf, const int32_t* k_sizes_host,
+                                         int32_t* packed, int64_t G, int64_t MN, int64_t K_tot,
+                                         void* stream);
+
+/*
  * fp32 power-of-two scales -> packed UE8M0 words (layout above), G batches:
  *   per_block == 0: sf [G, K/128, MN] fp32, one scale per (row, K block),
  *                   MN-major (the sfa layout, e.g. from dg_per_token_cast_to_fp8

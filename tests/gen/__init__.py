@@ -90,7 +90,7 @@ def quantize_blocks(w: np.ndarray | torch.Tensor, pow2: bool = False):
     return codes.numpy(), scale.contiguous().numpy()
 
 
-def quantize_cols(x: np.ndarray | torch.Tensor):
+def quantize_cols(x: np.ndarray | torch.Tensor, pow2: bool = False):
     """Per-column, per-128-row-block quantisation of an MN-major operand [Kt, C].
 
     Used by the K-grouped TN form: A is [K_total, M], B is [K_total, N].
@@ -101,7 +101,7 @@ def quantize_cols(x: np.ndarray | torch.Tensor):
     assert Kt % BLOCK == 0
     KB = Kt // BLOCK
     xb = xt.reshape(KB, BLOCK, C)
-    scale = _safe_scale(xb.abs().amax(dim=1))             # [KB, C]
+    scale = _safe_scale(xb.abs().amax(dim=1), pow2)       # [KB, C]
     codes = _cast_e4m3(xb / scale[:, None, :]).reshape(Kt, C)
     return codes.numpy(), scale.contiguous().numpy()
 
@@ -354,7 +354,7 @@ def to_ue8m0(sfa: np.ndarray, sfb: np.ndarray, N: int):
 def gen_k_grouped(G: int = 32, M: int = 2048, N: int = 4096, K_tot: int = 49152,
                   seed: int = 0, k_sizes: Optional[np.ndarray] = None,
                   c_std: float = 0.01, with_c: bool = True,
-                  zipf_s: float = 1.1) -> KGroupedInputs:
+                  zipf_s: float = 1.1, pow2: bool = False) -> KGroupedInputs:
     """Per-group K = 128 * multinomial(K_tot/128, Zipf(1.1)); inside a group of
     K_g > 0 the first K_g - U{0..127} tokens are N(0,1), the tail is zero (the
     padding).  C ~ N(0, c_std) fp32 [G, M, N]."""
@@ -373,9 +373,9 @@ def gen_k_grouped(G: int = 32, M: int = 2048, N: int = 4096, K_tot: int = 49152,
         a32[off + valid[g]: off + k_sizes[g]] = 0
         b32[off + valid[g]: off + k_sizes[g]] = 0
         off += int(k_sizes[g])
-    a, sfa = quantize_cols(a32)
+    a, sfa = quantize_cols(a32, pow2)
     del a32
-    b, sfb = quantize_cols(b32)
+    b, sfb = quantize_cols(b32, pow2)
     del b32
     c = _normal(rng, (G, M, N), c_std) if with_c else None
     return KGroupedInputs(a, sfa, b, sfb, k_sizes.astype(np.int32), valid, c,
@@ -557,3 +557,17 @@ def gen_mqa(S: int, S_kv: int, H: int = 64, D: int = 128, seed: int = 0,
     ks, ke = causal_ranges([S] if seq_lens is None else seq_lens, S_kv)
     return MqaInputs(q, kvc, np.ascontiguousarray(sf.reshape(-1)[:S_kv]) if D == BLOCK
                      else None, w, ks, ke, S, S_kv, H, D)
+
+
+def k_grouped_ue8m0_words(sf: np.ndarray, k_sizes) -> np.ndarray:
+    """Power-of-two fp32 scales [K_tot/128, MN] of a K-grouped operand ->
+    packed UE8M0 words, each group's blocks on their own ceil(KB_g / 4) rows."""
+    e = exponent_bytes(sf)
+    parts, kb = [], 0
+    for k in k_sizes:
+        nkb = int(k) // BLOCK
+        if nkb:
+            parts.append(ue8m0_words(e[kb:kb + nkb]))
+        kb += nkb
+    MN = sf.shape[1]
+    return np.concatenate(parts) if parts else np.zeros((0, MN), np.int32)

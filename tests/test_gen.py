@@ -145,3 +145,12 @@ def test_gen_dense_ue8m0_layout():
     assert x.sfb.shape == (2, 300)
     assert np.array_equal(x.sfa, oracle.pack_ue8m0(x.sfa_f32, False, 64, 640))
     assert np.array_equal(x.sfb, oracle.pack_ue8m0(x.sfb_f32, True, 300, 640))
+
+
+def test_k_grouped_ue8m0_words_match_the_oracle_packer():
+    import oracle
+    x = gen.gen_k_grouped(G=4, M=32, N=48, K_tot=1280, k_sizes=np.array([640, 0, 128, 512]),
+                          seed=2, pow2=True)
+    for sf in (x.sfa, x.sfb):
+        assert np.array_equal(gen.k_grouped_ue8m0_words(sf, x.k_sizes),
+                              oracle.pack_ue8m0_k_grouped(sf, x.k_sizes))

@@ -382,3 +382,86 @@ def test_graph_capture_replays_masked_ue8m0():
             if c < M_max:
                 assert d.untouched((gi, slice(c, None))), f"replay {rep} group {gi}"
         assert d.intact()
+
+
+# ------------------------------------------------------------------------------
+# K-grouped TN with per-group packed words
+# ------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k_sizes,MN", [([640, 0, 128, 1152], 300), ([128] * 9, 64),
+                                        ([0, 2048], 4096)])
+def test_pack_ue8m0_k_grouped_bit_exact(k_sizes, MN):
+    announce(f"pack_ue8m0 k-grouped k_sizes={k_sizes} MN={MN}")
+    rng = np.random.default_rng(MN)
+    KB = sum(k_sizes) // 128
+    sf = gen.pow2_scales(rng.integers(1, 255, size=(KB, MN)))
+    got = dg.pack_ue8m0_scales_k_grouped(dev(sf), k_sizes).cpu().numpy()
+    assert np.array_equal(got, oracle.pack_ue8m0_k_grouped(sf, np.array(k_sizes, np.int32)))
+
+
+def run_kg(x, wa, wb, c=None, in_place=False):
+    d = Guarded((x.G, x.M, x.N), torch.float32)
+    cc = None
+    if c is not None:
+        if in_place:
+            d.view.copy_(dev(c))
+            cc = d.view
+        else:
+            cc = dev(c)
+    dg.k_grouped_fp8_gemm_tn_contiguous((dev(x.a), dev(wa)), (dev(x.b), dev(wb)), d.view,
+                                        x.k_sizes, c=cc)
+    torch.cuda.synchronize()
+    assert d.intact()
+    return to64(d.view)
+
+
+@pytest.mark.parametrize("with_c,in_place", [(True, False), (False, False), (True, True)])
+def test_k_grouped_ue8m0_small(with_c, in_place):
+    announce(f"k-grouped ue8m0 small c={with_c} in_place={in_place}")
+    ks = np.array([384, 0, 640, 128, 1152], np.int32)
+    x = gen.gen_k_grouped(G=5, M=272, N=528, K_tot=int(ks.sum()), k_sizes=ks, seed=61,
+                          with_c=with_c, pow2=True)
+    wa, wb = gen.k_grouped_ue8m0_words(x.sfa, ks), gen.k_grouped_ue8m0_words(x.sfb, ks)
+    got = run_kg(x, wa, wb, c=x.c, in_place=in_place)
+    ref = oracle.k_grouped_tn_ue8m0(x.a, wa, x.b, wb, ks, x.c)
+    check_close(got, ref, "k-grouped ue8m0")
+    want_empty = x.c[1] if with_c else np.zeros((x.M, x.N))
+    assert np.array_equal(got[1], want_empty.astype(np.float64))   # K_g = 0: D = C
+
+
+def test_k_grouped_ue8m0_all_ones_bit_exact():
+    """A = B = 1.0 with per-column exponents in 124 .. 130: every partial sum
+    is a multiple of 2 below 2^19, exact in fp32."""
+    announce("k-grouped ue8m0 all-ones bit-exact")
+    ks = np.array([640, 128, 0, 1280], np.int32)
+    M, N = 144, 272
+    K_tot = int(ks.sum())
+    rng = np.random.default_rng(62)
+    ea = rng.integers(124, 131, size=(K_tot // 128, M))
+    eb = rng.integers(124, 131, size=(K_tot // 128, N))
+    x = gen.KGroupedInputs(np.full((K_tot, M), 0x38, np.uint8), gen.pow2_scales(ea),
+                           np.full((K_tot, N), 0x38, np.uint8), gen.pow2_scales(eb), ks,
+                           ks.astype(np.int64), None, len(ks), M, N, K_tot)
+    wa, wb = gen.k_grouped_ue8m0_words(x.sfa, ks), gen.k_grouped_ue8m0_words(x.sfb, ks)
+    got = run_kg(x, wa, wb)
+    kb = 0
+    for g, k in enumerate(ks):
+        nkb = int(k) // 128
+        want = 128.0 * (np.exp2(ea[kb:kb + nkb] - 127.0).T @ np.exp2(eb[kb:kb + nkb] - 127.0))
+        assert np.array_equal(got[g], want), g
+        kb += nkb
+
+
+def test_k_grouped_ue8m0_c5_sampled():
+    """The MoE weight-gradient workload (32 groups, M = 2048, N = 4096, Zipf K
+    split of 49152, fp32 C) with power-of-two scales: sampled rows."""
+    announce("k-grouped ue8m0 C5 full size, sampled rows")
+    x = gen.gen_k_grouped(seed=0, pow2=True)
+    wa, wb = gen.k_grouped_ue8m0_words(x.sfa, x.k_sizes), gen.k_grouped_ue8m0_words(x.sfb, x.k_sizes)
+    got = run_kg(x, wa, wb, c=x.c)
+    rng = np.random.default_rng(5)
+    groups = np.array([int(np.argmax(x.k_sizes)), int(np.argmin(x.k_sizes))] +
+                      rng.integers(0, x.G, 3).tolist(), np.int64)
+    rows = rng.integers(0, x.M, len(groups)).astype(np.int64)
+    ref = oracle.k_grouped_tn_ue8m0(x.a, wa, x.b, wb, x.k_sizes, x.c, groups=groups, rows=rows)
+    check_close(got[groups, rows], ref, "C5 ue8m0")

@@ -45,8 +45,10 @@ MUTANTS = {
     "tn_sfb_row_only": ("(double)sfb[kb * N + n];", "(double)sfb[kb * N];"),
     "tn_group_start": ("for (int64_t kb = k0 / KBLK; kb < k1 / KBLK; ++kb) {",
                        "for (int64_t kb = 0; kb < k1 / KBLK; ++kb) {"),
-    "tn_c_dropped": ("out[i * N + n] = acc + (c ? (double)c[(g * M + m) * N + n] : 0.0);",
-                     "out[i * N + n] = acc;"),
+    "tn_c_dropped": ("acc += s * p;\n            }\n            out[i * N + n] = acc + (c ? (double)c[(g * M + m) * N + n] : 0.0);",
+                     "acc += s * p;\n            }\n            out[i * N + n] = acc;"),
+    "kgu_c_dropped": ("ue8m0_scale(sfb + (w0 + j / 4) * N, N, n, j % 4) * p;\n            }\n            out[i * N + n] = acc + (c ? (double)c[(g * M + m) * N + n] : 0.0);",
+                      "ue8m0_scale(sfb + (w0 + j / 4) * N, N, n, j % 4) * p;\n            }\n            out[i * N + n] = acc;"),
     # FP8 casting
     "cast_fnuz_max": ("float s = amax / 448.0f;", "float s = amax / 240.0f;"),
     "cast_ties_away": ("code = (lo % 2 == 0) ? lo : hi;", "code = hi;"),
@@ -63,7 +65,9 @@ MUTANTS = {
     "ue8m0_byte_order": ("const int e = (int)((w >> (8 * (kb % 4))) & 0xFF);",
                          "const int e = (int)((w >> (8 * (3 - kb % 4))) & 0xFF);"),
     "ue8m0_b_per_block": ("ue8m0_scale(sfb, N, n, kb)", "ue8m0_scale(sfb, N, (n / KBLK) * KBLK, kb)"),
-    "ue8m0_pack_offset": ("const int e = x - 1 + 127;", "const int e = x + 127;"),
+    "ue8m0_pack_offset": ("const int e = x - 1 + 127;                /* s = 2^(x-1)",
+                          "const int e = x + 127;                /* s = 2^(x-1)"),
+    "kgu_pack_offset": ("const int e = x - 1 + 127;\n                    if", "const int e = x + 127;\n                    if"),
     "ue8m0_pack_broadcast": ("sf[(mn / KBLK) * KB + kb]", "sf[kb]"),
     "layout_a_ignores_storage": ("const uint8_t av = a_stored_mk ? a[m * K + k] : a[k * M + m];",
                                  "const uint8_t av = a[m * K + k];"),
