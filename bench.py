@@ -493,7 +493,7 @@ def median_ms(stream, fn, n):
 def bench_ue8m0(dg, gen, up, dev, stream, args):
     """The same workloads with power-of-two scales packed as UE8M0 words (the
     MFMA applies the scales; no separate promotion): the dense sweep shape by
-    shape, and the contiguous and masked MoE workloads."""
+    shape, and the contiguous, masked and K-grouped MoE workloads."""
     import torch
     reps = max(3, min(args.steps, 10))
     dense, t_sum, f_sum = [], 0.0, 0.0
@@ -540,6 +540,21 @@ def bench_ue8m0(dg, gen, up, dev, stream, args):
                                          gbs=round(byts / ms / 1e6, 1),
                                          frac_hbm=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
     del a, sa, b, sb, mm, d, x, wa, wb
+    torch.cuda.empty_cache()
+
+    x = gen.gen_k_grouped(seed=0, pow2=True)
+    wa, wb = gen.k_grouped_ue8m0_words(x.sfa, x.k_sizes), gen.k_grouped_ue8m0_words(x.sfb, x.k_sizes)
+    a, sa, b, sb, c = up(x.a), up(wa), up(x.b), up(wb), up(x.c)
+    d = torch.empty(x.G, x.M, x.N, dtype=torch.float32, device=dev)
+    ks = x.k_sizes
+    ms = median_ms(stream, lambda: dg.k_grouped_fp8_gemm_tn_contiguous((a, sa), (b, sb), d, ks, c=c),
+                   reps)
+    flop = 2.0 * x.M * x.N * x.K_tot
+    byts = x.a.nbytes + wa.nbytes + x.b.nbytes + wb.nbytes + 2 * 4 * x.G * x.M * x.N
+    out["k_grouped_32x2048x4096"] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
+                                        gbs=round(byts / ms / 1e6, 1),
+                                        frac_hbm=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
+    del a, sa, b, sb, c, d, x, wa, wb
     torch.cuda.empty_cache()
     return out
 

@@ -467,7 +467,11 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
             // the last two of a block are promoted under the next block's first
             // two, with the scale of the block they came from.
             constexpr int T = SM * SN;
-            static_assert(T % 2 == 0, "the product ring alternates between two slots");
+            // products are promoted R products later (four when the block's
+            // product count allows: with so few products per block, two steps do
+            // not cover the MFMA's result latency)
+            constexpr int R = (T % 4 == 0) ? 4 : 2;
+            static_assert(T % R == 0, "the product ring divides the block");
             struct Ops {
                 i32x8 a[SM];
                 i32x8 b[SN];
@@ -487,8 +491,13 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
             Ops cur, nxt;
             read_ops(smem, kb_lo, cur);
             // nothing is pending before block 0: zero products with zero scale
-            f32x4 ring[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-            float ring_s[2] = {0.f, 0.f};
+            f32x4 ring[R];
+            float ring_s[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                ring[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+                ring_s[r] = 0.f;
+            }
             int stage = 0;   // stage holding block it
             for (int it = 0; it < nkb; ++it) {
                 const int next = stage + 1 == Cfg::STAGES ? 0 : stage + 1;
@@ -513,10 +522,10 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                         __builtin_amdgcn_s_setprio(1);
                         const f32x4 pr = mfma_e4m3_block(cur.b[j], cur.a[i]);
                         __builtin_amdgcn_s_setprio(0);
-                        const int tp = t >= 2 ? t - 2 : T + t - 2;   // tile of the pending product
-                        promote1(tp / SN, tp % SN, ring[t & 1], ring_s[t & 1]);
-                        ring[t & 1] = pr;
-                        ring_s[t & 1] = cur.sa[i] * cur.sb;
+                        const int tp = t >= R ? t - R : T + t - R;   // tile of the pending product
+                        promote1(tp / SN, tp % SN, ring[t % R], ring_s[t % R]);
+                        ring[t % R] = pr;
+                        ring_s[t % R] = cur.sa[i] * cur.sb;
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -524,8 +533,10 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 stage = next;
             }
             if constexpr (!UE8M0) {
-                promote1((T - 2) / SN, (T - 2) % SN, ring[0], ring_s[0]);
-                promote1((T - 1) / SN, (T - 1) % SN, ring[1], ring_s[1]);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    promote1((T - R + r) / SN, (T - R + r) % SN, ring[(T - R + r) % R],
+                             ring_s[(T - R + r) % R]);
             }
         } else {
             // Row pipeline.  Products t = i * SN + j run row by row; A fragment
