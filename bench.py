@@ -381,35 +381,79 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, bench_json, out_path, co
     print(out_path)
 
 
+DETAIL_SUMMARIES = {
+    # file -> (title, kernel-name filter, bench detail key, template-argument note)
+    "grouped_moe__contiguous_masked_kgrouped.md": (
+        "Grouped MoE workloads (contiguous, masked, K-grouped), fp32 scales",
+        lambda k: ("nt_fp8_kernel" in k and (", 1, false, false>" in k or ", 2, false, false>" in k))
+        or ("tn_fp8_kernel" in k and "false, false, true, false, false>" in k),
+        "grouped",
+        "`nt_fp8_kernel<Cfg, FORM, OUT_F32, UE8M0>`: FORM 1 = contiguous, 2 = masked. "
+        "`tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M, UE8M0>` with "
+        "`false, false, true, false, false` = the K-grouped form."),
+    "ue8m0__dense_sweep_contiguous_masked_kgrouped.md": (
+        "Packed UE8M0 scales (block-scaled MFMA): dense sweep, contiguous, masked, K-grouped",
+        lambda k: ("nt_fp8_kernel" in k and "true>(dg::NtArgs" in k)
+        or ("tn_fp8_kernel" in k and "false, false, true, false, true>" in k)
+        or "pack_ue8m0" in k,
+        "ue8m0",
+        "Last template argument `true` = UE8M0 instance."),
+    "mn_major_layouts__nn_tn_tt_4096x4096x7168_and_nn_contiguous.md": (
+        "NN / TN / TT layouts and the M-grouped contiguous NN form (MN-major kernel)",
+        lambda k: "tn_fp8_kernel" in k and not ("false, false, true, false" in k),
+        "layouts",
+        "`tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M, UE8M0>`: A_MK = A stored [M, K], "
+        "B_NK = B stored [N, K], GROUPED_M = contiguous NN."),
+    "mqa_logits__causal_prefill_4096x4096_h64.md": (
+        "FP8 MQA logits, 64 heads, causal 4096 x 4096 and 8 packed sequences of 512",
+        lambda k: "mqa_logits_kernel" in k,
+        "mqa_logits",
+        "`mqa_logits_kernel<H>`, H = heads."),
+}
+
+
 def summarize_grouped(trace_dir, bench_json, out_path):
-    """profiles/ summary of the grouped MoE workloads (contiguous, masked,
-    K-grouped): rocprofv3 per-kernel averages next to bench.py's own
-    HIP-event timings of the same run."""
+    """profiles/ summaries of the bench detail workloads: for each kernel
+    family, the rocprofv3 per-kernel averages next to bench.py's own HIP-event
+    timings of the same run.  out_path names the grouped-MoE file; the other
+    families are written beside it."""
     import csv
     res = json.load(open(bench_json))
-    grouped = res["detail"]["grouped"]
     stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
-    lines = ["# Grouped MoE workloads (contiguous, masked, K-grouped) -- rocprofv3 kernel trace", "",
-             "Commands (run from the repository root on one MI355X):", ""]
-    lines += [f"    {c}" for c in GROUPED_PROFILE_COMMANDS]
-    lines += ["", "One bench.py run times the dense sweep and then each grouped workload (detail);",
-              "the trace below covers all of them.  Grouped kernels: form 1 = contiguous,",
-              "form 2 = masked (second template argument), `tn_fp8_kernel` = K-grouped.", "",
-              "## Kernel trace (--kernel-trace --stats)", "",
-              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
-    for r in stats:
-        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    lines += ["", "## bench.py HIP-event timings of the grouped workloads (same run)", "",
-              "| workload | us | TFLOP/s | GB/s (algorithmic) | fraction of roof |", "|---|---|---|---|---|"]
-    for name, v in grouped.items():
-        frac = v.get("frac_mfma", v.get("frac_hbm"))
-        roof = "MFMA" if "frac_mfma" in v else "HBM"
-        lines.append(f"| {name} | {v['us']} | {v['tflops']} | {v['gbs']} | {frac} ({roof}) |")
-    lines += ["", f"    kernel_source_sha256_16: nt {source_hash('nt')}, tn {source_hash('tn')}", ""]
-    with open(out_path, "w") as f:
-        f.write("\n".join(lines))
-    print(out_path)
+    out_dir = os.path.dirname(out_path) or "."
+    for fname, (title, match, key, note) in DETAIL_SUMMARIES.items():
+        detail = res["detail"].get(key, {})
+        lines = [f"# {title} -- rocprofv3 kernel trace", "",
+                 "Commands (run from the repository root on one MI355X):", ""]
+        lines += [f"    {c}" for c in GROUPED_PROFILE_COMMANDS]
+        lines += ["", "One bench.py run times the dense sweep and then every detail workload; the",
+                  "rows below are this family's kernels from that run's trace.", "", note, "",
+                  "## Kernel trace (--kernel-trace --stats)", "",
+                  "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for r in stats:
+            if match(r["Name"]):
+                lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                             f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+        lines += ["", "## bench.py HIP-event timings (same run)", "",
+                  "| workload | us | TFLOP/s | fraction of roof |", "|---|---|---|---|"]
+        items = list(detail.items()) if isinstance(detail, dict) else []
+        for name, v in items:
+            if name == "dense" and isinstance(v, list):
+                for dd in v:
+                    lines.append(f"| dense {dd['M']}x{dd['N']}x{dd['K']} | {dd['us']} | {dd['tflops']} | |")
+                continue
+            if not isinstance(v, dict):
+                lines.append(f"| {name} | {v} | | |")
+                continue
+            frac = v.get("frac_mfma", v.get("frac_hbm", ""))
+            roof = "MFMA" if "frac_mfma" in v else ("HBM" if "frac_hbm" in v else "")
+            lines.append(f"| {name} | {v.get('us')} | {v.get('tflops')} | {frac} {roof} |")
+        lines += ["", f"    kernel_source_sha256_16: nt {source_hash('nt')}, tn {source_hash('tn')}, "
+                      f"cast {source_hash('cast')}", ""]
+        path = os.path.join(out_dir, fname)
+        with open(path, "w") as f:
+            f.write("\n".join(lines))
+        print(path)
 
 
 def bench_grouped(dg, gen, up, dev, stream, args):
