@@ -540,21 +540,47 @@ def bench_ue8m0(dg, gen, up, dev, stream, args):
     shape, and the contiguous, masked and K-grouped MoE workloads."""
     import torch
     reps = max(3, min(args.steps, 10))
-    dense, t_sum, f_sum = [], 0.0, 0.0
+    # the dense sweep, timed like the fp32 sweep: whole-sweep steps without
+    # events, and per-shape medians from sweeps with an event pair per launch
+    ops = []
     for (M, N, K) in gen.DENSE_SWEEP:
         x = gen.gen_dense_ue8m0(M, N, K, seed=0)
-        a, sa, b, sb = up(x.a), up(x.sfa), up(x.b), up(x.sfb)
-        d = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        ms = median_ms(stream, lambda: dg.fp8_gemm_nt((a, sa), (b, sb), d), reps)
+        ops.append(((M, N, K), (up(x.a), up(x.sfa)), (up(x.b), up(x.sfb)),
+                    torch.empty(M, N, dtype=torch.bfloat16, device=dev)))
+        del x
+
+    def sweep(evs=None):
+        for i, (_, a, b, d) in enumerate(ops):
+            if evs is not None:
+                evs[i][0].record(stream)
+            dg.fp8_gemm_nt(a, b, d)
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(3):
+        sweep()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        sweep()
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / reps
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in ops] for _ in range(3)]
+    for e in evs:
+        sweep(e)
+    torch.cuda.synchronize()
+    per = np.median([[e[i][0].elapsed_time(e[i][1]) for i in range(len(ops))] for e in evs], axis=0)
+    dense, f_sum = [], 0.0
+    for ((M, N, K), _, _, _), ms in zip(ops, per):
         flop = 2.0 * M * N * K
         byts = M * K + N * K + 4 * ((K // 128 + 3) // 4) * (M + N) + 2 * M * N
         dense.append(dict(M=M, N=N, K=K, us=round(ms * 1e3, 2), tflops=round(flop / ms / 1e9, 1),
                           gbs=round(byts / ms / 1e6, 1)))
-        t_sum += ms
         f_sum += flop
-        del x, a, sa, b, sb, d
-    out = {"dense": dense,
-           "dense_sweep_sum_of_medians_tflops": round(f_sum / t_sum / 1e9, 1)}
+    out = {"dense": dense, "dense_sweep_step_ms": round(step_ms, 4),
+           "dense_sweep_tflops": round(f_sum / step_ms / 1e9, 1)}
+    del ops
     torch.cuda.empty_cache()
 
     x = gen.gen_contiguous(seed=0, pow2=True)

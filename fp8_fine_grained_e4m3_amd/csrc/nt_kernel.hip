@@ -468,8 +468,7 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
             // two, with the scale of the block they came from.
             constexpr int T = SM * SN;
             // products are promoted R products later (four when the block's
-            // product count allows: with so few products per block, two steps do
-            // not cover the MFMA's result latency)
+            // product count allows; measured the same as two in the sweep)
             constexpr int R = (T % 4 == 0) ? 4 : 2;
             static_assert(T % R == 0, "the product ring divides the block");
             struct Ops {
