@@ -254,3 +254,15 @@ def test_mqa_logits_rejects(lib):
     assert call(ke=NULL) == dg.DG_ERR_INVALID_ARG and "ke is NULL" in err(lib)
     assert call(S=-1) == dg.DG_ERR_INVALID_ARG
     assert call(S=0, q=NULL) == dg.DG_OK and call(S_kv=0, kv=NULL) == dg.DG_OK
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
+    """No fallback: with libdg.so absent, loading raises instead of running
+    anything else."""
+    monkeypatch.setattr(dg, "_lib", None)
+    with pytest.raises(ImportError, match="missing"):
+        dg.load_library(str(tmp_path / "libdg.so"))
+    monkeypatch.setattr(dg, "LIB_PATH", str(tmp_path / "libdg.so"))
+    with pytest.raises(ImportError):
+        dg.load_library()
+
