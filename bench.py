@@ -69,7 +69,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # 30 untimed sweeps by default: the GPU's clocks settle under sustained load
+    # (same box: 3 warmup steps 1649-1653 TFLOP/s, 30 steps 1729-1733, 100 steps
+    # 1720-1752)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
