@@ -51,7 +51,7 @@ GROUPED_PROFILE_COMMANDS = [
 
 PROFILE_COMMANDS = [
     "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o run -- "
-    "python3 bench.py --steps 5 --warmup 1 --no-detail --no-cpu --json-out gpurun_out/bench_prof.json",
+    "python3 bench.py --steps 20 --no-detail --no-cpu --json-out gpurun_out/bench_prof.json",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o run -- "
     "python3 bench.py --steps 1 --warmup 0 --no-detail --no-cpu --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o run -- "
