@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
@@ -68,7 +69,7 @@ struct DeviceInfo {
 };
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mutex;
-int g_cu_cap = 0;   // 0 = use every CU
+std::atomic<int> g_cu_cap{0};   // 0 = use every CU; process-wide, set from any thread
 
 dg_status current_device(int& dev, DeviceInfo& info) {
     hipError_t e = hipGetDevice(&dev);
@@ -94,7 +95,7 @@ dg_status current_device(int& dev, DeviceInfo& info) {
 }
 
 int cu_cap_for(const DeviceInfo& info) {
-    const int cap = g_cu_cap;
+    const int cap = g_cu_cap.load(std::memory_order_relaxed);
     return (cap > 0 && cap < info.cus) ? cap : info.cus;
 }
 
@@ -621,7 +622,7 @@ int dg_get_num_cus(void) {
 
 dg_status dg_set_num_cus(int n) {
     if (n == 0) {
-        g_cu_cap = 0;
+        g_cu_cap.store(0, std::memory_order_relaxed);
         return ok();
     }
     int dev = 0;
@@ -630,7 +631,7 @@ dg_status dg_set_num_cus(int n) {
     if (st != DG_OK) return st;
     if (n < 0 || n > info.cus)
         return fail(DG_ERR_INVALID_ARG, "num_cus=%d must be in [1, %d] (or 0 for all)", n, info.cus);
-    g_cu_cap = n;
+    g_cu_cap.store(n, std::memory_order_relaxed);
     return ok();
 }
 
