@@ -212,6 +212,8 @@ dg_status gemm_nt(const uint8_t* a, const void* sfa_, const uint8_t* b, const vo
     REQUIRE(M <= kOffsetLimit / (K > 0 ? K : 1) && N <= kOffsetLimit / (K > 0 ? K : 1),
             "M*K and N*K must stay below 2^31");
     REQUIRE(M <= INT_MAX && N <= INT_MAX, "size too large");
+    // work units: 64 x 64 tiles (the smallest) times up to 8 K splits
+    REQUIRE(((M + 63) / 64) * ((N + 63) / 64) <= INT_MAX / 8, "too many tiles");
     const int64_t dbytes = M * N * (d_dtype == DG_F32 ? 4 : 2);
     REQUIRE(alias_ok(c, d, dbytes), "c overlaps d without being equal to it");
     dg::NtProblem p{};
@@ -271,7 +273,8 @@ dg_status gemm_nt_masked(const uint8_t* a, const void* sfa_, const uint8_t* b, c
     REQUIRE_PTR(masked_m, 4);
     REQUIRE(M_max <= kOffsetLimit / (K > 0 ? K : 1) && N <= kOffsetLimit / (K > 0 ? K : 1),
             "M_max*K and N*K must stay below 2^31");
-    REQUIRE(G * ((M_max + 63) / 64) * ((N + 127) / 128) <= INT_MAX, "too many tiles");
+    // bound for the smallest tile (64 x 64) any configuration uses
+    REQUIRE(G * ((M_max + 63) / 64) * ((N + 63) / 64) <= INT_MAX, "too many tiles");
     dg::NtProblem p{};
     p.form = dg::kMasked;
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.c = nullptr; p.d = d;
