@@ -167,8 +167,10 @@ def main():
     for s_ in range(probe_steps):
         step(ev[s_])
     torch.cuda.synchronize()
-    avg_ms = np.array([[ev[s_][i][0].elapsed_time(ev[s_][i][1]) for i in range(len(ops))]
-                       for s_ in range(probe_steps)]).mean(axis=0)
+    # median over the sweeps: the first launches after the warmup's synchronize
+    # can run on clocks that have not yet come back up
+    avg_ms = np.median([[ev[s_][i][0].elapsed_time(ev[s_][i][1]) for i in range(len(ops))]
+                        for s_ in range(probe_steps)], axis=0)
     groups = {}
     for i, op in enumerate(ops):
         groups.setdefault(op["kernel"], []).append(i)
