@@ -154,3 +154,18 @@ def test_k_grouped_ue8m0_words_match_the_oracle_packer():
     for sf in (x.sfa, x.sfb):
         assert np.array_equal(gen.k_grouped_ue8m0_words(sf, x.k_sizes),
                               oracle.pack_ue8m0_k_grouped(sf, x.k_sizes))
+
+
+def test_gen_dense_sparse_structure():
+    """Zero outside the live rows / blocks, scale 1 there, and the live part
+    quantised (codes within e4m3 range, per-row and per-block scales)."""
+    M, N, K = 300, 400, 256
+    live = [0, 5, 150, 299]
+    x = gen.gen_dense_sparse(M, N, K, live, [1, 3], seed=3)
+    dead_rows = np.setdiff1d(np.arange(M), live)
+    assert not x.a[dead_rows].any() and np.all(x.sfa[:, dead_rows] == 1)
+    assert x.a[live].any(axis=1).all() and np.all(x.sfa[:, live] != 1)
+    assert not x.b[:128].any() and not x.b[256:384].any()
+    assert x.b[128:256].any(axis=1).all() and x.b[384:].any(axis=1).all()
+    assert np.all(x.sfb[[0, 2]] == 1) and np.all(x.sfb[[1, 3]] != 1)
+    assert x.sfa.shape == (K // 128, M) and x.sfb.shape == ((N + 127) // 128, K // 128)

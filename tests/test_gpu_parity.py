@@ -144,6 +144,53 @@ def test_c2_dense_sweep_full_size(idx):
 
 
 # ------------------------------------------------------------------------------
+# maximum sizes: the largest operands the entry point accepts (M*K and N*K just
+# below 2^31, where the kernels' 32-bit offsets inside one matrix end).  The
+# operands are zero outside a few live rows / blocks, so the oracle checks the
+# live outputs and every other output must be exactly zero.
+# ------------------------------------------------------------------------------
+
+MAX_K = 16384
+
+
+@pytest.mark.parametrize("N,tile", [(256, "128x128"), (1024, "256x256")])
+def test_dense_max_rows(N, tile):
+    M, K = (2**31 - 1) // MAX_K, MAX_K               # M = 131071: ragged last M tile
+    announce(f"dense max rows {M}x{N}x{K}")
+    assert dg.kernel_config_name(dg.FORM_DENSE, M, N, K) == f"nt_dense_bf16_{tile}"
+    rng = np.random.default_rng(31)
+    live = np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M),
+                                     rng.choice(M, size=16, replace=False)])).astype(np.int64)
+    x = gen.gen_dense_sparse(M, N, K, live, range(N // 128), seed=31)
+    out = run_dense(x)
+    live_t = torch.from_numpy(live).cuda()
+    ref = oracle.gemm_nt(x.a, x.sfa, x.b, x.sfb, rows=live)
+    print(check_close(to64(out[live_t]), ref, "max rows"))
+    dead = torch.ones(M, dtype=torch.bool, device="cuda")
+    dead[live_t] = False
+    assert int(torch.count_nonzero(out[dead])) == 0
+
+
+@pytest.mark.parametrize("M", [64, 128])
+def test_dense_max_cols(M):
+    K = MAX_K
+    N = ((2**31 - 1) // K) // 16 * 16                 # 131056: ragged last B block
+    NB = (N + 127) // 128
+    announce(f"dense max cols {M}x{N}x{K}")
+    blocks = [0, 517, NB - 1]
+    x = gen.gen_dense_sparse(M, N, K, range(M), blocks, seed=32)
+    out = run_dense(x)
+    cols = np.concatenate([np.arange(128 * b, min(N, 128 * b + 128)) for b in blocks])
+    ref = oracle.gemm_nt(x.a, x.sfa, np.ascontiguousarray(x.b[cols]),
+                         np.ascontiguousarray(x.sfb[blocks]))
+    cols_t = torch.from_numpy(cols).cuda()
+    print(check_close(to64(out[:, cols_t]), ref, "max cols"))
+    dead = torch.ones(N, dtype=torch.bool, device="cuda")
+    dead[cols_t] = False
+    assert int(torch.count_nonzero(out[:, dead])) == 0
+
+
+# ------------------------------------------------------------------------------
 # bit-exact pins on the GPU
 # ------------------------------------------------------------------------------
 
