@@ -601,7 +601,9 @@ dg_status dg_fp8_mqa_logits(const uint8_t* q, const uint8_t* kv, const float* kv
     REQUIRE_PTR(kv_sf, 4);
     REQUIRE_PTR(ks, 4);
     REQUIRE_PTR(ke, 4);
-    REQUIRE(S <= 65535LL * 16 && S_kv <= INT_MAX, "seq_len must be <= 1048560 and seq_len_kv < 2^31");
+    // token indices are 32-bit and run up to one workgroup (256 tokens) past S_kv
+    REQUIRE(S <= 65535LL * 16 && S_kv <= INT_MAX - 4096,
+            "seq_len must be <= 1048560 and seq_len_kv <= 2^31 - 4097");
     dg::MqaProblem p{};
     p.q = q; p.kv = kv; p.kv_sf = kv_sf; p.weights = weights; p.ks = ks; p.ke = ke;
     p.logits = logits; p.S = S; p.S_kv = S_kv; p.H = H; p.clean = clean_logits != 0;

@@ -367,7 +367,7 @@ dg_status dg_pack_ue8m0_scales(const float* sf, int per_block, int32_t* packed, 
  *   ks, ke  [S]        int32 device arrays; each range is clamped to
  *                      [0, S_kv], and ks >= ke selects nothing
  *   logits  [S, S_kv]  fp32, row-major
- * Rules: D == 128, H in {16, 32, 64}, S <= 1048560; q, kv, weights and logits
+ * Rules: D == 128, H in {16, 32, 64}, S <= 1048560, S_kv <= 2^31 - 4097; q, kv, weights and logits
  * 16-byte aligned, kv_sf / ks / ke 4-byte aligned.  One kernel launch on
  * `stream`, no workspace, deterministic.  The dot product over D runs on the
  * MFMA unit in fp32; the kv scale, being positive, is applied once after the

@@ -253,6 +253,8 @@ def test_mqa_logits_rejects(lib):
     assert call(q=BAD) == dg.DG_ERR_INVALID_ARG and "q is not 16-byte" in err(lib)
     assert call(ke=NULL) == dg.DG_ERR_INVALID_ARG and "ke is NULL" in err(lib)
     assert call(S=-1) == dg.DG_ERR_INVALID_ARG
+    assert call(S=1048561) == dg.DG_ERR_INVALID_ARG and "seq_len" in err(lib)
+    assert call(S_kv=2**31 - 4096) == dg.DG_ERR_INVALID_ARG and "seq_len_kv" in err(lib)
     assert call(S=0, q=NULL) == dg.DG_OK and call(S_kv=0, kv=NULL) == dg.DG_OK
 
 
