@@ -400,7 +400,9 @@ dg_status dg_pack_ue8m0_scales_k_grouped(const float* sf, const int32_t* k_sizes
     if (MN == 0 || words == 0) return ok();
     REQUIRE_PTR(sf, 4);
     REQUIRE_PTR(packed, 4);
-    REQUIRE(MN <= INT_MAX && words <= 65535, "too many packed word rows");
+    // the kernel's 32-bit column index runs up to one 256-thread block past MN
+    REQUIRE(MN <= INT_MAX - 256, "MN=%lld too large", (long long)MN);
+    REQUIRE(words <= 65535, "too many packed word rows");
     const uintptr_t s0 = reinterpret_cast<uintptr_t>(sf), p0 = reinterpret_cast<uintptr_t>(packed);
     REQUIRE(s0 + (uintptr_t)((K_tot / 128) * MN * 4) <= p0 || p0 + (uintptr_t)(words * MN * 4) <= s0,
             "sf and packed must not overlap");
