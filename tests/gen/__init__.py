@@ -236,6 +236,13 @@ def gen_dense(M: int, N: int, K: int, seed: int = 0, with_c: bool = False) -> De
     return DenseInputs(a, sfa, b, sfb, M, N, K, c)
 
 
+def _sparse_rows(a: np.ndarray, sfa: np.ndarray, rows, rng: np.random.Generator) -> None:
+    """Fill rows `rows` of a zero [R, K] code matrix (and its [K/128, R] scales)
+    with N(0,1) values quantised per row."""
+    rows = np.asarray(sorted(set(int(r) for r in rows)), np.int64)
+    a[rows], sfa[:, rows] = quantize_rows(_normal(rng, (len(rows), a.shape[1])))
+
+
 def gen_dense_sparse(M: int, N: int, K: int, a_rows, b_blocks, seed: int = 0) -> DenseInputs:
     """Dense inputs at sizes where a full random operand would be slow to build
     (an operand of up to 2 GiB): A is zero except the rows a_rows and B zero
@@ -245,8 +252,7 @@ def gen_dense_sparse(M: int, N: int, K: int, a_rows, b_blocks, seed: int = 0) ->
     rng = _rng(seed)
     a = np.zeros((M, K), np.uint8)
     sfa = np.ones((K // BLOCK, M), np.float32)
-    rows = np.asarray(sorted(set(int(r) for r in a_rows)), np.int64)
-    a[rows], sfa[:, rows] = quantize_rows(_normal(rng, (len(rows), K)))
+    _sparse_rows(a, sfa, a_rows, rng)
     NB = (N + BLOCK - 1) // BLOCK
     b = np.zeros((N, K), np.uint8)
     sfb = np.ones((NB, K // BLOCK), np.float32)
@@ -255,6 +261,40 @@ def gen_dense_sparse(M: int, N: int, K: int, a_rows, b_blocks, seed: int = 0) ->
         codes, sf = quantize_blocks(_normal(rng, (r1 - r0, K)))
         b[r0:r1], sfb[blk] = codes, sf[0]
     return DenseInputs(a, sfa, b, sfb, M, N, K)
+
+
+def gen_contiguous_sparse(m_indices: np.ndarray, N: int, K: int, G: int, a_rows,
+                          seed: int = 0) -> ContiguousInputs:
+    """The contiguous M-grouped workload with an A of up to 2 GiB: A is zero
+    except the rows a_rows (scale 1 elsewhere); every expert's B is N(0,1)
+    quantised per 128x128 block.  m_indices gives the segments (-1 padding)."""
+    rng = _rng(seed)
+    mi = np.ascontiguousarray(m_indices, np.int32)
+    M_tot = len(mi)
+    a = np.zeros((M_tot, K), np.uint8)
+    sfa = np.ones((K // BLOCK, M_tot), np.float32)
+    _sparse_rows(a, sfa, a_rows, rng)
+    parts = [quantize_blocks(_normal(rng, (N, K))) for _ in range(G)]
+    b = np.stack([q[0] for q in parts])
+    sfb = np.stack([q[1] for q in parts])
+    counts = np.array([int(np.count_nonzero(mi == e)) for e in range(G)], np.int64)
+    return ContiguousInputs(a, sfa, b, sfb, mi, counts, M_tot, N, K, G)
+
+
+def gen_masked_sparse(G: int, M_max: int, N: int, K: int, masked_m, a_rows,
+                      seed: int = 0) -> MaskedInputs:
+    """The masked M-grouped workload with an A of up to 2 GiB per group: A[g]
+    is zero except the rows a_rows[g] (scale 1 elsewhere); every group's B is
+    N(0,1) quantised per 128x128 block."""
+    rng = _rng(seed)
+    a = np.zeros((G, M_max, K), np.uint8)
+    sfa = np.ones((G, K // BLOCK, M_max), np.float32)
+    for g in range(G):
+        _sparse_rows(a[g], sfa[g], a_rows[g], rng)
+    parts = [quantize_blocks(_normal(rng, (N, K))) for _ in range(G)]
+    b = np.stack([q[0] for q in parts])
+    sfb = np.stack([q[1] for q in parts])
+    return MaskedInputs(a, sfa, b, sfb, np.ascontiguousarray(masked_m, np.int32), G, M_max, N, K)
 
 
 def gen_dense_ue8m0(M: int, N: int, K: int, seed: int = 0) -> DenseUe8m0Inputs:

@@ -368,6 +368,32 @@ def test_c3_contiguous_full_size():
     assert d.untouched(torch.from_numpy(pad).cuda())
 
 
+def test_contiguous_max_rows():
+    """M_tot * K just below 2^31 (the A operand is 2 GiB): segments of 32768
+    rows, an empty expert, a padding block, and a last segment that ends at
+    M_tot; A is zero except rows at the segment edges and a few random ones."""
+    K, N, G = MAX_K, 1024, 4
+    M_tot = ((2**31 - 1) // K) // 128 * 128          # 130944
+    announce(f"contiguous max rows {M_tot}x{N}x{K}")
+    mi = np.full(M_tot, -1, np.int32)
+    mi[:32768], mi[32768:65536], mi[65664:] = 0, 1, 3      # expert 2 empty, one padding block
+    rng = np.random.default_rng(33)
+    live = np.unique(np.concatenate([
+        np.arange(4), np.arange(32764, 32772), np.arange(65532, 65540), np.arange(65660, 65668),
+        np.arange(M_tot - 4, M_tot), rng.choice(M_tot, size=8, replace=False)])).astype(np.int64)
+    x = gen.gen_contiguous_sparse(mi, N, K, G, live, seed=33)
+    d = run_contiguous(x)
+    valid = mi >= 0
+    rows = live[valid[live]]
+    rows_t = torch.from_numpy(rows).cuda()
+    ref = oracle.m_grouped_contiguous(x.a, x.sfa, x.b, x.sfb, mi, rows=rows)
+    print(check_close(to64(d.view[rows_t]), ref, "contiguous max rows"))
+    assert d.untouched(torch.from_numpy(np.nonzero(~valid)[0]).cuda())
+    dead = torch.from_numpy(valid).cuda()
+    dead[rows_t] = False
+    assert int(torch.count_nonzero(d.view[dead])) == 0
+
+
 # ------------------------------------------------------------------------------
 # M-grouped masked
 # ------------------------------------------------------------------------------
@@ -409,6 +435,39 @@ def test_masked_two_m_tiles_per_group():
     ref = oracle.m_grouped_masked(x.a, x.sfa, x.b, x.sfb, mm)
     check_close(to64(d.view), ref, "masked 384")
     check_masked_rows_untouched(d, mm, 384)
+
+
+def test_masked_max_rows():
+    """M_max * K just below 2^31 per group (A is 2 x 2 GiB): one full group
+    and one that stops at masked_m = 70000, with live A rows past masked_m
+    that must not reach D."""
+    K, N, G = MAX_K, 512, 2
+    M_max = (2**31 - 1) // K                          # 131071
+    mm = np.array([M_max, 70000], np.int32)
+    announce(f"masked max rows G={G} M_max={M_max} N={N} K={K}")
+    rng = np.random.default_rng(34)
+    live = [np.unique(np.concatenate([np.arange(4), np.arange(M_max - 4, M_max),
+                                      rng.choice(M_max, size=4, replace=False)])),
+            np.unique(np.concatenate([np.arange(4), np.arange(69996, 70004),
+                                      rng.choice(70000, size=4, replace=False),
+                                      [M_max - 1]]))]
+    x = gen.gen_masked_sparse(G, M_max, N, K, mm, live, seed=34)
+    d = run_masked(x)
+    groups, rows = [], []
+    for g in range(G):
+        r = live[g][live[g] < mm[g]]
+        groups += [g] * len(r)
+        rows += r.tolist()
+    groups, rows = np.array(groups, np.int64), np.array(rows, np.int64)
+    got = to64(d.view[torch.from_numpy(groups).cuda(), torch.from_numpy(rows).cuda()])
+    ref = oracle.m_grouped_masked(x.a, x.sfa, x.b, x.sfb, mm, groups=groups, rows=rows)
+    print(check_close(got, ref, "masked max rows"))
+    check_masked_rows_untouched(d, mm, M_max)
+    dead = torch.zeros(G, M_max, dtype=torch.bool, device="cuda")
+    for g in range(G):
+        dead[g, :int(mm[g])] = True
+    dead[torch.from_numpy(groups).cuda(), torch.from_numpy(rows).cuda()] = False
+    assert int(torch.count_nonzero(d.view[dead])) == 0
 
 
 def test_masked_all_zero_writes_nothing():
