@@ -443,6 +443,33 @@ def gen_k_grouped(G: int = 32, M: int = 2048, N: int = 4096, K_tot: int = 49152,
                           G, M, N, K_tot)
 
 
+def gen_k_grouped_sparse(k_sizes, M: int, N: int, live_tokens, seed: int = 0,
+                         c_std: float = 0.01) -> KGroupedInputs:
+    """The K-grouped workload with operands of up to 2 GiB: A [K_tot, M] and
+    B [K_tot, N] are zero except the token rows live_tokens, which are N(0,1)
+    quantised per column per 128-token block as in gen_k_grouped (scale 1 in
+    blocks without live tokens).  C ~ N(0, c_std) fp32 [G, M, N]."""
+    rng = _rng(seed)
+    ks = np.asarray(k_sizes, np.int64)
+    assert np.all(ks % BLOCK == 0)
+    K_tot, G = int(ks.sum()), len(ks)
+    a = np.zeros((K_tot, M), np.uint8)
+    sfa = np.ones((K_tot // BLOCK, M), np.float32)
+    b = np.zeros((K_tot, N), np.uint8)
+    sfb = np.ones((K_tot // BLOCK, N), np.float32)
+    live = np.asarray(sorted(set(int(t) for t in live_tokens)), np.int64)
+    for blk in np.unique(live // BLOCK):
+        rows = live[live // BLOCK == blk] - BLOCK * blk
+        for codes, sf, cols in ((a, sfa, M), (b, sfb, N)):
+            x = np.zeros((BLOCK, cols), np.float32)
+            x[rows] = _normal(rng, (len(rows), cols))
+            q, s_ = quantize_cols(x)
+            codes[BLOCK * blk: BLOCK * blk + BLOCK] = q
+            sf[blk] = s_[0]
+    c = _normal(rng, (G, M, N), c_std)
+    return KGroupedInputs(a, sfa, b, sfb, ks.astype(np.int32), ks.copy(), c, G, M, N, K_tot)
+
+
 def gen_config(i: int, seed: int = 0):
     """The five named workloads by index 1..5 (2 returns the 15-shape list)."""
     if i == 1:

@@ -526,6 +526,29 @@ def run_tn(x, c=None, in_place=False):
     return d.view
 
 
+def test_k_grouped_max_k():
+    """K_tot * M just below 2^31 (A [K_tot, M] is 2 GiB): groups of 2^19 and
+    2^18 tokens, an empty group and a last group ending at K_tot; live tokens
+    sit at the group edges and at random places."""
+    M, N = 2048, 256
+    K_tot = ((2**31 - 1) // M) // 128 * 128          # 1048448
+    ks = np.array([2**19, 0, 2**18, K_tot - 2**19 - 2**18], np.int64)
+    announce(f"k-grouped max K_tot={K_tot} M={M} N={N} k_sizes={ks.tolist()}")
+    starts = np.concatenate([[0], np.cumsum(ks)[:-1]])
+    rng = np.random.default_rng(35)
+    live = [rng.choice(K_tot, size=8, replace=False)]
+    for g in np.nonzero(ks)[0]:
+        live += [starts[g] + np.arange(3), starts[g] + ks[g] - 3 + np.arange(3)]
+    x = gen.gen_k_grouped_sparse(ks, M, N, np.concatenate(live), seed=35)
+    d = run_tn(x, c=x.c)
+    groups = np.repeat(np.arange(4), 4).astype(np.int64)
+    rows = np.tile([0, 1, 1029, M - 1], 4).astype(np.int64)
+    got = to64(d[torch.from_numpy(groups).cuda(), torch.from_numpy(rows).cuda()])
+    ref = oracle.k_grouped_tn(x.a, x.sfa, x.b, x.sfb, x.k_sizes, x.c, groups=groups, rows=rows)
+    print(check_close(got, ref, "k-grouped max K"))
+    assert torch.equal(d[1], dev(x.c[1]))            # empty group: D = C
+
+
 @pytest.mark.parametrize("in_place", [False, True])
 def test_k_grouped_small_with_empty_groups(in_place):
     announce(f"k-grouped small in_place={in_place}")
