@@ -647,6 +647,25 @@ def gen_mqa(S: int, S_kv: int, H: int = 64, D: int = 128, seed: int = 0,
                      else None, w, ks, ke, S, S_kv, H, D)
 
 
+def gen_mqa_sparse(S: int, S_kv: int, H: int, live_queries, seed: int = 0) -> MqaInputs:
+    """MQA inputs with a q of many GiB: q is zero except the queries
+    live_queries (N(0,1) cast to e4m3 as in gen_mqa, with N(0,1) weights; the
+    other weights are 1); kv as in gen_mqa.  Ranges vary with i: ks = i mod
+    1024, ke = ks + 1 + (i mod 1021), clamped to [0, S_kv] by the kernel."""
+    rng = _rng(seed)
+    D = BLOCK
+    live = np.asarray(sorted(set(int(i) for i in live_queries)), np.int64)
+    q = np.zeros((S, H, D), np.uint8)
+    q[live] = _cast_e4m3(torch.from_numpy(_normal(rng, (len(live), H, D)))).numpy()
+    kvc, sf = quantize_rows(_normal(rng, (S_kv, D)))
+    w = np.ones((S, H), np.float32)
+    w[live] = _normal(rng, (len(live), H))
+    i = np.arange(S, dtype=np.int64)
+    ks = (i % 1024).astype(np.int32)
+    ke = (ks + 1 + i % 1021).astype(np.int32)
+    return MqaInputs(q, kvc, np.ascontiguousarray(sf.reshape(-1)), w, ks, ke, S, S_kv, H, D)
+
+
 def k_grouped_ue8m0_words(sf: np.ndarray, k_sizes) -> np.ndarray:
     """Power-of-two fp32 scales [K_tot/128, MN] of a K-grouped operand ->
     packed UE8M0 words, each group's blocks on their own ceil(KB_g / 4) rows."""

@@ -139,3 +139,33 @@ def test_mqa_graph_capture_replays_with_new_ranges():
         torch.cuda.synchronize()
         ref = oracle.mqa_logits(x.q, x.kv, x.kv_sf, x.weights, lo, hi, clean=True)
         compare(out.cpu().numpy(), ref, True, f"replay {rep}")
+
+
+def test_max_queries():
+    """The largest seq_len the entry point accepts (65535 workgroup rows of 16
+    queries), 64 heads: q is 8 GiB, so its offsets pass 2^32.  q is zero
+    except a few queries (the first, the last, random ones), checked against
+    the oracle; every other row must be exactly 0 inside its range and -inf
+    outside."""
+    S, S_kv, H = 65535 * 16, 2048, 64
+    announce(f"mqa max queries S={S} S_kv={S_kv} H={H}")
+    rng = np.random.default_rng(36)
+    live = np.unique(np.concatenate([np.arange(4), np.arange(S - 4, S),
+                                     rng.choice(S, size=8, replace=False)])).astype(np.int64)
+    x = gen.gen_mqa_sparse(S, S_kv, H, live, seed=36)
+    out = torch.empty((S, S_kv), dtype=torch.float32, device="cuda")
+    ks_t, ke_t = dev(x.ks), dev(x.ke)
+    dg.fp8_mqa_logits(dev(x.q), (dev(x.kv), dev(x.kv_sf)), dev(x.weights), ks_t, ke_t,
+                      clean_logits=True, out=out)
+    torch.cuda.synchronize()
+    live_t = torch.from_numpy(live).cuda()
+    ref = oracle.mqa_logits(x.q, x.kv, x.kv_sf, x.weights, x.ks, x.ke, rows=live)
+    compare(out[live_t].cpu().numpy(), ref, True, "mqa max queries")
+    dead = torch.ones(S, dtype=torch.bool, device="cuda")
+    dead[live_t] = False
+    j = torch.arange(S_kv, device="cuda")
+    for r0 in range(0, S, 1 << 16):
+        rr = slice(r0, min(S, r0 + (1 << 16)))
+        inside = (j[None] >= ks_t[rr, None].long()) & (j[None] < ke_t[rr, None].long())
+        expect = torch.where(inside, 0.0, float("-inf"))
+        assert bool(((out[rr] == expect) | ~dead[rr, None]).all()), f"rows {r0}.."
