@@ -553,6 +553,29 @@ def gen_layout(layout: str, M: int, N: int, K: int, seed: int = 0,
     return LayoutInputs(layout, a, sfa, bt, sfb, M, N, K, c)
 
 
+def gen_layout_sparse(layout: str, M: int, N: int, K: int, a_rows, seed: int = 0) -> LayoutInputs:
+    """gen_layout's workload with an A of up to 2 GiB: A(m, k) is zero except
+    the rows m in a_rows (N(0,1) quantised per row per 128-K block; scale 1
+    elsewhere), written straight into the layout's orientation; B is N(0,1)
+    quantised as in gen_layout."""
+    assert layout in ("nn", "tn", "tt")
+    rng = _rng(seed)
+    rows = np.asarray(sorted(set(int(r) for r in a_rows)), np.int64)
+    codes, sf_live = quantize_rows(_normal(rng, (len(rows), K)))
+    sfa = np.ones((K // BLOCK, M), np.float32)
+    sfa[:, rows] = sf_live
+    if layout[0] == "n":
+        a = np.zeros((M, K), np.uint8)
+        a[rows] = codes
+    else:
+        a = np.zeros((K, M), np.uint8)
+        a[:, rows] = codes.T
+    bt, sfb = quantize_rows(_normal(rng, (N, K)))
+    if layout[1] == "n":
+        bt = np.ascontiguousarray(bt.T)
+    return LayoutInputs(layout, a, sfa, bt, sfb, M, N, K, None)
+
+
 @dataclasses.dataclass
 class NNContiguousInputs:
     a: np.ndarray          # uint8 [M_tot, K]

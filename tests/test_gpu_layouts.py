@@ -210,3 +210,25 @@ def test_nn_large_sampled():
     got = to64(run(x))
     rows = np.array([0, 1, 255, 256, 2047, 4095], np.int64)
     check_close(got[rows], oracle.gemm_layout("nn", x.a, x.sfa, x.b, x.sfb, rows=rows), "nn large")
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+def test_layout_max_rows(layout):
+    """M * K just below 2^31 (A is 2 GiB in either orientation; M a multiple
+    of 16 when A is stored [K, M]).  A is zero except a few rows m (the first,
+    the last, random ones), checked against the oracle; every other row of D
+    must be exactly zero."""
+    K, N = 16384, 256
+    M = (2**31 - 1) // K if layout[0] == "n" else ((2**31 - 1) // K) // 16 * 16
+    announce(f"layout {layout} max rows {M}x{N}x{K}")
+    rng = np.random.default_rng(37)
+    live = np.unique(np.concatenate([np.arange(4), np.arange(M - 4, M),
+                                     rng.choice(M, size=8, replace=False)])).astype(np.int64)
+    x = gen.gen_layout_sparse(layout, M, N, K, live, seed=37)
+    d = run(x)
+    live_t = torch.from_numpy(live).cuda()
+    ref = oracle.gemm_layout(layout, x.a, x.sfa, x.b, x.sfb, rows=live)
+    print(check_close(to64(d[live_t]), ref, f"{layout} max rows"))
+    dead = torch.ones(M, dtype=torch.bool, device="cuda")
+    dead[live_t] = False
+    assert int(torch.count_nonzero(d[dead])) == 0
