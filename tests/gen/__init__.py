@@ -236,29 +236,32 @@ def gen_dense(M: int, N: int, K: int, seed: int = 0, with_c: bool = False) -> De
     return DenseInputs(a, sfa, b, sfb, M, N, K, c)
 
 
-def _sparse_rows(a: np.ndarray, sfa: np.ndarray, rows, rng: np.random.Generator) -> None:
+def _sparse_rows(a: np.ndarray, sfa: np.ndarray, rows, rng: np.random.Generator,
+                 pow2: bool = False) -> None:
     """Fill rows `rows` of a zero [R, K] code matrix (and its [K/128, R] scales)
     with N(0,1) values quantised per row."""
     rows = np.asarray(sorted(set(int(r) for r in rows)), np.int64)
-    a[rows], sfa[:, rows] = quantize_rows(_normal(rng, (len(rows), a.shape[1])))
+    a[rows], sfa[:, rows] = quantize_rows(_normal(rng, (len(rows), a.shape[1])), pow2)
 
 
-def gen_dense_sparse(M: int, N: int, K: int, a_rows, b_blocks, seed: int = 0) -> DenseInputs:
+def gen_dense_sparse(M: int, N: int, K: int, a_rows, b_blocks, seed: int = 0,
+                     pow2: bool = False) -> DenseInputs:
     """Dense inputs at sizes where a full random operand would be slow to build
     (an operand of up to 2 GiB): A is zero except the rows a_rows and B zero
     except the 128-row blocks b_blocks, whose values are N(0,1) quantised as in
-    gen_dense; every other scale is 1.  Outputs outside the live rows of A or
-    the live blocks of B are exactly zero."""
+    gen_dense (scales rounded up to powers of two with pow2); every other
+    scale is 1.  Outputs outside the live rows of A or the live blocks of B
+    are exactly zero."""
     rng = _rng(seed)
     a = np.zeros((M, K), np.uint8)
     sfa = np.ones((K // BLOCK, M), np.float32)
-    _sparse_rows(a, sfa, a_rows, rng)
+    _sparse_rows(a, sfa, a_rows, rng, pow2)
     NB = (N + BLOCK - 1) // BLOCK
     b = np.zeros((N, K), np.uint8)
     sfb = np.ones((NB, K // BLOCK), np.float32)
     for blk in sorted(set(int(x) for x in b_blocks)):
         r0, r1 = BLOCK * blk, min(N, BLOCK * blk + BLOCK)
-        codes, sf = quantize_blocks(_normal(rng, (r1 - r0, K)))
+        codes, sf = quantize_blocks(_normal(rng, (r1 - r0, K)), pow2)
         b[r0:r1], sfb[blk] = codes, sf[0]
     return DenseInputs(a, sfa, b, sfb, M, N, K)
 

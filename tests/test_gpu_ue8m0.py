@@ -465,3 +465,25 @@ def test_k_grouped_ue8m0_c5_sampled():
     rows = rng.integers(0, x.M, len(groups)).astype(np.int64)
     ref = oracle.k_grouped_tn_ue8m0(x.a, wa, x.b, wb, x.k_sizes, x.c, groups=groups, rows=rows)
     check_close(got[groups, rows], ref, "C5 ue8m0")
+
+
+def test_dense_ue8m0_max_rows():
+    """M * K just below 2^31 on the 256 x 256 tiles with packed scales (the A
+    word rows are 131071 wide): A is zero except a few rows, power-of-two
+    scales everywhere (1 on the zero rows); every other row must be exactly
+    zero."""
+    K, N = 16384, 1024
+    M = (2**31 - 1) // K
+    announce(f"ue8m0 dense max rows {M}x{N}x{K}")
+    rng = np.random.default_rng(38)
+    live = np.unique(np.concatenate([np.arange(4), np.arange(M - 4, M),
+                                     rng.choice(M, size=8, replace=False)])).astype(np.int64)
+    x = gen.gen_dense_sparse(M, N, K, live, range(N // 128), seed=38, pow2=True)
+    sfa_w, sfb_w = gen.to_ue8m0(x.sfa, x.sfb, N)
+    d = run_dense(x.a, sfa_w, x.b, sfb_w, M, N)
+    live_t = torch.from_numpy(live).cuda()
+    ref = oracle.gemm_nt_ue8m0(x.a, sfa_w, x.b, sfb_w, rows=live)
+    print(check_close(to64(d[live_t]), ref, "ue8m0 max rows"))
+    dead = torch.ones(M, dtype=torch.bool, device="cuda")
+    dead[live_t] = False
+    assert int(torch.count_nonzero(d[dead])) == 0
