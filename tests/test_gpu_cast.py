@@ -200,3 +200,66 @@ def test_per_block_full_size_sampled_blocks():
         ref = oracle.cast_blocks(w[blk].float().cpu().numpy())
         got = (codes[blk].cpu().numpy(), sf[g, nb:nb + 1, kb:kb + 1].cpu().numpy())
         assert_same(got, ref, f"block {(g, nb, kb)}")
+
+
+# ------------------------------------------------------------------------------
+# maximum sizes: rows * K just below 2^31 in each of two groups, so offsets
+# pass 2^32.  The input is zero except a few rows (blocks); those are checked
+# against the oracle, and every zero block must give zero codes and scale 1.
+# ------------------------------------------------------------------------------
+
+MAX_K = 16384
+
+
+def test_per_token_max_rows():
+    G, R, K = 2, (2**31 - 1) // MAX_K, MAX_K
+    announce(f"cast per token max G={G} R={R} K={K} bf16")
+    rng = np.random.default_rng(39)
+    live = sorted({(0, 0), (0, R - 1), (1, 0), (1, R - 1), (1, 65543)} |
+                  {(int(rng.integers(G)), int(rng.integers(R))) for _ in range(6)})
+    x = torch.zeros((G, R, K), dtype=torch.bfloat16, device="cuda")
+    tg = torch.Generator(device="cuda")
+    tg.manual_seed(39)
+    for g, r in live:
+        x[g, r] = (3 * torch.randn(K, generator=tg, device="cuda")).to(torch.bfloat16)
+    codes, sf = dg.per_token_cast_to_fp8(x)
+    torch.cuda.synchronize()
+    for g, r in live:
+        ref = oracle.cast_rows(x[g, r][None].float().cpu().numpy())
+        got = (codes[g, r][None].cpu().numpy(), sf[g, :, r][:, None].cpu().numpy())
+        assert_same(got, ref, f"row {(g, r)}")
+        codes[g, r] = 0
+        sf[g, :, r] = 1.0
+    assert int(torch.count_nonzero(codes)) == 0
+    assert bool((sf == 1.0).all())
+
+
+def test_per_block_max_rows():
+    N, K = (2**31 - 1) // MAX_K, MAX_K               # 131071 rows: ragged last block
+    NB, KB = (N + 127) // 128, K // 128
+    announce(f"cast per block max N={N} K={K} bf16")
+    rng = np.random.default_rng(40)
+    live = sorted({(0, 0), (NB - 1, KB - 1), (NB - 1, 0)} |
+                  {(int(rng.integers(NB)), int(rng.integers(KB))) for _ in range(5)})
+    w = torch.zeros((N, K), dtype=torch.bfloat16, device="cuda")
+    tg = torch.Generator(device="cuda")
+    tg.manual_seed(40)
+
+    def blk(nb, kb):
+        return slice(nb * 128, min(N, nb * 128 + 128)), slice(kb * 128, kb * 128 + 128)
+
+    for nb, kb in live:
+        rows, cols = blk(nb, kb)
+        shape = (rows.stop - rows.start, 128)
+        w[rows, cols] = (3 * torch.randn(shape, generator=tg, device="cuda")).to(torch.bfloat16)
+    codes, sf = dg.per_block_cast_to_fp8(w)
+    torch.cuda.synchronize()
+    for nb, kb in live:
+        rows, cols = blk(nb, kb)
+        ref = oracle.cast_blocks(w[rows, cols].float().cpu().numpy())
+        got = (codes[rows, cols].cpu().numpy(), sf[nb:nb + 1, kb:kb + 1].cpu().numpy())
+        assert_same(got, ref, f"block {(nb, kb)}")
+        codes[rows, cols] = 0
+        sf[nb, kb] = 1.0
+    assert int(torch.count_nonzero(codes)) == 0
+    assert bool((sf == 1.0).all())
