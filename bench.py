@@ -51,7 +51,7 @@ GROUPED_PROFILE_COMMANDS = [
 
 PROFILE_COMMANDS = [
     "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o run -- "
-    "python3 bench.py --steps 20 --no-detail --no-cpu --json-out gpurun_out/bench_prof.json",
+    "python3 bench.py --no-detail --no-cpu --json-out gpurun_out/bench_prof.json",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o run -- "
     "python3 bench.py --steps 1 --warmup 0 --no-detail --no-cpu --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o run -- "
@@ -68,11 +68,13 @@ def dense_bytes(M, N, K, d_bytes=2):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    # 30 untimed sweeps by default: the GPU's clocks settle under sustained load
-    # (same box: 3 warmup steps 1649-1653 TFLOP/s, 30 steps 1729-1733, 100 steps
-    # 1720-1752)
-    ap.add_argument("--warmup", type=int, default=30)
+    # 100 timed sweeps after 300 untimed ones by default (about 0.45 s of GPU
+    # time): the GPU leaves its idle power state and its clocks settle only
+    # under sustained load, and on some boxes that takes longer than a few
+    # tens of sweeps (one box, alternating runs: 30 warmup + 20 timed steps
+    # 1591-1608 TFLOP/s, 300 + 100 steps 1722-1723)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
