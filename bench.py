@@ -70,8 +70,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     # 100 timed sweeps after 300 untimed ones by default (about 0.45 s of GPU
     # time): the GPU leaves its idle power state and its clocks settle only
-    # under sustained load, and on some boxes that takes longer than a few
-    # tens of sweeps (one box, alternating runs: 30 warmup + 20 timed steps
+    # under sustained load, and on some machines that takes longer than a few
+    # tens of sweeps (one machine, alternating runs: 30 warmup + 20 timed steps
     # 1591-1608 TFLOP/s, 300 + 100 steps 1722-1723)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=300)
