@@ -13,7 +13,9 @@ Also reported on the same JSON line:
                   MFMA (fp8 dense 5.0 PFLOP/s) or HBM (8 TB/s) roof, whichever
                   bounds its arithmetic intensity;
   cpu_baseline -- the fp64 CPU oracle on a bounded sample of that shape's rows;
-  detail       -- per-shape times, the three grouped MoE workloads
+  detail       -- per-shape times (each launch after a 512 MiB write that
+                  flushes L2 and the Infinity Cache, median / min / p90 over
+                  --reps repetitions), the C1 shape, the three grouped MoE workloads
                   (contiguous, masked, K-grouped) timed the same way, the
                   FP8 casting kernels on bf16 operands of those shapes, and
                   the power-of-two (packed UE8M0) scale variant of the dense
@@ -21,7 +23,7 @@ Also reported on the same JSON line:
                   TN / TT layouts and the M-grouped contiguous NN form, and the
                   FP8 MQA logits kernel on a 64-head causal prefill.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-detail]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--no-detail]
                        [--no-cpu] [--json-out PATH]
 """
 from __future__ import annotations
@@ -38,27 +40,40 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (published)
+# the same peak from the chip's units at its peak engine clock:
+# 256 CUs x 8192 FP8 FLOP per clock x 2.4 GHz
+PEAK_FP8_TFLOPS_CLOCK = 256 * 8192 * 2.4e9 / 1e12
+FLUSH_BYTES = 512 << 20      # written before every detail repetition (L2 + 256 MB Infinity Cache)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
 MACHINE_BALANCE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # FLOP per byte
 
-# The rocprofv3 runs behind the profiles/ summaries (repository root, one GPU).
-GROUPED_PROFILE_COMMANDS = [
-    "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_grouped -o run -- "
-    "python3 bench.py --steps 3 --warmup 1 --no-cpu --json-out gpurun_out/bench_grouped.json",
-    "python3 bench.py --summarize-grouped gpurun_out/prof_grouped gpurun_out/bench_grouped.json "
-    "profiles/grouped_moe__contiguous_masked_kgrouped.md",
-]
+# The rocprofv3 runs behind the profiles/ summaries (repository root, one GPU):
+# a kernel trace, FETCH_SIZE and WRITE_SIZE passes (HBM-side bytes, scaled
+# by a 1 GiB device copy of known traffic), and an MFMA pass (MFMA busy
+# cycles per SIMD, GPU-active cycles for the clock, FP8 MFMA op counts).
+# Each counter pass is a run of its own.
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F8 "
+                 "SQ_INSTS_VALU_MFMA_MOPS_F6F4")
 
-PROFILE_COMMANDS = [
-    "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o run -- "
-    "python3 bench.py --no-detail --no-cpu --json-out gpurun_out/bench_prof.json",
-    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o run -- "
-    "python3 bench.py --steps 1 --warmup 0 --no-detail --no-cpu --copy-calibration",
-    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o run -- "
-    "python3 bench.py --steps 1 --warmup 0 --no-detail --no-cpu --copy-calibration",
-    "python3 bench.py --summarize-profiles gpurun_out/prof_trace gpurun_out/prof_fetch "
-    "gpurun_out/prof_write gpurun_out/bench_prof.json profiles/<kernel>__dense_sweep.md",
-]
+
+def _profile_commands(tag, trace_args, pmc_args, summarize):
+    pre = "rocprofv3 {} --output-format csv -d gpurun_out/prof_{}_{} -o run -- python3 bench.py "
+    return [pre.format("--kernel-trace --stats", tag, "trace") + trace_args
+            + f" --json-out gpurun_out/bench_{tag}.json",
+            pre.format("--pmc FETCH_SIZE", tag, "fetch") + pmc_args + " --copy-calibration",
+            pre.format("--pmc WRITE_SIZE", tag, "write") + pmc_args + " --copy-calibration",
+            pre.format("--pmc " + MFMA_COUNTERS, tag, "mfma") + pmc_args,
+            f"python3 bench.py {summarize} gpurun_out/prof_{tag} gpurun_out/bench_{tag}.json profiles"]
+
+
+# dense sweep: the roofline's dominant instance and the decode-size instances
+PROFILE_COMMANDS = _profile_commands(
+    "dense", "--no-detail --no-cpu", "--steps 2 --warmup 2 --reps 1 --no-detail --no-cpu",
+    "--summarize-dense")
+# every detail workload (C1, grouped MoE, casting, UE8M0, layouts, MQA logits)
+DETAIL_PROFILE_COMMANDS = _profile_commands(
+    "detail", "--steps 3 --warmup 1 --reps 10 --no-cpu", "--steps 1 --warmup 0 --reps 1 --no-cpu",
+    "--summarize-detail")
 
 
 def dense_bytes(M, N, K, d_bytes=2):
@@ -75,6 +90,8 @@ def main():
     # 1591-1608 TFLOP/s, 300 + 100 steps 1722-1723)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--reps", type=int, default=30,
+                    help="timed repetitions per detail workload (median / min / p90)")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -82,23 +99,18 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy before the GEMMs (a kernel of known "
                          "traffic, to scale hardware byte counters)")
-    ap.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE_DIR", "FETCH_DIR",
-                                                              "WRITE_DIR", "BENCH_JSON", "OUT_MD"),
-                    help="write a profiles/ summary from rocprofv3 CSV output and exit")
-    ap.add_argument("--summarize-cast", nargs=3, metavar=("TRACE_DIR", "BENCH_JSON", "OUT_MD"),
-                    help="write the profiles/ summary of the casting kernels")
-    ap.add_argument("--summarize-grouped", nargs=3, metavar=("TRACE_DIR", "BENCH_JSON", "OUT_MD"),
-                    help="write the profiles/ summary of the grouped-workload kernel trace and exit")
+    ap.add_argument("--summarize-dense", nargs=3, metavar=("PROF_PREFIX", "BENCH_JSON", "OUT_DIR"),
+                    help="write the dense-sweep profiles/ summaries from rocprofv3 CSV output")
+    ap.add_argument("--summarize-detail", nargs=3, metavar=("PROF_PREFIX", "BENCH_JSON", "OUT_DIR"),
+                    help="write the detail-workload profiles/ summaries from rocprofv3 CSV output")
     args = ap.parse_args()
 
-    if args.summarize_profiles:
-        summarize_profiles(*args.summarize_profiles, commands=PROFILE_COMMANDS)
+    if args.summarize_dense:
+        summarize_set(*args.summarize_dense, families=DENSE_FAMILIES, commands=PROFILE_COMMANDS)
         return
-    if args.summarize_cast:
-        summarize_cast(*args.summarize_cast)
-        return
-    if args.summarize_grouped:
-        summarize_grouped(*args.summarize_grouped)
+    if args.summarize_detail:
+        summarize_set(*args.summarize_detail, families=DETAIL_FAMILIES,
+                      commands=DETAIL_PROFILE_COMMANDS)
         return
 
     if args.gpus != 1:
@@ -123,6 +135,10 @@ def main():
     # ---- inputs (host generation, then resident in HBM) ---------------------------
     t0 = time.time()
     shapes = list(gen.DENSE_SWEEP)
+    # one caller-owned split-K workspace serves every shape: calls on one
+    # stream run in order and each leaves the counters zero for the next
+    ws_bytes = max(dg.get_fp8_gemm_nt_workspace_bytes(*s_) for s_ in shapes)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     ops = []
     for (M, N, K) in shapes:
         x = gen.gen_dense(M, N, K, seed=0)
@@ -143,12 +159,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    def launch(op):
+        dg.fp8_gemm_nt(*op["args"], workspace=ws)
+
     def step(events=None, only=None):
         for i, op in enumerate(ops):
             rec = events is not None and (only is None or op["kernel"] == only)
             if rec:
                 events[i][0].record(stream)
-            dg.fp8_gemm_nt(*op["args"])
+            launch(op)
             if rec:
                 events[i][1].record(stream)
 
@@ -160,19 +179,15 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # ---- per-launch pass (untimed): an event pair around every launch ------------
-    # gives the per-shape detail and picks the dominant kernel: the kernel
-    # instance (tile configuration) with the largest share of the step's time.
-    # Several shapes may share one instance.
-    probe_steps = 3
-    ev = new_events(probe_steps)
-    for s_ in range(probe_steps):
-        step(ev[s_])
-    torch.cuda.synchronize()
-    # median over the sweeps: the first launches after the warmup's synchronize
-    # can run on clocks that have not yet come back up
-    avg_ms = np.median([[ev[s_][i][0].elapsed_time(ev[s_][i][1]) for i in range(len(ops))]
-                        for s_ in range(probe_steps)], axis=0)
+    # ---- per-shape detail (untimed by the step clock) -------------------------------
+    # Each shape alone, --reps times, every repetition after a 512 MiB write
+    # that evicts its operands from L2 and the Infinity Cache (outside the
+    # event pair): median, min and p90.  It also picks the dominant kernel:
+    # the instance (tile configuration) with the largest share of the sweep's
+    # median time.  Several shapes may share one instance.
+    timer = Timer(stream, args.reps)
+    per_stats = [timer.measure(lambda op=op: launch(op)) for op in ops]
+    avg_ms = np.array([st["median_us"] for st in per_stats]) * 1e-3
     groups = {}
     for i, op in enumerate(ops):
         groups.setdefault(op["kernel"], []).append(i)
@@ -205,7 +220,8 @@ def main():
     if intensity >= MACHINE_BALANCE:
         achieved = launch_flop / (launch_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_FP8_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / PEAK_FP8_TFLOPS, 4), traffic=None)
+                    unit="TFLOP/s", frac=round(achieved / PEAK_FP8_TFLOPS, 4), traffic=None,
+                    frac_of_clock_peak=round(achieved / PEAK_FP8_TFLOPS_CLOCK, 4))
     else:
         achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
@@ -219,24 +235,32 @@ def main():
     roof["alg_bytes_per_launch"] = launch_bytes
     M, N, K = ops[max(idx, key=lambda i: avg_ms[i])]["shape"]
 
-    per_shape = []   # from the per-launch pass
-    for op, t in zip(ops, avg_ms):
+    per_shape = []   # from the per-shape pass (flushed, --reps repetitions)
+    for op, st in zip(ops, per_stats):
         m, n, k = op["shape"]
-        per_shape.append(dict(M=m, N=n, K=k, kernel=op["kernel"], us=round(t * 1e3, 2),
-                              tflops=round(op["flop"] / (t * 1e-3) / 1e12, 1),
-                              gbs=round(op["bytes"] / (t * 1e-3) / 1e9, 1)))
+        t = st["median_us"] * 1e-3
+        row = dict(M=m, N=n, K=k, kernel=op["kernel"], us=st["median_us"],
+                   us_min=st["min_us"], us_p90=st["p90_us"],
+                   tflops=round(op["flop"] / (t * 1e-3) / 1e12, 1),
+                   gbs=round(op["bytes"] / (t * 1e-3) / 1e9, 1))
+        if op["flop"] / op["bytes"] >= MACHINE_BALANCE:
+            row["frac_mfma"] = round(op["flop"] / (t * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)
+        else:
+            row["frac_hbm"] = round(op["bytes"] / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        per_shape.append(row)
     print(f"[bench] step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     # ---- grouped workloads (detail, timed the same way) ------------------------------
-    grouped, cast, ue8m0, layouts, mqa = {}, {}, {}, {}, {}
+    grouped, cast, ue8m0, layouts, mqa, c1 = {}, {}, {}, {}, {}, {}
     if not args.no_detail:
         del ops
         torch.cuda.empty_cache()
-        grouped = bench_grouped(dg, gen, up, dev, stream, args)
-        cast = bench_cast(dg, dev, stream, args)
-        ue8m0 = bench_ue8m0(dg, gen, up, dev, stream, args)
-        layouts = bench_layouts(dg, gen, up, dev, stream, args)
-        mqa = bench_mqa(dg, gen, up, dev, stream, args)
+        c1 = bench_c1(dg, gen, up, dev, timer)
+        grouped = bench_grouped(dg, gen, up, dev, timer)
+        cast = bench_cast(dg, dev, timer)
+        ue8m0 = bench_ue8m0(dg, gen, up, dev, timer)
+        layouts = bench_layouts(dg, gen, up, dev, timer)
+        mqa = bench_mqa(dg, gen, up, dev, timer)
 
     # ---- CPU baseline: the oracle on a bounded sample ----------------------------------
     cpu = None
@@ -262,7 +286,10 @@ def main():
                    "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "detail": {"dense": per_shape, "grouped": grouped, "cast": cast, "ue8m0": ue8m0,
+        "detail": {"timing": f"HIP events around each launch on its stream; a {FLUSH_BYTES >> 20} MiB "
+                             f"write before every repetition, outside the events; median, min and "
+                             f"p90 of {args.reps} repetitions after one untimed launch",
+                   "dense": per_shape, "c1": c1, "grouped": grouped, "cast": cast, "ue8m0": ue8m0,
                    "layouts": layouts, "mqa_logits": mqa},
     }
     line = json.dumps(result)
@@ -285,6 +312,9 @@ KERNEL_SOURCES = {
            "fp8_fine_grained_e4m3_amd/csrc/dg_internal.h"],
     "cast": ["fp8_fine_grained_e4m3_amd/csrc/cast_kernel.hip",
              "fp8_fine_grained_e4m3_amd/csrc/dg_internal.h"],
+    "mqa": ["fp8_fine_grained_e4m3_amd/csrc/mqa_kernel.hip",
+            "fp8_fine_grained_e4m3_amd/csrc/tile_common.h",
+            "fp8_fine_grained_e4m3_amd/csrc/dg_internal.h"],
 }
 
 
@@ -312,6 +342,67 @@ def measured_traffic(config_name: str):
     return None
 
 
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_rows(prefix, kind):
+    """{dispatch id: {"kernel", "ns", counter: value}} of one counter pass."""
+    out = {}
+    for r in _read_csv(os.path.join(f"{prefix}_{kind}", "run_counter_collection.csv")):
+        d = out.setdefault(int(r["Dispatch_Id"]), {
+            "kernel": r["Kernel_Name"],
+            "ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def _num_xcc(prefix):
+    try:
+        for r in _read_csv(os.path.join(f"{prefix}_mfma", "run_agent_info.csv")):
+            if r.get("Agent_Type", r.get("Type", "")).upper().endswith("GPU") or "gfx" in str(r):
+                for key in ("Num_Xcc", "Num_XCC", "num_xcc"):
+                    if key in r and r[key]:
+                        return int(float(r[key]))
+    except (OSError, KeyError, ValueError):
+        pass
+    return 8
+
+
+def instance_stats(prefix):
+    """Per kernel name: trace average (us, calls), scaled HBM fetch / write
+    bytes per dispatch, MFMA busy %, shader clock and counted MFMA FLOP per
+    dispatch, from the four runs of one profile set."""
+    stats = {r["Name"]: r for r in _read_csv(os.path.join(f"{prefix}_trace", "run_kernel_stats.csv"))}
+    fetch, write, mfma = (_counter_rows(prefix, k) for k in ("fetch", "write", "mfma"))
+    copy = float(1 << 30)
+    f_scale = copy / (max(d["FETCH_SIZE"] for d in fetch.values() if "copyBuffer" in d["kernel"]) * 1024)
+    w_scale = copy / (max(d["WRITE_SIZE"] for d in write.values() if "copyBuffer" in d["kernel"]) * 1024)
+    xcc = _num_xcc(prefix)
+    out = {}
+    for name, st in stats.items():
+        e = dict(calls=int(st["Calls"]), avg_us=float(st["AverageNs"]) / 1e3,
+                 min_us=float(st["MinNs"]) / 1e3, max_us=float(st["MaxNs"]) / 1e3)
+        fv = [d["FETCH_SIZE"] * 1024 * f_scale for d in fetch.values() if d["kernel"] == name]
+        wv = [d["WRITE_SIZE"] * 1024 * w_scale for d in write.values() if d["kernel"] == name]
+        if fv and wv:
+            e.update(fetch_b=float(np.mean(fv)), write_b=float(np.mean(wv)), n_pmc=len(fv))
+        mv = [d for d in mfma.values() if d["kernel"] == name and d.get("GRBM_GUI_ACTIVE", 0) > 0]
+        if mv:
+            grbm = np.array([d["GRBM_GUI_ACTIVE"] for d in mv]) / xcc      # cycles per XCC
+            busy = np.array([d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for d in mv])
+            mops = np.array([d.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0)
+                             + d.get("SQ_INSTS_VALU_MFMA_MOPS_F6F4", 0.0) for d in mv])
+            ns = np.array([d["ns"] for d in mv])
+            e.update(mfma_busy_pct=float(np.mean(busy / (grbm * 1024.0) * 100.0)),
+                     clock_ghz=float(np.mean(grbm / ns)),
+                     mfma_flop=float(np.mean(mops * 512.0)))
+        out[name] = e
+    return out, dict(fetch_scale=f_scale, write_scale=w_scale, xcc=xcc)
+
+
 def instance_matcher(name):
     """Predicate on demangled kernel names selecting the template instance
     behind a config name such as nt_dense_bf16_256x256 or
@@ -330,167 +421,235 @@ def instance_matcher(name):
     return (lambda k: "nt_fp8_kernel" in k and tag in k and tail in k), tag + " ...>" + tail
 
 
-def summarize_profiles(trace_dir, fetch_dir, write_dir, bench_json, out_path, commands):
-    """Write the profiles/ summary of one kernel instance from rocprofv3 CSVs."""
-    import csv
+def _nt(form, ue8m0="false", tile=None):
+    tail = f", {form}, false, {ue8m0}>"
+    return lambda k: "nt_fp8_kernel" in k and tail in k and (tile is None or f"NtCfg<{tile}," in k)
+
+
+def _tn(args):
+    return lambda k: "tn_fp8_kernel" in k and args in k
+
+
+# A family: one profiles/ file.  `match` picks its kernels; `workloads` map a
+# bench detail record to the single kernel instance that runs it (for the
+# bytes-per-algorithmic-byte ratio); `traffic_for` marks the dominant dense
+# instance, whose file carries the traffic figure bench.py reports.
+DENSE_FAMILIES = [
+    dict(file="{dominant}__dense_sweep.md", dominant=True,
+         title="Dominant instance of the dense FP8 NT sweep (the five M = 4096 shapes)",
+         note="`nt_fp8_kernel<Cfg, FORM, OUT_F32, UE8M0>`, FORM 0 = dense."),
+    dict(file="nt_dense_decode__64x64_128x64_m64_m128_shapes.md",
+         title="Decode-size dense instances (the ten M = 64 / 128 shapes of the sweep)",
+         match=lambda k: _nt(0, tile="64, 64")(k) or _nt(0, tile="128, 64")(k),
+         note="`NtCfg<64, 64, ...>` runs the M = 64 shapes, `NtCfg<128, 64, ...>` the M = 128 "
+              "shapes; K is split over workgroups (caller-owned workspace)."),
+]
+DETAIL_FAMILIES = [
+    dict(file="grouped_moe__contiguous_masked_kgrouped.md",
+         title="Grouped MoE workloads (contiguous, masked, K-grouped), fp32 scales",
+         match=lambda k: _nt(1)(k) or _nt(2)(k) or _tn("false, false, true, false, false>")(k),
+         workloads=[("grouped.contiguous_32x4096x4096", _nt(1)),
+                    ("grouped.masked_32x256x4096x2048", _nt(2)),
+                    ("grouped.k_grouped_32x2048x4096", _tn("false, false, true, false, false>"))],
+         note="`nt_fp8_kernel<Cfg, FORM, OUT_F32, UE8M0>`: FORM 1 = contiguous, 2 = masked. "
+              "`tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M, UE8M0>` with "
+              "`false, false, true, false, false` = the K-grouped form."),
+    dict(file="ue8m0__dense_sweep_contiguous_masked_kgrouped.md",
+         title="Packed UE8M0 scales (block-scaled MFMA): dense sweep, contiguous, masked, K-grouped",
+         match=lambda k: ("nt_fp8_kernel" in k and "true>(dg::NtArgs" in k)
+         or _tn("false, false, true, false, true>")(k) or "pack_ue8m0" in k,
+         workloads=[("ue8m0.contiguous_32x4096x4096", _nt(1, "true")),
+                    ("ue8m0.masked_32x256x4096x2048", _nt(2, "true")),
+                    ("ue8m0.k_grouped_32x2048x4096", _tn("false, false, true, false, true>"))],
+         note="Last template argument `true` = UE8M0 instance."),
+    dict(file="mn_major_layouts__nn_tn_tt_4096x4096x7168_and_nn_contiguous.md",
+         title="NN / TN / TT layouts and the M-grouped contiguous NN form (MN-major kernel)",
+         match=lambda k: "tn_fp8_kernel" in k and "false, false, true, false" not in k,
+         workloads=[("layouts.nn_4096x4096x7168", _tn("true, false, false, false, false>")),
+                    ("layouts.tn_4096x4096x7168", _tn("false, false, false, false, false>")),
+                    ("layouts.tt_4096x4096x7168", _tn("false, true, false, false, false>")),
+                    ("layouts.nn_contiguous_32x4096x4096", _tn("true, false, false, true, false>"))],
+         note="`tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M, UE8M0>`: A_MK = A stored [M, K], "
+              "B_NK = B stored [N, K], GROUPED_M = contiguous NN."),
+    dict(file="mqa_logits__causal_prefill_4096x4096_h64.md",
+         title="FP8 MQA logits, 64 heads, causal 4096 x 4096 and 8 packed sequences of 512",
+         match=lambda k: "mqa_logits_kernel" in k,
+         note="`mqa_logits_kernel<H>`, H = heads; both workloads run the same instance."),
+    dict(file="fp8_cast__per_token_per_block.md",
+         title="FP8 casting kernels (per token 1 x 128, per block 128 x 128)",
+         match=lambda k: "cast_kernel" in k,
+         note="Template arguments: input type (`unsigned short` = bf16 bits), rows per wave, "
+              "per-block flag (true = 128 x 128 weights)."),
+]
+
+
+def _detail(res, path):
+    v = res.get("detail", {})
+    for p in path.split("."):
+        v = v.get(p, {}) if isinstance(v, dict) else {}
+    return v
+
+
+def summarize_set(prefix, bench_json, out_dir, families, commands):
+    """Write the profiles/ summaries of one profile set (kernel trace plus the
+    three counter passes), one file per family."""
     res = json.load(open(bench_json))
+    inst, cal = instance_stats(prefix)
     roof = res["roofline"]
-    name = roof["kernel"]
-    stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
-
-    def counters(d, counter):
-        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
-        return [(r["Kernel_Name"], float(r["Counter_Value"]), int(r["Grid_Size"])) for r in rows
-                if r["Counter_Name"] == counter]
-
-    fetch = counters(fetch_dir, "FETCH_SIZE")
-    write = counters(write_dir, "WRITE_SIZE")
-    copy_bytes = float(1 << 30)
-    fetch_copy = max(v for k, v, g in fetch if "copyBuffer" in k) * 1024.0
-    write_copy = max(v for k, v, g in write if "copyBuffer" in k) * 1024.0
-    f_scale, w_scale = copy_bytes / fetch_copy, copy_bytes / write_copy
-    match, tag = instance_matcher(name)
-    f_k = [v for k, v, g in fetch if match(k)]
-    w_k = [v for k, v, g in write if match(k)]
-    fetch_b = float(np.mean(f_k)) * 1024.0 * f_scale
-    write_b = float(np.mean(w_k)) * 1024.0 * w_scale
-    lines = [f"# {name} -- dense FP8 NT sweep (M=4096 shapes), rocprofv3", "",
-             "Commands (run from the repository root on one MI355X):", ""]
-    lines += [f"    {c}" for c in commands]
-    lines += ["", "## Kernel trace (--kernel-trace --stats)", "",
-              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
-    for r in stats:
-        lines.append(f"| `{r['Name'][:80]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
-    avg_us = [float(r["AverageNs"]) / 1e3 for r in stats if match(r["Name"])][0]
-    lines += ["", f"Dominant instance `{tag}` = `{name}`: rocprofv3 average {avg_us:.2f} us per "
-              f"launch; bench.py's HIP-event average over its timed region {roof['avg_launch_us']} us.",
-              f"Launches of this instance per step: {roof['launches_per_step']} "
-              f"({', '.join(roof['shapes'])}).",
-              f"Algorithmic work per launch (mean over those shapes): "
-              f"{roof['alg_flop_per_launch'] / 1e9:.2f} GFLOP, {roof['alg_bytes_per_launch'] / 1e6:.2f} MB.",
-              "", "## Traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
-              f"Calibration: a 1 GiB device copy (`__amd_rocclr_copyBuffer`) reads FETCH_SIZE "
-              f"{fetch_copy / 1024:.0f} KiB and WRITE_SIZE {write_copy / 1024:.0f} KiB, so the "
-              f"scale factors are {f_scale:.4f} (fetch) and {w_scale:.4f} (write).",
-              "", "| dispatch of this instance | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|"]
-    for i, (fv, wv) in enumerate(zip(f_k, w_k)):
-        lines.append(f"| {i} | {fv:.1f} | {wv:.1f} |")
-    lines += ["", f"Scaled per launch: fetch {fetch_b / 1e6:.1f} MB + write {write_b / 1e6:.1f} MB "
-              f"= {(fetch_b + write_b) / 1e6:.1f} MB, {(fetch_b + write_b) / roof['alg_bytes_per_launch']:.2f}x "
-              f"the algorithmic bytes.",
-              "", "Machine-readable:", "",
-              f"    traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
-              f"    kernel_source_sha256_16: {source_hash(name.split('_')[0])}",
-              f"    bench_value_tflops: {res['value']}", ""]
-    with open(out_path, "w") as f:
-        f.write("\n".join(lines))
-    print(out_path)
-
-
-DETAIL_SUMMARIES = {
-    # file -> (title, kernel-name filter, bench detail key, template-argument note)
-    "grouped_moe__contiguous_masked_kgrouped.md": (
-        "Grouped MoE workloads (contiguous, masked, K-grouped), fp32 scales",
-        lambda k: ("nt_fp8_kernel" in k and (", 1, false, false>" in k or ", 2, false, false>" in k))
-        or ("tn_fp8_kernel" in k and "false, false, true, false, false>" in k),
-        "grouped",
-        "`nt_fp8_kernel<Cfg, FORM, OUT_F32, UE8M0>`: FORM 1 = contiguous, 2 = masked. "
-        "`tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M, UE8M0>` with "
-        "`false, false, true, false, false` = the K-grouped form."),
-    "ue8m0__dense_sweep_contiguous_masked_kgrouped.md": (
-        "Packed UE8M0 scales (block-scaled MFMA): dense sweep, contiguous, masked, K-grouped",
-        lambda k: ("nt_fp8_kernel" in k and "true>(dg::NtArgs" in k)
-        or ("tn_fp8_kernel" in k and "false, false, true, false, true>" in k)
-        or "pack_ue8m0" in k,
-        "ue8m0",
-        "Last template argument `true` = UE8M0 instance."),
-    "mn_major_layouts__nn_tn_tt_4096x4096x7168_and_nn_contiguous.md": (
-        "NN / TN / TT layouts and the M-grouped contiguous NN form (MN-major kernel)",
-        lambda k: "tn_fp8_kernel" in k and not ("false, false, true, false" in k),
-        "layouts",
-        "`tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M, UE8M0>`: A_MK = A stored [M, K], "
-        "B_NK = B stored [N, K], GROUPED_M = contiguous NN."),
-    "mqa_logits__causal_prefill_4096x4096_h64.md": (
-        "FP8 MQA logits, 64 heads, causal 4096 x 4096 and 8 packed sequences of 512",
-        lambda k: "mqa_logits_kernel" in k,
-        "mqa_logits",
-        "`mqa_logits_kernel<H>`, H = heads."),
-}
-
-
-def summarize_grouped(trace_dir, bench_json, out_path):
-    """profiles/ summaries of the bench detail workloads: for each kernel
-    family, the rocprofv3 per-kernel averages next to bench.py's own HIP-event
-    timings of the same run.  out_path names the grouped-MoE file; the other
-    families are written beside it."""
-    import csv
-    res = json.load(open(bench_json))
-    stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
-    out_dir = os.path.dirname(out_path) or "."
-    for fname, (title, match, key, note) in DETAIL_SUMMARIES.items():
-        detail = res["detail"].get(key, {})
-        lines = [f"# {title} -- rocprofv3 kernel trace", "",
+    for fam in families:
+        if fam.get("dominant"):
+            name = roof["kernel"]
+            match, tag = instance_matcher(name)
+            fname = fam["file"].format(dominant=name)
+        else:
+            match, fname = fam["match"], fam["file"]
+        rows = {k: v for k, v in inst.items() if match(k)}
+        lines = [f"# {fam['title']} -- rocprofv3", "",
                  "Commands (run from the repository root on one MI355X):", ""]
-        lines += [f"    {c}" for c in GROUPED_PROFILE_COMMANDS]
-        lines += ["", "One bench.py run times the dense sweep and then every detail workload; the",
-                  "rows below are this family's kernels from that run's trace.", "", note, "",
-                  "## Kernel trace (--kernel-trace --stats)", "",
-                  "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
-        for r in stats:
-            if match(r["Name"]):
-                lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                             f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-        lines += ["", "## bench.py HIP-event timings (same run)", "",
-                  "| workload | us | TFLOP/s | fraction of roof |", "|---|---|---|---|"]
-        items = list(detail.items()) if isinstance(detail, dict) else []
-        for name, v in items:
-            if name == "dense" and isinstance(v, list):
-                for dd in v:
-                    lines.append(f"| dense {dd['M']}x{dd['N']}x{dd['K']} | {dd['us']} | {dd['tflops']} | |")
-                continue
-            if not isinstance(v, dict):
-                lines.append(f"| {name} | {v} | | |")
-                continue
-            frac = v.get("frac_mfma", v.get("frac_hbm", ""))
-            roof = "MFMA" if "frac_mfma" in v else ("HBM" if "frac_hbm" in v else "")
-            lines.append(f"| {name} | {v.get('us')} | {v.get('tflops')} | {frac} {roof} |")
-        lines += ["", f"    kernel_source_sha256_16: nt {source_hash('nt')}, tn {source_hash('tn')}, "
-                      f"cast {source_hash('cast')}", ""]
+        lines += [f"    {c}" for c in commands]
+        lines += ["", fam["note"], "",
+                  "Counters: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read "
+                  f"for a 1 GiB device copy (`__amd_rocclr_copyBuffer`): fetch x{cal['fetch_scale']:.4f}, "
+                  f"write x{cal['write_scale']:.4f}.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+                  f"(GRBM_GUI_ACTIVE per XCC x 1024 SIMDs); clock = GRBM_GUI_ACTIVE per XCC / dispatch "
+                  f"time ({cal['xcc']} XCCs); MFMA FLOP = (SQ_INSTS_VALU_MFMA_MOPS_F8 + _F6F4) x 512.  "
+                  "Counter passes serialise dispatches, so their clock is that of isolated launches.",
+                  "", "## Per kernel instance", "",
+                  "| kernel | calls (trace) | trace avg us | min | max | HBM fetch MB / dispatch | "
+                  "HBM write MB / dispatch | MFMA busy % | clock GHz | MFMA GFLOP / dispatch |",
+                  "|---|---|---|---|---|---|---|---|---|---|"]
+        for k, e in sorted(rows.items(), key=lambda kv: -kv[1]["avg_us"] * kv[1]["calls"]):
+            f = lambda key, sc=1e-6, fmt="{:.1f}": fmt.format(e[key] * sc) if key in e else "-"
+            lines.append(f"| `{k[:110]}` | {e['calls']} | {e['avg_us']:.2f} | {e['min_us']:.2f} | "
+                         f"{e['max_us']:.2f} | {f('fetch_b')} | {f('write_b')} | "
+                         f"{f('mfma_busy_pct', 1.0)} | {f('clock_ghz', 1.0, '{:.2f}')} | "
+                         f"{f('mfma_flop', 1e-9, '{:.2f}')} |")
+        machine = []
+        if fam.get("dominant"):
+            e = [v for k, v in rows.items()]
+            e = e[0] if e else {}
+            lines += ["", f"Dominant instance `{tag}` = `{name}`: {roof['launches_per_step']} launches per "
+                          f"step ({', '.join(roof['shapes'])}); rocprofv3 trace average "
+                          f"{e.get('avg_us', float('nan')):.2f} us per launch, bench.py's HIP-event "
+                          f"average over its timed region {roof['avg_launch_us']} us.",
+                      f"Algorithmic work per launch (mean over those shapes): "
+                      f"{roof['alg_flop_per_launch'] / 1e9:.2f} GFLOP, "
+                      f"{roof['alg_bytes_per_launch'] / 1e6:.2f} MB."]
+            if "fetch_b" in e:
+                tot = e["fetch_b"] + e["write_b"]
+                lines.append(f"HBM traffic per launch: fetch {e['fetch_b'] / 1e6:.1f} MB + write "
+                             f"{e['write_b'] / 1e6:.1f} MB = {tot / 1e6:.1f} MB, "
+                             f"{tot / roof['alg_bytes_per_launch']:.2f}x the algorithmic bytes.")
+                machine.append(f"    traffic_bytes_per_launch: {tot:.0f}")
+            if "mfma_flop" in e:
+                lines.append(f"MFMA FLOP counted per launch {e['mfma_flop'] / 1e9:.2f} G against "
+                             f"{roof['alg_flop_per_launch'] / 1e9:.2f} G algorithmic; MFMA busy "
+                             f"{e['mfma_busy_pct']:.1f}% at {e['clock_ghz']:.2f} GHz.")
+        if fam.get("workloads"):
+            lines += ["", "## Workloads run by one instance each (bench.py, same trace run)", "",
+                      "| workload | bench median us | min | p90 | trace avg us | alg MB | "
+                      "HBM MB (fetch + write) | HBM / alg | alg GFLOP | MFMA GFLOP counted | "
+                      "MFMA busy % | frac of roof |", "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+            for label, pred in fam["workloads"]:
+                d = _detail(res, label)
+                hit = [v for k, v in rows.items() if pred(k)]
+                if not d or len(hit) != 1:
+                    continue
+                e = hit[0]
+                hbm = e.get("fetch_b", float("nan")) + e.get("write_b", float("nan"))
+                frac = d.get("frac_mfma", d.get("frac_hbm"))
+                roofname = "MFMA" if "frac_mfma" in d else "HBM"
+                lines.append(
+                    f"| {label} | {d.get('us')} | {d.get('us_min')} | {d.get('us_p90')} | "
+                    f"{e['avg_us']:.2f} | {d.get('alg_bytes', 0) / 1e6:.1f} | {hbm / 1e6:.1f} | "
+                    f"{hbm / max(d.get('alg_bytes', 1), 1):.2f} | {d.get('alg_flop', 0) / 1e9:.1f} | "
+                    f"{e.get('mfma_flop', float('nan')) / 1e9:.1f} | "
+                    f"{e.get('mfma_busy_pct', float('nan')):.1f} | {frac} {roofname} |")
+        lines += ["", "Machine-readable:", ""] + machine
+        fams = ("nt", "tn", "cast", "mqa")
+        lines += ["    kernel_source_sha256_16: " + ", ".join(f"{f} {source_hash(f)}" for f in fams),
+                  f"    bench_value_tflops: {res['value']}", ""]
         path = os.path.join(out_dir, fname)
-        with open(path, "w") as f:
-            f.write("\n".join(lines))
+        with open(path, "w") as fh:
+            fh.write("\n".join(lines))
         print(path)
 
 
-def bench_grouped(dg, gen, up, dev, stream, args):
+class Timer:
+    """Detail timing: an event pair around each launch on `stream`, and before
+    every repetition (outside the pair) a FLUSH_BYTES write that evicts the
+    operands from the L2 caches and the 256 MB Infinity Cache, so every
+    repetition reads its operands from HBM.  One untimed launch first."""
+
+    def __init__(self, stream, reps):
+        import torch
+        self.stream = stream
+        self.reps = max(1, int(reps))
+        self.flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=stream.device)
+        self.fill = 0.0
+
+    def measure(self, fn):
+        import torch
+        fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(self.reps)]
+        with torch.cuda.stream(self.stream):
+            for e0, e1 in evs:
+                self.fill += 1.0
+                self.flush.fill_(self.fill)
+                e0.record(self.stream)
+                fn()
+                e1.record(self.stream)
+        torch.cuda.synchronize()
+        t = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3
+        return dict(median_us=round(float(np.median(t)), 2), min_us=round(float(t.min()), 2),
+                    p90_us=round(float(np.percentile(t, 90)), 2), reps=self.reps)
+
+
+def entry(st, flop, byts, roof, **extra):
+    """One detail record: times, TFLOP/s, GB/s and the fraction of the binding
+    roof (MFMA: fp8 dense peak; HBM: 8 TB/s) at the median time."""
+    t = st["median_us"] * 1e-6
+    out = dict(us=st["median_us"], us_min=st["min_us"], us_p90=st["p90_us"], reps=st["reps"],
+               tflops=round(flop / t / 1e12, 1), gbs=round(byts / t / 1e9, 1),
+               alg_flop=flop, alg_bytes=byts)
+    if roof == "mfma":
+        out["frac_mfma"] = round(flop / t / 1e12 / PEAK_FP8_TFLOPS, 4)
+    else:
+        out["frac_hbm"] = round(byts / t / 1e9 / PEAK_HBM_GBS, 4)
+    out.update(extra)
+    return out
+
+
+def bench_c1(dg, gen, up, dev, timer):
+    """The smallest configuration, dense 128 x 256 x 512 (bound by launch
+    latency; reported, no roofline target)."""
+    print("[bench] detail: c1", file=sys.stderr, flush=True)
+    import torch
+    M, N, K = 128, 256, 512
+    x = gen.gen_dense(M, N, K, seed=0)
+    a, sa, b, sb = up(x.a), up(x.sfa), up(x.b), up(x.sfb)
+    d = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    ws = dg.make_fp8_gemm_nt_workspace(M, N, K, dev)
+    st = timer.measure(lambda: dg.fp8_gemm_nt((a, sa), (b, sb), d, workspace=ws))
+    return {"dense_128x256x512": entry(st, 2.0 * M * N * K, dense_bytes(M, N, K), "hbm",
+                                       kernel=dg.kernel_config_name(dg.FORM_DENSE, M, N, K))}
+
+
+def bench_grouped(dg, gen, up, dev, timer):
+    print("[bench] detail: grouped", file=sys.stderr, flush=True)
     import torch
     out = {}
-    reps = max(3, min(args.steps, 10))
-
-    def timed(fn, n):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n)]
-        fn()
-        torch.cuda.synchronize()
-        for e0, e1 in evs:
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
 
     # contiguous (MoE forward)
     x = gen.gen_contiguous(seed=0)
     a, sa, b, sb, mi = up(x.a), up(x.sfa), up(x.b), up(x.sfb), up(x.m_indices)
     d = torch.empty(x.M_tot, x.N, dtype=torch.bfloat16, device=dev)
-    ms = timed(lambda: dg.m_grouped_fp8_gemm_nt_contiguous((a, sa), (b, sb), d, mi), reps)
+    st = timer.measure(lambda: dg.m_grouped_fp8_gemm_nt_contiguous((a, sa), (b, sb), d, mi))
     valid = int(x.counts.sum())
     flop = 2.0 * valid * x.N * x.K
     byts = x.a.nbytes + x.sfa.nbytes + x.b.nbytes + x.sfb.nbytes + x.m_indices.nbytes + 2 * x.M_tot * x.N
-    out["contiguous_32x4096x4096"] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
-                                         frac_mfma=round(flop / ms / 1e9 / PEAK_FP8_TFLOPS, 4),
-                                         gbs=round(byts / ms / 1e6, 1))
+    out["contiguous_32x4096x4096"] = entry(st, flop, byts, "mfma")
     del a, sa, b, sb, mi, d, x
     torch.cuda.empty_cache()
 
@@ -498,15 +657,13 @@ def bench_grouped(dg, gen, up, dev, stream, args):
     x = gen.gen_masked(seed=0)
     a, sa, b, sb, mm = up(x.a), up(x.sfa), up(x.b), up(x.sfb), up(x.masked_m)
     d = torch.empty(x.G, x.M_max, x.N, dtype=torch.bfloat16, device=dev)
-    ms = timed(lambda: dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d, mm), reps)
+    st = timer.measure(lambda: dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d, mm))
     valid = int(x.masked_m.sum())
     live = int((x.masked_m > 0).sum())
     flop = 2.0 * valid * x.N * x.K
     byts = (valid * x.K + valid * 4 * (x.K // 128) + live * x.N * x.K
             + live * 4 * ((x.N + 127) // 128) * (x.K // 128) + 2 * valid * x.N + 4 * x.G)
-    out["masked_32x256x4096x2048"] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
-                                         gbs=round(byts / ms / 1e6, 1),
-                                         frac_hbm=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
+    out["masked_32x256x4096x2048"] = entry(st, flop, byts, "hbm")
     del a, sa, b, sb, mm, d, x
     torch.cuda.empty_cache()
 
@@ -515,78 +672,37 @@ def bench_grouped(dg, gen, up, dev, stream, args):
     a, sa, b, sb, c = up(x.a), up(x.sfa), up(x.b), up(x.sfb), up(x.c)
     d = torch.empty(x.G, x.M, x.N, dtype=torch.float32, device=dev)
     ks = x.k_sizes
-    ms = timed(lambda: dg.k_grouped_fp8_gemm_tn_contiguous((a, sa), (b, sb), d, ks, c=c), reps)
+    st = timer.measure(lambda: dg.k_grouped_fp8_gemm_tn_contiguous((a, sa), (b, sb), d, ks, c=c))
     flop = 2.0 * x.M * x.N * x.K_tot
     byts = x.a.nbytes + x.sfa.nbytes + x.b.nbytes + x.sfb.nbytes + 2 * 4 * x.G * x.M * x.N
-    out["k_grouped_32x2048x4096"] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
-                                        gbs=round(byts / ms / 1e6, 1),
-                                        frac_hbm=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
+    out["k_grouped_32x2048x4096"] = entry(st, flop, byts, "hbm")
     del a, sa, b, sb, c, d, x
     torch.cuda.empty_cache()
     return out
 
 
-def median_ms(stream, fn, n):
-    """Median HIP-event time of n launches of fn on `stream` (after one warm-up)."""
-    import torch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)]
-    fn()
-    torch.cuda.synchronize()
-    for e0, e1 in evs:
-        e0.record(stream)
-        fn()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
-
-
-def bench_ue8m0(dg, gen, up, dev, stream, args):
+def bench_ue8m0(dg, gen, up, dev, timer):
     """The same workloads with power-of-two scales packed as UE8M0 words (the
     MFMA applies the scales; no separate promotion): the dense sweep shape by
     shape, and the contiguous, masked and K-grouped MoE workloads."""
+    print("[bench] detail: ue8m0", file=sys.stderr, flush=True)
     import torch
-    reps = max(3, min(args.steps, 10))
-    # the dense sweep, timed like the fp32 sweep: whole-sweep steps without
-    # events, and per-shape medians from sweeps with an event pair per launch
     ops = []
     for (M, N, K) in gen.DENSE_SWEEP:
         x = gen.gen_dense_ue8m0(M, N, K, seed=0)
         ops.append(((M, N, K), (up(x.a), up(x.sfa)), (up(x.b), up(x.sfb)),
                     torch.empty(M, N, dtype=torch.bfloat16, device=dev)))
         del x
-
-    def sweep(evs=None):
-        for i, (_, a, b, d) in enumerate(ops):
-            if evs is not None:
-                evs[i][0].record(stream)
-            dg.fp8_gemm_nt(a, b, d)
-            if evs is not None:
-                evs[i][1].record(stream)
-
-    for _ in range(3):
-        sweep()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        sweep()
-    torch.cuda.synchronize()
-    step_ms = (time.perf_counter() - t0) * 1e3 / reps
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in ops] for _ in range(3)]
-    for e in evs:
-        sweep(e)
-    torch.cuda.synchronize()
-    per = np.median([[e[i][0].elapsed_time(e[i][1]) for i in range(len(ops))] for e in evs], axis=0)
-    dense, f_sum = [], 0.0
-    for ((M, N, K), _, _, _), ms in zip(ops, per):
+    ws_bytes = max(dg.get_fp8_gemm_nt_workspace_bytes(*o[0]) for o in ops)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    dense = []
+    for (M, N, K), a, b, d in ops:
+        st = timer.measure(lambda: dg.fp8_gemm_nt(a, b, d, workspace=ws))
         flop = 2.0 * M * N * K
         byts = M * K + N * K + 4 * ((K // 128 + 3) // 4) * (M + N) + 2 * M * N
-        dense.append(dict(M=M, N=N, K=K, us=round(ms * 1e3, 2), tflops=round(flop / ms / 1e9, 1),
-                          gbs=round(byts / ms / 1e6, 1)))
-        f_sum += flop
-    out = {"dense": dense, "dense_sweep_step_ms": round(step_ms, 4),
-           "dense_sweep_tflops": round(f_sum / step_ms / 1e9, 1)}
+        dense.append(dict(M=M, N=N, K=K, **entry(st, flop, byts,
+                                                 "mfma" if flop / byts >= MACHINE_BALANCE else "hbm")))
+    out = {"dense": dense}
     del ops
     torch.cuda.empty_cache()
 
@@ -594,11 +710,10 @@ def bench_ue8m0(dg, gen, up, dev, stream, args):
     wa, wb = gen.to_ue8m0(x.sfa, x.sfb, x.N)
     a, sa, b, sb, mi = up(x.a), up(wa), up(x.b), up(wb), up(x.m_indices)
     d = torch.empty(x.M_tot, x.N, dtype=torch.bfloat16, device=dev)
-    ms = median_ms(stream, lambda: dg.m_grouped_fp8_gemm_nt_contiguous((a, sa), (b, sb), d, mi),
-                   reps)
+    st = timer.measure(lambda: dg.m_grouped_fp8_gemm_nt_contiguous((a, sa), (b, sb), d, mi))
     flop = 2.0 * int(x.counts.sum()) * x.N * x.K
-    out["contiguous_32x4096x4096"] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
-                                         frac_mfma=round(flop / ms / 1e9 / PEAK_FP8_TFLOPS, 4))
+    byts = x.a.nbytes + wa.nbytes + x.b.nbytes + wb.nbytes + x.m_indices.nbytes + 2 * x.M_tot * x.N
+    out["contiguous_32x4096x4096"] = entry(st, flop, byts, "mfma")
     del a, sa, b, sb, mi, d, x, wa, wb
     torch.cuda.empty_cache()
 
@@ -606,16 +721,13 @@ def bench_ue8m0(dg, gen, up, dev, stream, args):
     wa, wb = gen.to_ue8m0(x.sfa, x.sfb, x.N)
     a, sa, b, sb, mm = up(x.a), up(wa), up(x.b), up(wb), up(x.masked_m)
     d = torch.empty(x.G, x.M_max, x.N, dtype=torch.bfloat16, device=dev)
-    ms = median_ms(stream, lambda: dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d, mm), reps)
+    st = timer.measure(lambda: dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d, mm))
     valid = int(x.masked_m.sum())
     live = int((x.masked_m > 0).sum())
     k4 = (x.K // 128 + 3) // 4
     byts = (valid * x.K + valid * 4 * k4 + live * x.N * x.K + live * 4 * k4 * x.N
             + 2 * valid * x.N + 4 * x.G)
-    out["masked_32x256x4096x2048"] = dict(us=round(ms * 1e3, 1),
-                                         tflops=round(2.0 * valid * x.N * x.K / ms / 1e9, 1),
-                                         gbs=round(byts / ms / 1e6, 1),
-                                         frac_hbm=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
+    out["masked_32x256x4096x2048"] = entry(st, 2.0 * valid * x.N * x.K, byts, "hbm")
     del a, sa, b, sb, mm, d, x, wa, wb
     torch.cuda.empty_cache()
 
@@ -624,24 +736,21 @@ def bench_ue8m0(dg, gen, up, dev, stream, args):
     a, sa, b, sb, c = up(x.a), up(wa), up(x.b), up(wb), up(x.c)
     d = torch.empty(x.G, x.M, x.N, dtype=torch.float32, device=dev)
     ks = x.k_sizes
-    ms = median_ms(stream, lambda: dg.k_grouped_fp8_gemm_tn_contiguous((a, sa), (b, sb), d, ks, c=c),
-                   reps)
+    st = timer.measure(lambda: dg.k_grouped_fp8_gemm_tn_contiguous((a, sa), (b, sb), d, ks, c=c))
     flop = 2.0 * x.M * x.N * x.K_tot
     byts = x.a.nbytes + wa.nbytes + x.b.nbytes + wb.nbytes + 2 * 4 * x.G * x.M * x.N
-    out["k_grouped_32x2048x4096"] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
-                                        gbs=round(byts / ms / 1e6, 1),
-                                        frac_hbm=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
+    out["k_grouped_32x2048x4096"] = entry(st, flop, byts, "hbm")
     del a, sa, b, sb, c, d, x, wa, wb
     torch.cuda.empty_cache()
     return out
 
 
-def bench_layouts(dg, gen, up, dev, stream, args):
+def bench_layouts(dg, gen, up, dev, timer):
     """The NN, TN and TT layouts on the 4096 x 4096 x 7168 shape of the dense
     sweep (per-row scales on both operands), and the M-grouped contiguous NN
     form on the contiguous MoE workload (32 experts, N = K = 4096)."""
+    print("[bench] detail: layouts", file=sys.stderr, flush=True)
     import torch
-    reps = max(3, min(args.steps, 10))
     out = {}
     M, N, K = 4096, 4096, 7168
     fns = {"nn": dg.fp8_gemm_nn, "tn": dg.fp8_gemm_tn, "tt": dg.fp8_gemm_tt}
@@ -649,48 +758,44 @@ def bench_layouts(dg, gen, up, dev, stream, args):
         x = gen.gen_layout(layout, M, N, K, seed=0)
         a, sa, b, sb = up(x.a), up(x.sfa), up(x.b), up(x.sfb)
         d = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        ms = median_ms(stream, lambda: fn((a, sa), (b, sb), d), reps)
-        flop = 2.0 * M * N * K
-        out[f"{layout}_{M}x{N}x{K}"] = dict(
+        st = timer.measure(lambda: fn((a, sa), (b, sb), d))
+        byts = x.a.nbytes + x.sfa.nbytes + x.b.nbytes + x.sfb.nbytes + 2 * M * N
+        out[f"{layout}_{M}x{N}x{K}"] = entry(
+            st, 2.0 * M * N * K, byts, "mfma",
             kernel=dg.kernel_config_name({"nn": dg.FORM_NN, "tn": dg.FORM_TN, "tt": dg.FORM_TT}[layout],
-                                         M, N, K),
-            us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
-            frac_mfma=round(flop / ms / 1e9 / PEAK_FP8_TFLOPS, 4))
+                                         M, N, K))
         del x, a, sa, b, sb, d
     torch.cuda.empty_cache()
     x = gen.gen_nn_contiguous(seed=0)
     a, sa, b, sb, mi = up(x.a), up(x.sfa), up(x.b), up(x.sfb), up(x.m_indices)
     d = torch.empty(x.M_tot, x.N, dtype=torch.bfloat16, device=dev)
-    ms = median_ms(stream, lambda: dg.m_grouped_fp8_gemm_nn_contiguous((a, sa), (b, sb), d, mi),
-                   reps)
+    st = timer.measure(lambda: dg.m_grouped_fp8_gemm_nn_contiguous((a, sa), (b, sb), d, mi))
     flop = 2.0 * int(x.counts.sum()) * x.N * x.K
-    out["nn_contiguous_32x4096x4096"] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
-                                             frac_mfma=round(flop / ms / 1e9 / PEAK_FP8_TFLOPS, 4))
+    byts = x.a.nbytes + x.sfa.nbytes + x.b.nbytes + x.sfb.nbytes + x.m_indices.nbytes + 2 * x.M_tot * x.N
+    out["nn_contiguous_32x4096x4096"] = entry(st, flop, byts, "mfma")
     del a, sa, b, sb, mi, d, x
     torch.cuda.empty_cache()
     return out
 
 
-def bench_mqa(dg, gen, up, dev, stream, args):
+def bench_mqa(dg, gen, up, dev, timer):
     """FP8 MQA logits: 64 heads, head_dim 128, one causal sequence of 4096
     queries over 4096 kv tokens (and 8 packed sequences of 512), -inf cleaning.
     Algorithmic FLOP = 2 * H * D per in-range (query, token) pair; bytes =
     q + kv + kv scales + weights + ranges + the fp32 logits written."""
+    print("[bench] detail: mqa", file=sys.stderr, flush=True)
     import torch
-    reps = max(3, min(args.steps, 10))
     out = {}
     for name, lens in (("causal_4096x4096_h64", None), ("packed_8x512_h64", [512] * 8)):
         x = gen.gen_mqa(4096, 4096, H=64, seed=0, seq_lens=lens)
         q, kv, sf, w, ks, ke = up(x.q), up(x.kv), up(x.kv_sf), up(x.weights), up(x.ks), up(x.ke)
         o = torch.empty(x.S, x.S_kv, dtype=torch.float32, device=dev)
-        ms = median_ms(stream, lambda: dg.fp8_mqa_logits(q, (kv, sf), w, ks, ke, True, out=o), reps)
+        st = timer.measure(lambda: dg.fp8_mqa_logits(q, (kv, sf), w, ks, ke, True, out=o))
         pairs = int(np.clip(x.ke, 0, x.S_kv).astype(np.int64).sum()
                     - np.clip(x.ks, 0, x.S_kv).astype(np.int64).sum())
         flop = 2.0 * x.H * x.D * pairs
         byts = x.q.nbytes + x.kv.nbytes + x.kv_sf.nbytes + x.weights.nbytes + 8 * x.S + 4 * x.S * x.S_kv
-        out[name] = dict(us=round(ms * 1e3, 1), tflops=round(flop / ms / 1e9, 1),
-                         frac_mfma=round(flop / ms / 1e9 / PEAK_FP8_TFLOPS, 4),
-                         gbs=round(byts / ms / 1e6, 1), pairs=pairs)
+        out[name] = entry(st, flop, byts, "mfma", pairs=pairs)
         del x, q, kv, sf, w, ks, ke, o
     torch.cuda.empty_cache()
     return out
@@ -720,64 +825,37 @@ def cast_bytes(per_block, shape):
     return 2 * n + n + 4 * n_sf
 
 
-def bench_cast(dg, dev, stream, args):
+def bench_cast(dg, dev, timer):
     """HIP-event times of the casting kernels on bf16 operands of the GEMM
     workloads' shapes (inputs resident in HBM), against the HBM roof."""
+    print("[bench] detail: cast", file=sys.stderr, flush=True)
     import torch
     out = {}
-    reps = max(3, min(args.steps, 10))
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     for name, (per_block, shape) in CAST_WORKLOADS.items():
         x = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
         fn = dg.per_block_cast_to_fp8 if per_block else dg.per_token_cast_to_fp8
         codes, sf = fn(x)
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        for e0, e1 in evs:
-            e0.record(stream)
-            fn(x, out=(codes, sf))
-            e1.record(stream)
-        torch.cuda.synchronize()
-        ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+        st = timer.measure(lambda: fn(x, out=(codes, sf)))
         byts = cast_bytes(per_block, shape)
-        out[name] = dict(us=round(ms * 1e3, 1), gbs=round(byts / ms / 1e6, 1),
-                         frac_hbm=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4), bytes=byts)
+        out[name] = entry(st, 0.0, byts, "hbm", bytes=byts)
         del x, codes, sf
         torch.cuda.empty_cache()
     return out
 
 
-def summarize_cast(trace_dir, bench_json, out_path):
-    """profiles/ summary of the casting kernels: rocprofv3 per-kernel averages
-    next to bench.py's HIP-event timings of the same run."""
-    import csv
-    res = json.load(open(bench_json))
-    cast = res["detail"]["cast"]
-    stats = [r for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv")))
-             if "cast_kernel" in r["Name"]]
-    lines = ["# FP8 casting kernels (per token 1x128, per block 128x128) -- rocprofv3 kernel trace",
-             "", "Commands (run from the repository root on one MI355X):", ""]
-    lines += [f"    {c}" for c in GROUPED_PROFILE_COMMANDS[:1]]
-    lines += [f"    python3 bench.py --summarize-cast gpurun_out/prof_grouped "
-              f"gpurun_out/bench_grouped.json {os.path.relpath(out_path, ROOT)}"]
-    lines += ["", "Template arguments: input type (`unsigned short` = bf16 bits), rows per wave,",
-              "per-block flag (true = 128 x 128 weights).", "",
-              "## Kernel trace (--kernel-trace --stats)", "",
-              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
-    for r in stats:
-        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    lines += ["", "## bench.py HIP-event timings (same run; bf16 in, e4m3 + fp32 scales out)", "",
-              "| workload | us | algorithmic MB | GB/s | fraction of HBM roof (8 TB/s) |",
-              "|---|---|---|---|---|"]
-    for name, v in cast.items():
-        lines.append(f"| {name} | {v['us']} | {v['bytes'] / 1e6:.1f} | {v['gbs']} | {v['frac_hbm']} |")
-    lines += ["", f"    kernel_source_sha256_16: cast {source_hash('cast')}", ""]
-    with open(out_path, "w") as f:
-        f.write("\n".join(lines))
-    print(out_path)
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu), for the CPU-baseline record."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return "unknown"
 
 
 def cpu_baseline(gen, shape, target_s):
@@ -798,7 +876,7 @@ def cpu_baseline(gen, shape, target_s):
     t = time.perf_counter() - t0
     flop = 2.0 * n * N * K
     return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{n} of {M} rows of the dense {M}x{N}x{K} shape (all {N} columns), "
                       f"{t:.1f} s, fp64 exact block sums"}
 

@@ -53,6 +53,7 @@ EXPORTED = (
     "dg_fp8_mqa_logits",
     "dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0",
     "dg_pack_ue8m0_scales_k_grouped",
+    "dg_fp8_gemm_nt_workspace_bytes",
 )
 DG_CAST_POW2_SCALE = 1
 
@@ -76,7 +77,9 @@ def load_library(path: Optional[str] = None):
                           "(or __graft_entry__.build())")
     lib = ctypes.CDLL(p)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    lib.dg_fp8_gemm_nt.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
+    lib.dg_fp8_gemm_nt.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P, I64, P]
+    lib.dg_fp8_gemm_nt_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.dg_fp8_gemm_nt_workspace_bytes.restype = I64
     lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
     lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
     lib.dg_k_grouped_fp8_gemm_tn_contiguous.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, P]
@@ -95,7 +98,7 @@ def load_library(path: Optional[str] = None):
     for name in ("dg_per_token_cast_to_fp8", "dg_per_block_cast_to_fp8"):
         getattr(lib, name).argtypes = [P, I, P, P, I64, I64, I64, I, P]
         getattr(lib, name).restype = I
-    lib.dg_fp8_gemm_nt_ue8m0.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
+    lib.dg_fp8_gemm_nt_ue8m0.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P, I64, P]
     lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0.argtypes = [P, P, P, P, P, P, I64, I64, I64,
                                                               I64, P]
     lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
@@ -173,11 +176,31 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def get_fp8_gemm_nt_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Split-K workspace bytes a dense NT call of this shape needs (0: none)."""
+    return int(load_library().dg_fp8_gemm_nt_workspace_bytes(M, N, K))
+
+
+def make_fp8_gemm_nt_workspace(M: int, N: int, K: int, device=None) -> Optional[torch.Tensor]:
+    """A zero-filled workspace for dense NT calls of this shape (None when the
+    shape needs none).  Stream-ordered calls may reuse it: every call leaves
+    its counters zero again."""
+    n = get_fp8_gemm_nt_workspace_bytes(M, N, K)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device or torch.cuda.current_device())
+
+
 def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, torch.Tensor],
-                d: torch.Tensor, c: Optional[torch.Tensor] = None) -> torch.Tensor:
+                d: torch.Tensor, c: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """d[M,N] = c + a @ b^T.  a = (A [M,K], SFA [K/128, M]), b = (B [N,K],
     SFB [ceil(N/128), K/128]); d bf16 or fp32; c None or like d (may be d).
-    Packed UE8M0 scales (int32): SFA [ceil(K/512), M], SFB [ceil(K/512), N]."""
+    Packed UE8M0 scales (int32): SFA [ceil(K/512), M], SFB [ceil(K/512), N].
+    workspace: a uint8 device buffer of at least
+    get_fp8_gemm_nt_workspace_bytes(M, N, K) bytes whose counters are zero
+    (make_fp8_gemm_nt_workspace); when None and the shape splits K, a
+    zero-filled one is allocated for this call from torch's allocator."""
     A, B = _fp8(a[0], "A"), _fp8(b[0], "B")
     SA, SB, ue8m0 = _scales(a[1], b[1])
     d = _dev(d, "d")
@@ -197,9 +220,19 @@ def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, tor
         raise ValueError(f"scale shapes: SFA {tuple(SA.shape)} SFB {tuple(SB.shape)}, want {want}")
     fn = "dg_fp8_gemm_nt_ue8m0" if ue8m0 else "dg_fp8_gemm_nt"
     with torch.cuda.device(d.device):
+        need = get_fp8_gemm_nt_workspace_bytes(M, N, K)
+        if workspace is None and need > 0:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=d.device)
+        ws_bytes = 0
+        if workspace is not None:
+            workspace = _dev(workspace, "workspace")
+            if workspace.dtype != torch.uint8:
+                raise TypeError("workspace must be uint8")
+            ws_bytes = workspace.numel()
         _check(getattr(load_library(), fn)(
             _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(c), _ptr(d),
-            DG_F32 if d.dtype == torch.float32 else DG_BF16, M, N, K, _stream(d)))
+            DG_F32 if d.dtype == torch.float32 else DG_BF16, M, N, K,
+            _ptr(workspace), ws_bytes, _stream(d)))
     return d
 
 

@@ -11,10 +11,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <map>
 #include <mutex>
 #include <string>
-#include <utility>
 
 namespace {
 
@@ -100,23 +98,13 @@ int cu_cap_for(const DeviceInfo& info) {
 }
 
 bool print_configs() {
-    static int v = -1;
-    if (v < 0) {
+    // read once; the initialisation of a function-local static is thread-safe
+    static const bool v = [] {
         const char* s = getenv("DG_PRINT_CONFIGS");
-        v = (s && s[0] == '1') ? 1 : 0;
-    }
-    return v == 1;
+        return s != nullptr && s[0] == '1';
+    }();
+    return v;
 }
-
-// ---- split-K workspace ------------------------------------------------------------
-
-struct Workspace {
-    float* part = nullptr;
-    int32_t* counters = nullptr;
-    size_t part_floats = 0, n_counters = 0;
-};
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-std::mutex g_ws_mutex;
 
 dg_status run_tn(const dg::TnProblem& p, void* stream) {
     int dev = 0;
@@ -134,65 +122,23 @@ dg_status run_nt(dg::NtProblem p, void* stream) {
     DeviceInfo info;
     dg_status st = current_device(dev, info);
     if (st != DG_OK) return st;
-    p.device_cus = info.cus;
     if (print_configs()) fprintf(stderr, "[dg] %s\n", dg::describe_nt_config(p));
     hipError_t e = dg::launch_nt(p, cu_cap_for(info), reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     return ok();
 }
 
-}  // namespace
-
-namespace dg {
-
-bool split_workspace(hipStream_t stream, size_t part_floats, size_t n_counters,
-                     SplitWorkspace* ws) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return false;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace& w = g_ws[{dev, stream}];
-    if (w.part_floats < part_floats || w.n_counters < n_counters) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
-            return false;
-        // grow to cover this request and every earlier one
-        const size_t pf = part_floats > w.part_floats ? part_floats : w.part_floats;
-        const size_t nc = n_counters > w.n_counters ? n_counters : w.n_counters;
-        // the old buffers may still be in use by work queued on this stream
-        if (w.part || w.counters) {
-            if (hipStreamSynchronize(stream) != hipSuccess) return false;
-            (void)hipFree(w.part);
-            (void)hipFree(w.counters);
-            w = Workspace{};
-        }
-        float* part = nullptr;
-        int32_t* counters = nullptr;
-        if (hipMalloc(&part, pf * sizeof(float)) != hipSuccess) return false;
-        if (hipMalloc(&counters, nc * sizeof(int32_t)) != hipSuccess ||
-            hipMemsetAsync(counters, 0, nc * sizeof(int32_t), stream) != hipSuccess) {
-            (void)hipFree(part);
-            if (counters) (void)hipFree(counters);
-            return false;
-        }
-        w.part = part;
-        w.counters = counters;
-        w.part_floats = pf;
-        w.n_counters = nc;
-    }
-    ws->part = w.part;
-    ws->counters = w.counters;
-    return true;
+// [p0, p0 + n0) and [p1, p1 + n1) do not overlap
+bool disjoint(const void* p0, int64_t n0, const void* p1, int64_t n1) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p0), a1 = reinterpret_cast<uintptr_t>(p1);
+    return a0 + (uintptr_t)n0 <= a1 || a1 + (uintptr_t)n1 <= a0;
 }
-
-}  // namespace dg
-
-namespace {
 
 // The three NT forms take either fp32 scales or packed UE8M0 words; both are
 // 4-byte elements, passed through as raw pointers.
 dg_status gemm_nt(const uint8_t* a, const void* sfa_, const uint8_t* b, const void* sfb_,
                   const void* c, void* d, dg_dtype d_dtype, int64_t M, int64_t N, int64_t K,
-                  bool ue8m0, void* stream) {
+                  void* workspace, int64_t workspace_bytes, bool ue8m0, void* stream) {
     const float* sfa = static_cast<const float*>(sfa_);
     const float* sfb = static_cast<const float*>(sfb_);
     REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size (M=%lld N=%lld K=%lld)", (long long)M,
@@ -206,8 +152,8 @@ dg_status gemm_nt(const uint8_t* a, const void* sfa_, const uint8_t* b, const vo
     if (K > 0) {   // with K == 0 the operands are empty: D = C (or 0)
         REQUIRE_PTR(a, 16);
         REQUIRE_PTR(b, 16);
-        REQUIRE_PTR(sfa, 4);
-        REQUIRE_PTR(sfb, 4);
+        REQUIRE_PTR(sfa, 16);
+        REQUIRE_PTR(sfb, 16);
     }
     REQUIRE(M <= kOffsetLimit / (K > 0 ? K : 1) && N <= kOffsetLimit / (K > 0 ? K : 1),
             "M*K and N*K must stay below 2^31");
@@ -216,12 +162,30 @@ dg_status gemm_nt(const uint8_t* a, const void* sfa_, const uint8_t* b, const vo
     REQUIRE(((M + 63) / 64) * ((N + 63) / 64) <= INT_MAX / 8, "too many tiles");
     const int64_t dbytes = M * N * (d_dtype == DG_F32 ? 4 : 2);
     REQUIRE(alias_ok(c, d, dbytes), "c overlaps d without being equal to it");
+    REQUIRE(workspace_bytes >= 0, "workspace_bytes=%lld is negative", (long long)workspace_bytes);
+    const int64_t need = dg::nt_dense_workspace_bytes(M, N, K);
+    if (need > 0) {
+        REQUIRE(workspace != nullptr,
+                "this shape splits K and needs a workspace of %lld bytes "
+                "(dg_fp8_gemm_nt_workspace_bytes); workspace is NULL", (long long)need);
+        REQUIRE_PTR(workspace, 16);
+        REQUIRE(workspace_bytes >= need, "workspace_bytes=%lld < %lld needed for this shape",
+                (long long)workspace_bytes, (long long)need);
+        const int64_t KB = K / 128, sf_w = ue8m0 ? (KB + 3) / 4 : KB;
+        const int64_t sfb_n = ue8m0 ? sf_w * N : ((N + 127) / 128) * KB;
+        REQUIRE(disjoint(workspace, need, d, dbytes) && (c == nullptr || disjoint(workspace, need, c, dbytes)) &&
+                    disjoint(workspace, need, a, M * K) && disjoint(workspace, need, b, N * K) &&
+                    disjoint(workspace, need, sfa, 4 * sf_w * M) && disjoint(workspace, need, sfb, 4 * sfb_n),
+                "workspace overlaps an operand or the output");
+    }
     dg::NtProblem p{};
     p.form = dg::kDense;
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.c = c; p.d = d;
     p.rows = M; p.N = N; p.K = K; p.G = 1;
     p.out_f32 = d_dtype == DG_F32;
     p.ue8m0 = ue8m0;
+    p.workspace = need > 0 ? workspace : nullptr;
+    p.workspace_bytes = need > 0 ? workspace_bytes : 0;
     return run_nt(p, stream);
 }
 
@@ -240,9 +204,9 @@ dg_status gemm_nt_contiguous(const uint8_t* a, const void* sfa_, const uint8_t* 
     REQUIRE_PTR(a, 16);
     REQUIRE_PTR(b, 16);
     REQUIRE_PTR(d, 16);
-    REQUIRE_PTR(sfa, 4);
-    REQUIRE_PTR(sfb, 4);
-    REQUIRE_PTR(m_indices, 4);
+    REQUIRE_PTR(sfa, 16);
+    REQUIRE_PTR(sfb, 16);
+    REQUIRE_PTR(m_indices, 16);
     REQUIRE(M_tot <= kOffsetLimit / (K > 0 ? K : 1) && N <= kOffsetLimit / (K > 0 ? K : 1),
             "M_tot*K and N*K must stay below 2^31");
     REQUIRE(G <= INT_MAX, "G too large");
@@ -268,9 +232,9 @@ dg_status gemm_nt_masked(const uint8_t* a, const void* sfa_, const uint8_t* b, c
     REQUIRE_PTR(a, 16);
     REQUIRE_PTR(b, 16);
     REQUIRE_PTR(d, 16);
-    REQUIRE_PTR(sfa, 4);
-    REQUIRE_PTR(sfb, 4);
-    REQUIRE_PTR(masked_m, 4);
+    REQUIRE_PTR(sfa, 16);
+    REQUIRE_PTR(sfb, 16);
+    REQUIRE_PTR(masked_m, 16);
     REQUIRE(M_max <= kOffsetLimit / (K > 0 ? K : 1) && N <= kOffsetLimit / (K > 0 ? K : 1),
             "M_max*K and N*K must stay below 2^31");
     // bound for the smallest tile (64 x 64) any configuration uses
@@ -291,8 +255,15 @@ extern "C" {
 
 dg_status dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                          const void* c, void* d, dg_dtype d_dtype, int64_t M, int64_t N,
-                         int64_t K, void* stream) {
-    return gemm_nt(a, sfa, b, sfb, c, d, d_dtype, M, N, K, false, stream);
+                         int64_t K, void* workspace, int64_t workspace_bytes, void* stream) {
+    return gemm_nt(a, sfa, b, sfb, c, d, d_dtype, M, N, K, workspace, workspace_bytes, false,
+                   stream);
+}
+
+int64_t dg_fp8_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || N % 16 != 0) return 0;
+    if (M > kOffsetLimit / K || N > kOffsetLimit / K) return 0;
+    return dg::nt_dense_workspace_bytes(M, N, K);
 }
 
 dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa,
@@ -311,8 +282,10 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, co
 
 dg_status dg_fp8_gemm_nt_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
                                const int32_t* sfb, const void* c, void* d, dg_dtype d_dtype,
-                               int64_t M, int64_t N, int64_t K, void* stream) {
-    return gemm_nt(a, sfa, b, sfb, c, d, d_dtype, M, N, K, true, stream);
+                               int64_t M, int64_t N, int64_t K, void* workspace,
+                               int64_t workspace_bytes, void* stream) {
+    return gemm_nt(a, sfa, b, sfb, c, d, d_dtype, M, N, K, workspace, workspace_bytes, true,
+                   stream);
 }
 
 dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const uint8_t* a, const int32_t* sfa,
@@ -338,8 +311,8 @@ dg_status dg_pack_ue8m0_scales(const float* sf, int per_block, int32_t* packed, 
     REQUIRE(K % 128 == 0, "K=%lld is not a multiple of 128", (long long)K);
     REQUIRE(per_block == 0 || per_block == 1, "per_block must be 0 or 1");
     if (G == 0 || MN == 0 || K == 0) return ok();
-    REQUIRE_PTR(sf, 4);
-    REQUIRE_PTR(packed, 4);
+    REQUIRE_PTR(sf, 16);
+    REQUIRE_PTR(packed, 16);
     const int64_t kb = K / 128, k4 = (kb + 3) / 4;
     REQUIRE(MN <= INT_MAX && G <= kOffsetLimit / k4 && G * k4 <= kOffsetLimit / MN,
             "G*ceil(K/512)*MN must stay below 2^31");
@@ -398,8 +371,8 @@ dg_status dg_pack_ue8m0_scales_k_grouped(const float* sf, const int32_t* k_sizes
     REQUIRE(total == K_tot, "sum of k_sizes_host (%lld) != K_tot (%lld)", (long long)total,
             (long long)K_tot);
     if (MN == 0 || words == 0) return ok();
-    REQUIRE_PTR(sf, 4);
-    REQUIRE_PTR(packed, 4);
+    REQUIRE_PTR(sf, 16);
+    REQUIRE_PTR(packed, 16);
     // the kernel's 32-bit column index runs up to one 256-thread block past MN
     REQUIRE(MN <= INT_MAX - 256, "MN=%lld too large", (long long)MN);
     REQUIRE(words <= 65535, "too many packed word rows");
@@ -525,7 +498,7 @@ dg_status dg_m_grouped_fp8_gemm_nn_contiguous(const uint8_t* a, const float* sfa
     REQUIRE_PTR(d, 16);
     REQUIRE_PTR(sfa, 16);
     REQUIRE_PTR(sfb, 16);
-    REQUIRE_PTR(m_indices, 4);
+    REQUIRE_PTR(m_indices, 16);
     REQUIRE(M_tot <= kOffsetLimit / (K > 0 ? K : 1) && N <= kOffsetLimit / (K > 0 ? K : 1),
             "M_tot*K and K*N must stay below 2^31");
     REQUIRE(G <= INT_MAX && (M_tot / 128) * ((N + 255) / 256) <= INT_MAX, "too many tiles");
@@ -547,7 +520,7 @@ static dg_status run_cast(const void* x, dg_dtype dtype, uint8_t* codes, float* 
     if (G == 0 || R == 0 || K == 0) return ok();
     REQUIRE_PTR(x, 16);
     REQUIRE_PTR(codes, 16);
-    REQUIRE_PTR(sf, 4);
+    REQUIRE_PTR(sf, 16);
     REQUIRE(R <= kOffsetLimit && K <= kOffsetLimit, "size too large");
     REQUIRE(G <= kOffsetLimit && R <= kOffsetLimit / K, "rows*K must stay below 2^31");
     const int64_t n = G * R * K;   // < 2^62
@@ -600,9 +573,9 @@ dg_status dg_fp8_mqa_logits(const uint8_t* q, const uint8_t* kv, const float* kv
     REQUIRE_PTR(kv, 16);
     REQUIRE_PTR(weights, 16);
     REQUIRE_PTR(logits, 16);
-    REQUIRE_PTR(kv_sf, 4);
-    REQUIRE_PTR(ks, 4);
-    REQUIRE_PTR(ke, 4);
+    REQUIRE_PTR(kv_sf, 16);
+    REQUIRE_PTR(ks, 16);
+    REQUIRE_PTR(ke, 16);
     // token indices are 32-bit and run up to one workgroup (256 tokens) past S_kv
     REQUIRE(S <= 65535LL * 16 && S_kv <= INT_MAX - 4096,
             "seq_len must be <= 1048560 and seq_len_kv <= 2^31 - 4097");

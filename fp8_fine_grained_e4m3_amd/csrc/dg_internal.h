@@ -27,8 +27,15 @@ struct NtProblem {
     // 4 k4 + i), sfa [K4, rows] (masked: [G, K4, M_max]), sfb [G, K4, N],
     // K4 = ceil(KB / 4).
     bool ue8m0;
-    int device_cus;           // CUs of the device (not the cap): sizes the K split
+    // Dense only: caller-owned split-K workspace (nt_dense_workspace_bytes;
+    // NULL / 0 when that is 0).
+    void* workspace;
+    int64_t workspace_bytes;
 };
+
+// Bytes of split-K workspace a dense NT problem needs (0: K is not split).
+// A function of the shape alone: no device query, no HIP call.
+int64_t nt_dense_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // MN-major kernel family: the K-grouped TN form, the dense NN / TN / TT
 // layouts and the M-grouped contiguous NN form.  Both operands carry one fp32
@@ -97,20 +104,6 @@ struct MqaProblem {
     bool clean;
 };
 hipError_t launch_mqa(const MqaProblem& p, hipStream_t stream);
-
-// Device memory for split-K partial tiles, one buffer per (device, stream),
-// grown on demand and kept until the process ends.  `counters` are zero
-// whenever no kernel using them is running (each launch leaves them zero).
-struct SplitWorkspace {
-    float* part = nullptr;
-    int32_t* counters = nullptr;
-};
-// Provide at least part_floats floats and n_counters counters for kernels on
-// `stream`.  Returns false when that is not possible (allocation failure, or
-// the buffer would have to grow while the stream is being captured); the
-// caller then runs without splitting K.
-bool split_workspace(hipStream_t stream, size_t part_floats, size_t n_counters,
-                     SplitWorkspace* ws);
 
 // Launch on `stream`; `cu_cap` bounds the persistent grid.  Return the HIP
 // status of the launch.  Shapes have already been validated.

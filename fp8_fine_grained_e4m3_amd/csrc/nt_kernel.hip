@@ -120,6 +120,12 @@ struct NtCfg {
     static_assert(BN % 16 == 0 && 64 % (BN / 4) == 0 && (WTM * EPI_WAVE_ROWS) % (64 / (BN / 4)) == 0,
                   "staged rows split evenly into wave instructions");
     static_assert(!(FULL_PREFETCH && EARLY_B), "whole-block prefetch uses the plain stage ring");
+    // Workgroups resident per CU: bounded by the 160 KiB of LDS and by the
+    // two waves per SIMD every instance is compiled for (8 waves per CU).
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + 256 * WAVES;
+    static constexpr int WG_PER_CU =
+        (160 * 1024 / LDS_BYTES) < (8 / WAVES) ? (160 * 1024 / LDS_BYTES) : (8 / WAVES);
+    static_assert(WG_PER_CU >= 1, "one workgroup fits a CU");
 };
 
 // Row and LDS maps.
@@ -822,35 +828,56 @@ namespace {
 constexpr int kBandMDense = 4;        // M tiles per rasterisation band, dense
 constexpr int kBandMContiguous = 8;   // contiguous groups (expert panels are larger)
 
+constexpr int64_t kRefCus = 256;   // MI355X CU count: tile and split choices are functions of the shape
 constexpr int kMinSplitBlocks = 8;   // K blocks per split work unit, at least
 constexpr int kMaxSplits = 8;
 
-template <class Cfg, int FORM, bool OUT_F32, bool UE8M0>
-int occupancy_of() {
-    static int occupancy = -1;   // workgroups per CU for this instance
-    if (occupancy < 0) {
-        int occ = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &occ, reinterpret_cast<const void*>(&nt_fp8_kernel<Cfg, FORM, OUT_F32, UE8M0>),
-                Cfg::THREADS, 0) != hipSuccess || occ < 1)
-            occ = 1;
-        occupancy = occ;
-    }
-    return occupancy;
-}
-
 // K split for a dense problem with too few output tiles to give every
 // resident workgroup slot of the device work: as many splits as fill the
-// slots, each split keeping at least kMinSplitBlocks K blocks.  It depends on
-// the shape and the device's CU count only (not on the CU cap), so results
-// are the same under any cap.
-int split_count(int64_t tiles, int KB, int device_cus, int occupancy) {
-    const int64_t slots = (int64_t)device_cus * occupancy;
+// slots, each split keeping at least kMinSplitBlocks K blocks.  It is a
+// function of the shape alone (slots are counted on the 256-CU part, with
+// the configuration's designed workgroups per CU), so results and the
+// workspace size do not depend on the device, the CU cap or the caller.
+int split_count(int64_t tiles, int KB, int wg_per_cu) {
+    const int64_t slots = kRefCus * wg_per_cu;
     if (tiles <= 0 || tiles * 2 > slots || KB < 2 * kMinSplitBlocks) return 1;
     int64_t sp = slots / tiles;
     if (sp > KB / kMinSplitBlocks) sp = KB / kMinSplitBlocks;
     if (sp > kMaxSplits) sp = kMaxSplits;
     return sp < 1 ? 1 : (int)sp;
+}
+
+// Split-K workspace of a dense problem: a fixed region of arrival counters
+// (one int32 per output tile), then the fp32 partial tiles
+// [tiles][splits][BM * BN].  The counter region has the same place and size
+// for every shape -- a split problem has at most kMaxSplitTiles tiles -- so
+// one workspace serves any sequence of shapes: no shape's partials ever land
+// on another shape's counters, and every call leaves all counters zero.
+// Zero bytes when K is not split.
+constexpr int64_t kMaxSplitTiles = kRefCus;        // tiles * 2 <= kRefCus * WG_PER_CU, WG_PER_CU <= 2
+constexpr int64_t kCounterBytes = 4 * kMaxSplitTiles;
+
+struct SplitPlan {
+    int64_t tiles = 0;
+    int splits = 1;
+    int64_t bytes = 0;
+};
+
+template <class Cfg>
+SplitPlan split_plan(int64_t rows, int64_t N, int64_t K) {
+    static_assert(!Cfg::SPLIT_OK || Cfg::WG_PER_CU <= 2, "split tiles fit the counter region");
+    SplitPlan sp;
+    if (!Cfg::SPLIT_OK) return sp;
+    sp.tiles = ((rows + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
+    sp.splits = split_count(sp.tiles, (int)(K / kKBlk), Cfg::WG_PER_CU);
+    if (sp.splits > 1) {
+        if (sp.tiles > kMaxSplitTiles) {   // excluded by split_count; kept as a guard
+            sp.splits = 1;
+            return sp;
+        }
+        sp.bytes = kCounterBytes + sp.tiles * sp.splits * Cfg::BM * Cfg::BN * 4;
+    }
+    return sp;
 }
 
 template <class Cfg, int FORM, bool OUT_F32, bool UE8M0>
@@ -870,24 +897,23 @@ hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     const int64_t groups = (FORM == kMasked) ? pr.G : (FORM == kContiguous ? 2 : 1);
     const int64_t tiles = groups * a.tiles_m * a.tiles_n;
     if (tiles <= 0) return hipSuccess;
-    const int occupancy = occupancy_of<Cfg, FORM, OUT_F32, UE8M0>();
 
     a.splits = 1;
     a.part = nullptr;
     a.counters = nullptr;
-    if (FORM == kDense && Cfg::SPLIT_OK) {
-        const int sp = split_count(tiles, (int)(pr.K / kKBlk), pr.device_cus, occupancy);
-        SplitWorkspace ws;
-        if (sp > 1 && split_workspace(stream, (size_t)tiles * sp * Cfg::BM * Cfg::BN,
-                                      (size_t)tiles, &ws)) {
-            a.splits = sp;
-            a.part = ws.part;
-            a.counters = ws.counters;
+    if (FORM == kDense) {
+        const SplitPlan sp = split_plan<Cfg>(pr.rows, pr.N, pr.K);
+        if (sp.splits > 1) {
+            // the C-ABI layer has checked the caller's workspace against the plan
+            if (pr.workspace == nullptr || pr.workspace_bytes < sp.bytes) return hipErrorInvalidValue;
+            a.splits = sp.splits;
+            a.counters = static_cast<int32_t*>(pr.workspace);
+            a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(pr.workspace) + kCounterBytes);
         }
     }
     a.num_tiles = (int)(tiles * a.splits);
 
-    const int64_t resident = (int64_t)cu_cap * occupancy;
+    const int64_t resident = (int64_t)cu_cap * Cfg::WG_PER_CU;
     const int grid = (int)(a.num_tiles < resident ? a.num_tiles : resident);
     a.xcd_blk_m = 0;
     a.xcd_units = 0;
@@ -917,7 +943,6 @@ using Cfg64x64 = NtCfg<64, 64, 1, 4, 4>;
 // every B byte is used once) narrow 64-column tiles with deeper pipelines, so
 // more workgroups stream B with more bytes in flight each.
 enum NtTile { kT64x64, kT128x64, kT128x128, kT256x256 };
-constexpr int64_t kRefCus = 256;   // MI355X CU count: the tile choice is a function of the shape
 
 NtTile choose_tile(const NtProblem& pr) {
     if (pr.form == kContiguous) return kT256x256;
@@ -934,6 +959,18 @@ NtTile choose_tile(const NtProblem& pr) {
         ((pr.rows + 255) / 256) * ((pr.N + 255) / 256) * 2 >= (int64_t)kRefCus)
         return kT256x256;
     return kT128x128;
+}
+
+SplitPlan dense_split_plan(int64_t M, int64_t N, int64_t K) {
+    NtProblem pr{};
+    pr.form = kDense;
+    pr.rows = M; pr.N = N; pr.K = K; pr.G = 1;
+    switch (choose_tile(pr)) {
+    case kT64x64: return split_plan<Cfg64x64>(M, N, K);
+    case kT128x64: return split_plan<Cfg128x64>(M, N, K);
+    case kT256x256: return split_plan<Cfg256x256>(M, N, K);
+    default: return split_plan<Cfg128x128>(M, N, K);
+    }
 }
 
 template <int FORM, bool OUT_F32, bool UE8M0>
@@ -969,6 +1006,10 @@ hipError_t dispatch_forms(const NtProblem& pr, int cu_cap, hipStream_t stream) {
 }
 
 }  // namespace
+
+int64_t nt_dense_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    return dense_split_plan(M, N, K).bytes;
+}
 
 hipError_t launch_nt(const NtProblem& pr, int cu_cap, hipStream_t stream) {
     return pr.ue8m0 ? dispatch_forms<true>(pr, cu_cap, stream)

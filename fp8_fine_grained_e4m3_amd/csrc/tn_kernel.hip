@@ -109,6 +109,12 @@ struct TnCfg {
     static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "row widths");
     static_assert(WTM % 64 == 0 && WTN % 16 == 0, "wave tile");
     static_assert(STAGES >= 2 && (STAGES - 2) * VM_PER_STAGE <= 63, "vmcnt range");
+    // Workgroups resident per CU: bounded by the 160 KiB of LDS and by the
+    // two waves per SIMD the kernel is compiled for (8 waves per CU).
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int WG_PER_CU =
+        (160 * 1024 / LDS_BYTES) < (8 / WAVES) ? (160 * 1024 / LDS_BYTES) : (8 / WAVES);
+    static_assert(WG_PER_CU >= 1, "one workgroup fits a CU");
 };
 
 // Swizzle of an MN-major LDS tile with W-byte rows: 16-byte chunk c of K row
@@ -506,18 +512,7 @@ hipError_t launch_tn_cfg(const TnProblem& pr, int cu_cap, hipStream_t stream) {
     std::stable_sort(a.order, a.order + n_order,
                      [&](int x, int y) { return a.kb_count[x] > a.kb_count[y]; });
 
-    static int occupancy = -1;
-    if (occupancy < 0) {
-        int occ = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &occ, reinterpret_cast<const void*>(&tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M, UE8M0>),
-                Cfg::THREADS, 0) !=
-                hipSuccess ||
-            occ < 1)
-            occ = 1;
-        occupancy = occ;
-    }
-    const int64_t resident = (int64_t)cu_cap * occupancy;
+    const int64_t resident = (int64_t)cu_cap * Cfg::WG_PER_CU;
     const int grid = (int)(tiles < resident ? tiles : resident);
     hipLaunchKernelGGL((tn_fp8_kernel<Cfg, A_MK, B_NK, OUT_F32, GROUPED_M, UE8M0>), dim3(grid),
                        dim3(Cfg::THREADS), 0, stream, a);

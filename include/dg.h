@@ -36,33 +36,47 @@
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Each call
  *     enqueues one kernel on it and returns; there is no host synchronisation
  *     in the steady state, so calls may be captured into a HIP graph.
- *   - Workspace (dg_fp8_gemm_nt only): a dense problem with too few output
- *     tiles to occupy the device splits K over several workgroups, whose fp32
- *     partial tiles meet in a device buffer the library owns, one per (device,
- *     stream), kept until the process ends.  It is allocated, or grown, by
- *     the first call on that stream that needs more than it has (that call
- *     synchronises the stream once).  During stream capture the library never
- *     allocates: a capture that would need a larger workspace runs that call
- *     without splitting K (same result up to the order of the K-block sums).
- *     A captured graph keeps the workspace of its capture stream; do not
- *     replay it concurrently with other work that uses that stream's
- *     workspace.  The split depends only on the shape and the device's CU
- *     count (not on dg_set_num_cus), and the partial sums are added in a
- *     fixed order, so results are bitwise reproducible.
+ *   - Workspace (the dense NT entry points only): a dense problem with too
+ *     few output tiles to occupy the device splits K over several
+ *     workgroups, whose fp32 partial tiles meet in a CALLER-OWNED device
+ *     buffer passed as `workspace` / `workspace_bytes`.  The size a shape
+ *     needs is dg_fp8_gemm_nt_workspace_bytes(M, N, K): a pure function of
+ *     the shape (no HIP call, the same on every device), 0 when K is not
+ *     split (then workspace may be NULL).  A split shape called with a NULL
+ *     or smaller workspace is rejected (DG_ERR_INVALID_ARG), never run a
+ *     different way, so a shape always has one summation order.  The first
+ *     1 KiB of the buffer holds per-tile arrival counters, at the same place
+ *     for every shape: they must be zero when a call starts (zero-fill a new
+ *     buffer once) and every call leaves them zero when it completes, so one
+ *     buffer serves any sequence of shapes.  The library allocates nothing, frees
+ *     nothing, keeps no state between calls and never synchronises;
+ *     stream-ordered calls may reuse one buffer, calls that may run
+ *     concurrently (other streams, concurrent graph replays) need their
+ *     own.  The workspace must not overlap any operand or the output.
  *   - FP8 operands are raw e4m3 bytes (uint8_t).  Scale factors are fp32.
  *   - Outputs: bf16 is stored as uint16_t bit patterns (round to nearest
  *     even, once, from the fp32 accumulator); fp32 as float.
  *   - Host-side validation runs before any HIP call.  On a non-OK status
  *     nothing is launched and no output is touched; dg_last_error() explains
  *     the failure.  A zero-sized problem returns DG_OK without launching.
- *   - Every device pointer must be 16-byte aligned except the scale-factor and
- *     metadata pointers, which must be 4-byte aligned.
+ *   - Every device pointer (operands, scale factors, metadata, outputs,
+ *     workspace) must be 16-byte aligned.
  *   - Device-side metadata cannot be checked without a synchronisation, so it
  *     gets fixed readings instead: masked_m values are clamped to [0, M_max];
  *     m_indices values outside [0, G) mark padding rows.
  *   - Results are deterministic: the same inputs give bitwise identical
  *     outputs on a given device, whatever the CU cap (fixed summation order;
  *     the only atomics are split-K arrival counters, never sums).
+ *   - Split-K ordering: each workgroup writes its fp32 partial tile with
+ *     agent-scope atomic stores (on gfx950 these are write-through stores
+ *     with the device-coherence bit set, which reach the point every XCD
+ *     reads from), waits until they have completed (s_waitcnt vmcnt(0)),
+ *     and only then increments the tile's counter with an agent-scope
+ *     atomic; the workgroup that takes the last ticket reads the partials
+ *     with agent-scope atomic loads (which read at that same point), issued
+ *     after its increment has returned.  The order therefore rests on the
+ *     ISA's completion order of these device-coherent accesses; no release
+ *     fence is used because on this part it would write back the whole L2.
  */
 #ifndef DG_H
 #define DG_H
@@ -94,14 +108,29 @@ typedef enum {
  *   c    NULL (treated as 0), or [M, N] of d_dtype; c == d (in-place
  *        accumulate) is allowed, any other overlap with d is rejected
  *   d    [M, N] of d_dtype (DG_BF16 or DG_F32)
+ *   workspace, workspace_bytes
+ *        caller-owned split-K buffer of at least
+ *        dg_fp8_gemm_nt_workspace_bytes(M, N, K) bytes (counters zero at
+ *        the start of the call; see "Workspace" above); NULL / 0 when that
+ *        size is 0
  * Rules: K % 128 == 0, N % 16 == 0, M >= 0.
  * Source: "DeepGEMM" README, "Interfaces", "Notices" and "Normal dense GEMMs
- * (non-grouped)".
+ * (non-grouped)" (the caller allocates every buffer and passes it in).
  */
 dg_status dg_fp8_gemm_nt(const uint8_t* a, const float* sfa,
                          const uint8_t* b, const float* sfb,
                          const void* c, void* d, dg_dtype d_dtype,
-                         int64_t M, int64_t N, int64_t K, void* stream);
+                         int64_t M, int64_t N, int64_t K,
+                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes a dense NT call (dg_fp8_gemm_nt or dg_fp8_gemm_nt_ue8m0)
+ * of this shape needs: 0 when K is not split (and for sizes the entry
+ * points would reject).  A function of the shape alone: no HIP call, the
+ * same value on every device.  At most 32 MiB + 1 KiB for any shape (at
+ * most 512 split work units of at most 128 x 128 fp32, plus the counters).
+ */
+int64_t dg_fp8_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
  * M-grouped contiguous NT GEMM (MoE forward / prefill):
@@ -215,7 +244,7 @@ dg_status dg_fp8_gemm_tt(const uint8_t* a, const float* sfa,
  *   d         [M_tot, N]     bf16; rows whose index differs from their 128-row
  *                            block's expert (padding) are not written
  * Rules: M_tot % 128 == 0, K % 128 == 0, N % 16 == 0, G >= 1; pointers
- * 16-byte aligned (m_indices 4).  A block whose first index is outside
+ * 16-byte aligned.  A block whose first index is outside
  * [0, G) is skipped.
  */
 dg_status dg_m_grouped_fp8_gemm_nn_contiguous(const uint8_t* a, const float* sfa,
@@ -252,8 +281,8 @@ dg_status dg_m_grouped_fp8_gemm_nn_contiguous(const uint8_t* a, const float* sfa
  *   w      [G, N, K]  DG_BF16 or DG_F32 (finite)
  *   codes  [G, N, K]  e4m3 bytes
  *   sf     [G, ceil(N/128), K/128] fp32 (the sfb of the GEMM entry points)
- * Rules: K % 128 == 0; G, R / N >= 0; x / w and codes 16-byte aligned, sf
- * 4-byte aligned; flags is 0 or DG_CAST_POW2_SCALE; outputs must not overlap
+ * Rules: K % 128 == 0; G, R / N >= 0; x / w, codes and sf 16-byte aligned;
+ * flags is 0 or DG_CAST_POW2_SCALE; outputs must not overlap
  * the input.  One kernel launch on `stream`, no synchronisation, no
  * workspace.  Results are deterministic and bit-exact (no rounding freedom).
  */
@@ -286,13 +315,15 @@ dg_status dg_per_block_cast_to_fp8(const void* w, dg_dtype w_dtype, uint8_t* cod
  *   dg_fp8_gemm_nt_ue8m0:                   sfa [K4, M],  sfb [K4, N]
  *   dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0: sfa [K4, M_tot], sfb [G, K4, N]
  *   dg_m_grouped_fp8_gemm_nt_masked_ue8m0:  sfa [G, K4, M_max], sfb [G, K4, N]
- * (int32 words, 4-byte aligned).  The dense form splits K over workgroups
- * like dg_fp8_gemm_nt (same workspace rules).
+ * (int32 words, 16-byte aligned).  The dense form splits K over workgroups
+ * like dg_fp8_gemm_nt and takes the same caller-owned workspace (same size
+ * query, same rules).
  */
 dg_status dg_fp8_gemm_nt_ue8m0(const uint8_t* a, const int32_t* sfa,
                                const uint8_t* b, const int32_t* sfb,
                                const void* c, void* d, dg_dtype d_dtype,
-                               int64_t M, int64_t N, int64_t K, void* stream);
+                               int64_t M, int64_t N, int64_t K,
+                               void* workspace, int64_t workspace_bytes, void* stream);
 dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const uint8_t* a, const int32_t* sfa,
                                                     const uint8_t* b, const int32_t* sfb,
                                                     const int32_t* m_indices, void* d,
@@ -325,7 +356,7 @@ dg_status dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0(const uint8_t* a, const int3
  * block) -> the per-group packed words above, [W, MN] int32.  Byte i of a word
  * is the fp32 exponent field (the UE8M0 code of a positive power of two in
  * [2^-126, 2^127]); unused bytes are 0.  Rules as the K-grouped GEMM's for
- * k_sizes_host; sf and packed 4-byte aligned, not overlapping. */
+ * k_sizes_host; sf and packed 16-byte aligned, not overlapping. */
 dg_status dg_pack_ue8m0_scales_k_grouped(const float* sf, const int32_t* k_sizes_host,
                                          int32_t* packed, int64_t G, int64_t MN, int64_t K_tot,
                                          void* stream);
@@ -344,7 +375,7 @@ dg_status dg_pack_ue8m0_scales_k_grouped(const float* sf, const int32_t* k_sizes
  * in [2^-126, 2^127] (the precondition; other values give the exponent field
  * regardless, i.e. the mantissa and sign are dropped).  Bytes past the last
  * K block are 0.
- * Rules: K % 128 == 0; sf and packed 4-byte aligned and not overlapping.
+ * Rules: K % 128 == 0; sf and packed 16-byte aligned and not overlapping.
  * One kernel launch on `stream`; errors as for the GEMMs.
  * Source: DeepGEMM Documentation, section 10 (the packed-UE8M0 MN-major
  * layout utility).
@@ -367,8 +398,8 @@ dg_status dg_pack_ue8m0_scales(const float* sf, int per_block, int32_t* packed, 
  *   ks, ke  [S]        int32 device arrays; each range is clamped to
  *                      [0, S_kv], and ks >= ke selects nothing
  *   logits  [S, S_kv]  fp32, row-major
- * Rules: D == 128, H in {16, 32, 64}, S <= 1048560, S_kv <= 2^31 - 4097; q, kv, weights and logits
- * 16-byte aligned, kv_sf / ks / ke 4-byte aligned.  One kernel launch on
+ * Rules: D == 128, H in {16, 32, 64}, S <= 1048560, S_kv <= 2^31 - 4097;
+ * every pointer 16-byte aligned.  One kernel launch on
  * `stream`, no workspace, deterministic.  The dot product over D runs on the
  * MFMA unit in fp32; the kv scale, being positive, is applied once after the
  * head sum (relu(x * s) = s * relu(x)).

@@ -12,7 +12,7 @@ Layout reading ("DeepGEMM" README, "Interfaces", "Notices"): first letter A's
   (every partial sum exact in fp32), one-hot B, and dense TN equal to the
   K-grouped TN form with one group.
 * Grouped NN: parity per expert, padding rows untouched, equal bit for bit to
-  the dense NN form on each segment, and the 32-expert MoE shape on sampled rows.
+  the dense NN form on each segment, and the 32-expert MoE shape on every valid row.
 """
 import numpy as np
 import pytest
@@ -21,7 +21,7 @@ import torch
 import fp8_fine_grained_e4m3_amd as dg
 import oracle
 from tests import gen
-from tests.parity import Guarded, announce, check_close, dev, to64
+from tests.parity import FullCheck, Guarded, announce, check_close, check_full_rows, dev, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -189,27 +189,44 @@ def test_nn_contiguous_all_padding_untouched():
     assert d.untouched(slice(None))
 
 
-def test_nn_contiguous_moe_shape_sampled():
-    """32 experts, N = K = 4096, Zipf top-6 routing of 8192 tokens: sampled rows."""
-    announce("nn contiguous 32x4096x4096 sampled rows")
+def test_nn_contiguous_moe_shape_full_output():
+    """32 experts, N = K = 4096, Zipf top-6 routing of 8192 tokens: every valid row."""
+    announce("nn contiguous 32x4096x4096 full output")
     x = gen.gen_nn_contiguous(seed=0)
     d = run_nn_contiguous(x)
-    got = to64(d.view)
-    rng = np.random.default_rng(2)
-    rows = np.array(sorted(rng.choice(np.nonzero(x.m_indices >= 0)[0], 24, replace=False)), np.int64)
-    ref = oracle.m_grouped_nn_contiguous(x.a, x.sfa, x.b, x.sfb, x.m_indices, rows=rows)
-    check_close(got[rows], ref, "nn contiguous MoE shape")
+    got = d.view.float().cpu().numpy()
+    # expert e's rows against the layout oracle's K-contiguous route on the
+    # expert's transposed B (the NN definition, read without a stride per K step)
+    fc = FullCheck("nn contiguous MoE shape")
+    for e in range(x.G):
+        rows_e = np.nonzero(x.m_indices == e)[0].astype(np.int64)
+        if len(rows_e) == 0:
+            continue
+        bt = np.ascontiguousarray(x.b[e].T)
+        for r0 in range(0, len(rows_e), 1024):
+            rows = rows_e[r0:r0 + 1024]
+            fc.add(got[rows], oracle.gemm_layout("nt", x.a, x.sfa, bt, x.sfb[e], rows=rows),
+                   label=f"expert {e}")
+    fc.finish(expect_n=int(x.counts.sum()) * x.N)
     pad = torch.from_numpy(np.nonzero(x.m_indices < 0)[0])
     assert d.untouched(pad.cuda())
 
 
-def test_nn_large_sampled():
-    M, N, K = 4096, 4096, 4096
-    announce(f"layout nn {M}x{N}x{K} sampled rows")
-    x = gen.gen_layout("nn", M, N, K, seed=0)
-    got = to64(run(x))
-    rows = np.array([0, 1, 255, 256, 2047, 4095], np.int64)
-    check_close(got[rows], oracle.gemm_layout("nn", x.a, x.sfa, x.b, x.sfb, rows=rows), "nn large")
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+def test_layout_bench_shape_full_output(layout):
+    """The 4096 x 4096 x 7168 shape bench.py times in each layout: every
+    output element."""
+    M, N, K = 4096, 4096, 7168
+    announce(f"layout {layout} {M}x{N}x{K} full output")
+    x = gen.gen_layout(layout, M, N, K, seed=0)
+    got = run(x).float().cpu().numpy()
+    # the layout oracle's K-contiguous route on transposed copies of the
+    # MN-major operands: the same elements in the same summation order
+    at = x.a if layout[0] == "n" else np.ascontiguousarray(x.a.T)
+    bt = x.b if layout[1] == "t" else np.ascontiguousarray(x.b.T)
+    check_full_rows(f"{layout} {M}x{N}x{K}", got,
+                    lambda rows: oracle.gemm_layout("nt", at, x.sfa, bt, x.sfb, rows=rows), M,
+                    expect_n=M * N)
 
 
 @pytest.mark.parametrize("layout", ["nn", "tn", "tt"])

@@ -13,7 +13,7 @@ for j in [ks[i], ke[i]), -inf elsewhere when cleaning.
   bytes) without it.
 * Closed forms, bit-exact: all q negative against positive kv gives 0; one
   head with weight 0.5 and all-ones operands gives 64 sf[j].
-* The 4096 x 4096 x 64-head causal prefill shape on sampled rows.
+* The 4096 x 4096 x 64-head causal prefill shape over every output entry.
 """
 import numpy as np
 import pytest
@@ -22,7 +22,7 @@ import torch
 import fp8_fine_grained_e4m3_amd as dg
 import oracle
 from tests import gen
-from tests.parity import announce, check_close, dev
+from tests.parity import FullCheck, announce, check_close, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -101,14 +101,22 @@ def test_mqa_closed_forms_bit_exact():
     assert np.array_equal(run(x, True), np.broadcast_to(want, (S, S_kv)))
 
 
-def test_mqa_prefill_4096_sampled():
-    """4096 queries x 4096 kv tokens, 64 heads, one causal sequence."""
-    announce("mqa 4096x4096 H=64 causal sampled rows")
+def test_mqa_prefill_4096_full_output():
+    """4096 queries x 4096 kv tokens, 64 heads, one causal sequence: every
+    in-range logit against the oracle (streamed over query chunks), every
+    other entry -inf."""
+    announce("mqa 4096x4096 H=64 causal full output")
     x = gen.gen_mqa(4096, 4096, H=64, seed=0)
     got = run(x, True)
-    rows = np.array([0, 1, 255, 256, 1000, 2047, 4095], np.int64)
-    ref = oracle.mqa_logits(x.q, x.kv, x.kv_sf, x.weights, x.ks, x.ke, clean=True, rows=rows)
-    compare(got[rows], ref, True, "prefill 4096")
+    fc = FullCheck("prefill 4096")
+    for r0 in range(0, x.S, 512):
+        rows = np.arange(r0, min(x.S, r0 + 512), dtype=np.int64)
+        ref = oracle.mqa_logits(x.q, x.kv, x.kv_sf, x.weights, x.ks, x.ke, clean=True, rows=rows)
+        inside = np.isfinite(ref)
+        assert np.all(np.isneginf(got[rows][~inside])), "out-of-range entries not -inf"
+        fc.add(got[rows], np.where(inside, ref, np.nan), label=f"queries {r0}..")
+    pairs = int((np.clip(x.ke, 0, x.S_kv) - np.clip(x.ks, 0, x.S_kv)).clip(0).sum())
+    fc.finish(expect_n=pairs)
 
 
 def test_mqa_graph_capture_replays_with_new_ranges():

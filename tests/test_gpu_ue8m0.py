@@ -25,7 +25,7 @@ import torch
 import fp8_fine_grained_e4m3_amd as dg
 import oracle
 from tests import gen
-from tests.parity import Guarded, announce, check_close, dev, to64
+from tests.parity import FullCheck, Guarded, announce, check_close, check_full_rows, dev, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -115,14 +115,14 @@ def test_dense_ue8m0_shapes(M, N, K):
 
 
 def test_dense_ue8m0_full_size_dominant_shape():
-    """4096 x 7168 x 16384, the launch bench.py times: sampled rows."""
+    """4096 x 7168 x 16384, the launch bench.py times: every output element."""
     M, N, K = 4096, 7168, 16384
-    announce(f"dense ue8m0 {M}x{N}x{K} sampled rows")
+    announce(f"dense ue8m0 {M}x{N}x{K} full output")
     x = gen.gen_dense_ue8m0(M, N, K, seed=0)
-    got = to64(run_dense(x.a, x.sfa, x.b, x.sfb, M, N))
-    rows = sample_rows(M, 6, np.random.default_rng(7))
-    ref = oracle.gemm_nt_ue8m0(x.a, x.sfa, x.b, x.sfb, rows=rows)
-    print(check_close(got[rows], ref, "ue8m0 dominant shape"))
+    got = run_dense(x.a, x.sfa, x.b, x.sfb, M, N).float().cpu().numpy()
+    check_full_rows("ue8m0 dominant shape", got,
+                    lambda rows: oracle.gemm_nt_ue8m0(x.a, x.sfa, x.b, x.sfb, rows=rows), M,
+                    expect_n=M * N)
 
 
 @pytest.mark.parametrize("M,N,K", [(200, 272, 640), (64, 2112, 4096)])
@@ -276,22 +276,23 @@ def test_contiguous_ue8m0(counts, N, K):
     assert d.untouched(pad.cuda())
 
 
-def test_contiguous_ue8m0_c3_sampled():
+def test_contiguous_ue8m0_c3_full_output():
     """The contiguous MoE workload (32 experts, N = K = 4096, Zipf top-6
-    routing of 8192 tokens) with power-of-two scales: sampled rows."""
-    announce("contiguous ue8m0 C3 full size, sampled rows")
+    routing of 8192 tokens) with power-of-two scales: every valid row, each
+    against the dense definition with its expert's weights."""
+    announce("contiguous ue8m0 C3 full output")
     x = gen.gen_contiguous(seed=0, pow2=True)
     wa, wb = gen.to_ue8m0(x.sfa, x.sfb, x.N)
     d = run_contiguous(x, wa, wb)
-    got = to64(d.view)
-    rng = np.random.default_rng(3)
-    for e in rng.choice(x.G, size=4, replace=False):
-        rows = np.nonzero(x.m_indices == e)[0]
-        rows = np.array(sorted(set([rows[0], rows[-1]]) |
-                               set(rng.choice(rows, size=min(3, len(rows)), replace=False))),
-                        dtype=np.int64)
-        ref = oracle.gemm_nt_ue8m0(x.a, wa, x.b[e], wb[e], rows=rows)
-        check_close(got[rows], ref, f"C3 expert {e}")
+    got = d.view.float().cpu().numpy()
+    fc = FullCheck("C3 ue8m0")
+    for e in range(x.G):
+        rows_e = np.nonzero(x.m_indices == e)[0].astype(np.int64)
+        for r0 in range(0, len(rows_e), 1024):
+            rows = rows_e[r0:r0 + 1024]
+            fc.add(got[rows], oracle.gemm_nt_ue8m0(x.a, wa, x.b[e], wb[e], rows=rows),
+                   label=f"expert {e}")
+    fc.finish(expect_n=int(x.counts.sum()) * x.N)
     pad = torch.from_numpy(np.nonzero(x.m_indices < 0)[0])
     assert d.untouched(pad.cuda())
 
@@ -324,10 +325,10 @@ def test_masked_ue8m0(M_max, masked):
             assert d.untouched((g, slice(mm, None))), f"group {g} rows >= masked_m written"
 
 
-def test_masked_ue8m0_c4_sampled():
+def test_masked_ue8m0_c4_full_output():
     """The masked decode workload (32 groups, M_max = 256, N = 4096, K = 2048)
-    with power-of-two scales: sampled rows, untouched rows past masked_m."""
-    announce("masked ue8m0 C4 full size, sampled rows")
+    with power-of-two scales: every valid row, untouched rows past masked_m."""
+    announce("masked ue8m0 C4 full output")
     x = gen.gen_masked(seed=0, pow2=True)
     wa, wb = gen.to_ue8m0(x.sfa, x.sfb, x.N)
     d = Guarded((x.G, x.M_max, x.N), torch.bfloat16)
@@ -335,16 +336,17 @@ def test_masked_ue8m0_c4_sampled():
                                     dev(x.masked_m))
     torch.cuda.synchronize()
     assert d.intact()
-    got = to64(d.view)
-    rng = np.random.default_rng(4)
-    for g in rng.choice(x.G, size=5, replace=False):
+    got = d.view.float().cpu().numpy()
+    fc = FullCheck("C4 ue8m0")
+    for g in range(x.G):
         mm = int(x.masked_m[g])
         if mm:
-            rows = np.array(sorted({0, mm - 1} | set(rng.integers(0, mm, 2).tolist())), np.int64)
-            ref = oracle.gemm_nt_ue8m0(x.a[g], wa[g], x.b[g], wb[g], rows=rows)
-            check_close(got[g][rows], ref, f"C4 group {g}")
+            rows = np.arange(mm, dtype=np.int64)
+            fc.add(got[g, :mm], oracle.gemm_nt_ue8m0(x.a[g], wa[g], x.b[g], wb[g], rows=rows),
+                   label=f"group {g}")
         if mm < x.M_max:
             assert d.untouched((int(g), slice(mm, None)))
+    fc.finish(expect_n=int(x.masked_m.sum()) * x.N)
 
 
 def test_graph_capture_replays_masked_ue8m0():
@@ -452,19 +454,30 @@ def test_k_grouped_ue8m0_all_ones_bit_exact():
         kb += nkb
 
 
-def test_k_grouped_ue8m0_c5_sampled():
+def test_k_grouped_ue8m0_c5_full_output():
     """The MoE weight-gradient workload (32 groups, M = 2048, N = 4096, Zipf K
-    split of 49152, fp32 C) with power-of-two scales: sampled rows."""
-    announce("k-grouped ue8m0 C5 full size, sampled rows")
+    split of 49152, fp32 C) with power-of-two scales: every (group, m) row."""
+    announce("k-grouped ue8m0 C5 full output")
     x = gen.gen_k_grouped(seed=0, pow2=True)
     wa, wb = gen.k_grouped_ue8m0_words(x.sfa, x.k_sizes), gen.k_grouped_ue8m0_words(x.sfb, x.k_sizes)
     got = run_kg(x, wa, wb, c=x.c)
-    rng = np.random.default_rng(5)
-    groups = np.array([int(np.argmax(x.k_sizes)), int(np.argmin(x.k_sizes))] +
-                      rng.integers(0, x.G, 3).tolist(), np.int64)
-    rows = rng.integers(0, x.M, len(groups)).astype(np.int64)
-    ref = oracle.k_grouped_tn_ue8m0(x.a, wa, x.b, wb, x.k_sizes, x.c, groups=groups, rows=rows)
-    check_close(got[groups, rows], ref, "C5 ue8m0")
+    # group g against the dense UE8M0 oracle on its transposed K segment and
+    # its own word rows (each group's blocks start on a word boundary): the
+    # same definition, read K-contiguously
+    fc = FullCheck("C5 ue8m0")
+    k0 = w0 = 0
+    for g in range(x.G):
+        kg = int(x.k_sizes[g])
+        nw = (kg // 128 + 3) // 4
+        if kg == 0:
+            ref = x.c[g].astype(np.float64)
+        else:
+            ref = oracle.gemm_nt_ue8m0(np.ascontiguousarray(x.a[k0:k0 + kg].T), wa[w0:w0 + nw],
+                                       np.ascontiguousarray(x.b[k0:k0 + kg].T), wb[w0:w0 + nw],
+                                       c=x.c[g])
+        fc.add(got[g], ref, label=f"group {g}")
+        k0, w0 = k0 + kg, w0 + nw
+    fc.finish(expect_n=x.G * x.M * x.N)
 
 
 def test_dense_ue8m0_max_rows():

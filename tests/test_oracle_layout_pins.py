@@ -143,3 +143,32 @@ def test_grouped_nn_contiguous_is_nn_per_expert():
     rows = np.array([1, 200, 300], np.int64)
     assert np.array_equal(oracle.m_grouped_nn_contiguous(a, sfa, b, sfb, m_idx, rows=rows),
                           got[rows], equal_nan=True)
+
+
+def test_k_grouped_equals_the_nt_route_on_transposed_group_segments():
+    """The K-grouped TN form, group by group, equals the layout oracle's NT
+    route on each group's K segment transposed to K-contiguous storage (same
+    elements, same summation order: bit for bit), including an empty group
+    (D = C).  The whole-output GPU checks use this route, which reads without
+    a stride per K step."""
+    rng = np.random.default_rng(41)
+    M, N, ks = 48, 32, np.array([256, 0, 384, 128], np.int32)
+    K = int(ks.sum())
+    a = rng.integers(0, 256, (K, M), dtype=np.uint8)
+    b = rng.integers(0, 256, (K, N), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0
+    b[(b & 0x7F) == 0x7F] = 0
+    sfa = rng.uniform(0.5, 2, (K // 128, M)).astype(np.float32)
+    sfb = rng.uniform(0.5, 2, (K // 128, N)).astype(np.float32)
+    c = rng.standard_normal((len(ks), M, N)).astype(np.float32)
+    want = oracle.k_grouped_tn(a, sfa, b, sfb, ks, c)
+    k0 = 0
+    for g, kg in enumerate(ks):
+        k1 = k0 + int(kg)
+        if kg == 0:
+            got = c[g].astype(np.float64)
+        else:
+            got = oracle.gemm_layout("nt", np.ascontiguousarray(a[k0:k1].T), sfa[k0 // 128:k1 // 128],
+                                     np.ascontiguousarray(b[k0:k1].T), sfb[k0 // 128:k1 // 128], c=c[g])
+        assert np.array_equal(got, want[g]), g
+        k0 = k1

@@ -155,3 +155,32 @@ def test_k_grouped_ue8m0_equals_the_fp32_scale_definition():
                                     oracle.pack_ue8m0_k_grouped(sfb, k_sizes), k_sizes, c)
     assert np.array_equal(got, ref)
     assert np.array_equal(got[1], c[1].astype(np.float64))   # empty group: D = C
+
+
+def test_k_grouped_ue8m0_equals_dense_ue8m0_on_transposed_group_segments():
+    """The K-grouped UE8M0 form, group by group, equals the dense UE8M0 oracle
+    on the group's K segment transposed to K-contiguous storage with the
+    group's own word rows (bit for bit; an empty group gives C).  The
+    whole-output GPU checks use this route."""
+    rng = np.random.default_rng(43)
+    M, N, ks = 32, 48, np.array([640, 0, 128, 512], np.int32)
+    K = int(ks.sum())
+    a = rng.integers(0, 256, (K, M), dtype=np.uint8)
+    b = rng.integers(0, 256, (K, N), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0
+    b[(b & 0x7F) == 0x7F] = 0
+    sfa = np.exp2(rng.integers(-6, 6, (K // 128, M))).astype(np.float32)
+    sfb = np.exp2(rng.integers(-6, 6, (K // 128, N))).astype(np.float32)
+    wa, wb = oracle.pack_ue8m0_k_grouped(sfa, ks), oracle.pack_ue8m0_k_grouped(sfb, ks)
+    c = rng.standard_normal((len(ks), M, N)).astype(np.float32)
+    want = oracle.k_grouped_tn_ue8m0(a, wa, b, wb, ks, c)
+    k0 = w0 = 0
+    for g, kg in enumerate(ks):
+        nw = (int(kg) // 128 + 3) // 4
+        if kg == 0:
+            got = c[g].astype(np.float64)
+        else:
+            got = oracle.gemm_nt_ue8m0(np.ascontiguousarray(a[k0:k0 + kg].T), wa[w0:w0 + nw],
+                                       np.ascontiguousarray(b[k0:k0 + kg].T), wb[w0:w0 + nw], c=c[g])
+        assert np.array_equal(got, want[g]), g
+        k0, w0 = k0 + int(kg), w0 + nw
