@@ -54,6 +54,7 @@ EXPORTED = (
     "dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0",
     "dg_pack_ue8m0_scales_k_grouped",
     "dg_fp8_gemm_nt_workspace_bytes",
+    "dg_fp8_gemm_nt_noalloc",
 )
 DG_CAST_POW2_SCALE = 1
 
@@ -78,6 +79,8 @@ def load_library(path: Optional[str] = None):
     lib = ctypes.CDLL(p)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.dg_fp8_gemm_nt.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P, I64, P]
+    lib.dg_fp8_gemm_nt_noalloc.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
+    lib.dg_fp8_gemm_nt_noalloc.restype = I
     lib.dg_fp8_gemm_nt_workspace_bytes.argtypes = [I64, I64, I64]
     lib.dg_fp8_gemm_nt_workspace_bytes.restype = I64
     lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
@@ -233,6 +236,34 @@ def fp8_gemm_nt(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, tor
             _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(c), _ptr(d),
             DG_F32 if d.dtype == torch.float32 else DG_BF16, M, N, K,
             _ptr(workspace), ws_bytes, _stream(d)))
+    return d
+
+
+def fp8_gemm_nt_noalloc(a: Tuple[torch.Tensor, torch.Tensor], b: Tuple[torch.Tensor, torch.Tensor],
+                        d: torch.Tensor, c: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp8_gemm_nt (fp32 scales) with the split-K workspace taken from the
+    library's static per-GPU scratch: nothing is allocated on any call.
+    Calls that may overlap on one GPU race on that scratch."""
+    A, B = _fp8(a[0], "A"), _fp8(b[0], "B")
+    SA, SB = _f32(a[1], "SFA"), _f32(b[1], "SFB")
+    d = _dev(d, "d")
+    if d.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("d must be bfloat16 or float32")
+    if c is not None:
+        c = _dev(c, "c")
+        if c.dtype != d.dtype or c.shape != d.shape:
+            raise ValueError("c must match d in dtype and shape")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(d.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)} B {tuple(B.shape)} d {tuple(d.shape)}")
+    want = ((K // 128, M), ((N + 127) // 128, K // 128))
+    if (tuple(SA.shape), tuple(SB.shape)) != want:
+        raise ValueError(f"scale shapes: SFA {tuple(SA.shape)} SFB {tuple(SB.shape)}, want {want}")
+    with torch.cuda.device(d.device):
+        _check(load_library().dg_fp8_gemm_nt_noalloc(
+            _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(c), _ptr(d),
+            DG_F32 if d.dtype == torch.float32 else DG_BF16, M, N, K, _stream(d)))
     return d
 
 

@@ -136,9 +136,12 @@ bool disjoint(const void* p0, int64_t n0, const void* p1, int64_t n1) {
 
 // The three NT forms take either fp32 scales or packed UE8M0 words; both are
 // 4-byte elements, passed through as raw pointers.
+// noalloc: the split-K workspace is the library's static scratch instead of
+// the caller's (workspace / workspace_bytes are ignored).
 dg_status gemm_nt(const uint8_t* a, const void* sfa_, const uint8_t* b, const void* sfb_,
                   const void* c, void* d, dg_dtype d_dtype, int64_t M, int64_t N, int64_t K,
-                  void* workspace, int64_t workspace_bytes, bool ue8m0, void* stream) {
+                  void* workspace, int64_t workspace_bytes, bool ue8m0, void* stream,
+                  bool noalloc = false) {
     const float* sfa = static_cast<const float*>(sfa_);
     const float* sfb = static_cast<const float*>(sfb_);
     REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size (M=%lld N=%lld K=%lld)", (long long)M,
@@ -162,9 +165,17 @@ dg_status gemm_nt(const uint8_t* a, const void* sfa_, const uint8_t* b, const vo
     REQUIRE(((M + 63) / 64) * ((N + 63) / 64) <= INT_MAX / 8, "too many tiles");
     const int64_t dbytes = M * N * (d_dtype == DG_F32 ? 4 : 2);
     REQUIRE(alias_ok(c, d, dbytes), "c overlaps d without being equal to it");
-    REQUIRE(workspace_bytes >= 0, "workspace_bytes=%lld is negative", (long long)workspace_bytes);
     const int64_t need = dg::nt_dense_workspace_bytes(M, N, K);
-    if (need > 0) {
+    if (noalloc) {
+        if (need > dg::nt_noalloc_scratch_bytes())
+            return fail(DG_ERR_UNSUPPORTED,
+                        "this shape needs %lld bytes of split-K scratch; the static scratch "
+                        "holds %lld", (long long)need, (long long)dg::nt_noalloc_scratch_bytes());
+        workspace = nullptr;
+        workspace_bytes = 0;
+    }
+    REQUIRE(workspace_bytes >= 0, "workspace_bytes=%lld is negative", (long long)workspace_bytes);
+    if (need > 0 && !noalloc) {
         REQUIRE(workspace != nullptr,
                 "this shape splits K and needs a workspace of %lld bytes "
                 "(dg_fp8_gemm_nt_workspace_bytes); workspace is NULL", (long long)need);
@@ -184,6 +195,17 @@ dg_status gemm_nt(const uint8_t* a, const void* sfa_, const uint8_t* b, const vo
     p.rows = M; p.N = N; p.K = K; p.G = 1;
     p.out_f32 = d_dtype == DG_F32;
     p.ue8m0 = ue8m0;
+    if (noalloc && need > 0) {
+        // after host validation: the device check, then this device's scratch
+        int dev = 0;
+        DeviceInfo info;
+        dg_status st = current_device(dev, info);
+        if (st != DG_OK) return st;
+        hipError_t e = dg::nt_noalloc_scratch(&workspace);
+        if (e != hipSuccess)
+            return fail(DG_ERR_HIP, "static scratch lookup: %s", hipGetErrorString(e));
+        workspace_bytes = dg::nt_noalloc_scratch_bytes();
+    }
     p.workspace = need > 0 ? workspace : nullptr;
     p.workspace_bytes = need > 0 ? workspace_bytes : 0;
     return run_nt(p, stream);
@@ -258,6 +280,12 @@ dg_status dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, c
                          int64_t K, void* workspace, int64_t workspace_bytes, void* stream) {
     return gemm_nt(a, sfa, b, sfb, c, d, d_dtype, M, N, K, workspace, workspace_bytes, false,
                    stream);
+}
+
+dg_status dg_fp8_gemm_nt_noalloc(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                 const float* sfb, const void* c, void* d, dg_dtype d_dtype,
+                                 int64_t M, int64_t N, int64_t K, void* stream) {
+    return gemm_nt(a, sfa, b, sfb, c, d, d_dtype, M, N, K, nullptr, 0, false, stream, true);
 }
 
 int64_t dg_fp8_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K) {

@@ -37,6 +37,12 @@ struct NtProblem {
 // A function of the shape alone: no device query, no HIP call.
 int64_t nt_dense_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+// The library's static split-K scratch (for callers that cannot allocate):
+// its capacity in bytes (host constant) and its device address on the current
+// device (looked up once per device; a HIP call).
+int64_t nt_noalloc_scratch_bytes();
+hipError_t nt_noalloc_scratch(void** ptr);
+
 // MN-major kernel family: the K-grouped TN form, the dense NN / TN / TT
 // layouts and the M-grouped contiguous NN form.  Both operands carry one fp32
 // scale per output row (m) / column (n) per 128-K block: sfa [KB, M],

@@ -33,6 +33,8 @@
 
 #include <stdio.h>
 
+#include <mutex>
+
 namespace dg {
 
 struct NtArgs {
@@ -1009,6 +1011,46 @@ hipError_t dispatch_forms(const NtProblem& pr, int cu_cap, hipStream_t stream) {
 
 int64_t nt_dense_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     return dense_split_plan(M, N, K).bytes;
+}
+
+// ------------------------------------------------------------------------------
+// Split-K workspace for callers that cannot allocate: one static device array
+// per GPU (each device that loads this code object holds its own copy until
+// the process ends).  Capacity: the counter region plus the largest partial
+// set a split shape can need -- at most kRefCus * 2 work units (the slots of
+// the 256-CU part at two workgroups per CU) of at most 128 x 128 fp32.  The
+// array starts zero (a zero-initialised device variable), and every call
+// leaves its counters zero again.
+// ------------------------------------------------------------------------------
+
+namespace {
+constexpr int64_t kNoAllocScratchBytes = kCounterBytes + kRefCus * 2 * 128 * 128 * 4;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+int64_t nt_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t nt_noalloc_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        // the device address of this device's copy of `scratch`; in host code
+        // the array's name is only a host-side stand-in, never passed on
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_nt(const NtProblem& pr, int cu_cap, hipStream_t stream) {

@@ -124,6 +124,26 @@ dg_status dg_fp8_gemm_nt(const uint8_t* a, const float* sfa,
                          void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * dg_fp8_gemm_nt for callers that cannot allocate device memory or manage a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, rules, results (bit for bit) and
+ * errors as dg_fp8_gemm_nt without the workspace pair: a split-K shape uses
+ * the library's static device scratch instead, a file-scope array of
+ * 32 MiB + 1 KiB per GPU (every dense shape fits it; a larger need would be
+ * DG_ERR_UNSUPPORTED), which each GPU the library runs on holds until the
+ * process ends.  Nothing is allocated, freed or synchronised; the scratch's
+ * device address is looked up once per device (hipGetSymbolAddress) on the
+ * first call that needs it.  Every call on a GPU shares that GPU's scratch:
+ * calls that may overlap on one GPU (concurrent streams, concurrent graph
+ * replays) race and must not be issued.  The scratch's arrival counters
+ * start at zero and every call leaves them zero.
+ */
+dg_status dg_fp8_gemm_nt_noalloc(const uint8_t* a, const float* sfa,
+                                 const uint8_t* b, const float* sfb,
+                                 const void* c, void* d, dg_dtype d_dtype,
+                                 int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * Workspace bytes a dense NT call (dg_fp8_gemm_nt or dg_fp8_gemm_nt_ue8m0)
  * of this shape needs: 0 when K is not split (and for sizes the entry
  * points would reject).  A function of the shape alone: no HIP call, the
