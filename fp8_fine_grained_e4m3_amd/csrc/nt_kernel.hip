@@ -64,6 +64,9 @@ struct NtArgs {
     // Split K (dense only): each output tile is computed as `splits` partial
     // sums over consecutive K-block ranges; see the epilogue.
     int splits;
+    // 1: every B row is read by exactly one tile (one M tile per group), so
+    // the B copies use the nontemporal cache policy
+    int b_nt;
     float* part;       // [tiles][splits][SM * SN * 4][THREADS] fp32 partials
     int32_t* counters; // [tiles], zero between launches
 };
@@ -281,6 +284,10 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
             if (e < 0 || e >= p.G) continue;
             if (half == 1 && p.m_indices[r0] == e) continue;   // pass 0 already covers it
         }
+        // this tile's prologue derives its lane offsets from a fresh copy of
+        // the thread index (not hoisted out of the tile loop, so not kept live
+        // across the K loop)
+        const int lane_t = opaque(tid) & 63;
         // Contiguous groups: the expert of every row this wave stores in the
         // epilogue, requested now so its latency hides under the K loop.  With
         // one row per store instruction, wave w stores tile rows w + 8 j
@@ -288,7 +295,7 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
         int row_expert = -1;
         if constexpr (FORM == kContiguous && BN == 256) {
             static_assert(Cfg::WAVES == 8 && BM == 256, "row map of the contiguous epilogue");
-            const int row = r0 + wave + 8 * (lane & 31);
+            const int row = r0 + wave + 8 * (lane_t & 31);
             if (row < p.rows) row_expert = p.m_indices[row];
         }
 
@@ -312,8 +319,8 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
         for (int q = 0; q < Cfg::DMA_PER_WAVE; ++q) {
             const int u = wave * Cfg::DMA_PER_WAVE + q;
             const bool is_a = u < Cfg::A_DMA;
-            const int lrow = 8 * (is_a ? u : u - Cfg::A_DMA) + (lane >> 3);
-            const int chunk = sigma((lane & 7) ^ (is_a ? pos_a<SM>(lrow) : pos_b(lrow)));
+            const int lrow = 8 * (is_a ? u : u - Cfg::A_DMA) + (lane_t >> 3);
+            const int chunk = sigma((lane_t & 7) ^ (is_a ? pos_a<SM>(lrow) : pos_b(lrow)));
             const int row = is_a ? min(r0 + lrow, grp_rows - 1) : min(n0 + lrow, p.N - 1);
             goff[q] = (uint32_t)row * (uint32_t)p.K + (uint32_t)(chunk * 16);
         }
@@ -326,7 +333,7 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
         // A-scale slot t of the stage holds the scale of the row that lane
         // r = (u % 64) / 4 of wave-row wm reads as fragment i = 4 (u / 64) + u % 4
         // (u = t % WTM, wm = t / WTM)
-        const int sa_slot = 64 * wave + lane;
+        const int sa_slot = 64 * wave + lane_t;
         const int sa_u = sa_slot % Cfg::WTM, sa_r = (sa_u % 64) / 4;
         const int sa_row = (sa_slot / Cfg::WTM) * Cfg::WTM + SM * sa_r +
                            ((4 * (sa_u / 64) + (sa_u % 4)) ^ (sa_r & 1));
@@ -335,8 +342,8 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
         // UE8M0: wave w >= SA_DMA copies the words of tile columns
         // 64 (w - SA_DMA) + lane (clamped to the last column) into slot w - SA_DMA
         const uint32_t sb_off =
-            UE8M0 ? 4u * (uint32_t)min(n0 + 64 * max(wave - Cfg::SA_DMA, 0) + lane, p.N - 1)
-                  : 4u * (uint32_t)(min(n0 / kKBlk + lane, nb_last) * KB);
+            UE8M0 ? 4u * (uint32_t)min(n0 + 64 * max(wave - Cfg::SA_DMA, 0) + lane_t, p.N - 1)
+                  : 4u * (uint32_t)(min(n0 / kKBlk + lane_t, nb_last) * KB);
         const uint32_t lds0 = lds_addr(smem);
         auto issue_stage = [&](int kbr, int stage) {
             const int kb = kb_lo + kbr;
@@ -351,6 +358,8 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 // count on).
                 if (FORM == kMasked && u < Cfg::A_DMA && r0 + 8 * u >= store_rows)
                     dma4(src, 0, lds0 + Cfg::STAGES * Cfg::STAGE_BYTES + wave * 256);
+                else if (u >= Cfg::A_DMA && p.b_nt)
+                    dma16_nt(src, goff[q], dst + u * 1024);
                 else
                     dma16(src, goff[q], dst + u * 1024);
             }
@@ -759,6 +768,9 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
         // here, so the stores are nontemporal (they do not displace operand
         // panels from L2).
         {
+            // the epilogue's lane offsets derive from a fresh copy of the thread index
+            const int lane_e = opaque(tid) & 63;
+            const int r16_e = lane_e & 15;
             constexpr int WMP = Cfg::EPI_WAVE_ROWS;          // wave rows per phase
             constexpr int PH_ROWS = WMP * Cfg::WTM;           // tile rows per phase
             constexpr int ROW_CHUNKS = BN / 4;                // 16-byte fp32 chunks per row
@@ -769,10 +781,10 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 if (wm / WMP == ph) {
 #pragma unroll
                     for (int i = 0; i < SM; ++i) {
-                        const int rl = (wm % WMP) * Cfg::WTM + SM * r16 + (i ^ (r16 & 1));
+                        const int rl = (wm % WMP) * Cfg::WTM + SM * r16_e + (i ^ (r16_e & 1));
 #pragma unroll
                         for (int j = 0; j < SN; ++j) {
-                            const int ch = (wn * Cfg::WTN + 16 * j) / 4 + (lane >> 4);
+                            const int ch = (wn * Cfg::WTN + 16 * j) / 4 + (lane_e >> 4);
                             *reinterpret_cast<f32x4*>(stg + rl * BN + 4 * (ch ^ ((rl / SM) & 15))) =
                                 acc[i][j];
                         }
@@ -782,8 +794,8 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 constexpr int NR = PH_ROWS / (Cfg::WAVES * RPI);   // row steps per wave
 #pragma unroll 4
                 for (int k = 0; k < NR; ++k) {
-                    const int rl = wave * RPI + k * Cfg::WAVES * RPI + lane / ROW_CHUNKS;
-                    const int ch = lane % ROW_CHUNKS;
+                    const int rl = wave * RPI + k * Cfg::WAVES * RPI + lane_e / ROW_CHUNKS;
+                    const int ch = lane_e % ROW_CHUNKS;
                     f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * BN + 4 * (ch ^ ((rl / SM) & 15)));
                     const int m = r0 + ph * PH_ROWS + rl;   // row within the group
                     const int n = n0 + 4 * ch;
@@ -914,6 +926,11 @@ hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
         }
     }
     a.num_tiles = (int)(tiles * a.splits);
+    // Decode-size launches (one M tile per group) read each B row once: stream
+    // B past the caches.  Measured with the caches flushed before each launch:
+    // the ten decode-size dense shapes 288 -> 243 us in total (64 x 7168 x 16384:
+    // 60 -> 38 us), masked 32 x 256 x 4096 x 2048: 121 -> 86-91 us.
+    a.b_nt = (FORM != kContiguous && a.tiles_m == 1) ? 1 : 0;
 
     const int64_t resident = (int64_t)cu_cap * Cfg::WG_PER_CU;
     const int grid = (int)(a.num_tiles < resident ? a.num_tiles : resident);

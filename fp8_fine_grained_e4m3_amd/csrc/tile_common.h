@@ -117,11 +117,32 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                  : "memory");
 }
 
+// The same copy with the nontemporal cache policy, for operand rows read
+// exactly once by the whole launch (streamed from HBM without displacing
+// reused data).
+__device__ __forceinline__ void dma16_nt(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(base), "{m0}"(lds)
+                 : "memory");
+}
+
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1"
                  :
                  : "v"(voff), "s"(base), "{m0}"(lds)
                  : "memory");
+}
+
+// A copy of v that the compiler cannot see through.  Values derived from it
+// are computed where the copy is taken: the per-tile prologue and epilogue
+// derive their lane-dependent offsets from a fresh copy of the thread index,
+// so the compiler does not hoist them out of the tile loop and keep them live
+// (spilled) across the K loop, where the accumulators hold the registers.
+__device__ __forceinline__ int opaque(int v) {
+    int r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
 }
 
 // Wait for this wave's outstanding vector-memory loads (including the LDS

@@ -165,7 +165,10 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
     // fragment 0 (row r16); fragment c adds 16 * 128 * c
     const int k_c0 = 2 * (lane >> 4);
     const int k_lo = r16 * kKBlk + (k_pos(r16, k_c0) << 4);
-    const int k_hi = r16 * kKBlk + (k_pos(r16, k_c0 + 1) << 4);
+    // chunk k_c0 + 1 sits at position k_pos(r16, k_c0) ^ 2 (k_c0 is even, so
+    // k_sigma only sets bit 1 for the odd chunk): 32 bytes across, and the
+    // row term has no bit 5
+    static_assert(kKBlk % 64 == 0, "row term clear of bit 5");
 
     for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
         // M-grouped: every tile is listed twice; pass `gi` computes it with the
@@ -204,6 +207,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         }
         const uint8_t* __restrict__ b_e = p.b + (int64_t)e * p.K * p.N;
         const float* __restrict__ sfb_e = p.sfb + (int64_t)e * (p.K / kKBlk) * p.N;
+        const int lane_t = opaque(tid) & 63;   // this tile's prologue derives its offsets from it
 
         // Copy offsets.  Copy u of A moves 1024 / BM K rows: lane l fills LDS
         // chunk position l % (BM / 16) of row u * (1024 / BM) + l / (BM / 16),
@@ -216,23 +220,23 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
             if (u < Cfg::A_DMA) {
                 if constexpr (A_MK) {
                     // 8 matrix rows of 128 K bytes; rows past M re-read the last one
-                    const int row = 8 * u + (lane >> 3);
-                    const int ch = k_sigma((lane & 7) ^ ((row >> 1) & 7));   // chunk at position lane & 7
+                    const int row = 8 * u + (lane_t >> 3);
+                    const int ch = k_sigma((lane_t & 7) ^ ((row >> 1) & 7));   // chunk at position lane & 7
                     goff[q] = (uint32_t)min(m0 + row, p.M - 1) * (uint32_t)p.K + (uint32_t)(ch * 16);
                 } else {
-                    const int row = u * (1024 / BM) + lane / (BM / 16);
-                    const int ch = (lane % (BM / 16)) ^ tn_swz<BM>(row);
+                    const int row = u * (1024 / BM) + lane_t / (BM / 16);
+                    const int ch = (lane_t % (BM / 16)) ^ tn_swz<BM>(row);
                     goff[q] = (uint32_t)row * (uint32_t)p.M + (uint32_t)min(m0 + 16 * ch, p.M - 16);
                 }
             } else {
                 const int uu = u - Cfg::A_DMA;
                 if constexpr (B_NK) {
-                    const int row = 8 * uu + (lane >> 3);
-                    const int ch = k_sigma((lane & 7) ^ ((row >> 1) & 7));
+                    const int row = 8 * uu + (lane_t >> 3);
+                    const int ch = k_sigma((lane_t & 7) ^ ((row >> 1) & 7));
                     goff[q] = (uint32_t)min(n0 + row, p.N - 1) * (uint32_t)p.K + (uint32_t)(ch * 16);
                 } else {
-                    const int row = uu * (1024 / BN) + lane / (BN / 16);
-                    const int ch = (lane % (BN / 16)) ^ tn_swz<BN>(row);
+                    const int row = uu * (1024 / BN) + lane_t / (BN / 16);
+                    const int ch = (lane_t % (BN / 16)) ^ tn_swz<BN>(row);
                     goff[q] = (uint32_t)row * (uint32_t)p.N + (uint32_t)min(n0 + 16 * ch, p.N - 16);
                 }
             }
@@ -243,17 +247,17 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         // holds the scale of column wm*WTM + 16 i + r: lane r reads its scales
         // as float4s and each float4 read of 16 lanes covers 256 contiguous
         // bytes (no bank conflicts).
-        const int scopy = wave % (Cfg::SA_DMA + Cfg::SB_DMA);
+        const int scopy = __builtin_amdgcn_readfirstlane(wave % (Cfg::SA_DMA + Cfg::SB_DMA));
         const bool s_is_a = scopy < Cfg::SA_DMA;
         uint32_t s_off, s_lds;
         if (s_is_a) {
-            const int slot = 64 * scopy + lane;
+            const int slot = 64 * scopy + lane_t;
             const int wms = slot / Cfg::WTM, u = slot % Cfg::WTM;
             const int col = wms * Cfg::WTM + 16 * (4 * (u / 64) + u % 4) + (u % 64) / 4;
             s_off = 4u * (uint32_t)min(m0 + col, p.M - 1);
             s_lds = Cfg::SA_OFF + 256 * scopy;
         } else {
-            const int slot = 64 * (scopy - Cfg::SA_DMA) + lane;
+            const int slot = 64 * (scopy - Cfg::SA_DMA) + lane_t;
             s_off = 4u * (uint32_t)min(n0 + slot, p.N - 1);
             s_lds = Cfg::SB_OFF + 256 * (scopy - Cfg::SA_DMA);
         }
@@ -276,10 +280,10 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         f32x4 acc[SM][SN];
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
-            const int m = min(m0 + wm * Cfg::WTM + 16 * i + r16, p.M - 1);
+            const int m = min(m0 + wm * Cfg::WTM + 16 * i + (lane_t & 15), p.M - 1);
 #pragma unroll
             for (int j = 0; j < SN; ++j) {
-                const int n = min(n0 + wn * Cfg::WTN + 16 * j + 4 * (lane >> 4), p.N - 4);
+                const int n = min(n0 + wn * Cfg::WTN + 16 * j + 4 * (lane_t >> 4), p.N - 4);
                 const int64_t off = gbase + (int64_t)m * p.N + n;
                 if (!p.c) {
                     acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
             // fragment of 16 columns (tile columns 16 c .. 16 c + 15) of A or B
             auto k_frag = [&](const uint8_t* tile, int c) {
                 const i32x4 lo = *reinterpret_cast<const i32x4*>(tile + c * 16 * kKBlk + k_lo);
-                const i32x4 hi = *reinterpret_cast<const i32x4*>(tile + c * 16 * kKBlk + k_hi);
+                const i32x4 hi = *reinterpret_cast<const i32x4*>(tile + c * 16 * kKBlk + (k_lo ^ 32));
                 i32x8 r;
                 r.s0 = lo.x; r.s1 = lo.y; r.s2 = lo.z; r.s3 = lo.w;
                 r.s4 = hi.x; r.s5 = hi.y; r.s6 = hi.z; r.s7 = hi.w;
@@ -435,16 +439,18 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         float* const stg = reinterpret_cast<float*>(smem);
         constexpr int ROW_CHUNKS = BN / 4;
         static_assert(ROW_CHUNKS == 64, "one row per store instruction");
+        const int lane_e = opaque(tid) & 63;   // the epilogue's offsets derive from it
+        const int r16_e = lane_e & 15;
         static_assert(Cfg::WTM * BN * 4 <= Cfg::STAGES * Cfg::STAGE_BYTES, "a wave row of the tile fits in LDS");
 #pragma unroll
         for (int ph = 0; ph < Cfg::WAVES_M; ++ph) {
             if (wm == ph) {
 #pragma unroll
                 for (int i = 0; i < SM; ++i) {
-                    const int rl = 16 * i + r16;
+                    const int rl = 16 * i + r16_e;
 #pragma unroll
                     for (int j = 0; j < SN; ++j) {
-                        const int ch = (wn * Cfg::WTN + 16 * j) / 4 + (lane >> 4);
+                        const int ch = (wn * Cfg::WTN + 16 * j) / 4 + (lane_e >> 4);
                         *reinterpret_cast<f32x4*>(stg + rl * BN + 4 * (ch ^ (rl & 15))) = acc[i][j];
                     }
                 }
@@ -453,12 +459,12 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
 #pragma unroll 4
             for (int rl = wave; rl < Cfg::WTM; rl += Cfg::WAVES) {
                 const int m = m0 + ph * Cfg::WTM + rl;
-                const int n = n0 + 4 * lane;
+                const int n = n0 + 4 * lane_e;
                 if (m >= p.M || n >= p.N) continue;
                 if constexpr (GROUPED_M) {
                     if (p.m_indices[m] != e) continue;   // padding row of the segment
                 }
-                const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * BN + 4 * (lane ^ (rl & 15)));
+                const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * BN + 4 * (lane_e ^ (rl & 15)));
                 const int64_t off = gbase + (int64_t)m * p.N + n;
                 if constexpr (OUT_F32)
                     __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(p.d) + off));
