@@ -15,7 +15,8 @@ sfb [K/128, N].
   with one group, bit for bit (block-constant B scales where NT needs them).
 * All-ones operands with power-of-two scales: D = 128 * sum_kb sa[kb,m] sb[kb,n].
 * One-hot B: a single element of A times its two scales.
-* The grouped NN form equals NN per expert; padding rows have no reference.
+* The grouped NN form equals NN per expert, and exact rationals with each row's
+  own expert; padding rows have no reference.
 """
 from fractions import Fraction
 
@@ -143,6 +144,24 @@ def test_grouped_nn_contiguous_is_nn_per_expert():
     rows = np.array([1, 200, 300], np.int64)
     assert np.array_equal(oracle.m_grouped_nn_contiguous(a, sfa, b, sfb, m_idx, rows=rows),
                           got[rows], equal_nan=True)
+
+
+def test_grouped_nn_contiguous_matches_exact_rationals():
+    """Each valid row of the grouped NN form against exact rational sums with
+    the B operand and scales of that row's expert (a row picks its expert from
+    m_indices; nothing else ties it to the per-expert NN route)."""
+    rng = np.random.default_rng(78)
+    G, N, K = 3, 4, 256
+    m_idx = np.array([1] * 2 + [-1] * 126 + [0] * 3 + [2] * 125, np.int32)
+    M = len(m_idx)
+    a = random_codes(rng, (M, K)); sfa = random_scales(rng, (K // 128, M))
+    b = random_codes(rng, (G, K, N)); sfb = random_scales(rng, (G, K // 128, N))
+    rows = np.array([0, 1, 128, 130, 131, 255], np.int64)
+    got = oracle.m_grouped_nn_contiguous(a, sfa, b, sfb, m_idx, rows=rows)
+    for r_i, r in enumerate(rows):
+        e = int(m_idx[r])
+        want, bound = exact_layout("nn", a[r:r + 1], sfa[:, r:r + 1], b[e], sfb[e])
+        assert_exact(got[r_i:r_i + 1], want, bound)
 
 
 def test_k_grouped_equals_the_nt_route_on_transposed_group_segments():
