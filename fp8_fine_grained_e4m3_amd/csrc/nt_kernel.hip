@@ -34,6 +34,7 @@
 #include <stdio.h>
 
 #include <mutex>
+#include <type_traits>
 
 namespace dg {
 
@@ -392,6 +393,20 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
         const int s_b = Cfg::SB_OFF + 256 * (Cfg::WAVES - 1) + 4 * ((wn * Cfg::WTN) / kKBlk);
         const int s_be = Cfg::SB_OFF + 4 * (wn * Cfg::WTN + r16);   // UE8M0: word of B fragment 0
 
+        // Whether this wave's tile rows (WTM rows from r0 + wm * WTM) hold any
+        // row the pass stores: masked groups store rows below masked_m;
+        // contiguous passes store the rows of expert e, and a wave's rows are
+        // one 128-row block, which belongs to a single expert (or is padding);
+        // dense tiles store rows below M.
+        bool wave_live = true;
+        {
+            const int rw = r0 + wm * Cfg::WTM;
+            if (FORM == kMasked) wave_live = rw < store_rows;
+            else if (FORM == kContiguous) wave_live = rw < p.rows && p.m_indices[rw] == e;
+            else wave_live = rw < p.rows;
+            wave_live = __builtin_amdgcn_readfirstlane((int)wave_live) != 0;
+        }
+        static_assert(FORM != kContiguous || Cfg::WTM == kKBlk, "a wave's rows are one expert block");
         f32x4 acc[SM][SN];
 #pragma unroll
         for (int i = 0; i < SM; ++i)
@@ -565,117 +580,133 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
             // past it, rows SM - 2 and SM - 1 request the next block's scales,
             // its first two A fragments and (after the last product that uses
             // each) its B fragments.
-            constexpr int T = SM * SN;
-            static_assert(SM % 4 == 0 && T % 2 == 0, "A ring of four rows, product ring of two");
-            i32x8 af[4];
-            i32x8 bfr[SN];
-            float sa[SM], sb, sa_n[SM], sb_n;
-            int ea[SM], eb[SN], ea_n[SM], eb_n[SN];   // UE8M0 exponents
-            f32x4 ring[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-            float ring_s[2] = {0.f, 0.f};   // nothing pending before block 0
-            if constexpr (UE8M0) load_exps(smem, kb_lo, ea, eb);
-            else load_scales(smem, sa, sb);
-#pragma unroll
-            for (int j = 0; j < SN; ++j) bfr[j] = bfrag_at(smem, j);
-            af[0] = afrag_at(smem, 0);
-            af[1] = afrag_at(smem, 1);
+            // A wave whose tile rows hold nothing this pass stores (rows past
+            // masked_m, another expert's block, rows past M) runs the same
+            // copies, waits and barriers as the others but no fragment reads
+            // and no products; its accumulators stay zero and are never stored.
+            auto row_pipeline = [&](auto live_tag) {
+                constexpr bool LIVE = decltype(live_tag)::value;
+                constexpr int T = SM * SN;
+                static_assert(SM % 4 == 0 && T % 2 == 0, "A ring of four rows, product ring of two");
+                i32x8 af[4];
+                i32x8 bfr[SN];
+                float sa[SM], sb, sa_n[SM], sb_n;
+                int ea[SM], eb[SN], ea_n[SM], eb_n[SN];   // UE8M0 exponents
+                f32x4 ring[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+                float ring_s[2] = {0.f, 0.f};   // nothing pending before block 0
+                if constexpr (LIVE) {
+                    if constexpr (UE8M0) load_exps(smem, kb_lo, ea, eb);
+                    else load_scales(smem, sa, sb);
+    #pragma unroll
+                    for (int j = 0; j < SN; ++j) bfr[j] = bfrag_at(smem, j);
+                    af[0] = afrag_at(smem, 0);
+                    af[1] = afrag_at(smem, 1);
+                }
 
-            // one product step: block product (i, j) (issued at raised wave
-            // priority, so a wave with products ready keeps the MFMA unit busy
-            // while its SIMD partner waits on LDS) and the promotion of the
-            // product two steps back
-            // (UE8M0: the MFMA applies the exponents and accumulates itself)
-            auto step = [&](int i, int j, float s_row) {
-                if constexpr (UE8M0) {
-                    __builtin_amdgcn_s_setprio(1);
-                    acc[i][j] = mfma_e4m3_block_ue8m0(bfr[j], af[i & 3], acc[i][j], eb[j], ea[i]);
-                    // pins the product here: with nothing reading acc until the
-                    // epilogue, the compiler would otherwise sink every product of
-                    // the block past the LDS reads it is meant to overlap
-                    asm volatile("" : "+v"(acc[i][j]));
-                    __builtin_amdgcn_s_setprio(0);
-                } else {
-                    const int t = i * SN + j;
-                    __builtin_amdgcn_s_setprio(1);
-                    const f32x4 pr = mfma_e4m3_block(bfr[j], af[i & 3]);
-                    __builtin_amdgcn_s_setprio(0);
-                    const int tp = t >= 2 ? t - 2 : T + t - 2;   // tile of the pending product
-                    promote1(tp / SN, tp % SN, ring[t & 1], ring_s[t & 1]);
-                    ring[t & 1] = pr;
-                    ring_s[t & 1] = s_row;
+                // one product step: block product (i, j) (issued at raised wave
+                // priority, so a wave with products ready keeps the MFMA unit busy
+                // while its SIMD partner waits on LDS) and the promotion of the
+                // product two steps back
+                // (UE8M0: the MFMA applies the exponents and accumulates itself)
+                auto step = [&](int i, int j, float s_row) {
+                    if constexpr (!LIVE) {
+                        return;
+                    } else if constexpr (UE8M0) {
+                        __builtin_amdgcn_s_setprio(1);
+                        acc[i][j] = mfma_e4m3_block_ue8m0(bfr[j], af[i & 3], acc[i][j], eb[j], ea[i]);
+                        // pins the product here: with nothing reading acc until the
+                        // epilogue, the compiler would otherwise sink every product of
+                        // the block past the LDS reads it is meant to overlap
+                        asm volatile("" : "+v"(acc[i][j]));
+                        __builtin_amdgcn_s_setprio(0);
+                    } else {
+                        const int t = i * SN + j;
+                        __builtin_amdgcn_s_setprio(1);
+                        const f32x4 pr = mfma_e4m3_block(bfr[j], af[i & 3]);
+                        __builtin_amdgcn_s_setprio(0);
+                        const int tp = t >= 2 ? t - 2 : T + t - 2;   // tile of the pending product
+                        promote1(tp / SN, tp % SN, ring[t & 1], ring_s[t & 1]);
+                        ring[t & 1] = pr;
+                        ring_s[t & 1] = s_row;
+                    }
+                };
+
+                int stage = 0;   // stage holding block it
+                for (int it = 0; it < nkb; ++it) {
+                    const uint8_t* st = smem + stage * Cfg::STAGE_BYTES;
+                    const int next = stage + 1 == Cfg::STAGES ? 0 : stage + 1;
+                    const uint8_t* st_next = smem + next * Cfg::STAGE_BYTES;
+    #pragma unroll
+                    for (int i = 0; i + 2 < SM; ++i) {
+                        const float s_row = (UE8M0 || !LIVE) ? 0.f : sa[i] * sb;
+    #pragma unroll
+                        for (int j = 0; j < SN; ++j) {
+                            step(i, j, s_row);
+                            if (LIVE && j == 0) af[(i + 2) & 3] = afrag_at(st, i + 2);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        if constexpr (Cfg::EARLY_B) if (i == 0) {
+                            // Row 0 has consumed every B fragment and the B scale of
+                            // this block (read during the previous block), so every
+                            // wave past this barrier is done with the stage's B half.
+                            // No LDS drain: the A fragments requested since are
+                            // still in flight and unaffected.
+                            asm volatile("s_barrier" ::: "memory");
+                            if (!a_wave && it + 2 < nkb) issue_stage(it + 2, stage);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                    // Block it+1 landed for every wave and every read of block it
+                    // done: refill (the A half, with early B refill).
+                    if constexpr (Cfg::EARLY_B) {
+                        // a B wave may have block it+2's B copies in flight behind
+                        if (!a_wave && it + 2 < nkb) wait_vmcnt<Cfg::VM_PER_STAGE>();
+                        else wait_vmcnt<0>();
+                        lgkm_drain_barrier();
+                        if (a_wave && it + 2 < nkb) issue_stage(it + 2, stage);
+                    } else {
+                        wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(
+                            max(0, min(Cfg::STAGES - 2, nkb - 2 - it)));
+                        lgkm_drain_barrier();
+                        if (it + Cfg::STAGES < nkb) issue_stage(it + Cfg::STAGES, stage);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    // (after the last block these reads see a stale stage; unused)
+                    if constexpr (LIVE) {
+                        if constexpr (UE8M0) load_exps(st_next, kb_lo + it + 1, ea_n, eb_n);
+                        else load_scales(st_next, sa_n, sb_n);
+                    }
+    #pragma unroll
+                    for (int i = SM - 2; i < SM; ++i) {
+                        const float s_row = (UE8M0 || !LIVE) ? 0.f : sa[i] * sb;
+    #pragma unroll
+                        for (int j = 0; j < SN; ++j) {
+                            step(i, j, s_row);
+                            if (LIVE && j == 0) af[(i + 2) & 3] = afrag_at(st_next, i + 2 - SM);
+                            if (LIVE && i == SM - 1) bfr[j] = bfrag_at(st_next, j);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                    if constexpr (!LIVE) {
+                    } else if constexpr (UE8M0) {
+    #pragma unroll
+                        for (int i = 0; i < SM; ++i) ea[i] = ea_n[i];
+    #pragma unroll
+                        for (int j = 0; j < SN; ++j) eb[j] = eb_n[j];
+                    } else {
+    #pragma unroll
+                        for (int i = 0; i < SM; ++i) sa[i] = sa_n[i];
+                        sb = sb_n;
+                    }
+                    stage = next;
+                }
+                if constexpr (LIVE && !UE8M0) {
+                    promote1((T - 2) / SN, (T - 2) % SN, ring[0], ring_s[0]);
+                    promote1((T - 1) / SN, (T - 1) % SN, ring[1], ring_s[1]);
                 }
             };
-
-            int stage = 0;   // stage holding block it
-            for (int it = 0; it < nkb; ++it) {
-                const uint8_t* st = smem + stage * Cfg::STAGE_BYTES;
-                const int next = stage + 1 == Cfg::STAGES ? 0 : stage + 1;
-                const uint8_t* st_next = smem + next * Cfg::STAGE_BYTES;
-#pragma unroll
-                for (int i = 0; i + 2 < SM; ++i) {
-                    const float s_row = UE8M0 ? 0.f : sa[i] * sb;
-#pragma unroll
-                    for (int j = 0; j < SN; ++j) {
-                        step(i, j, s_row);
-                        if (j == 0) af[(i + 2) & 3] = afrag_at(st, i + 2);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                    if constexpr (Cfg::EARLY_B) if (i == 0) {
-                        // Row 0 has consumed every B fragment and the B scale of
-                        // this block (read during the previous block), so every
-                        // wave past this barrier is done with the stage's B half.
-                        // No LDS drain: the A fragments requested since are
-                        // still in flight and unaffected.
-                        asm volatile("s_barrier" ::: "memory");
-                        if (!a_wave && it + 2 < nkb) issue_stage(it + 2, stage);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-                // Block it+1 landed for every wave and every read of block it
-                // done: refill (the A half, with early B refill).
-                if constexpr (Cfg::EARLY_B) {
-                    // a B wave may have block it+2's B copies in flight behind
-                    if (!a_wave && it + 2 < nkb) wait_vmcnt<Cfg::VM_PER_STAGE>();
-                    else wait_vmcnt<0>();
-                    lgkm_drain_barrier();
-                    if (a_wave && it + 2 < nkb) issue_stage(it + 2, stage);
-                } else {
-                    wait_stage_copies<Cfg::STAGES - 2, Cfg::VM_PER_STAGE>(
-                        max(0, min(Cfg::STAGES - 2, nkb - 2 - it)));
-                    lgkm_drain_barrier();
-                    if (it + Cfg::STAGES < nkb) issue_stage(it + Cfg::STAGES, stage);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                // (after the last block these reads see a stale stage; unused)
-                if constexpr (UE8M0) load_exps(st_next, kb_lo + it + 1, ea_n, eb_n);
-                else load_scales(st_next, sa_n, sb_n);
-#pragma unroll
-                for (int i = SM - 2; i < SM; ++i) {
-                    const float s_row = UE8M0 ? 0.f : sa[i] * sb;
-#pragma unroll
-                    for (int j = 0; j < SN; ++j) {
-                        step(i, j, s_row);
-                        if (j == 0) af[(i + 2) & 3] = afrag_at(st_next, i + 2 - SM);
-                        if (i == SM - 1) bfr[j] = bfrag_at(st_next, j);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-                if constexpr (UE8M0) {
-#pragma unroll
-                    for (int i = 0; i < SM; ++i) ea[i] = ea_n[i];
-#pragma unroll
-                    for (int j = 0; j < SN; ++j) eb[j] = eb_n[j];
-                } else {
-#pragma unroll
-                    for (int i = 0; i < SM; ++i) sa[i] = sa_n[i];
-                    sb = sb_n;
-                }
-                stage = next;
-            }
-            if constexpr (!UE8M0) {
-                promote1((T - 2) / SN, (T - 2) % SN, ring[0], ring_s[0]);
-                promote1((T - 1) / SN, (T - 1) % SN, ring[1], ring_s[1]);
-            }
+            if (wave_live) row_pipeline(std::true_type{});
+            else row_pipeline(std::false_type{});
         }
         // every wave is past its last LDS read before the next tile's copies
         lds_barrier();
