@@ -984,7 +984,7 @@ hipError_t launch_cfg(const NtProblem& pr, int cu_cap, hipStream_t stream) {
 using Cfg256x256 = NtCfg<256, 256, 2, 4, 2>;
 using Cfg128x128 = NtCfg<128, 128, 2, 2, 2>;
 using Cfg128x64 = NtCfg<128, 64, 2, 2, 3>;
-using Cfg64x64 = NtCfg<64, 64, 1, 4, 4>;
+using Cfg64x64 = NtCfg<64, 64, 1, 4, 3>;
 
 
 // Tile choice: 256 x 256 (8 waves of 128 x 64) for large dense problems and
