@@ -300,6 +300,21 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
             if (row < p.rows) row_expert = p.m_indices[row];
         }
 
+        // Contiguous passes: bit b is set when the tile's 128-row block b holds
+        // rows of expert e (a block belongs to one expert or is padding).  The
+        // other block's rows are not stored in this pass: its A copies shrink to
+        // placeholders (as rows past masked_m do) and its waves compute nothing.
+        int live_blk = (1 << (BM / kKBlk)) - 1;
+        if constexpr (FORM == kContiguous) {
+            live_blk = 0;
+#pragma unroll
+            for (int bb = 0; bb < BM / kKBlk; ++bb) {
+                const int rb = r0 + bb * kKBlk;
+                if (rb < p.rows && p.m_indices[rb] == e) live_blk |= 1 << bb;
+            }
+            live_blk = __builtin_amdgcn_readfirstlane(live_blk);
+        }
+
         // K blocks [kb_lo, kb_lo + nkb) of this work unit (all of K unless split)
         const int kb_lo = (int)(((int64_t)split * KB) / p.splits);
         const int nkb = (int)(((int64_t)(split + 1) * KB) / p.splits) - kb_lo;
@@ -356,8 +371,9 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 // Masked groups: A rows at or past masked_m are never stored,
                 // so their copy shrinks to a 256-byte placeholder (every wave
                 // keeps the same number of copies per stage, which the waits
-                // count on).
-                if (FORM == kMasked && u < Cfg::A_DMA && r0 + 8 * u >= store_rows)
+                // count on); so do the A rows of a contiguous pass's other block.
+                if ((FORM == kMasked && u < Cfg::A_DMA && r0 + 8 * u >= store_rows) ||
+                    (FORM == kContiguous && u < Cfg::A_DMA && !((live_blk >> ((8 * u) / kKBlk)) & 1)))
                     dma4(src, 0, lds0 + Cfg::STAGES * Cfg::STAGE_BYTES + wave * 256);
                 else if (u >= Cfg::A_DMA && p.b_nt)
                     dma16_nt(src, goff[q], dst + u * 1024);
@@ -396,13 +412,12 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
         // Whether this wave's tile rows (WTM rows from r0 + wm * WTM) hold any
         // row the pass stores: masked groups store rows below masked_m;
         // contiguous passes store the rows of expert e, and a wave's rows are
-        // one 128-row block, which belongs to a single expert (or is padding);
-        // dense tiles store rows below M.
+        // one 128-row block (live_blk); dense tiles store rows below M.
         bool wave_live = true;
         {
             const int rw = r0 + wm * Cfg::WTM;
             if (FORM == kMasked) wave_live = rw < store_rows;
-            else if (FORM == kContiguous) wave_live = rw < p.rows && p.m_indices[rw] == e;
+            else if (FORM == kContiguous) wave_live = (live_blk >> wm) & 1;
             else wave_live = rw < p.rows;
             wave_live = __builtin_amdgcn_readfirstlane((int)wave_live) != 0;
         }
