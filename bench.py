@@ -450,11 +450,13 @@ DENSE_FAMILIES = [
     dict(file="{dominant}__dense_sweep.md", dominant=True,
          title="Dominant instance of the dense FP8 NT sweep (the five M = 4096 shapes)",
          note="`nt_fp8_kernel<Cfg, FORM, OUT_F32, UE8M0>`, FORM 0 = dense."),
-    dict(file="nt_dense_decode__64x64_128x64_m64_m128_shapes.md",
+    dict(file="nt_dense_decode__m64_m128_shapes.md",
          title="Decode-size dense instances (the ten M = 64 / 128 shapes of the sweep)",
-         match=lambda k: _nt(0, tile="64, 64")(k) or _nt(0, tile="128, 64")(k),
-         note="`NtCfg<64, 64, ...>` runs the M = 64 shapes, `NtCfg<128, 64, ...>` the M = 128 "
-              "shapes; K is split over workgroups (caller-owned workspace)."),
+         match=lambda k: (_nt(0, tile="64, 64")(k) or _nt(0, tile="64, 256")(k)
+                          or _nt(0, tile="128, 64")(k)),
+         note="`NtCfg<64, 256, ...>` runs 64x7168x16384 (N * K >= 64 Mi), `NtCfg<64, 64, ...>` "
+              "the other M = 64 shapes, `NtCfg<128, 64, ...>` the M = 128 shapes; K is split "
+              "over workgroups (caller-owned workspace)."),
 ]
 DETAIL_FAMILIES = [
     dict(file="grouped_moe__contiguous_masked_kgrouped.md",
