@@ -453,10 +453,10 @@ DENSE_FAMILIES = [
     dict(file="nt_dense_decode__m64_m128_shapes.md",
          title="Decode-size dense instances (the ten M = 64 / 128 shapes of the sweep)",
          match=lambda k: (_nt(0, tile="64, 64")(k) or _nt(0, tile="64, 256")(k)
-                          or _nt(0, tile="128, 64")(k)),
-         note="`NtCfg<64, 256, ...>` runs 64x7168x16384 (N * K >= 64 Mi), `NtCfg<64, 64, ...>` "
-              "the other M = 64 shapes, `NtCfg<128, 64, ...>` the M = 128 shapes; K is split "
-              "over workgroups (caller-owned workspace)."),
+                          or _nt(0, tile="128, 64")(k) or _nt(0, tile="128, 256")(k)),
+         note="`NtCfg<64, 256, ...>` and `NtCfg<128, 256, ...>` run M x 7168 x 16384 (N * K >= "
+              "64 Mi), `NtCfg<64, 64, ...>` and `NtCfg<128, 64, ...>` the other M = 64 and M = 128 "
+              "shapes; K is split over workgroups (caller-owned workspace)."),
 ]
 DETAIL_FAMILIES = [
     dict(file="grouped_moe__contiguous_masked_kgrouped.md",

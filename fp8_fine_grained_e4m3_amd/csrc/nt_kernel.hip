@@ -1001,6 +1001,7 @@ using Cfg128x128 = NtCfg<128, 128, 2, 2, 2>;
 using Cfg128x64 = NtCfg<128, 64, 2, 2, 3>;
 using Cfg64x64 = NtCfg<64, 64, 1, 4, 3>;
 using Cfg64x256 = NtCfg<64, 256, 1, 8, 3>;
+using Cfg128x256 = NtCfg<128, 256, 2, 4, 3>;
 
 
 // Tile choice: 256 x 256 (8 waves of 128 x 64) for large dense problems and
@@ -1008,16 +1009,17 @@ using Cfg64x256 = NtCfg<64, 256, 1, 8, 3>;
 // two 128-row blocks), 128 x 128 for mid-size rows, and for decode-size rows (HBM-bound:
 // every B byte is used once) narrow 64-column tiles with deeper pipelines, so
 // more workgroups stream B with more bytes in flight each.
-enum NtTile { kT64x64, kT128x64, kT128x128, kT256x256, kT64x256 };
+enum NtTile { kT64x64, kT128x64, kT128x128, kT256x256, kT64x256, kT128x256 };
 
 NtTile choose_tile(const NtProblem& pr) {
     if (pr.form == kContiguous) return kT256x256;
     // Decode-size rows with a large B (N * K >= 64 Mi): 256-column tiles, one
     // workgroup of 8 waves per CU, stream B with a quarter of the A re-reads
     // per B byte of 64-column tiles; smaller B keeps the 64-column tiles,
-    // whose fixed costs are lower.
+    // whose fixed costs are lower.  The same holds for up to 128 rows.
     if (pr.form == kDense && pr.rows <= 64 && pr.N * pr.K >= (int64_t(64) << 20)) return kT64x256;
     if (pr.form == kDense && pr.rows <= 64) return kT64x64;
+    if (pr.form == kDense && pr.rows <= 128 && pr.N * pr.K >= (int64_t(64) << 20)) return kT128x256;
     if (pr.form == kDense && pr.rows <= 128) return kT128x64;
     if (pr.rows <= 64) return kT64x64;
     // Masked groups of more than 128 rows: 256 x 256 tiles, so each A row
@@ -1041,6 +1043,7 @@ SplitPlan dense_split_plan(int64_t M, int64_t N, int64_t K) {
     case kT128x64: return split_plan<Cfg128x64>(M, N, K);
     case kT256x256: return split_plan<Cfg256x256>(M, N, K);
     case kT64x256: return split_plan<Cfg64x256>(M, N, K);
+    case kT128x256: return split_plan<Cfg128x256>(M, N, K);
     default: return split_plan<Cfg128x128>(M, N, K);
     }
 }
@@ -1058,6 +1061,11 @@ hipError_t dispatch_tiles(const NtProblem& pr, int cu_cap, hipStream_t stream) {
         else
             return hipErrorInvalidValue;   // chosen for dense problems only
     case kT256x256: return launch_cfg<Cfg256x256, FORM, OUT_F32, UE8M0>(pr, cu_cap, stream);
+    case kT128x256:
+        if constexpr (FORM == kDense)
+            return launch_cfg<Cfg128x256, FORM, OUT_F32, UE8M0>(pr, cu_cap, stream);
+        else
+            return hipErrorInvalidValue;
     case kT64x256:
         if constexpr (FORM == kDense)
             return launch_cfg<Cfg64x256, FORM, OUT_F32, UE8M0>(pr, cu_cap, stream);
@@ -1134,7 +1142,7 @@ hipError_t launch_nt(const NtProblem& pr, int cu_cap, hipStream_t stream) {
 }
 
 const char* nt_config_name(const NtProblem& pr) {
-    static const char* tiles[] = {"64x64", "128x64", "128x128", "256x256", "64x256"};
+    static const char* tiles[] = {"64x64", "128x64", "128x128", "256x256", "64x256", "128x256"};
     static const char* forms[] = {"dense", "contiguous", "masked"};
     static thread_local char buf[64];
     snprintf(buf, sizeof buf, "nt_%s_%s%s_%s", forms[(int)pr.form],

@@ -85,11 +85,13 @@ def test_dense_with_c_and_in_place(out):
 
 @pytest.mark.parametrize("M,N,K,out", [(64, 256, 4096, "bf16"), (96, 1024, 4096, "f32"),
                                        (200, 384, 2048, "f32"), (1024, 1024, 8192, "bf16"),
-                                       (64, 4096, 16384, "f32"), (37, 4160, 16384, "bf16")])
+                                       (64, 4096, 16384, "f32"), (37, 4160, 16384, "bf16"),
+                                       (96, 4160, 16384, "f32")])
 def test_dense_split_k_with_c_in_place_and_reproducible(M, N, K, out):
     """Shapes with far fewer output tiles than workgroup slots run with K split
     over several workgroups (64x64, 128x64, 128x128 and, for decode-size rows
-    with N * K >= 64 Mi, 64x256 tiles here, the last with a ragged N).  With C,
+    with N * K >= 64 Mi, 64x256 and 128x256 tiles here, the last two with a
+    ragged N).  With C,
     in place, both output types: parity with the oracle, bitwise identical
     across runs (the partial sums are added in a fixed order), in place equal
     to out of place, and unchanged under a CU cap."""

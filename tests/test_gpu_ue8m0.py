@@ -9,7 +9,7 @@ oracle.gemm_nt_ue8m0 / oracle.pack_ue8m0 (fp64, exact block sums).
 * The packer, bit-exact against the oracle's packer (both layouts, batches,
   ragged row counts, partial last words).
 * Dense GEMM: tolerance parity on every tile configuration (64x64, 64x256, 128x64,
-  128x128, 256x256) and on split-K shapes, ragged M / N, fp32 out with C and
+  128x256, 128x128, 256x256) and on split-K shapes, ragged M / N, fp32 out with C and
   in place, and bit-exact results where the arithmetic is exact (all-ones
   operands with per-row, per-K-block exponents; one-hot B).
 * B exponents that differ row by row inside a 128-row block (the packed
@@ -103,6 +103,7 @@ def test_dense_ue8m0_128x256x512_full():
     (64, 2112, 7168),      # 64x64 tiles, split along K
     (64, 4224, 16384),     # 64x256 tiles (N * K >= 64 Mi), split along K, ragged N
     (128, 4096, 7168),     # 128x64 tiles, split along K
+    (100, 4224, 16384),    # 128x256 tiles (N * K >= 64 Mi), split along K, ragged M and N
     (640, 1024, 2048),     # 128x128 tiles
     (4096, 2048, 1024),    # 256x256 tiles
 ])
