@@ -612,7 +612,7 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 if constexpr (LIVE) {
                     if constexpr (UE8M0) load_exps(smem, kb_lo, ea, eb);
                     else load_scales(smem, sa, sb);
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < SN; ++j) bfr[j] = bfrag_at(smem, j);
                     af[0] = afrag_at(smem, 0);
                     af[1] = afrag_at(smem, 1);
@@ -651,10 +651,10 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                     const uint8_t* st = smem + stage * Cfg::STAGE_BYTES;
                     const int next = stage + 1 == Cfg::STAGES ? 0 : stage + 1;
                     const uint8_t* st_next = smem + next * Cfg::STAGE_BYTES;
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i + 2 < SM; ++i) {
                         const float s_row = (UE8M0 || !LIVE) ? 0.f : sa[i] * sb;
-    #pragma unroll
+#pragma unroll
                         for (int j = 0; j < SN; ++j) {
                             step(i, j, s_row);
                             if (LIVE && j == 0) af[(i + 2) & 3] = afrag_at(st, i + 2);
@@ -691,10 +691,10 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                         if constexpr (UE8M0) load_exps(st_next, kb_lo + it + 1, ea_n, eb_n);
                         else load_scales(st_next, sa_n, sb_n);
                     }
-    #pragma unroll
+#pragma unroll
                     for (int i = SM - 2; i < SM; ++i) {
                         const float s_row = (UE8M0 || !LIVE) ? 0.f : sa[i] * sb;
-    #pragma unroll
+#pragma unroll
                         for (int j = 0; j < SN; ++j) {
                             step(i, j, s_row);
                             if (LIVE && j == 0) af[(i + 2) & 3] = afrag_at(st_next, i + 2 - SM);
@@ -704,12 +704,12 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                     }
                     if constexpr (!LIVE) {
                     } else if constexpr (UE8M0) {
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < SM; ++i) ea[i] = ea_n[i];
-    #pragma unroll
+#pragma unroll
                         for (int j = 0; j < SN; ++j) eb[j] = eb_n[j];
                     } else {
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < SM; ++i) sa[i] = sa_n[i];
                         sb = sb_n;
                     }
