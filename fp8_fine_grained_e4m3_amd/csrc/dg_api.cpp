@@ -259,7 +259,9 @@ dg_status gemm_nt_masked(const uint8_t* a, const void* sfa_, const uint8_t* b, c
     REQUIRE_PTR(masked_m, 16);
     REQUIRE(M_max <= kOffsetLimit / (K > 0 ? K : 1) && N <= kOffsetLimit / (K > 0 ? K : 1),
             "M_max*K and N*K must stay below 2^31");
-    // bound for the smallest tile (64 x 64) any configuration uses
+    // bound for the smallest tile (64 x 64) any configuration uses (G first, so
+    // the product below cannot overflow)
+    REQUIRE(G <= INT_MAX, "G too large");
     REQUIRE(G * ((M_max + 63) / 64) * ((N + 63) / 64) <= INT_MAX, "too many tiles");
     dg::NtProblem p{};
     p.form = dg::kMasked;

@@ -109,6 +109,11 @@ def test_masked_rejects(lib):
     assert "masked_m is NULL" in err(lib)
     assert f(P16, P16, P16b, P16, P16, P16c, 4, 256, 250, 512, None) == dg.DG_ERR_INVALID_ARG
     assert f(P16, P16, P16b, P16, P16, P16c, 0, 256, 256, 512, None) == dg.DG_OK
+    # a group count whose tile count would overflow is rejected before any product
+    assert f(P16, P16, P16b, P16, P16, P16c, 2**40, 256, 256, 512, None) == dg.DG_ERR_INVALID_ARG
+    assert "G too large" in err(lib)
+    assert f(P16, P16, P16b, P16, P16, P16c, 2**20, 2**14, 2**14, 128, None) == dg.DG_ERR_INVALID_ARG
+    assert "too many tiles" in err(lib)
 
 
 def test_k_grouped_rejects(lib):
