@@ -163,12 +163,17 @@ def main():
         dg.fp8_gemm_nt(*op["args"], workspace=ws)
 
     def step(events=None, only=None):
+        # with `only`, one event pair spans each run of consecutive launches
+        # of that instance (its start before the run's first launch, its end
+        # after the last); otherwise one pair per launch
         for i, op in enumerate(ops):
-            rec = events is not None and (only is None or op["kernel"] == only)
-            if rec:
+            mine = events is not None and (only is None or op["kernel"] == only)
+            first = mine and (only is None or i == 0 or ops[i - 1]["kernel"] != only)
+            last = mine and (only is None or i + 1 == len(ops) or ops[i + 1]["kernel"] != only)
+            if first:
                 events[i][0].record(stream)
             launch(op)
-            if rec:
+            if last:
                 events[i][1].record(stream)
 
     def new_events(n):
@@ -195,8 +200,15 @@ def main():
     idx = groups[dom_name]
 
     # ---- timed region: exactly K steps ---------------------------------------------
-    # Event pairs only around the dominant instance's launches (an event pair
-    # around every launch adds several microseconds per launch to the step).
+    # Event pairs only around the dominant instance's launches, one pair per
+    # run of consecutive launches of it (an event pair around every launch
+    # adds several microseconds per launch to the step and to the launch).
+    runs = []
+    for i in idx:
+        if runs and runs[-1][-1] == i - 1:
+            runs[-1].append(i)
+        else:
+            runs.append([i])
     ev = new_events(args.steps)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -204,8 +216,9 @@ def main():
         step(ev[s_], only=dom_name)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    dom_ms = np.array([[ev[s_][i][0].elapsed_time(ev[s_][i][1]) for i in idx]
-                       for s_ in range(args.steps)])
+    # per step: the runs' spans in ms, and their launch counts
+    dom_span = np.array([[ev[s_][r[0]][0].elapsed_time(ev[s_][r[-1]][1]) for r in runs]
+                         for s_ in range(args.steps)])
     flop_step = sum(op["flop"] for op in ops)
     value = flop_step * args.steps / elapsed / 1e12
     ms_per_step = elapsed * 1e3 / args.steps
@@ -213,7 +226,7 @@ def main():
     # Per-launch figures of the dominant instance: averages over its launches
     # in the timed region -- the same average a kernel-trace profile reports
     # for that kernel name.
-    launch_ms = float(dom_ms.mean())
+    launch_ms = float(dom_span.sum() / (args.steps * len(idx)))
     launch_flop = float(np.mean([ops[i]["flop"] for i in idx]))
     launch_bytes = float(np.mean([ops[i]["bytes"] for i in idx]))
     intensity = launch_flop / launch_bytes
