@@ -59,6 +59,7 @@
 #include "dg_internal.h"
 #include "tile_common.h"
 
+#include <limits.h>
 #include <stdio.h>
 #include <algorithm>
 #include <numeric>
@@ -76,6 +77,7 @@ struct TnArgs {
     int M, N, G;
     int K;             // row length of operands stored with K contiguous
     int tiles_m, tiles_n, num_tiles;
+    int xcd_bm, xcd_bn;   // XCD blocks of a group's tiles (0: column order)
     int32_t order[kMaxTnGroups];      // processing order of the groups
     int32_t kb_start[kMaxTnGroups];   // first 128-K block of group g
     int32_t kb_count[kMaxTnGroups];   // number of 128-K blocks of group g
@@ -179,7 +181,20 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         const int g = GROUPED_M ? 0 : p.order[gi];
         int tm = local % p.tiles_m;
         int tn = local / p.tiles_m;
-        if constexpr (GROUPED_M) {
+        if constexpr (!GROUPED_M) {
+            // XCD blocks: workgroups are dealt to the 8 XCDs round-robin and a
+            // group's tiles start at a multiple of 8, so tile `local` runs on
+            // XCD local % 8, which takes one xcd_bm x xcd_bn block of the
+            // group's tiles.  The tiles an XCD has in flight then share
+            // xcd_bm A panels and xcd_bn B panels in its L2 (column order
+            // gives each XCD one A panel but every B panel).
+            if (p.xcd_bm > 0) {
+                const int x = local & 7, j = local >> 3;
+                const int bxm = p.tiles_m / p.xcd_bm;
+                tm = (x % bxm) * p.xcd_bm + j % p.xcd_bm;
+                tn = (x / bxm) * p.xcd_bn + j / p.xcd_bm;
+            }
+        } else {
             // bands of kGroupedBand M tiles, N advancing after each tile
             // of a band: the tiles in flight share a few A blocks (each read
             // once for all N tiles) and the B panels of the band's experts
@@ -483,6 +498,26 @@ namespace {
 
 using TnCfg256 = TnCfg<256, 256, 2, 4, 2>;
 
+// The XCD blocks of a tiles_m x tiles_n group: 8 equal blocks (one per XCD)
+// whose side lengths divide the grid, chosen to need the fewest panels per
+// XCD (xcd_bm + xcd_bn); 0, 0 (column order) when the group's tiles do not
+// split that way or `enable` is false.
+void xcd_blocks(int tiles_m, int tiles_n, bool enable, int* xcd_bm, int* xcd_bn) {
+    *xcd_bm = *xcd_bn = 0;
+    if (!enable || tiles_m <= 0 || tiles_n <= 0 || (int64_t)tiles_m * tiles_n % 8 != 0) return;
+    int best = INT_MAX;
+    for (int bxm = 1; bxm <= 8; bxm *= 2) {
+        const int bxn = 8 / bxm;
+        if (tiles_m % bxm || tiles_n % bxn) continue;
+        const int cost = tiles_m / bxm + tiles_n / bxn;
+        if (cost < best) {
+            best = cost;
+            *xcd_bm = tiles_m / bxm;
+            *xcd_bn = tiles_n / bxn;
+        }
+    }
+}
+
 template <class Cfg, bool A_MK, bool B_NK, bool OUT_F32, bool GROUPED_M, bool UE8M0 = false>
 hipError_t launch_tn_cfg(const TnProblem& pr, int cu_cap, hipStream_t stream) {
     TnArgs a;
@@ -498,6 +533,7 @@ hipError_t launch_tn_cfg(const TnProblem& pr, int cu_cap, hipStream_t stream) {
     const int64_t tiles = groups * a.tiles_m * a.tiles_n;
     if (tiles <= 0) return hipSuccess;
     a.num_tiles = (int)tiles;
+    xcd_blocks(a.tiles_m, a.tiles_n, pr.form != kMGroupedNN, &a.xcd_bm, &a.xcd_bn);
     if (pr.form == kKGrouped) {
         int32_t start = 0, words = 0;
         for (int g = 0; g < a.G; ++g) {

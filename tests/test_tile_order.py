@@ -1,4 +1,4 @@
-"""CPU checks of the NT kernel's tile order (no GPU).
+"""CPU checks of the NT and MN-major kernels' tile orders (no GPU).
 
 The persistent grid walks work units t = blockIdx.x, blockIdx.x + gridDim.x, ...
 and maps each unit to an output tile.  The maps are restated here from the
@@ -84,3 +84,51 @@ def test_dense_order_is_a_bijection(tiles_m, tiles_n, splits):
     num = tiles_m * tiles_n * splits
     got = sorted(dense_tile(t, tiles_m, tiles_n, splits) for t in range(num))
     assert got == [(m, n, s) for m in range(tiles_m) for n in range(tiles_n) for s in range(splits)]
+
+
+def tn_xcd_blocks(tiles_m, tiles_n):
+    """Host side of the MN-major kernel's order: 8 equal blocks whose sides
+    divide the grid, fewest panels (block height + width) first."""
+    best, blk = None, (0, 0)
+    if (tiles_m * tiles_n) % 8:
+        return blk
+    for bxm in (1, 2, 4, 8):
+        bxn = 8 // bxm
+        if tiles_m % bxm or tiles_n % bxn:
+            continue
+        cost = tiles_m // bxm + tiles_n // bxn
+        if best is None or cost < best:
+            best, blk = cost, (tiles_m // bxm, tiles_n // bxn)
+    return blk
+
+
+def tn_tile(local, tiles_m, tiles_n, blk):
+    tm, tn = local % tiles_m, local // tiles_m
+    bm, bn = blk
+    if bm:
+        x, j = local & 7, local >> 3
+        bxm = tiles_m // bm
+        tm, tn = (x % bxm) * bm + j % bm, (x // bxm) * bn + j // bm
+    return tm, tn
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n", [(8, 16), (16, 16), (1, 8), (2, 4), (8, 1), (3, 8), (12, 16),
+                                             (5, 8), (16, 2), (7, 7), (1, 1), (6, 4), (32, 64)])
+def test_tn_order_is_a_bijection(tiles_m, tiles_n):
+    blk = tn_xcd_blocks(tiles_m, tiles_n)
+    got = sorted(tn_tile(l, tiles_m, tiles_n, blk) for l in range(tiles_m * tiles_n))
+    assert got == [(m, n) for m in range(tiles_m) for n in range(tiles_n)]
+
+
+def test_tn_xcd_blocks_are_compact():
+    """K-grouped MoE weight gradient (M = 2048, N = 4096: 8 x 16 tiles per
+    group): each XCD takes a 4 x 4 block of every group, so its tiles share 4 A
+    and 4 B panels instead of 1 A panel and all 16 B panels."""
+    tiles_m, tiles_n = 8, 16
+    blk = tn_xcd_blocks(tiles_m, tiles_n)
+    assert blk == (4, 4)
+    for x in range(8):
+        mine = [tn_tile(l, tiles_m, tiles_n, blk) for l in range(x, tiles_m * tiles_n, 8)]
+        assert len({m for m, _ in mine}) == 4 and len({n for _, n in mine}) == 4
+    assert tn_xcd_blocks(16, 16) == (8, 4)     # 4096 x 4096 dense layouts: 12 panels per XCD
+    assert tn_xcd_blocks(7, 7) == (0, 0)       # 49 tiles do not split into 8 blocks
