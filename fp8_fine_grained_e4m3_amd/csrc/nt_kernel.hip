@@ -291,8 +291,8 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
         const int lane_t = opaque(tid) & 63;
         // Contiguous groups: the expert of every row this wave stores in the
         // epilogue, requested now so its latency hides under the K loop.  With
-        // one row per store instruction, wave w stores tile rows w + 8 j
-        // (j = 0 .. 31 over both phases); lane j holds that row's expert.
+        // two rows per store instruction, wave w stores tile rows w + 8 j
+        // (j = 0 .. 31); lane j holds that row's expert.
         int row_expert = -1;
         if constexpr (FORM == kContiguous && BN == 256) {
             static_assert(Cfg::WAVES == 8 && BM == 256, "row map of the contiguous epilogue");
@@ -803,77 +803,130 @@ __global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2)
                 __hip_atomic_store(p.counters + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 
-        // ---- epilogue: staged through LDS, (+C), convert once, masked store ----------
-        // The fp32 tile goes to LDS (the stages are idle now), then every wave
-        // writes whole rows: lane q of a row owns its 16-byte fp32 chunk q, so
-        // each store instruction covers full contiguous rows of D.  Staging
-        // runs in phases of WMP wave rows when the whole tile does not fit.
-        // Chunk c of staged row r sits at position c ^ ((r / SM) & 15), which
-        // keeps both the writes (a lane's SM rows are SM apart) and the row
-        // reads free of LDS bank conflicts.  D is written once and never read
-        // here, so the stores are nontemporal (they do not displace operand
-        // panels from L2).
-        {
-            // the epilogue's lane offsets derive from a fresh copy of the thread index
+        // ---- epilogue of the grouped 256 x 256 tiles: rounded once, staged in bf16 ----
+        // The grouped forms write bf16 with no C, so every accumulator is
+        // rounded to bf16 before staging: the whole 128 KB tile fits the idle
+        // stages in one phase (the fp32 staging below needs two), and all
+        // eight waves stage at once.  Row r of the staged tile holds 32 16-byte
+        // chunks (8 columns each), chunk c at position c ^ ((r / SM) & 15); a
+        // lane's 8-byte write (4 columns of one row) goes to half
+        // ((lane >> 4) & 1) ^ ((r >> 6) & 1) of its chunk, so rows with bit 6
+        // set hold their chunks' halves swapped (the reads swap them back).
+        // gfx950 serves an 8-byte LDS write in four groups of 16 consecutive
+        // lanes, each conflict-free when its lanes hit 16 distinct 8-byte slots
+        // modulo 128 bytes (measured with the bank-conflict counter): the 16
+        // rows of a group differ in (r / SM) & 7 and in bit 6, which together
+        // give the 16 slots.  The row reads take 32 distinct chunks of one row
+        // per half-wave, conflict-free under the 16-byte read rule.  Each store
+        // instruction then writes two whole rows of D (512 bytes each).  Same
+        // bits as the fp32 route, which rounds the same fp32 values once.
+        if constexpr (FORM != kDense && BM == 256 && BN == 256) {
+            static_assert(!OUT_F32 && Cfg::WAVES == 8 && SM == 8, "grouped forms write bf16 from 8 waves of 128 rows");
             const int lane_e = opaque(tid) & 63;
             const int r16_e = lane_e & 15;
-            constexpr int WMP = Cfg::EPI_WAVE_ROWS;          // wave rows per phase
-            constexpr int PH_ROWS = WMP * Cfg::WTM;           // tile rows per phase
-            constexpr int ROW_CHUNKS = BN / 4;                // 16-byte fp32 chunks per row
-            constexpr int RPI = 64 / ROW_CHUNKS;              // rows per wave instruction
-            float* const stg = reinterpret_cast<float*>(smem);
+            uint8_t* const stg8 = smem;
 #pragma unroll
-            for (int ph = 0; ph < Cfg::WAVES_M / WMP; ++ph) {
-                if (wm / WMP == ph) {
+            for (int i = 0; i < SM; ++i) {
+                const int rl = wm * Cfg::WTM + SM * r16_e + (i ^ (r16_e & 1));
 #pragma unroll
-                    for (int i = 0; i < SM; ++i) {
-                        const int rl = (wm % WMP) * Cfg::WTM + SM * r16_e + (i ^ (r16_e & 1));
-#pragma unroll
-                        for (int j = 0; j < SN; ++j) {
-                            const int ch = (wn * Cfg::WTN + 16 * j) / 4 + (lane_e >> 4);
-                            *reinterpret_cast<f32x4*>(stg + rl * BN + 4 * (ch ^ ((rl / SM) & 15))) =
-                                acc[i][j];
-                        }
-                    }
+                for (int j = 0; j < SN; ++j) {
+                    const int c = (wn * Cfg::WTN + 16 * j) / 8 + (lane_e >> 5);
+                    const int pos = c ^ ((rl / SM) & 15);
+                    const int hx = ((lane_e >> 4) & 1) ^ ((rl >> 6) & 1);
+                    *reinterpret_cast<i32x2*>(stg8 + rl * 512 + 16 * pos + 8 * hx) =
+                        pack_bf16x4(acc[i][j].x, acc[i][j].y, acc[i][j].z, acc[i][j].w);
                 }
-                lds_barrier();
-                constexpr int NR = PH_ROWS / (Cfg::WAVES * RPI);   // row steps per wave
+            }
+            lds_barrier();
+            // wave w stores tile rows w + 8 j, two per instruction (j = 2 k, 2 k + 1)
 #pragma unroll 4
-                for (int k = 0; k < NR; ++k) {
-                    const int rl = wave * RPI + k * Cfg::WAVES * RPI + lane_e / ROW_CHUNKS;
-                    const int ch = lane_e % ROW_CHUNKS;
-                    f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * BN + 4 * (ch ^ ((rl / SM) & 15)));
-                    const int m = r0 + ph * PH_ROWS + rl;   // row within the group
-                    const int n = n0 + 4 * ch;
-                    bool ok = m < store_rows && n < p.N;
-                    if constexpr (FORM == kContiguous && BN == 256) {
-                        // one row per instruction: row step j of this wave
-                        if (ok) ok = __builtin_amdgcn_readlane(
-                                         row_expert, (ph * PH_ROWS + rl - wave) / 8) == e;
-                    } else if (FORM == kContiguous && ok) {
-                        ok = p.m_indices[m] == e;
-                    }
-                    if (!ok) continue;
-                    const int64_t off = (grp_row0 + m) * (int64_t)p.N + n;
-                    if (OUT_F32) {
-                        if (p.c) v += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.c) + off);
-                        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.d) + off));
-                    } else {
-                        if (p.c) {
-                            const i32x2 cv = *reinterpret_cast<const i32x2*>(
-                                reinterpret_cast<const uint16_t*>(p.c) + off);
-                            v.x += bf16_bits_to_f32((uint32_t)cv.x & 0xFFFFu);
-                            v.y += bf16_bits_to_f32((uint32_t)cv.x >> 16);
-                            v.z += bf16_bits_to_f32((uint32_t)cv.y & 0xFFFFu);
-                            v.w += bf16_bits_to_f32((uint32_t)cv.y >> 16);
-                        }
-                        __builtin_nontemporal_store(pack_bf16x4(v.x, v.y, v.z, v.w),
-                            reinterpret_cast<i32x2*>(reinterpret_cast<uint16_t*>(p.d) + off));
-                    }
+            for (int k = 0; k < BM / 16; ++k) {
+                const int half = lane_e >> 5;
+                const int rl = wave + 16 * k + 8 * half;
+                const int c = lane_e & 31;
+                i32x4 v = *reinterpret_cast<const i32x4*>(stg8 + rl * 512 + 16 * (c ^ ((rl / SM) & 15)));
+                if ((rl >> 6) & 1) v = i32x4{v.z, v.w, v.x, v.y};   // halves stored swapped
+                const int m = r0 + rl;   // row within the group
+                const int n = n0 + 8 * c;
+                bool ok = m < store_rows && n < p.N;
+                if constexpr (FORM == kContiguous) {
+                    const int e0 = __builtin_amdgcn_readlane(row_expert, 2 * k);
+                    const int e1 = __builtin_amdgcn_readlane(row_expert, 2 * k + 1);
+                    if (ok) ok = (half ? e1 : e0) == e;
                 }
-                // every wave is done reading the staged rows before they (or the
-                // next tile's copies) are overwritten
-                lds_barrier();
+                if (!ok) continue;
+                const int64_t off = (grp_row0 + m) * (int64_t)p.N + n;
+                __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(reinterpret_cast<uint16_t*>(p.d) + off));
+            }
+            // every wave is done reading the staged rows before the next tile's copies
+            lds_barrier();
+        } else {
+            // ---- epilogue: staged through LDS, (+C), convert once, masked store ----------
+            // The fp32 tile goes to LDS (the stages are idle now), then every wave
+            // writes whole rows: lane q of a row owns its 16-byte fp32 chunk q, so
+            // each store instruction covers full contiguous rows of D.  Staging
+            // runs in phases of WMP wave rows when the whole tile does not fit.
+            // Chunk c of staged row r sits at position c ^ ((r / SM) & 15), which
+            // keeps both the writes (a lane's SM rows are SM apart) and the row
+            // reads free of LDS bank conflicts.  D is written once and never read
+            // here, so the stores are nontemporal (they do not displace operand
+            // panels from L2).
+            {
+                static_assert(FORM != kContiguous, "contiguous tiles take the bf16 staging above");
+                // the epilogue's lane offsets derive from a fresh copy of the thread index
+                const int lane_e = opaque(tid) & 63;
+                const int r16_e = lane_e & 15;
+                constexpr int WMP = Cfg::EPI_WAVE_ROWS;          // wave rows per phase
+                constexpr int PH_ROWS = WMP * Cfg::WTM;           // tile rows per phase
+                constexpr int ROW_CHUNKS = BN / 4;                // 16-byte fp32 chunks per row
+                constexpr int RPI = 64 / ROW_CHUNKS;              // rows per wave instruction
+                float* const stg = reinterpret_cast<float*>(smem);
+#pragma unroll
+                for (int ph = 0; ph < Cfg::WAVES_M / WMP; ++ph) {
+                    if (wm / WMP == ph) {
+#pragma unroll
+                        for (int i = 0; i < SM; ++i) {
+                            const int rl = (wm % WMP) * Cfg::WTM + SM * r16_e + (i ^ (r16_e & 1));
+#pragma unroll
+                            for (int j = 0; j < SN; ++j) {
+                                const int ch = (wn * Cfg::WTN + 16 * j) / 4 + (lane_e >> 4);
+                                *reinterpret_cast<f32x4*>(stg + rl * BN + 4 * (ch ^ ((rl / SM) & 15))) =
+                                    acc[i][j];
+                            }
+                        }
+                    }
+                    lds_barrier();
+                    constexpr int NR = PH_ROWS / (Cfg::WAVES * RPI);   // row steps per wave
+#pragma unroll 4
+                    for (int k = 0; k < NR; ++k) {
+                        const int rl = wave * RPI + k * Cfg::WAVES * RPI + lane_e / ROW_CHUNKS;
+                        const int ch = lane_e % ROW_CHUNKS;
+                        f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * BN + 4 * (ch ^ ((rl / SM) & 15)));
+                        const int m = r0 + ph * PH_ROWS + rl;   // row within the group
+                        const int n = n0 + 4 * ch;
+                        const bool ok = m < store_rows && n < p.N;
+                        if (!ok) continue;
+                        const int64_t off = (grp_row0 + m) * (int64_t)p.N + n;
+                        if (OUT_F32) {
+                            if (p.c) v += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.c) + off);
+                            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.d) + off));
+                        } else {
+                            if (p.c) {
+                                const i32x2 cv = *reinterpret_cast<const i32x2*>(
+                                    reinterpret_cast<const uint16_t*>(p.c) + off);
+                                v.x += bf16_bits_to_f32((uint32_t)cv.x & 0xFFFFu);
+                                v.y += bf16_bits_to_f32((uint32_t)cv.x >> 16);
+                                v.z += bf16_bits_to_f32((uint32_t)cv.y & 0xFFFFu);
+                                v.w += bf16_bits_to_f32((uint32_t)cv.y >> 16);
+                            }
+                            __builtin_nontemporal_store(pack_bf16x4(v.x, v.y, v.z, v.w),
+                                reinterpret_cast<i32x2*>(reinterpret_cast<uint16_t*>(p.d) + off));
+                        }
+                    }
+                    // every wave is done reading the staged rows before they (or the
+                    // next tile's copies) are overwritten
+                    lds_barrier();
+                }
             }
         }
     }

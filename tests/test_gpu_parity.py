@@ -593,6 +593,25 @@ def test_k_grouped_shapes(M, N, ks):
     check_close(d.cpu().numpy().astype(np.float64), ref, f"tn {M}x{N}")
 
 
+def test_k_grouped_xcd_blocks_deterministic_under_cu_cap():
+    """Groups of 2 x 8 tiles take the XCD-block tile order (each XCD a 2 x 1
+    block of every group); capping the grid to 5 workgroups (not a multiple of
+    8, each walking many tiles) must give the same bits, and both match the
+    oracle."""
+    announce("k-grouped xcd blocks + cu cap")
+    ks = np.array([384, 0, 1024, 128], np.int32)
+    x = gen.gen_k_grouped(G=len(ks), M=512, N=2048, K_tot=int(ks.sum()), k_sizes=ks, seed=41)
+    d1 = run_tn(x, c=x.c)
+    dg.set_num_cus(5)
+    try:
+        d2 = run_tn(x, c=x.c)
+    finally:
+        dg.set_num_cus(0)
+    assert torch.equal(d1, d2)
+    ref = oracle.k_grouped_tn(x.a, x.sfa, x.b, x.sfb, x.k_sizes, x.c)
+    check_close(d1.cpu().numpy().astype(np.float64), ref, "tn xcd blocks")
+
+
 def test_k_grouped_one_hot_k_mapping_is_bit_exact():
     """Column m of A and column n of B each hold a single 1.0 at a random K
     index inside the group; D[g][m, n] = 1 exactly where the two indices meet,

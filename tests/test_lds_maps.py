@@ -161,3 +161,69 @@ def test_k_contiguous_staging_of_the_mn_kernel_is_a_bijection_and_conflict_free(
                 grp = 2 * ((l >> 5) & 1) + (((l >> 2) ^ (l >> 3) ^ (l >> 4)) & 1)
                 slots.setdefault(grp, set()).add((byte % 256) // 16)
             assert all(len(v) == 16 for v in slots.values()), (frag, half, slots)
+
+
+def b64_write_conflict_free(addrs):
+    for g in range(4):
+        seen = {}
+        for l in range(16 * g, 16 * g + 16):
+            s = (addrs[l] >> 3) & 15
+            if seen.setdefault(s, addrs[l]) != addrs[l]:
+                return False
+    return True
+
+
+def test_b64_write_rule_matches_the_measured_patterns():
+    """The rule reproduces the counter's verdicts: 16 lanes at an 8-byte
+    stride (or 256 + 8) are conflict-free, at a 16-byte stride (or 256 + 16)
+    they conflict."""
+    for stride, free in [(8, True), (264, True), (520, True), (16, False), (272, False), (32, False)]:
+        addrs = [(l & 15) * stride + 8 * ((l >> 4) & 1) for l in range(64)]
+        assert b64_write_conflict_free(addrs) == free, stride
+
+
+def test_grouped_bf16_staging_round_trip_and_banks():
+    """The grouped forms' 256 x 256 epilogue stages the tile once in bf16: row
+    r holds 32 16-byte chunks, chunk c at position c ^ ((r / 8) & 15).  Lane
+    l of wave (wm, wn) writes MFMA tile (i, j) -- row 128 wm + 8 (l & 15) +
+    (i ^ (l & 1)), columns 64 wn + 16 j + 4 (l >> 4) .. +3 -- as 8 bytes into
+    half ((l >> 4) & 1) ^ ((row >> 6) & 1) of chunk (64 wn + 16 j) / 8 + (l >> 5)
+    (rows with bit 6 set hold their chunks' halves swapped; the reads swap them
+    back).  The writes must tile the 128 KB exactly once and land where the row
+    reads (lane l: chunk l & 31 of row wave + 16 k + 8 (l >> 5)) find them.
+    Bank rules, measured on gfx950 with the bank-conflict counter: the reads by
+    the ds_read_b128 rule above; an 8-byte write is served in four groups of
+    16 consecutive lanes, each conflict-free when its lanes hit 16 distinct
+    8-byte slots modulo 128 bytes (16 lanes at a 16-byte stride conflict
+    2-way, at an 8-byte stride not at all)."""
+    SM, SN, WTM, WTN, ROW = 8, 4, 128, 64, 512
+    pos = lambda r, c: c ^ ((r // SM) & 15)
+    stg = {}
+    for wm in range(2):
+        for wn in range(4):
+            for i in range(SM):
+                for j in range(SN):
+                    addrs = []
+                    for l in range(64):
+                        r16 = l & 15
+                        row = wm * WTM + SM * r16 + (i ^ (r16 & 1))
+                        c = (wn * WTN + 16 * j) // 8 + (l >> 5)
+                        a = row * ROW + 16 * pos(row, c) + 8 * (((l >> 4) & 1) ^ ((row >> 6) & 1))
+                        addrs.append(a)
+                        assert a not in stg
+                        stg[a] = (row, wn * WTN + 16 * j + 4 * (l >> 4))   # first of 4 columns
+                    assert b64_write_conflict_free(addrs), (wm, wn, i, j)
+    assert len(stg) == 256 * ROW // 8
+    for wave in range(8):
+        for k in range(16):
+            addrs = []
+            for l in range(64):
+                row, c = wave + 16 * k + 8 * (l >> 5), l & 31
+                a = row * ROW + 16 * pos(row, c)
+                addrs.append(a)
+                lo, hi = (a + 8, a) if (row >> 6) & 1 else (a, a + 8)   # halves swapped back
+                assert stg[lo] == (row, 8 * c) and stg[hi] == (row, 8 * c + 4)
+            assert b128_conflict_free(addrs), (wave, k)
+        # wave w stores rows w + 8 j, j = 0 .. 31, two per instruction
+        assert sorted(wave + 16 * k + 8 * h for k in range(16) for h in range(2)) == \
+            [wave + 8 * j for j in range(32)]
