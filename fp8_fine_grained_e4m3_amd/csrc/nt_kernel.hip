@@ -20,8 +20,9 @@
 //     LDS by direct global -> LDS copies (a ring of STAGES stages: the copies
 //     of the next blocks are in flight while block kb is multiplied), rows of
 //     128 bytes with an XOR-swizzled 16-byte chunk order.
-//   * The epilogue stages the fp32 tile through the idle stages and writes D
-//     (+ C, one rounding) in whole-row stores.
+//   * The epilogue stages the tile through the idle stages and writes D in
+//     whole-row stores: dense tiles in fp32 (+ C, then one rounding), the
+//     grouped forms' 256 x 256 tiles (bf16, no C) already rounded to bf16.
 //   * Each wave owns a WTM x WTN sub-tile made of 16 x 16 MFMA tiles.  The MFMA
 //     takes the B fragment as its row operand and the A fragment as its column
 //     operand, so every lane's four results share one m (one A scale) and
