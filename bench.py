@@ -56,14 +56,17 @@ MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MO
                  "SQ_INSTS_VALU_MFMA_MOPS_F6F4")
 
 
+PROF_OUT = "rocprof_out"   # where the profiling runs write (not versioned)
+
+
 def _profile_commands(tag, trace_args, pmc_args, summarize):
-    pre = "rocprofv3 {} --output-format csv -d gpurun_out/prof_{}_{} -o run -- python3 bench.py "
+    pre = "rocprofv3 {} --output-format csv -d " + PROF_OUT + "/prof_{}_{} -o run -- python3 bench.py "
     return [pre.format("--kernel-trace --stats", tag, "trace") + trace_args
-            + f" --json-out gpurun_out/bench_{tag}.json",
+            + f" --json-out {PROF_OUT}/bench_{tag}.json",
             pre.format("--pmc FETCH_SIZE", tag, "fetch") + pmc_args + " --copy-calibration",
             pre.format("--pmc WRITE_SIZE", tag, "write") + pmc_args + " --copy-calibration",
             pre.format("--pmc " + MFMA_COUNTERS, tag, "mfma") + pmc_args,
-            f"python3 bench.py {summarize} gpurun_out/prof_{tag} gpurun_out/bench_{tag}.json profiles"]
+            f"python3 bench.py {summarize} {PROF_OUT}/prof_{tag} {PROF_OUT}/bench_{tag}.json profiles"]
 
 
 # dense sweep: the roofline's dominant instance and the decode-size instances
