@@ -223,6 +223,14 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         const uint8_t* __restrict__ b_e = p.b + (int64_t)e * p.K * p.N;
         const float* __restrict__ sfb_e = p.sfb + (int64_t)e * (p.K / kKBlk) * p.N;
         const int lane_t = opaque(tid) & 63;   // this tile's prologue derives its offsets from it
+        // M-grouped: the expert of every row this wave stores in the epilogue
+        // (rows wave + 8 j, j = 0 .. 31; lane j holds row j's), requested now so
+        // its latency hides under the K loop
+        int row_expert = -1;
+        if constexpr (GROUPED_M) {
+            const int row = m0 + wave + 8 * (lane_t & 31);
+            if (row < p.M) row_expert = p.m_indices[row];
+        }
 
         // Copy offsets.  Copy u of A moves 1024 / BM K rows: lane l fills LDS
         // chunk position l % (BM / 16) of row u * (1024 / BM) + l / (BM / 16),
@@ -444,52 +452,97 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         // every wave is past its last LDS read before the next tile's copies
         lds_barrier();
 
-        // Epilogue: D[g] = acc (C already included), fp32, inside [M, N],
-        // staged through LDS one wave row (WTM tile rows) at a time so that
-        // each store instruction writes one whole row (lane q: 16-byte chunk
-        // q).  Chunk c of staged row r sits at position c ^ (r & 15): the 16
-        // lanes that write one chunk column hold 16 consecutive rows, so both
-        // the writes and the row reads hit 16 distinct 16-byte bank slots.
-        // D is written once and never read here: nontemporal stores.
-        float* const stg = reinterpret_cast<float*>(smem);
-        constexpr int ROW_CHUNKS = BN / 4;
-        static_assert(ROW_CHUNKS == 64, "one row per store instruction");
-        const int lane_e = opaque(tid) & 63;   // the epilogue's offsets derive from it
-        const int r16_e = lane_e & 15;
-        static_assert(Cfg::WTM * BN * 4 <= Cfg::STAGES * Cfg::STAGE_BYTES, "a wave row of the tile fits in LDS");
+        if constexpr (GROUPED_M) {
+            // M-grouped NN (bf16, no C): every accumulator is rounded to bf16
+            // before staging (the same single rounding as below, so the same
+            // bits), and the whole 128 KB tile goes through LDS in one phase.
+            // Row r holds 32 16-byte chunks, chunk c at position c ^ (r & 15);
+            // a lane's 8-byte write (4 columns of one row) goes to half
+            // ((lane >> 4) & 1) ^ ((r >> 3) & 1) of its chunk and the reads swap
+            // the halves back.  An 8-byte LDS write is served in groups of 16
+            // consecutive lanes that must hit 16 distinct 8-byte slots modulo
+            // 128 bytes; a group's 16 consecutive rows differ in r & 7 and in
+            // bit 3, which gives the 16 slots.  The row reads take 32 distinct
+            // chunks of one row per half-wave.  Each store writes two rows.
+            static_assert(!OUT_F32 && BM == 256 && BN == 256 && Cfg::WAVES == 8,
+                          "grouped NN writes bf16 256 x 256 tiles from 8 waves");
+            uint8_t* const stg8 = smem;
+            const int lane_e = opaque(tid) & 63;
+            const int r16_e = lane_e & 15;
 #pragma unroll
-        for (int ph = 0; ph < Cfg::WAVES_M; ++ph) {
-            if (wm == ph) {
+            for (int i = 0; i < SM; ++i) {
+                const int rl = wm * Cfg::WTM + 16 * i + r16_e;
 #pragma unroll
-                for (int i = 0; i < SM; ++i) {
-                    const int rl = 16 * i + r16_e;
-#pragma unroll
-                    for (int j = 0; j < SN; ++j) {
-                        const int ch = (wn * Cfg::WTN + 16 * j) / 4 + (lane_e >> 4);
-                        *reinterpret_cast<f32x4*>(stg + rl * BN + 4 * (ch ^ (rl & 15))) = acc[i][j];
-                    }
+                for (int j = 0; j < SN; ++j) {
+                    const int c = (wn * Cfg::WTN + 16 * j) / 8 + (lane_e >> 5);
+                    const int hx = ((lane_e >> 4) & 1) ^ ((rl >> 3) & 1);
+                    *reinterpret_cast<i32x2*>(stg8 + rl * 512 + 16 * (c ^ (rl & 15)) + 8 * hx) =
+                        pack_bf16x4(acc[i][j].x, acc[i][j].y, acc[i][j].z, acc[i][j].w);
                 }
             }
             lds_barrier();
 #pragma unroll 4
-            for (int rl = wave; rl < Cfg::WTM; rl += Cfg::WAVES) {
-                const int m = m0 + ph * Cfg::WTM + rl;
-                const int n = n0 + 4 * lane_e;
-                if (m >= p.M || n >= p.N) continue;
-                if constexpr (GROUPED_M) {
-                    if (p.m_indices[m] != e) continue;   // padding row of the segment
-                }
-                const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * BN + 4 * (lane_e ^ (rl & 15)));
+            for (int k = 0; k < BM / 16; ++k) {
+                const int half = lane_e >> 5;
+                const int rl = wave + 16 * k + 8 * half;
+                const int c = lane_e & 31;
+                i32x4 v = *reinterpret_cast<const i32x4*>(stg8 + rl * 512 + 16 * (c ^ (rl & 15)));
+                if ((rl >> 3) & 1) v = i32x4{v.z, v.w, v.x, v.y};   // halves stored swapped
+                const int m = m0 + rl;
+                const int n = n0 + 8 * c;
+                const int e0 = __builtin_amdgcn_readlane(row_expert, 2 * k);
+                const int e1 = __builtin_amdgcn_readlane(row_expert, 2 * k + 1);
+                if (m >= p.M || n >= p.N || (half ? e1 : e0) != e) continue;   // padding rows
                 const int64_t off = gbase + (int64_t)m * p.N + n;
-                if constexpr (OUT_F32)
-                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(p.d) + off));
-                else
-                    __builtin_nontemporal_store(pack_bf16x4(v.x, v.y, v.z, v.w),
-                                                reinterpret_cast<i32x2*>(static_cast<uint16_t*>(p.d) + off));
+                __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(static_cast<uint16_t*>(p.d) + off));
             }
-            // every wave is done reading the staged rows before they (or the
-            // next tile's copies) are overwritten
+            // every wave is done reading the staged rows before the next tile's copies
             lds_barrier();
+        } else {
+            // Epilogue: D[g] = acc (C already included), fp32, inside [M, N],
+            // staged through LDS one wave row (WTM tile rows) at a time so that
+            // each store instruction writes one whole row (lane q: 16-byte chunk
+            // q).  Chunk c of staged row r sits at position c ^ (r & 15): the 16
+            // lanes that write one chunk column hold 16 consecutive rows, so both
+            // the writes and the row reads hit 16 distinct 16-byte bank slots.
+            // D is written once and never read here: nontemporal stores.
+            float* const stg = reinterpret_cast<float*>(smem);
+            constexpr int ROW_CHUNKS = BN / 4;
+            static_assert(ROW_CHUNKS == 64, "one row per store instruction");
+            const int lane_e = opaque(tid) & 63;   // the epilogue's offsets derive from it
+            const int r16_e = lane_e & 15;
+            static_assert(Cfg::WTM * BN * 4 <= Cfg::STAGES * Cfg::STAGE_BYTES, "a wave row of the tile fits in LDS");
+#pragma unroll
+            for (int ph = 0; ph < Cfg::WAVES_M; ++ph) {
+                if (wm == ph) {
+#pragma unroll
+                    for (int i = 0; i < SM; ++i) {
+                        const int rl = 16 * i + r16_e;
+#pragma unroll
+                        for (int j = 0; j < SN; ++j) {
+                            const int ch = (wn * Cfg::WTN + 16 * j) / 4 + (lane_e >> 4);
+                            *reinterpret_cast<f32x4*>(stg + rl * BN + 4 * (ch ^ (rl & 15))) = acc[i][j];
+                        }
+                    }
+                }
+                lds_barrier();
+#pragma unroll 4
+                for (int rl = wave; rl < Cfg::WTM; rl += Cfg::WAVES) {
+                    const int m = m0 + ph * Cfg::WTM + rl;
+                    const int n = n0 + 4 * lane_e;
+                    if (m >= p.M || n >= p.N) continue;
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * BN + 4 * (lane_e ^ (rl & 15)));
+                    const int64_t off = gbase + (int64_t)m * p.N + n;
+                    if constexpr (OUT_F32)
+                        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(p.d) + off));
+                    else
+                        __builtin_nontemporal_store(pack_bf16x4(v.x, v.y, v.z, v.w),
+                                                    reinterpret_cast<i32x2*>(static_cast<uint16_t*>(p.d) + off));
+                }
+                // every wave is done reading the staged rows before they (or the
+                // next tile's copies) are overwritten
+                lds_barrier();
+            }
         }
     }
 }

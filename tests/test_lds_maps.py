@@ -11,6 +11,7 @@ address).  The transposing ds_read_b64_tr_b8 is served in two groups of 32
 consecutive lanes, each needing distinct 8-byte slots modulo 256 bytes.
 """
 import numpy as np
+import pytest
 
 
 def sigma(c):
@@ -182,22 +183,30 @@ def test_b64_write_rule_matches_the_measured_patterns():
         assert b64_write_conflict_free(addrs) == free, stride
 
 
-def test_grouped_bf16_staging_round_trip_and_banks():
-    """The grouped forms' 256 x 256 epilogue stages the tile once in bf16: row
-    r holds 32 16-byte chunks, chunk c at position c ^ ((r / 8) & 15).  Lane
-    l of wave (wm, wn) writes MFMA tile (i, j) -- row 128 wm + 8 (l & 15) +
-    (i ^ (l & 1)), columns 64 wn + 16 j + 4 (l >> 4) .. +3 -- as 8 bytes into
-    half ((l >> 4) & 1) ^ ((row >> 6) & 1) of chunk (64 wn + 16 j) / 8 + (l >> 5)
-    (rows with bit 6 set hold their chunks' halves swapped; the reads swap them
-    back).  The writes must tile the 128 KB exactly once and land where the row
-    reads (lane l: chunk l & 31 of row wave + 16 k + 8 (l >> 5)) find them.
-    Bank rules, measured on gfx950 with the bank-conflict counter: the reads by
-    the ds_read_b128 rule above; an 8-byte write is served in four groups of
-    16 consecutive lanes, each conflict-free when its lanes hit 16 distinct
-    8-byte slots modulo 128 bytes (16 lanes at a 16-byte stride conflict
-    2-way, at an 8-byte stride not at all)."""
+@pytest.mark.parametrize("kind", ["nt", "tn"])
+def test_grouped_bf16_staging_round_trip_and_banks(kind):
+    """The grouped 256 x 256 epilogues (NT contiguous / masked, MN-major
+    grouped NN) stage the tile once in bf16: row r holds 32 16-byte chunks,
+    chunk c at position c ^ f(r), and a lane's 8-byte write (4 columns of one
+    row) goes to half ((l >> 4) & 1) ^ g(r) of chunk (64 wn + 16 j) / 8 +
+    (l >> 5); rows with g(r) = 1 hold their chunks' halves swapped and the
+    reads swap them back.  NT: lane rows 128 wm + 8 (l & 15) + (i ^ (l & 1)),
+    f(r) = (r / 8) & 15, g(r) = bit 6 of r.  MN-major: rows 128 wm + 16 i +
+    (l & 15), f(r) = r & 15, g(r) = bit 3 of r.  The writes must tile the 128 KB
+    exactly once and land where the row reads (lane l: chunk l & 31 of row
+    wave + 16 k + 8 (l >> 5)) find them.  Bank rules, measured on gfx950 with
+    the bank-conflict counter: the reads by the ds_read_b128 rule above; an
+    8-byte write is served in four groups of 16 consecutive lanes, each
+    conflict-free when its lanes hit 16 distinct 8-byte slots modulo 128 bytes
+    (16 lanes at a 16-byte stride conflict 2-way, at an 8-byte stride not at
+    all)."""
     SM, SN, WTM, WTN, ROW = 8, 4, 128, 64, 512
-    pos = lambda r, c: c ^ ((r // SM) & 15)
+    if kind == "nt":
+        lane_row = lambda wm, i, r16: wm * WTM + SM * r16 + (i ^ (r16 & 1))
+        f, g = (lambda r: (r // SM) & 15), (lambda r: (r >> 6) & 1)
+    else:
+        lane_row = lambda wm, i, r16: wm * WTM + 16 * i + r16
+        f, g = (lambda r: r & 15), (lambda r: (r >> 3) & 1)
     stg = {}
     for wm in range(2):
         for wn in range(4):
@@ -205,25 +214,24 @@ def test_grouped_bf16_staging_round_trip_and_banks():
                 for j in range(SN):
                     addrs = []
                     for l in range(64):
-                        r16 = l & 15
-                        row = wm * WTM + SM * r16 + (i ^ (r16 & 1))
+                        row = lane_row(wm, i, l & 15)
                         c = (wn * WTN + 16 * j) // 8 + (l >> 5)
-                        a = row * ROW + 16 * pos(row, c) + 8 * (((l >> 4) & 1) ^ ((row >> 6) & 1))
+                        a = row * ROW + 16 * (c ^ f(row)) + 8 * (((l >> 4) & 1) ^ g(row))
                         addrs.append(a)
                         assert a not in stg
                         stg[a] = (row, wn * WTN + 16 * j + 4 * (l >> 4))   # first of 4 columns
-                    assert b64_write_conflict_free(addrs), (wm, wn, i, j)
+                    assert b64_write_conflict_free(addrs), (kind, wm, wn, i, j)
     assert len(stg) == 256 * ROW // 8
     for wave in range(8):
         for k in range(16):
             addrs = []
             for l in range(64):
                 row, c = wave + 16 * k + 8 * (l >> 5), l & 31
-                a = row * ROW + 16 * pos(row, c)
+                a = row * ROW + 16 * (c ^ f(row))
                 addrs.append(a)
-                lo, hi = (a + 8, a) if (row >> 6) & 1 else (a, a + 8)   # halves swapped back
+                lo, hi = (a + 8, a) if g(row) else (a, a + 8)   # halves swapped back
                 assert stg[lo] == (row, 8 * c) and stg[hi] == (row, 8 * c + 4)
-            assert b128_conflict_free(addrs), (wave, k)
+            assert b128_conflict_free(addrs), (kind, wave, k)
         # wave w stores rows w + 8 j, j = 0 .. 31, two per instruction
         assert sorted(wave + 16 * k + 8 * h for k in range(16) for h in range(2)) == \
             [wave + 8 * j for j in range(32)]
