@@ -452,10 +452,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
         // every wave is past its last LDS read before the next tile's copies
         lds_barrier();
 
-        if constexpr (GROUPED_M) {
-            // M-grouped NN (bf16, no C): every accumulator is rounded to bf16
-            // before staging (the same single rounding as below, so the same
-            // bits), and the whole 128 KB tile goes through LDS in one phase.
+        if (GROUPED_M || (!OUT_F32 && p.c == nullptr)) {
+            // bf16 out without C (M-grouped NN always; the dense layouts when no
+            // C is given): every accumulator is rounded to bf16 before staging
+            // (the same single rounding as below, so the same bits), and the
+            // whole 128 KB tile goes through LDS in one phase.
             // Row r holds 32 16-byte chunks, chunk c at position c ^ (r & 15);
             // a lane's 8-byte write (4 columns of one row) goes to half
             // ((lane >> 4) & 1) ^ ((r >> 3) & 1) of its chunk and the reads swap
@@ -464,8 +465,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
             // 128 bytes; a group's 16 consecutive rows differ in r & 7 and in
             // bit 3, which gives the 16 slots.  The row reads take 32 distinct
             // chunks of one row per half-wave.  Each store writes two rows.
-            static_assert(!OUT_F32 && BM == 256 && BN == 256 && Cfg::WAVES == 8,
-                          "grouped NN writes bf16 256 x 256 tiles from 8 waves");
+            static_assert(BM == 256 && BN == 256 && Cfg::WAVES == 8, "256 x 256 tiles from 8 waves");
             uint8_t* const stg8 = smem;
             const int lane_e = opaque(tid) & 63;
             const int r16_e = lane_e & 15;
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
                 const int n = n0 + 8 * c;
                 const int e0 = __builtin_amdgcn_readlane(row_expert, 2 * k);
                 const int e1 = __builtin_amdgcn_readlane(row_expert, 2 * k + 1);
-                if (m >= p.M || n >= p.N || (half ? e1 : e0) != e) continue;   // padding rows
+                if (m >= p.M || n >= p.N || (GROUPED_M && (half ? e1 : e0) != e)) continue;   // padding rows
                 const int64_t off = gbase + (int64_t)m * p.N + n;
                 __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(static_cast<uint16_t*>(p.d) + off));
             }
