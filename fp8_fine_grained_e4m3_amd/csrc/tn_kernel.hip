@@ -186,8 +186,9 @@ __global__ __launch_bounds__(Cfg::THREADS) void tn_fp8_kernel(TnArgs p) {
             // group's tiles start at a multiple of 8, so tile `local` runs on
             // XCD local % 8, which takes one xcd_bm x xcd_bn block of the
             // group's tiles.  The tiles an XCD has in flight then share
-            // xcd_bm A panels and xcd_bn B panels in its L2 (column order
-            // gives each XCD one A panel but every B panel).
+            // xcd_bm A panels and xcd_bn B panels in its L2 (in column order
+            // a group of 8 M tiles would give each XCD one A panel but every
+            // B panel).
             if (p.xcd_bm > 0) {
                 const int x = local & 7, j = local >> 3;
                 const int bxm = p.tiles_m / p.xcd_bm;
