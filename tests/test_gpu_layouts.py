@@ -56,6 +56,25 @@ def test_layout_parity(layout, M, N, K):
     print(check_close(got, ref, f"{layout} {M}x{N}x{K}"))
 
 
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+def test_layout_xcd_blocks_deterministic_under_cu_cap(layout):
+    """1024 x 2048 gives 4 x 8 = 32 tiles, which take the XCD-block tile order
+    (each XCD a 2 x 2 block); a grid capped to 5 workgroups (not a multiple of
+    8) walks the same tiles in another order and must give the same bits, both
+    with bf16 staging (no C) and with fp32 staging (C given)."""
+    announce(f"layout {layout} xcd blocks + cu cap")
+    x = gen.gen_layout(layout, 1024, 2048, 512, seed=77, with_c=True)
+    c = dev(x.c).to(torch.bfloat16)
+    d1, d1c = run(x), run(x, c=c)
+    dg.set_num_cus(5)
+    try:
+        d2, d2c = run(x), run(x, c=c)
+    finally:
+        dg.set_num_cus(0)
+    assert torch.equal(d1, d2) and torch.equal(d1c, d2c)
+    print(check_close(to64(d1), oracle.gemm_layout(layout, x.a, x.sfa, x.b, x.sfb), f"{layout} xcd"))
+
+
 @pytest.mark.parametrize("M", [1, 65, 300])
 def test_nn_ragged_m(M):
     """NN takes any M (A rows are K-contiguous)."""
